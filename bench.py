@@ -1,0 +1,190 @@
+"""Benchmark of the DiffKV-style compaction + mixed-precision paged decode hot path on one
+MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input resident in HBM:
+release the layer's pages, score_tokens -> compact_pages -> quantize_and_place for the
+full prompt, then the workload's decode steps of paged_decode_attention (fresh queries).
+Default workload: one layer, 16 requests x 32,768 tokens, 64 query / 8 KV heads, Zipf(1.1)
+accumulators, 2^18 pages, 64 decode steps.
+
+Prints one JSON line (rank 0).  `value` = KV token-heads compacted per second over the
+compaction part of the step; `decode_GBps` = algorithmic bytes of paged decode attention
+per second; `roofline` is for the dominant kernel (decode attention main kernel, timed per
+launch with HIP events on the stream it runs on); `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    return ap.parse_args()
+
+
+def decode_algorithmic_bytes(count, B, Hq):
+    """Bytes the decode must read/write: per live HIGH token 128 + 64 code bytes + 8 bytes of
+    scale/zero, per live LOW token 64 + 32 + 8, 4 bytes per page id, q and fp32 output."""
+    nh = count[..., 0].astype(np.int64)
+    nl = count[..., 1].astype(np.int64)
+    pages = -(-nh // 16) + -(-nl // 32)
+    return int((nh * 200 + nl * 104 + pages * 4).sum() + B * Hq * 128 * (2 + 4))
+
+
+def compaction_algorithmic_bytes(count, T, Hkv, Hq):
+    """Read K+V fp16 (512 B) and accumulators (4 B per query head) of every token-head; write
+    200 B per HIGH and 104 B per LOW token-head (codes + scale/zero) + 4 B position, tier byte."""
+    nh = count[..., 0].astype(np.int64).sum()
+    nl = count[..., 1].astype(np.int64).sum()
+    return int(T * Hkv * 512 + T * Hq * 4 + T * Hkv + nh * 204 + nl * 108)
+
+
+def cpu_baseline(w, k, v, acc, qs, nreq):
+    """Oracle (as it is) on the first `nreq` requests: score, allocation, page images and one
+    decode step; returns (token-heads per second, seconds, description)."""
+    from oracle import attention as oatt, place, pool as opool, score as osc
+    import dataclasses
+    ws = dataclasses.replace(w, batch=nreq, seqlens=w.seqlens[:nreq])
+    T = ws.total_tokens
+    kc = k[:T].cpu().numpy()
+    vc = v[:T].cpu().numpy()
+    ac = acc[:T].cpu().numpy()
+    qc = qs[0][:nreq].cpu().numpy()
+    t0 = time.perf_counter()
+    tier, count, _ = osc.score_tokens(ac, ws.cu_seqlens(), ws.num_kv_heads, ws.alpha_h,
+                                      ws.alpha_l, ws.window)
+    pl = opool.Pool(1, nreq, ws.num_kv_heads, ws.row_capacity, ws.num_pages)
+    pl.compact(0, count)
+    cu = ws.cu_seqlens()
+    G = ws.group
+    for b in range(nreq):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for h in range(ws.num_kv_heads):
+            place.head_pages(kc[lo:hi, h], vc[lo:hi, h], tier[lo:hi, h])
+            kd, vd = place.head_dequantized(kc[lo:hi, h], vc[lo:hi, h], tier[lo:hi, h])
+            oatt.decode_group(qc[b, h * G:(h + 1) * G], kd, vd, 1 / math.sqrt(128))
+    dt = time.perf_counter() - t0
+    return T * ws.num_kv_heads / dt, dt, (f"{nreq} request(s) x {ws.seqlens[0]} tokens x "
+                                          f"{ws.num_kv_heads} KV heads: score, allocation, "
+                                          f"page images, one decode step")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    from mixed_precision_paged_score_amd import kvc, pipeline, workloads
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = workloads.workload(a.workload)
+    nsteps_dec = a.decode_steps if a.decode_steps is not None else w.decode_steps
+    k, v = workloads.make_kv(w, dev)
+    acc = workloads.make_acc(w, k, dev)
+    qs = [workloads.make_queries(w, dev, s) for s in range(nsteps_dec)]
+    path = pipeline.PromptPath(w, dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    def step(record):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        path.release(0)
+        path.prompt(0, acc, k, v)
+        e1.record(stream)
+        dec = []
+        for s in range(nsteps_dec):
+            d0, d1 = ev(), ev()
+            d0.record(stream)
+            path.decode(0, qs[s], out)
+            d1.record(stream)
+            dec.append((d0, d1))
+        if record is not None:
+            record.append(((e0, e1), dec))
+
+    for _ in range(a.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    status = path.pool.status()
+    recs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    comp_ms = [r[0][0].elapsed_time(r[0][1]) for r in recs]
+    dec_ms = [d0.elapsed_time(d1) for r in recs for (d0, d1) in r[1]]
+    count = path.new_count.cpu().numpy()
+    T, Hkv, Hq, B = w.total_tokens, w.num_kv_heads, w.num_q_heads, w.batch
+    token_heads = T * Hkv
+    comp_s = float(np.mean(comp_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    dbytes = decode_algorithmic_bytes(count, B, Hq)
+    cbytes = compaction_algorithmic_bytes(count, T, Hkv, Hq)
+    dec_gbps = dbytes / dec_s / 1e9
+    comp_gbps = cbytes / comp_s / 1e9
+    ms_per_step = wall / a.steps * 1e3
+    nh, nl = int(count[..., 0].sum()), int(count[..., 1].sum())
+    res = {
+        "metric": "KV tokens compacted/s + paged decode attn GB/s (fraction of HBM peak)",
+        "value": token_heads / comp_s,
+        "unit": "KV token-heads compacted/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in, u8 codes, fp32 scale math",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.num_layers, "batch": B,
+                   "seq_len": w.seqlens[0] if len(set(w.seqlens)) == 1 else "ragged",
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "pages": w.num_pages,
+                   "decode_steps": nsteps_dec, "alpha_h": w.alpha_h, "alpha_l": w.alpha_l,
+                   "window": w.window},
+        "compaction": {"ms": comp_s * 1e3, "GBps": comp_gbps, "frac_hbm": comp_gbps / HBM_PEAK_GBPS,
+                       "algorithmic_bytes": cbytes, "token_heads": token_heads,
+                       "high": nh, "low": nl, "pruned": token_heads - nh - nl},
+        "decode_GBps": dec_gbps,
+        "decode": {"us_per_call": dec_s * 1e6, "GBps": dec_gbps,
+                   "frac_hbm": dec_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes},
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
+                     "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "pool_status": status,
+    }
+    if not a.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            rate, secs, desc = cpu_baseline(w, k, v, acc, qs, a.cpu_sample_requests)
+        res["cpu_baseline"] = {"value": rate, "unit": "KV token-heads compacted/s",
+                               "cores": 1, "kind": "oracle", "sample": desc,
+                               "seconds": secs}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

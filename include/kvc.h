@@ -1,0 +1,192 @@
+/*
+ * kvc.h -- C ABI of libkvc: differentiated KV compaction and mixed-precision paged decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method is DiffKV's (pith.science review of arXiv 2412.03131, "DiffKV: Differentiated
+ * Memory Management for Large Language Models with Parallel KV Compaction"):
+ *   - "What carries the argument": a token's significance is the mean attention it receives
+ *     from subsequent tokens, max-aggregated over its GQA group, compared with alpha_h/N
+ *     and alpha_l/N (high precision, low precision, pruned); after every head has decided
+ *     how many high- and low-precision pages it needs, a parallel prefix sum over the
+ *     circular free page list gives each head a disjoint contiguous region of page ids.
+ *   - "Core claim": K8V4 high tier, K4V2 low tier, unified pages, a circular free page list
+ *     and a bidirectional page table, all GPU-resident.
+ *   - free-parameter ledger: the most recent W = 64 tokens are always high precision.
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers unless stated otherwise.  Every buffer is owned by the
+ *     caller; the library allocates nothing, keeps no pointer after returning, and never
+ *     synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream).
+ *   - A negative return value is a synchronous error: nothing was enqueued.
+ *   - Errors found on the device are sticky bits OR-ed into pool->dev_status (and, for
+ *     kvc_score_tokens, into its own dev_status argument).  Every kernel that changes pool
+ *     state first reads dev_status and does nothing if any bit is set, so a failed call
+ *     leaves the pool exactly as it was and turns the rest of the round into no-ops.  The
+ *     caller reads the word after a stream synchronization and clears it.
+ *   - Calls that share a pool must be ordered on one stream (or by the caller's events).
+ *   - Query head hq reads KV head hq / G, G = num_q_heads / num_kv_heads.
+ *   - Head dimension is fixed at 128.  K, V and q are IEEE fp16 bit patterns.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *kvc_stream_t; /* hipStream_t */
+
+/* synchronous status codes */
+enum {
+    KVC_OK = 0,
+    KVC_E_NULL = -1,        /* a required pointer is NULL                                   */
+    KVC_E_ALIGN = -2,       /* K/V/q/pages/out not 16-byte aligned                          */
+    KVC_E_SHAPE = -3,       /* inconsistent geometry or sizes (see each call)               */
+    KVC_E_WORKSPACE = -4,   /* workspace NULL or smaller than kvc_workspace_bytes()         */
+    KVC_E_HIP = -5,         /* a HIP launch failed; kvc_last_error() has the message        */
+    KVC_E_UNSUPPORTED = -6  /* argument combination not implemented                         */
+};
+
+/* device-side status bits (OR-ed into *dev_status) */
+enum {
+    KVC_DEV_POOL_EXHAUSTED = 1, /* compaction needs more pages than are free                */
+    KVC_DEV_ROW_OVERFLOW = 2,   /* a head would need more than row_capacity pages           */
+    KVC_DEV_SHRINK = 4,         /* a head not marked changed would lose pages               */
+    KVC_DEV_COUNT_MISMATCH = 8, /* tier array disagrees with the pool's per-head counts     */
+    KVC_DEV_SEQLEN = 16,        /* a request is longer than the max_seqlen argument         */
+    KVC_DEV_INTERNAL = 32       /* a scan's look-back gave up waiting (a library bug)       */
+};
+
+/* tier codes */
+enum { KVC_PRUNE = 0, KVC_LOW = 1, KVC_HIGH = 2, KVC_FRESH = 3 };
+
+/* unified page format (both tiers share one 3456-byte page):
+ *   [   0, 2048)  key codes: HIGH 16 slots x 128 B (8-bit), LOW 32 slots x 64 B (4-bit)
+ *   [2048, 3072)  value codes, 64 units of 16 B laid out for the decode kernel's matrix
+ *                 operands: HIGH 4-bit, LOW 2-bit (exact bit positions: the design doc)
+ *   [3072, 3328)  per slot: key scale, key zero, value scale, value zero (fp16)
+ *   [3328, 3456)  per slot: token position (int32), -1 for an empty slot            */
+#define KVC_HEAD_DIM 128
+#define KVC_HIGH_SLOTS 16
+#define KVC_LOW_SLOTS 32
+#define KVC_PAGE_BYTES 3456
+
+typedef struct {
+    int32_t num_layers;   /* L: layers sharing the pool                                   */
+    int32_t batch;        /* B: requests                                                  */
+    int32_t num_q_heads;  /* Hq                                                           */
+    int32_t num_kv_heads; /* Hkv (Hq % Hkv == 0)                                          */
+    int32_t row_capacity; /* C: page-table slots per (layer, request, KV head)            */
+    int64_t num_pages;    /* P: pages in the pool                                         */
+} kvc_geom;
+
+typedef struct {
+    uint8_t *pages;      /* [P][3456]                                                      */
+    int32_t *page_table; /* [L][B][Hkv][C]: HIGH page ids from position 0 upward, LOW page
+                            ids from position C-1 downward, -1 elsewhere                    */
+    int32_t *count;      /* [L][B][Hkv][2]: live (#HIGH, #LOW) tokens per head              */
+    int32_t *owner;      /* [P]: reverse map, gid*C + row position with
+                            gid = (layer*B + b)*Hkv + h; -1 for a free page                */
+    int32_t *free_ring;  /* [P]: circular free list; free pages are
+                            free_ring[(head + k) % P] for k < tail - head                  */
+    uint64_t *ring_ctr;  /* [2]: head, tail (monotone counters)                            */
+    int32_t *dev_status; /* [1]: sticky KVC_DEV_* bits                                     */
+} kvc_pool;
+
+/* Operation ids for kvc_workspace_bytes */
+enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3 };
+
+/* Version string of the library. */
+const char *kvc_version(void);
+
+/* Message of the last KVC_E_HIP failure in this thread ("" if none). */
+const char *kvc_last_error(void);
+
+/* Bytes of workspace `op` needs for this geometry.  max_seqlen is the longest request
+ * (KVC_OP_QUANTIZE), unused otherwise.  Returns 0 for an unknown op. */
+size_t kvc_workspace_bytes(const kvc_geom *geom, int32_t op, int32_t max_seqlen);
+
+/* Empty pool: free_ring = 0..P-1, head = 0, tail = P, page table and owner = -1,
+ * counts = 0, dev_status = 0.  Page bytes are left as they are.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (non-positive sizes, L*B*Hkv*C >= 2^31, P >= 2^31). */
+int kvc_pool_init(const kvc_geom *geom, const kvc_pool *pool, kvc_stream_t stream);
+
+/* Significance score and tier of every (token, KV head) of one layer (DiffKV review page,
+ * "What carries the argument"; free-parameter ledger for W).
+ *   acc_sum    float32 [T][Hq]: for each token, the sum of the softmax weight it received
+ *              from strictly later queries of each query head (>= 0, finite)
+ *   cu_seqlens int32 [B+1]: request b owns rows cu[b]..cu[b+1]-1, positions 0..N_b-1
+ *   For token t of request b (N = N_b, cnt = N-1-t): score = +inf if cnt == 0, else
+ *   max over the G query heads of fl32(acc/cnt); tier = HIGH if score >= fl32(alpha_h/N),
+ *   LOW if score >= fl32(alpha_l/N), else PRUNE; HIGH when t >= N - window; with
+ *   prev_tier (uint8 [T][Hkv], or NULL), tier = min(tier, prev) wherever prev != FRESH.
+ *   Outputs: tier uint8 [T][Hkv]; new_count int32 [B][Hkv][2] = (#HIGH, #LOW);
+ *   changed uint8 [B][Hkv] = 1 where some already-tiered token dropped a tier (may be NULL
+ *   when prev_tier is NULL).  max_seqlen bounds every N_b (else KVC_DEV_SEQLEN is set in
+ *   *dev_status and the request is skipped; dev_status may be NULL).
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (Hq % Hkv, window < 0, total_tokens < 0). */
+int kvc_score_tokens(const kvc_geom *geom, const float *acc_sum, const int32_t *cu_seqlens,
+                     int64_t total_tokens, int32_t max_seqlen, float alpha_h, float alpha_l,
+                     int32_t window, const uint8_t *prev_tier, uint8_t *tier,
+                     int32_t *new_count, uint8_t *changed, int32_t *dev_status,
+                     kvc_stream_t stream);
+
+/* One allocation round for one layer: prefix sums over the B*Hkv heads (request-major) of
+ * their page demand give each head a contiguous segment of the circular free list
+ * (DiffKV review page, "What carries the argument").  Per head, pages needed are
+ * ceil(n_high/16) HIGH and ceil(n_low/32) LOW.  With changed == NULL (prompt mode) or
+ * changed[b][h] != 0 the head is rebuilt: it takes fresh pages for all its tokens and its
+ * old pages are returned to the ring's tail (HIGH in row order, then LOW from the right
+ * end); other heads grow in place.  Only pages free when the call starts are handed out,
+ * so old pages stay readable until the next call.  All or nothing: on exhaustion, row
+ * overflow or a shrink of a non-rebuilt head, a KVC_DEV_* bit is set and nothing changes.
+ *   new_count      int32 [B][Hkv][2] (from kvc_score_tokens)
+ *   old_rows_out   int32 [B][Hkv][C] or NULL: the layer's page table before the call
+ *   old_count_out  int32 [B][Hkv][2] or NULL: the layer's counts before the call
+ *   workspace      >= kvc_workspace_bytes(geom, KVC_OP_COMPACT, 0) bytes, 256-B aligned
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (layer out of range), KVC_E_WORKSPACE. */
+int kvc_compact_pages(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                      const int32_t *new_count, const uint8_t *changed,
+                      int32_t *old_rows_out, int32_t *old_count_out, void *workspace,
+                      size_t workspace_bytes, kvc_stream_t stream);
+
+/* Quantize and place one layer's kept tokens into the pages compact_pages assigned (prompt
+ * mode).  HIGH tokens become K8V4, LOW tokens K4V2 (DiffKV review page, "Core claim"):
+ * per token and head, asymmetric min/max codes over the 128 channels, scale and zero
+ * computed in float32 with round-to-nearest-even and stored as fp16.  Within a head and a
+ * tier, tokens take slots in ascending position order; every page of the head is written
+ * whole (empty slots zeroed, position -1).
+ *   k, v       fp16 [T][Hkv][128] (T = cu_seqlens[B]), 16-byte aligned
+ *   tier       uint8 [T][Hkv] (from kvc_score_tokens)
+ *   prev_tier, changed, old_rows, old_count: must be NULL (re-tier rounds: not yet)
+ *   A head whose tier counts differ from the pool's counts is skipped and
+ *   KVC_DEV_COUNT_MISMATCH is set.
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE, KVC_E_UNSUPPORTED. */
+int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                           const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
+                           int64_t total_tokens, int32_t max_seqlen, const uint8_t *tier,
+                           const uint8_t *prev_tier, const uint8_t *changed,
+                           const int32_t *old_rows, const int32_t *old_count,
+                           void *workspace, size_t workspace_bytes, kvc_stream_t stream);
+
+/* Decode attention of one new query per request over its KV head's live tokens (HIGH
+ * slots < n_high, LOW slots < n_low), keys and values reconstructed on the fly as
+ * code*scale + zero: o = softmax(softmax_scale * q.k) v.  No mask (every cached token
+ * precedes the query).  A head with no live token yields zeros.
+ *   q    fp16 [B][Hq][128];  out  [B][Hq][128], float32 if out_is_fp32 else fp16
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE, 0) bytes
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE. */
+int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                               const uint16_t *q, float softmax_scale, void *out,
+                               int32_t out_is_fp32, void *workspace, size_t workspace_bytes,
+                               kvc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

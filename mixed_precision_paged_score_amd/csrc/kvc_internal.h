@@ -1,0 +1,78 @@
+// Internal definitions shared by the libkvc HIP sources (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int D = KVC_HEAD_DIM;
+constexpr int PAGE = KVC_PAGE_BYTES;
+constexpr int HS = KVC_HIGH_SLOTS;   // HIGH tokens per page
+constexpr int LS = KVC_LOW_SLOTS;    // LOW tokens per page
+constexpr int K_OFF = 0;
+constexpr int V_OFF = 2048;
+constexpr int PARAM_OFF = 3072;      // 8 bytes per slot: k_scale, k_zero, v_scale, v_zero
+constexpr int POS_OFF = 3328;        // int32 per slot
+
+constexpr int PRUNE = KVC_PRUNE, LOW = KVC_LOW, HIGH = KVC_HIGH, FRESH = KVC_FRESH;
+
+void set_error(const char *what, hipError_t e);
+
+inline int launch_check(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error(what, e);
+        return KVC_E_HIP;
+    }
+    return KVC_OK;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int check_geom(const kvc_geom *g) {
+    if (!g) return KVC_E_NULL;
+    if (g->num_layers <= 0 || g->batch <= 0 || g->num_q_heads <= 0 || g->num_kv_heads <= 0 ||
+        g->row_capacity <= 0 || g->num_pages <= 0)
+        return KVC_E_SHAPE;
+    if (g->num_q_heads % g->num_kv_heads) return KVC_E_SHAPE;
+    if (g->num_pages >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+    int64_t rows = int64_t(g->num_layers) * g->batch * g->num_kv_heads * g->row_capacity;
+    if (rows >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+    return KVC_OK;
+}
+
+inline int check_pool(const kvc_pool *p) {
+    if (!p || !p->pages || !p->page_table || !p->count || !p->owner || !p->free_ring ||
+        !p->ring_ctr || !p->dev_status)
+        return KVC_E_NULL;
+    if (!aligned16(p->pages)) return KVC_E_ALIGN;
+    return KVC_OK;
+}
+
+// ---- device helpers -------------------------------------------------------------------
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// request index owning global row r, by binary search over cu_seqlens[0..B]
+__device__ __forceinline__ int find_request(const int32_t *cu, int B, int64_t r) {
+    int lo = 0, hi = B;   // cu[lo] <= r < cu[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= r) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+    return __half2float(__ushort_as_half(b));
+}
+__device__ __forceinline__ uint16_t f2h_rn(float f) {
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+}  // namespace kvc

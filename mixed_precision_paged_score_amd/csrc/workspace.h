@@ -1,0 +1,79 @@
+// Workspace layouts of the libkvc calls.  Each call carves its caller-provided workspace
+// into the arrays below (offsets 256-byte aligned); kvc_workspace_bytes() reports the size.
+#pragma once
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- compact_pages -------------------------------------------------------------------
+constexpr int SCAN_TILE = 256;    // heads per scan workgroup (one per thread)
+
+struct CompactHdr {
+    uint32_t ticket;       // dynamic tile index counter (tiles start in ticket order)
+    uint32_t err;          // KVC_DEV_* bits found by the scan (row overflow, shrink)
+    int64_t total_alloc;   // pages handed out by the whole call
+    int64_t total_free;    // pages returned by the whole call
+    uint64_t head0, tail0; // ring counters when the call started
+    int32_t entry_status;  // pool status when the call started
+};
+
+struct CompactWs {
+    int nheads, ntiles;
+    size_t hdr, st, off, foff, bytes;
+    explicit CompactWs(const kvc_geom *g) {
+        nheads = g->batch * g->num_kv_heads;
+        ntiles = (nheads + SCAN_TILE - 1) / SCAN_TILE;
+        hdr = 0;
+        st = align256(sizeof(CompactHdr));
+        off = st + align256(sizeof(uint64_t) * ntiles);
+        foff = off + align256(sizeof(int32_t) * nheads);
+        bytes = foff + align256(sizeof(int32_t) * nheads);
+    }
+};
+
+// ---- quantize_and_place ----------------------------------------------------------------
+constexpr int QTILE = 256;        // tokens per rank tile
+
+struct QuantWs {
+    int ntq;
+    size_t tile_cnt, tile_base, ok, poslist, bytes;
+    QuantWs(const kvc_geom *g, int max_seqlen) {
+        ntq = (max_seqlen + QTILE - 1) / QTILE;
+        if (ntq < 1) ntq = 1;
+        size_t cnt = sizeof(int32_t) * size_t(g->batch) * ntq * g->num_kv_heads * 2;
+        tile_cnt = 0;
+        tile_base = align256(cnt);
+        ok = tile_base + align256(cnt);
+        poslist = ok + align256(sizeof(int32_t) * (size_t(g->batch) * g->num_kv_heads + 1));
+        size_t pl = sizeof(int32_t) * size_t(g->batch) * g->num_kv_heads *
+                    size_t(max_seqlen > 0 ? max_seqlen : 1);
+        bytes = poslist + align256(pl);
+    }
+};
+
+// ---- paged_decode_attention ------------------------------------------------------------
+constexpr int PART_STRIDE = 132;  // floats per partial: m, l, pad, pad, o[128]
+
+inline int decode_splits(const kvc_geom *g) {
+    int heads = g->batch * g->num_kv_heads;
+    int s = (2048 + heads - 1) / heads;
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+    return s;
+}
+
+struct DecodeWs {
+    int splits;
+    size_t part, bytes;
+    explicit DecodeWs(const kvc_geom *g) {
+        splits = decode_splits(g);
+        part = 0;
+        bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
+                         splits);
+    }
+};
+
+}  // namespace kvc

@@ -8,7 +8,7 @@ per-token, per-head asymmetric min/max scheme over the 128 channels of one key o
     mn, mx  = min and max of the row's fp16 values (exact in float32)
     s32     = fl32( fl32(mx - mn) / (2^b - 1) )        two float32 round-to-nearest-even ops
     s16     = fp16(s32) rounded to nearest even; if that is 0 while mx > mn, 2^-24 instead
-    z16     = mn  (an fp16 value already, stored as is)
+    z16     = mn + 0  (an fp16 value already; adding +0 stores a -0 minimum as +0)
     inv     = fl32(1 / s16) when s16 > 0, else 0
     code_i  = min( rint_even( fl32( fl32(x_i - z16) * inv ) ), 2^b - 1 )
     x_hat_i = fl32( code_i * s16 + z16 )                one rounding (a fused multiply-add)
@@ -35,7 +35,7 @@ def quantize_rows(x, bits):
     s16 = s32.astype(np.float16)                       # round to nearest even
     tiny = np.float16(2.0 ** -24)
     s16 = np.where((s16 == 0) & (mx > mn), tiny, s16).astype(np.float16)
-    z16 = mn.astype(np.float16)                        # exact: mn is an fp16 value
+    z16 = (mn + np.float32(0)).astype(np.float16)      # exact; -0 becomes +0
     sf = s16.astype(np.float32)
     pos = sf > 0
     inv = np.zeros_like(sf)

@@ -1,0 +1,66 @@
+"""The C ABI library loads without a GPU, exports every function include/kvc.h declares, and
+rejects bad arguments synchronously (no device work is started by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    from mixed_precision_paged_score_amd import kvc
+    lib = ctypes.CDLL(kvc.LIB_PATH)
+    names = _declared()
+    assert set(names) == set(kvc.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_workspace_sizes():
+    from mixed_precision_paged_score_amd import kvc
+    assert "gfx950" in kvc.version()
+    g = kvc.make_geom(1, 16, 64, 8, 2049, 1 << 18)
+    assert kvc.workspace_bytes(g, kvc.OP_COMPACT) > 0
+    assert kvc.workspace_bytes(g, kvc.OP_QUANTIZE, 32768) >= 16 * 8 * 32768 * 4
+    assert kvc.workspace_bytes(g, kvc.OP_DECODE) > 0
+    assert kvc.workspace_bytes(g, 99) == 0
+    bad = kvc.make_geom(1, 16, 60, 8, 2049, 1 << 18)        # Hq % Hkv != 0
+    assert kvc.workspace_bytes(bad, kvc.OP_COMPACT) == 0
+
+
+def test_synchronous_errors_enqueue_nothing():
+    from mixed_precision_paged_score_amd import kvc
+    lib = kvc._lib
+    g = kvc.make_geom(1, 2, 8, 2, 10, 100)
+    assert lib.kvc_pool_init(ctypes.byref(g), None, None) == kvc.E_NULL
+    bad = kvc.make_geom(1, 2, 8, 3, 10, 100)
+    p = kvc.PoolPtrs(16, 16, 16, 16, 16, 16, 16)
+    assert lib.kvc_pool_init(ctypes.byref(bad), ctypes.byref(p), None) == kvc.E_SHAPE
+    huge = kvc.make_geom(1, 2, 8, 2, 10, 1 << 31)
+    assert lib.kvc_pool_init(ctypes.byref(huge), ctypes.byref(p), None) == kvc.E_SHAPE
+    p_unaligned = kvc.PoolPtrs(18, 16, 16, 16, 16, 16, 16)
+    assert lib.kvc_pool_init(ctypes.byref(g), ctypes.byref(p_unaligned), None) == kvc.E_ALIGN
+    # compact: layer out of range, workspace too small
+    assert lib.kvc_compact_pages(ctypes.byref(g), 1, ctypes.byref(p), 16, None, None, None,
+                                 256, 1 << 20, None) == kvc.E_SHAPE
+    assert lib.kvc_compact_pages(ctypes.byref(g), 0, ctypes.byref(p), 16, None, None, None,
+                                 256, 8, None) == kvc.E_WORKSPACE
+    # quantize: re-tier inputs not implemented yet
+    assert lib.kvc_quantize_and_place(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, 10, 5,
+                                      16, 16, None, None, None, 256, 1 << 20,
+                                      None) == kvc.E_UNSUPPORTED
+    # decode: misaligned query
+    assert lib.kvc_paged_decode_attention(ctypes.byref(g), 0, ctypes.byref(p), 18, 1.0, 16, 1,
+                                          256, 1 << 20, None) == kvc.E_ALIGN
+    # score: negative window
+    assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
+                                ctypes.c_float(0.1), -1, None, 16, 16, None, None,
+                                None) == kvc.E_SHAPE
