@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         } else {
             uint32_t w = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w |= code_of(x[e], q) << (4 * ((e >> 1) + 4 * (e & 1)));
+            for (int e = 0; e < 8; ++e)
+                w |= code_of(x[e], q) << (4 * ((e & 1) + 2 * (e >> 2) + 4 * ((e >> 1) & 1)));
             if (!live) w = 0;
             *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = w;
         }

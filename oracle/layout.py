@@ -10,7 +10,8 @@ One page is 3456 bytes and holds either 16 HIGH (K8V4) tokens or 32 LOW (K4V2) t
   [   0, 2048)  key codes, one row per slot
                   HIGH: slot s at 128*s, byte i = 8-bit code of channel i
                   LOW : slot s at  64*s, 16 little-endian 32-bit words; word w holds
-                        channels 8w..8w+7, channel 8w+e in nibble (e>>1) + 4*(e&1)
+                        channels 8w..8w+7, channel 8w+e in nibble
+                        (e & 1) + 2*(e >> 2) + 4*((e >> 1) & 1)
   [2048, 3072)  value codes, 64 units of 16 bytes; unit u = 16*j + l (j in 0..3, l in 0..15)
                 at 2048 + 16*u, four little-endian 32-bit words q = 0..3
                   HIGH (4-bit): slot s = 4*j + r, channel c = 16*n + l,
@@ -44,7 +45,7 @@ def _k_map(tier):
                 shift[s, c] = 0
             else:
                 w, e = c // 8, c % 8
-                nib = (e >> 1) + 4 * (e & 1)
+                nib = (e & 1) + 2 * (e >> 2) + 4 * ((e >> 1) & 1)
                 byte[s, c] = K_OFF + 64 * s + 4 * w + nib // 2
                 shift[s, c] = 4 * (nib % 2)
     return byte, shift

@@ -17,12 +17,12 @@ def test_field_coverage_is_exact():
 
 
 def test_k4_word_hand_derived():
-    # channels 0..7 with codes 0..7: channel e sits in nibble (e>>1) + 4(e&1), so nibbles
-    # 0..7 hold codes 0,2,4,6,1,3,5,7 -> word 0x75316420 -> bytes 20 64 31 75
+    # channels 0..7 with codes 0..7: channel e sits in nibble (e&1) + 2(e>>2) + 4((e>>1)&1),
+    # so nibbles 0..7 hold codes 0,1,4,5,2,3,6,7 -> word 0x76325410 -> bytes 10 54 32 76
     k = np.zeros((1, 128), np.uint8)
     k[0, :8] = np.arange(8)
     page = layout.build_page(1, k, np.zeros((1, 128), np.uint8), [0], [0], [0], [0], [9])
-    assert page[:4].tolist() == [0x20, 0x64, 0x31, 0x75]
+    assert page[:4].tolist() == [0x10, 0x54, 0x32, 0x76]
     assert np.all(page[4:64] == 0)
 
 
