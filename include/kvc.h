@@ -178,7 +178,8 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
  * code*scale + zero: o = softmax(softmax_scale * q.k) v.  No mask (every cached token
  * precedes the query).  A head with no live token yields zeros.
  *   q    fp16 [B][Hq][128];  out  [B][Hq][128], float32 if out_is_fp32 else fp16
- *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE, 0) bytes
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE, 0) bytes, 256-B aligned (split
+ *        partials); calls that share a decode workspace must not overlap.
  * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE. */
 int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                                const uint16_t *q, float softmax_scale, void *out,

@@ -20,8 +20,12 @@
 //   * the running max is only moved when a tile exceeds it by more than 2^8 (in log2 units),
 //     so the accumulator rescale (a cross-lane shuffle) is rare;
 //   * four waves per workgroup take consecutive slices of one head's tiles (balanced by
-//     bytes: a HIGH tile counts twice a LOW tile) and merge in LDS; a second kernel merges
-//     the workgroups' (max, sum, output) partials of each query head in float32.
+//     bytes: a HIGH tile counts twice a LOW tile) and merge in LDS; each wave keeps DEPTH
+//     tiles in flight in registers, with the page ids of up to 64 tiles preloaded in one
+//     lane-indexed register (no load waits on another load);
+//   * a second kernel merges each query head's S (max, sum, output) partials in float32 (a
+//     fused last-workgroup merge needs device-scope fences, which on a multi-XCD part write
+//     back and invalidate L2 and cost more than the extra launch).
 #include "kvc_internal.h"
 #include "workspace.h"
 
@@ -29,158 +33,326 @@ namespace kvc {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_MARGIN = 8.0f;      // log2 units
+constexpr float M_INIT = -1.0e30f;          // finite "minus infinity" for the running max
 constexpr int DEC_WAVES = 4;
-constexpr float MAGIC = 1024.0f;
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ h4 cat(h2 a, h2 b) { return h4{a[0], a[1], b[0], b[1]}; }
-__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ h8 cat4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
 }
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pick4(const uint4 &u, int k) {
+    return k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
+}
+__device__ __forceinline__ float half_lo(uint32_t u) { return h2f(uint16_t(u & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t u) { return h2f(uint16_t(u >> 16)); }
 
-// raw per-lane bytes of one tile
-struct Tile {
-    uint4 k0, k1;      // HIGH: 32 key bytes (8-bit codes); LOW: k0 = 16 key bytes (4-bit)
-    uint4 v;           // HIGH: value unit (4 words); LOW: v.x, v.y = this half's 2 words
-    uint4 p0, p1;      // parameters of the lane group's 4 tokens (8 bytes each)
+// A 4- or 2-bit code moved to mantissa bits 6..9 of each fp16 half and OR-ed with 16.0
+// (0x4C00) is the exact fp16 number 16 + code.  SH > 0 shifts left, < 0 right.  `mg` holds
+// 0x4C004C00 in a register the compiler cannot see through, so shift + v_and_or_b32 is two
+// instructions per pair of codes.
+template <int SH, uint32_t MASK>
+__device__ __forceinline__ uint32_t code16(uint32_t w, uint32_t mg) {
+    const uint32_t x = SH >= 0 ? (w << SH) : (w >> (-SH));
+    return (x & MASK) | mg;
+}
+constexpr uint32_t NIB = 0x03C003C0u;    // bits 6..9 of both halves
+constexpr uint32_t CRB = 0x00C000C0u;    // bits 6..7 of both halves
+constexpr float KOFF_HIGH = 1024.0f;     // 8-bit key codes: byte -> 1024 + code
+constexpr float COFF = 16.0f;            // 4/2-bit codes: 16 + code
+
+// Per-lane bytes of a pair of 16-token tiles (A, B) of one tier.  A HIGH tile is one HIGH
+// page; a LOW tile is one half (16 slots) of a LOW page.  Keys and values of both tiles are
+// needed by every lane (matrix operands); parameters only for the lane's own tile.
+template <bool HIGH> struct Pair;
+template <> struct Pair<true> {
+    uint4 ka0, ka1, kb0, kb1;   // channels 32j..32j+31 of token (lane & 15), 8-bit codes
+    uint4 va, vb;               // value unit 16j + (lane & 15): tokens 4j..4j+3, 8 channels
+    uint4 p0, p1;               // parameters of tokens 4j..4j+3 of the lane's tile
+};
+template <> struct Pair<false> {
+    uint4 ka, kb;               // channels 32j..32j+31 of token (lane & 15), 4-bit codes
+    uint2 va, vb;               // the tiles' halves of value unit 16j + (lane & 15)
+    uint4 p0, p1;
 };
 
-struct TileRef {
-    const uint8_t *pg;
-    int high, f, live;  // f: half of a LOW page (slots 16f..16f+15)
-};
-
-__device__ __forceinline__ TileRef tile_ref(int u, int qH, int nh, int nl,
-                                            const int32_t *row, int C,
-                                            const uint8_t *pages) {
-    TileRef t;
-    if (u < qH) {
-        t.high = 1;
-        t.f = 0;
-        t.live = min(HS, nh - HS * u);
-        t.pg = pages + int64_t(row[u]) * PAGE;
-    } else {
-        const int v = u - qH, lp = v >> 1;
-        t.high = 0;
-        t.f = v & 1;
-        t.live = min(16, nl - LS * lp - 16 * t.f);
-        t.pg = pages + int64_t(row[C - 1 - lp]) * PAGE;
-    }
-    return t;
-}
-
-__device__ __forceinline__ Tile load_tile(const TileRef &t, int lane) {
+template <bool HIGH>
+__device__ __forceinline__ Pair<HIGH> load_pair(const uint8_t *pga, const uint8_t *pgb, int fa,
+                                                int fb, int lane, bool own_b) {
     const int j = lane >> 4, tok = lane & 15;
-    Tile d;
-    if (t.high) {
-        const uint4 *kp = reinterpret_cast<const uint4 *>(t.pg + K_OFF + tok * 128 + 32 * j);
-        d.k0 = kp[0];
-        d.k1 = kp[1];
-        d.v = *reinterpret_cast<const uint4 *>(t.pg + V_OFF + 16 * lane);
-        const uint4 *pp = reinterpret_cast<const uint4 *>(t.pg + PARAM_OFF + 32 * j);
+    Pair<HIGH> d;
+    const uint8_t *pgo = own_b ? pgb : pga;
+    const int fo = own_b ? fb : fa;
+    if constexpr (HIGH) {
+        const uint4 *a = reinterpret_cast<const uint4 *>(pga + K_OFF + tok * 128 + 32 * j);
+        const uint4 *b = reinterpret_cast<const uint4 *>(pgb + K_OFF + tok * 128 + 32 * j);
+        d.ka0 = a[0];
+        d.ka1 = a[1];
+        d.kb0 = b[0];
+        d.kb1 = b[1];
+        d.va = *reinterpret_cast<const uint4 *>(pga + V_OFF + 16 * lane);
+        d.vb = *reinterpret_cast<const uint4 *>(pgb + V_OFF + 16 * lane);
+        const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 32 * j);
         d.p0 = pp[0];
         d.p1 = pp[1];
     } else {
-        const int slot = 16 * t.f + tok;
-        d.k0 = *reinterpret_cast<const uint4 *>(t.pg + K_OFF + slot * 64 + 16 * j);
-        d.k1 = make_uint4(0, 0, 0, 0);
-        const uint2 vv = *reinterpret_cast<const uint2 *>(t.pg + V_OFF + 16 * lane + 8 * t.f);
-        d.v = make_uint4(vv.x, vv.y, 0, 0);
-        const uint4 *pp = reinterpret_cast<const uint4 *>(t.pg + PARAM_OFF + 8 * (16 * t.f + 4 * j));
+        d.ka = *reinterpret_cast<const uint4 *>(pga + K_OFF + (16 * fa + tok) * 64 + 16 * j);
+        d.kb = *reinterpret_cast<const uint4 *>(pgb + K_OFF + (16 * fb + tok) * 64 + 16 * j);
+        d.va = *reinterpret_cast<const uint2 *>(pga + V_OFF + 16 * lane + 8 * fa);
+        d.vb = *reinterpret_cast<const uint2 *>(pgb + V_OFF + 16 * lane + 8 * fb);
+        const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 8 * (16 * fo + 4 * j));
         d.p0 = pp[0];
         d.p1 = pp[1];
     }
     return d;
 }
 
-// key operand of MFMA m: channels 32j + 4m + {0, 2, 1, 3} of the lane's token, as 1024 + code
-__device__ __forceinline__ h4 key_operand(const Tile &d, int high, int m) {
-    if (high) {
-        const uint32_t w = m == 0 ? d.k0.x : m == 1 ? d.k0.y : m == 2 ? d.k0.z : m == 3 ? d.k0.w
-                         : m == 4 ? d.k1.x : m == 5 ? d.k1.y : m == 6 ? d.k1.z : d.k1.w;
-        const uint32_t a = (w & 0x00FF00FFu) | 0x64006400u;          // channels 0, 2
-        const uint32_t b = ((w >> 8) & 0x00FF00FFu) | 0x64006400u;   // channels 1, 3
-        return cat(as_h2(a), as_h2(b));
-    }
-    const uint32_t w = (m >> 1) == 0 ? d.k0.x : (m >> 1) == 1 ? d.k0.y : (m >> 1) == 2 ? d.k0.z : d.k0.w;
-    const int sh = 8 * (m & 1);
-    const uint32_t a = ((w >> sh) & 0x000F000Fu) | 0x64006400u;        // channels 0, 2
-    const uint32_t b = ((w >> (sh + 4)) & 0x000F000Fu) | 0x64006400u;  // channels 1, 3
-    return cat(as_h2(a), as_h2(b));
+// key operand of 16x16x32 MFMA m (0..3): channels 32j + 8m + {0,2,1,3,4,6,5,7}
+__device__ __forceinline__ h8 key_op_high(const uint4 &k0, const uint4 &k1, int m, uint32_t mg) {
+    const uint32_t w0 = m < 2 ? pick4(k0, 2 * m) : pick4(k1, 2 * m - 4);
+    const uint32_t w1 = m < 2 ? pick4(k0, 2 * m + 1) : pick4(k1, 2 * m - 3);
+    // mg = 0x64646464: byte b of a key word becomes the fp16 number 1024 + b
+    return cat4(__builtin_amdgcn_perm(mg, w0, 0x04020400u), __builtin_amdgcn_perm(mg, w0, 0x04030401u),
+                __builtin_amdgcn_perm(mg, w1, 0x04020400u), __builtin_amdgcn_perm(mg, w1, 0x04030401u));
+}
+__device__ __forceinline__ h8 key_op_low(const uint4 &k, int m, uint32_t mg) {
+    const uint32_t w = pick4(k, m);    // nibble p holds channel order {0,1,4,5,2,3,6,7}
+    return cat4(code16<6, NIB>(w, mg), code16<2, NIB>(w, mg), code16<-2, NIB>(w, mg),
+                code16<-6, NIB>(w, mg));
 }
 
-// value operand of MFMA n: tokens 4j + {0,1,2,3} of channel 16n + (lane & 15), as the exact
-// code (1024 + code built by the bit trick, then 1024 subtracted exactly in fp16: the output
-// is a small difference of large sums, so the offset must not reach the accumulator)
-__device__ __forceinline__ h4 value_operand(const Tile &d, int high, int n) {
-    const h2 off = {_Float16(MAGIC), _Float16(MAGIC)};
-    uint32_t a, b;
-    if (high) {
-        const uint32_t w = (n >> 1) == 0 ? d.v.x : (n >> 1) == 1 ? d.v.y : (n >> 1) == 2 ? d.v.z : d.v.w;
-        const int sh = 8 * (n & 1);
-        a = ((w >> sh) & 0x000F000Fu) | 0x64006400u;
-        b = ((w >> (sh + 4)) & 0x000F000Fu) | 0x64006400u;
+// value operand (B, tokens x channels) of 16x16x32 MFMA n: k = 8j + e, e < 4 tile A token
+// 4j + e, e >= 4 tile B token 4j + e - 4, channel 16n + (lane & 15); entries 16 + code
+__device__ __forceinline__ void val_pair_high(uint32_t w, int nlow, uint32_t mg, uint32_t &r01,
+                                              uint32_t &r23) {
+    // unit word: channel-block n = 2q + nlow, token r at nibble 2*nlow + (r>>1) + 4*(r&1)
+    if (nlow == 0) {
+        r01 = code16<6, NIB>(w, mg);
+        r23 = code16<2, NIB>(w, mg);
     } else {
-        const uint32_t w = (n >> 2) == 0 ? d.v.x : d.v.y;
-        const int sh = 4 * (n & 3);
-        a = ((w >> sh) & 0x00030003u) | 0x64006400u;
-        b = ((w >> (sh + 2)) & 0x00030003u) | 0x64006400u;
+        r01 = code16<-2, NIB>(w, mg);
+        r23 = code16<-6, NIB>(w, mg);
     }
-    return cat(as_h2(a) - off, as_h2(b) - off);
 }
-
-__device__ __forceinline__ float half_lo(uint32_t u) { return h2f(uint16_t(u & 0xffffu)); }
-__device__ __forceinline__ float half_hi(uint32_t u) { return h2f(uint16_t(u >> 16)); }
+__device__ __forceinline__ h8 val_op_high(const uint4 &va, const uint4 &vb, int n, uint32_t mg) {
+    uint32_t a01, a23, b01, b23;
+    val_pair_high(pick4(va, n >> 1), n & 1, mg, a01, a23);
+    val_pair_high(pick4(vb, n >> 1), n & 1, mg, b01, b23);
+    return cat4(a01, a23, b01, b23);
+}
+template <int NL>
+__device__ __forceinline__ void val_pair_low(uint32_t w, uint32_t mg, uint32_t &r01,
+                                             uint32_t &r23) {
+    // 2-bit field 2*NL + (r>>1) + 8*(r&1) of the word; fields f, f+8 share a 16-bit lane
+    r01 = code16<6 - 4 * NL, CRB>(w, mg);
+    r23 = code16<4 - 4 * NL, CRB>(w, mg);
+}
+template <int N>
+__device__ __forceinline__ h8 val_op_low(const uint2 &va, const uint2 &vb, uint32_t mg) {
+    const uint32_t wa = (N >> 2) == 0 ? va.x : va.y, wb = (N >> 2) == 0 ? vb.x : vb.y;
+    uint32_t a01, a23, b01, b23;
+    val_pair_low<N & 3>(wa, mg, a01, a23);
+    val_pair_low<N & 3>(wb, mg, b01, b23);
+    return cat4(a01, a23, b01, b23);
+}
 
 struct WaveState {
-    f4 o[8];                  // O[g = 4j + r][16n + (lane & 15)], n = 0..7
-    float m, l, lz;           // per column g = lane & 15: running max (log2), sums
+    f4 o[8];         // O[row 4j + r][16n + (lane & 15)]; row c < 8: tile-A half, >= 8: tile-B half
+    float m;         // running max (log2 units) of query head (lane & 7), shared by c and c^8
+    float l, lz, lp; // partial sums of the lane's own scores: p, p*zero_v, P' (offset removal)
 };
 
-__global__ __launch_bounds__(64 * DEC_WAVES) void decode_mfma_kernel(
-    const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
-    const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
-    int C, int S, float *__restrict__ part) {
+struct Magic {
+    uint32_t k8;     // 0x64646464 (key bytes -> 1024 + code)
+    uint32_t c16;    // 0x4C004C00 (4/2-bit codes -> 16 + code)
+};
+
+// One pair of tiles.  The query operand repeats the 8 query heads in columns 0..7 and
+// 8..15; lane column c = lane & 15 keeps tile A's scores when c < 8 and tile B's when c >= 8,
+// so every lane's softmax work is useful although G <= 8.
+template <bool HIGH>
+__device__ __forceinline__ void attend_pair(const Pair<HIGH> &d, int live_own,
+                                            const h8 (&qo)[4], float sumq, float scale_log2,
+                                            int lane, const Magic &mg, WaveState &st) {
+    const int j = lane >> 4, c = lane & 15;
+    const bool own_b = c >= 8;
+    f4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if constexpr (HIGH) {
+            acc_a = mfma32(key_op_high(d.ka0, d.ka1, m, mg.k8), qo[m], acc_a);
+            acc_b = mfma32(key_op_high(d.kb0, d.kb1, m, mg.k8), qo[m], acc_b);
+        } else {
+            acc_a = mfma32(key_op_low(d.ka, m, mg.c16), qo[m], acc_a);
+            acc_b = mfma32(key_op_low(d.kb, m, mg.c16), qo[m], acc_b);
+        }
+    }
+    f4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = own_b ? acc_b[r] : acc_a[r];
+    constexpr float KOFF = HIGH ? KOFF_HIGH : COFF;
+    const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
+    float L[4], vs[4], vz[4];
+    float tmax = M_INIT;
+    const float koff_sum = KOFF * sumq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float ks = half_lo(pw[2 * r]), kz = half_hi(pw[2 * r]);
+        vs[r] = half_lo(pw[2 * r + 1]);
+        vz[r] = half_hi(pw[2 * r + 1]);
+        const float x = (ks * (acc[r] - koff_sum) + kz * sumq) * scale_log2;   // q.k_hat
+        L[r] = (4 * j + r < live_own) ? x : -__builtin_inff();
+        tmax = fmaxf(tmax, L[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));      // both tiles of the pair
+    if (__ballot(tmax > st.m + RESCALE_MARGIN) != 0ull) {
+        const float mn = fmaxf(st.m, tmax);
+        const float corr = __builtin_amdgcn_exp2f(st.m - mn);
+        st.l *= corr;
+        st.lz *= corr;
+        st.lp *= corr;
+        st.m = mn;
+        float cr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * j + r, 64);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.o[n][r] *= cr[r];
+    }
+    // P' = p * scale_v, as fp16 hi + lo, placed in the lane's half of the k dimension
+    _Float16 hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(L[r] - st.m);     // exp2(-inf) = 0
+        const float pv = p * vs[r];
+        hi[r] = _Float16(pv);
+        lo[r] = _Float16(pv - float(hi[r]));
+        st.l += p;
+        st.lz += p * vz[r];
+        st.lp += pv;          // the 16 + code offset is removed with this sum at the end
+    }
+    const uint32_t h01 = __builtin_bit_cast(uint32_t, h2{hi[0], hi[1]});
+    const uint32_t h23 = __builtin_bit_cast(uint32_t, h2{hi[2], hi[3]});
+    const uint32_t l01 = __builtin_bit_cast(uint32_t, h2{lo[0], lo[1]});
+    const uint32_t l23 = __builtin_bit_cast(uint32_t, h2{lo[2], lo[3]});
+    const h8 phi = cat4(own_b ? 0u : h01, own_b ? 0u : h23, own_b ? h01 : 0u, own_b ? h23 : 0u);
+    const h8 plo = cat4(own_b ? 0u : l01, own_b ? 0u : l23, own_b ? l01 : 0u, own_b ? l23 : 0u);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        h8 vop;
+        if constexpr (HIGH) {
+            vop = val_op_high(d.va, d.vb, n, mg.c16);
+        } else {
+            switch (n) {
+                case 0: vop = val_op_low<0>(d.va, d.vb, mg.c16); break;
+                case 1: vop = val_op_low<1>(d.va, d.vb, mg.c16); break;
+                case 2: vop = val_op_low<2>(d.va, d.vb, mg.c16); break;
+                case 3: vop = val_op_low<3>(d.va, d.vb, mg.c16); break;
+                case 4: vop = val_op_low<4>(d.va, d.vb, mg.c16); break;
+                case 5: vop = val_op_low<5>(d.va, d.vb, mg.c16); break;
+                case 6: vop = val_op_low<6>(d.va, d.vb, mg.c16); break;
+                default: vop = val_op_low<7>(d.va, d.vb, mg.c16); break;
+            }
+        }
+        st.o[n] = mfma32(phi, vop, st.o[n]);
+        st.o[n] = mfma32(plo, vop, st.o[n]);
+    }
+}
+
+// tiles [t0, t1) of one tier of a head, two at a time; page ids of up to 64 pages come from
+// one lane-indexed register, so no load waits on another load; one pair in flight ahead
+template <bool HIGH>
+__device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
+                                             int C, const uint8_t *pages, const h8 (&qo)[4],
+                                             float sumq, float scale_log2, int lane,
+                                             const Magic &mg, WaveState &st) {
+    constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
+    const bool own_b = (lane & 15) >= 8;
+    for (int c0 = t0; c0 < t1; c0 += 64 * TPP) {
+        const int c1 = min(t1, c0 + 64 * TPP);
+        const int p0 = c0 / TPP;
+        const int np = (c1 - 1) / TPP - p0 + 1;
+        int pid = 0;
+        if (lane < np) pid = HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)];
+        auto page_of = [&](int t) -> const uint8_t * {
+            return pages + int64_t(__builtin_amdgcn_readlane(pid, t / TPP - p0)) * PAGE;
+        };
+        auto live_of = [&](int t) -> int {
+            return t >= c1 ? 0 : (HIGH ? min(HS, n_tier - HS * t) : min(16, n_tier - 16 * t));
+        };
+        auto load = [&](int t) -> Pair<HIGH> {
+            const int tb = t + 1 < c1 ? t + 1 : t;    // a missing tile B re-reads tile A
+            return load_pair<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane, own_b);
+        };
+        Pair<HIGH> cur = load(c0);
+        for (int t = c0; t < c1; t += 2) {
+            Pair<HIGH> nxt = cur;
+            if (t + 2 < c1) nxt = load(t + 2);
+            const int live_own = own_b ? live_of(t + 1) : live_of(t);
+            attend_pair<HIGH>(cur, live_own, qo, sumq, scale_log2, lane, mg, st);
+            cur = nxt;
+        }
+    }
+}
+
+// grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
+// take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
+__global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
+                        const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
+                        const int32_t *__restrict__ count_l, int Hkv, int GT, int C, int S,
+                        float *__restrict__ part) {
     __shared__ float s_o[DEC_WAVES][32][64];
-    __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16];
+    __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16],
+        s_lp[DEC_WAVES][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane & 15, j = lane >> 4;
-    // block -> (split, KV head, request)
+    const int c = lane & 15, j = lane >> 4, gq = c & 7;
+    const int NGP = (GT + 7) >> 3;             // groups of 8 query heads per KV head
     const int s = blockIdx.x % S;
-    const int i = blockIdx.x / S;             // head index b*Hkv + h
+    const int gp = (blockIdx.x / S) % NGP;
+    const int i = blockIdx.x / (S * NGP);      // head index b*Hkv + h
     const int b = i / Hkv, h = i - b * Hkv;
-    const int Hq = Hkv * G;
+    const int Hq = Hkv * GT;
+    const int G = min(8, GT - 8 * gp);         // query heads of this group
+    const int g0 = 8 * gp;
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     const int qH = ceil_div(nh, HS);
     const int tL = ceil_div(nl, 16);
-    const int64_t W = 2 * int64_t(qH) + tL;   // work units: HIGH tile 2, LOW tile 1
+    // work units: HIGH tile 2, LOW tile 1; slices start on even tiles (pairs stay in a page)
+    const int64_t W = 2 * int64_t(qH) + tL;
     const int NC = S * DEC_WAVES;
-    const int c = s * DEC_WAVES + wave;
+    const int cc = s * DEC_WAVES + wave;
     auto tile_of = [&](int64_t x) -> int {
-        return x <= 2 * int64_t(qH) ? int((x + 1) >> 1) : qH + int(x - 2 * int64_t(qH));
+        int t = x <= 2 * int64_t(qH) ? int((x + 1) >> 1) : qH + int(x - 2 * int64_t(qH));
+        if (t > qH) t = qH + ((t - qH + 1) & ~1);     // LOW pairs start on even LOW tiles
+        return min(t, qH + tL);
     };
-    const int u0 = tile_of(W * c / NC), u1 = tile_of(W * (c + 1) / NC);
+    const int u0 = tile_of(W * cc / NC), u1 = tile_of(W * (cc + 1) / NC);
 
-    // query operand: lane (g, j) holds q[g][32j + 4m + {0,2,1,3}] for m = 0..7
-    h4 qop[8];
+    // query operand: lane (c, j) holds q[gq][32j + 8m + {0,2,1,3,4,6,5,7}], gq = c & 7
+    h8 qo[4];
     float sumq = 0.0f;
     {
-        uint4 qa[4] = {};
-        if (g < G) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (int64_t(b) * Hq + h * G + g) * D + 32 * j);
-            qa[0] = qp[0]; qa[1] = qp[1]; qa[2] = qp[2]; qa[3] = qp[3];
+        uint4 qv[4] = {};
+        if (gq < G) {
+            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (int64_t(b) * Hq + h * GT + g0 + gq) * D + 32 * j);
+            qv[0] = qp[0]; qv[1] = qp[1]; qv[2] = qp[2]; qv[3] = qp[3];
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const uint4 &u = qa[m >> 1];
-            const uint32_t w0 = (m & 1) ? u.z : u.x, w1 = (m & 1) ? u.w : u.y;  // ch 0,1 | 2,3
-            const h2 a = as_h2(w0), bq = as_h2(w1);
-            qop[m] = h4{a[0], bq[0], a[1], bq[1]};
-            sumq += float(a[0]) + float(a[1]) + float(bq[0]) + float(bq[1]);
+        for (int m = 0; m < 4; ++m) {
+            const h2 x0 = as_h2(qv[m].x), x1 = as_h2(qv[m].y), x2 = as_h2(qv[m].z), x3 = as_h2(qv[m].w);
+            qo[m] = h8{x0[0], x1[0], x0[1], x1[1], x2[0], x3[0], x2[1], x3[1]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sumq += float(qo[m][e]);
         }
         sumq += __shfl_xor(sumq, 16, 64);
         sumq += __shfl_xor(sumq, 32, 64);
@@ -189,113 +361,55 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_mfma_kernel(
     WaveState st;
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = f4{0.f, 0.f, 0.f, 0.f};
-    st.m = -__builtin_inff();
-    st.l = st.lz = 0.0f;
+    st.m = M_INIT;
+    st.l = st.lz = st.lp = 0.0f;
 
+    Magic mg{0x64646464u, 0x4C004C00u};
+    asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
     const int32_t *row = rows_l + int64_t(i) * C;
-    if (u0 < u1) {
-        TileRef tr = tile_ref(u0, qH, nh, nl, row, C, pages);
-        Tile cur = load_tile(tr, lane);
-        for (int u = u0; u < u1; ++u) {
-            const TileRef trc = tr;
-            Tile nxt = cur;
-            if (u + 1 < u1) {
-                tr = tile_ref(u + 1, qH, nh, nl, row, C, pages);
-                nxt = load_tile(tr, lane);
-            }
-            // ---- S^T = K * Q^T (codes offset by 1024) -------------------------------------
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+    attend_range<true>(u0, min(u1, qH), nh, row, C, pages, qo, sumq, scale_log2, lane, mg, st);
+    attend_range<false>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, qo, sumq, scale_log2, lane,
+                        mg, st);
+    // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
-            for (int m = 0; m < 8; ++m) acc = mfma16(key_operand(cur, trc.high, m), qop[m], acc);
-            const uint32_t pw[8] = {cur.p0.x, cur.p0.y, cur.p0.z, cur.p0.w,
-                                    cur.p1.x, cur.p1.y, cur.p1.z, cur.p1.w};
-            float L[4], vs[4], vz[4];
-            float tmax = -__builtin_inff();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ks = half_lo(pw[2 * r]), kz = half_hi(pw[2 * r]);
-                vs[r] = half_lo(pw[2 * r + 1]);
-                vz[r] = half_hi(pw[2 * r + 1]);
-                const float dot = acc[r] - MAGIC * sumq;           // q . code
-                const float x = (ks * dot + kz * sumq) * scale_log2;
-                L[r] = (4 * j + r < trc.live) ? x : -__builtin_inff();
-                tmax = fmaxf(tmax, L[r]);
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            // ---- lazy rescale of the running max --------------------------------------------
-            if (__ballot(tmax > st.m + RESCALE_MARGIN) != 0ull) {
-                const float mn = fmaxf(st.m, tmax);
-                const float corr = (st.m == -__builtin_inff()) ? 0.0f : exp2f(st.m - mn);
-                st.l *= corr;
-                st.lz *= corr;
-                st.m = mn;
-                float cr[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * j + r, 64);
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) st.o[n][r] *= cr[r];
-            }
-            // ---- P' = p * scale_v as fp16 hi + lo ---------------------------------------------
-            h4 phi, plo;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = (L[r] == -__builtin_inff()) ? 0.0f : exp2f(L[r] - st.m);
-                const float pv = p * vs[r];
-                const _Float16 hi = _Float16(pv);
-                const _Float16 lo = _Float16(pv - float(hi));
-                phi[r] = hi;
-                plo[r] = lo;
-                st.l += p;
-                st.lz += p * vz[r];
-            }
-            // ---- O += P' * V_codes ----------------------------------------------------------
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const h4 vop = value_operand(cur, trc.high, n);
-                st.o[n] = mfma16(phi, vop, st.o[n]);
-                st.o[n] = mfma16(plo, vop, st.o[n]);
-            }
-            cur = nxt;
+    for (int o = 8; o <= 32; o <<= 1) {
+        if (o == 8 || o == 16 || o == 32) {
+            st.l += __shfl_xor(st.l, o, 64);
+            st.lz += __shfl_xor(st.lz, o, 64);
+            st.lp += __shfl_xor(st.lp, o, 64);
         }
     }
-    // column sums over the four lane groups
-    st.l += __shfl_xor(st.l, 16, 64);
-    st.l += __shfl_xor(st.l, 32, 64);
-    st.lz += __shfl_xor(st.lz, 16, 64);
-    st.lz += __shfl_xor(st.lz, 32, 64);
     // ---- merge the four waves in LDS and write this workgroup's partial --------------------
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_o[wave][4 * n + r][lane] = st.o[n][r];
-    if (lane < 16) {
+    if (lane < 8) {
         s_m[wave][lane] = st.m;
         s_l[wave][lane] = st.l;
         s_lz[wave][lane] = st.lz;
+        s_lp[wave][lane] = st.lp;
     }
     __syncthreads();
+    float *hp = part + int64_t(i) * S * GT * PART_STRIDE;    // this head's partials [s][g]
     for (int e = threadIdx.x; e < G * D; e += 64 * DEC_WAVES) {
         const int gg = e / D, d = e - gg * D;
-        float M = -__builtin_inff();
+        float M = M_INIT;
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, s_m[w][gg]);
         float Ls = 0.0f, O = 0.0f;
-        if (M != -__builtin_inff()) {
-            const int n = d >> 4, dl = d & 15, jj = gg >> 2, r = gg & 3;
+        const int n = d >> 4, dl = d & 15;
 #pragma unroll
-            for (int w = 0; w < DEC_WAVES; ++w) {
-                const float mw = s_m[w][gg];
-                if (mw == -__builtin_inff()) continue;
-                const float f = exp2f(mw - M);
-                const float ow = s_o[w][4 * n + r][16 * jj + dl] + s_lz[w][gg];
-                O += ow * f;
-                Ls += s_l[w][gg] * f;
-            }
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_m[w][gg] - M);
+            // rows gg (tile-A half) and gg + 8 (tile-B half) of the wave's accumulator
+            const int ra = gg, rb = gg + 8;
+            const float oa = s_o[w][4 * n + (ra & 3)][16 * (ra >> 2) + dl];
+            const float ob = s_o[w][4 * n + (rb & 3)][16 * (rb >> 2) + dl];
+            O += (oa + ob - COFF * s_lp[w][gg] + s_lz[w][gg]) * f;
+            Ls += s_l[w][gg] * f;
         }
-        float *pp = part + ((int64_t(b) * Hq + h * G + gg) * S + s) * PART_STRIDE;
+        float *pp = hp + (int64_t(s) * GT + g0 + gg) * PART_STRIDE;
         if (d == 0) {
             pp[0] = M;
             pp[1] = Ls;
@@ -304,28 +418,62 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_mfma_kernel(
     }
 }
 
-// merge the S partials of one (request, query head); m is in log2 units
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float *__restrict__ part,
-                                                             int Hq, int S, void *out,
-                                                             int out_fp32) {
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const float *pp = part + (int64_t(b) * Hq + hq) * S * PART_STRIDE;
-    float M = -__builtin_inff();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * PART_STRIDE]);
-    float L = 0.0f, O = 0.0f;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < S; ++s) {
-            const float ms = pp[s * PART_STRIDE];
-            if (ms == -__builtin_inff()) continue;
-            const float w = exp2f(ms - M);
-            L += pp[s * PART_STRIDE + 1] * w;
-            O += pp[s * PART_STRIDE + 4 + d] * w;
+// merge the S partials of one (request, query head): one wave per query head; lane s < S
+// holds split s's max, the weights are broadcast, each lane accumulates 2 channels
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
+                                                             int Hq, int G, int S, int nqh,
+                                                             void *out, int out_fp32) {
+    const int lane = threadIdx.x & 63;
+    const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);    // b*Hq + hq
+    if (qh >= nqh) return;
+    const int b = qh / Hq, hq = qh - b * Hq;
+    const int h = hq / G, gg = hq - h * G;
+    const int Hkv = Hq / G;
+    const float *hp = part + (int64_t(b) * Hkv + h) * S * G * PART_STRIDE;
+    float r0 = 0.0f, r1 = 0.0f;
+    float M = M_INIT, Ls = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        float ms = M_INIT, ls = 0.0f;
+        if (s < S) {
+            ms = hp[(int64_t(s) * G + gg) * PART_STRIDE];
+            ls = hp[(int64_t(s) * G + gg) * PART_STRIDE + 1];
+        }
+        float cm = ms;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+        const float Mn = fmaxf(M, cm);
+        const float corr = __builtin_amdgcn_exp2f(M - Mn);
+        r0 *= corr;
+        r1 *= corr;
+        Ls *= corr;
+        M = Mn;
+        const float w = __builtin_amdgcn_exp2f(ms - M);
+        float lw = ls * w;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lw += __shfl_xor(lw, o, 64);
+        Ls += lw;
+        const int n = min(64, S - s0);
+        for (int k = 0; k < n; ++k) {
+            const float wk = __shfl(w, k, 64);
+            if (wk == 0.0f) continue;
+            const float2 o2 = *reinterpret_cast<const float2 *>(
+                hp + (int64_t(s0 + k) * G + gg) * PART_STRIDE + 4 + 2 * lane);
+            r0 += o2.x * wk;
+            r1 += o2.y * wk;
         }
     }
-    const float r = L > 0.0f ? O / L : 0.0f;
-    const int64_t idx = (int64_t(b) * Hq + hq) * D + d;
-    if (out_fp32) static_cast<float *>(out)[idx] = r;
-    else static_cast<uint16_t *>(out)[idx] = f2h_rn(r);
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    const int64_t idx = int64_t(qh) * D + 2 * lane;
+    if (out_fp32) {
+        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) =
+            make_float2(Ls > 0.0f ? r0 / Ls : 0.0f, Ls > 0.0f ? r1 / Ls : 0.0f);
+    } else {
+        const uint32_t v = uint32_t(f2h_rn(Ls > 0.0f ? r0 / Ls : 0.0f)) |
+                           (uint32_t(f2h_rn(Ls > 0.0f ? r1 / Ls : 0.0f)) << 16);
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(out) + idx) = v;
+    }
+    (void)inv;
 }
 
 }  // namespace kvc
@@ -354,12 +502,14 @@ extern "C" int kvc_paged_decode_attention(const kvc_geom *g, int32_t layer, cons
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3(L.splits * nheads), dim3(64 * DEC_WAVES), 0, s,
+    const int ngp = (G + 7) / 8;
+    hipLaunchKernelGGL(decode_mfma_kernel, dim3(L.splits * nheads * ngp), dim3(64 * DEC_WAVES), 0, s,
                        q, softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
                        part);
     rc = launch_check("kvc_paged_decode_attention/main");
     if (rc) return rc;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(g->num_q_heads, B), dim3(128), 0, s, part,
-                       g->num_q_heads, L.splits, out, out_is_fp32);
+    const int nqh = B * g->num_q_heads;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((nqh + 3) / 4), dim3(256), 0, s, part,
+                       g->num_q_heads, G, L.splits, nqh, out, out_is_fp32);
     return launch_check("kvc_paged_decode_attention/combine");
 }

@@ -70,7 +70,7 @@ struct DecodeWs {
     size_t part, bytes;
     explicit DecodeWs(const kvc_geom *g) {
         splits = decode_splits(g);
-        part = 0;
+        part = 0;          // float [B][Hkv][S][G][PART_STRIDE]
         bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
                          splits);
     }
