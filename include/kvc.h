@@ -58,7 +58,8 @@ enum {
     KVC_DEV_SHRINK = 4,         /* a head not marked changed would lose pages               */
     KVC_DEV_COUNT_MISMATCH = 8, /* tier array disagrees with the pool's per-head counts     */
     KVC_DEV_SEQLEN = 16,        /* a request is longer than the max_seqlen argument         */
-    KVC_DEV_INTERNAL = 32       /* a scan's look-back gave up waiting (a library bug)       */
+    KVC_DEV_INTERNAL = 32,      /* a scan's look-back gave up waiting (a library bug)       */
+    KVC_DEV_BAD_TIER = 64       /* re-tiering: a tier rose, or a fresh token had no fp16 row */
 };
 
 /* tier codes */
@@ -98,7 +99,7 @@ typedef struct {
 } kvc_pool;
 
 /* Operation ids for kvc_workspace_bytes */
-enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3 };
+enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4 };
 
 /* Version string of the library. */
 const char *kvc_version(void);
@@ -125,8 +126,9 @@ int kvc_pool_init(const kvc_geom *geom, const kvc_pool *pool, kvc_stream_t strea
  *   LOW if score >= fl32(alpha_l/N), else PRUNE; HIGH when t >= N - window; with
  *   prev_tier (uint8 [T][Hkv], or NULL), tier = min(tier, prev) wherever prev != FRESH.
  *   Outputs: tier uint8 [T][Hkv]; new_count int32 [B][Hkv][2] = (#HIGH, #LOW);
- *   changed uint8 [B][Hkv] = 1 where some already-tiered token dropped a tier (may be NULL
- *   when prev_tier is NULL).  max_seqlen bounds every N_b (else KVC_DEV_SEQLEN is set in
+ *   changed uint8 [B][Hkv] = 1 where some already-tiered token dropped a tier or a FRESH
+ *   token was kept, i.e. where the head's pages must be rebuilt (may be NULL when prev_tier
+ *   is NULL).  max_seqlen bounds every N_b (else KVC_DEV_SEQLEN is set in
  *   *dev_status and the request is skipped; dev_status may be NULL).
  * Errors: KVC_E_NULL, KVC_E_SHAPE (Hq % Hkv, window < 0, total_tokens < 0). */
 int kvc_score_tokens(const kvc_geom *geom, const float *acc_sum, const int32_t *cu_seqlens,
@@ -154,24 +156,47 @@ int kvc_compact_pages(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                       int32_t *old_rows_out, int32_t *old_count_out, void *workspace,
                       size_t workspace_bytes, kvc_stream_t stream);
 
-/* Quantize and place one layer's kept tokens into the pages compact_pages assigned (prompt
- * mode).  HIGH tokens become K8V4, LOW tokens K4V2 (DiffKV review page, "Core claim"):
- * per token and head, asymmetric min/max codes over the 128 channels, scale and zero
- * computed in float32 with round-to-nearest-even and stored as fp16.  Within a head and a
- * tier, tokens take slots in ascending position order; every page of the head is written
- * whole (empty slots zeroed, position -1).
+/* Quantize and place one layer's kept tokens into the pages compact_pages assigned.  HIGH
+ * tokens are K8V4, LOW tokens K4V2 (DiffKV review page, "Core claim"): per token and head,
+ * asymmetric min/max codes over the 128 channels, scale and zero computed in float32 with
+ * round-to-nearest-even and stored as fp16.  Within a head and a tier, tokens take slots in
+ * ascending position order; every page of a written head is written whole (empty slots
+ * zeroed, position -1).
  *   k, v       fp16 [T][Hkv][128] (T = cu_seqlens[B]), 16-byte aligned
  *   tier       uint8 [T][Hkv] (from kvc_score_tokens)
- *   prev_tier, changed, old_rows, old_count: must be NULL (re-tier rounds: not yet)
+ * Prompt mode (prev_tier, changed, old_rows, old_count all NULL): every head is written, all
+ * tokens quantized from k, v.
+ * Re-tier mode (all four given; after kvc_compact_pages with the same `changed`): only heads
+ * with changed[b][h] != 0 are written.  A token whose tier is unchanged keeps its codes and
+ * parameters bit for bit (copied from its old page, found through old_rows / old_count from
+ * kvc_compact_pages); a HIGH token demoted to LOW is re-quantized from the fp16 rounding of its
+ * K8V4 reconstruction (referee major comment 3: demotion is irreversible); a FRESH token is
+ * quantized from k, v (which may be NULL when no token is FRESH).  A token whose tier rose,
+ * or a FRESH one without k/v, is left zero and sets KVC_DEV_BAD_TIER.
  *   A head whose tier counts differ from the pool's counts is skipped and
  *   KVC_DEV_COUNT_MISMATCH is set.
- * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE, KVC_E_UNSUPPORTED. */
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE, KVC_E_UNSUPPORTED (only some
+ * of the four re-tier arguments given). */
 int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                            const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
                            int64_t total_tokens, int32_t max_seqlen, const uint8_t *tier,
                            const uint8_t *prev_tier, const uint8_t *changed,
                            const int32_t *old_rows, const int32_t *old_count,
                            void *workspace, size_t workspace_bytes, kvc_stream_t stream);
+
+/* Append one freshly generated token per (request, KV head) to layer `layer` during
+ * decoding: the token enters its head's HIGH tier (DiffKV review page, free-parameter ledger:
+ * the recent window is always high precision) as K8V4 codes in the next HIGH slot; a head
+ * whose last HIGH page is full first receives one page from the circular free list in an
+ * allocation round like kvc_compact_pages (no head is rebuilt).  The slot's position field
+ * is positions[b].  On pool exhaustion or row overflow the round sets its status bit and no
+ * token is written.
+ *   k_new, v_new  fp16 [B][Hkv][128], 16-byte aligned;  positions int32 [B]
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_APPEND, 0) bytes, 256-B aligned
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE, KVC_E_WORKSPACE. */
+int kvc_append_tokens(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                      const uint16_t *k_new, const uint16_t *v_new, const int32_t *positions,
+                      void *workspace, size_t workspace_bytes, kvc_stream_t stream);
 
 /* Decode attention of one new query per request over its KV head's live tokens (HIGH
  * slots < n_high, LOW slots < n_low), keys and values reconstructed on the fly as

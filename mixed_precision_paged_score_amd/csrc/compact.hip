@@ -225,6 +225,39 @@ __global__ __launch_bounds__(256) void compact_commit_kernel(
 
 using namespace kvc;
 
+namespace kvc {
+
+// the three launches of one allocation round (arguments already validated)
+int launch_compact(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                   const int32_t *new_count, const uint8_t *changed, int32_t *old_rows_out,
+                   int32_t *old_count_out, void *ws, hipStream_t s) {
+    CompactWs L(g);
+    char *w = static_cast<char *>(ws);
+    CompactHdr *hdr = reinterpret_cast<CompactHdr *>(w + L.hdr);
+    uint64_t *st = reinterpret_cast<uint64_t *>(w + L.st);
+    int32_t *off = reinterpret_cast<int32_t *>(w + L.off);
+    int32_t *foff = reinterpret_cast<int32_t *>(w + L.foff);
+    const int C = g->row_capacity;
+    int32_t *rows_l = p->page_table + int64_t(layer) * L.nheads * C;
+    int32_t *count_l = p->count + int64_t(layer) * L.nheads * 2;
+    hipLaunchKernelGGL(compact_zero_kernel, dim3((L.ntiles + 255) / 256), dim3(256), 0, s, hdr,
+                       st, L.ntiles);
+    int rc = launch_check("compact/zero");
+    if (rc) return rc;
+    hipLaunchKernelGGL(compact_scan_kernel, dim3(L.ntiles), dim3(SCAN_TILE), 0, s, count_l,
+                       new_count, changed, L.nheads, C, p->dev_status, p->ring_ctr, hdr, st,
+                       off, foff);
+    rc = launch_check("compact/scan");
+    if (rc) return rc;
+    hipLaunchKernelGGL(compact_commit_kernel, dim3(L.nheads), dim3(256), 0, s, rows_l, count_l,
+                       new_count, changed, C, g->num_pages, layer * L.nheads, p->dev_status,
+                       p->ring_ctr, p->free_ring, p->owner, hdr, off, foff, old_rows_out,
+                       old_count_out);
+    return launch_check("compact/commit");
+}
+
+}  // namespace kvc
+
 extern "C" int kvc_compact_pages(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                                  const int32_t *new_count, const uint8_t *changed,
                                  int32_t *old_rows_out, int32_t *old_count_out, void *ws,
@@ -240,27 +273,6 @@ extern "C" int kvc_compact_pages(const kvc_geom *g, int32_t layer, const kvc_poo
     if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
     // sums of pages per call must fit 31 bits
     if (int64_t(L.nheads) * g->row_capacity >= (int64_t(1) << 31)) return KVC_E_SHAPE;
-    char *w = static_cast<char *>(ws);
-    CompactHdr *hdr = reinterpret_cast<CompactHdr *>(w + L.hdr);
-    uint64_t *st = reinterpret_cast<uint64_t *>(w + L.st);
-    int32_t *off = reinterpret_cast<int32_t *>(w + L.off);
-    int32_t *foff = reinterpret_cast<int32_t *>(w + L.foff);
-    const int C = g->row_capacity;
-    int32_t *rows_l = p->page_table + int64_t(layer) * L.nheads * C;
-    int32_t *count_l = p->count + int64_t(layer) * L.nheads * 2;
-    hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(compact_zero_kernel, dim3((L.ntiles + 255) / 256), dim3(256), 0, s, hdr,
-                       st, L.ntiles);
-    rc = launch_check("kvc_compact_pages/zero");
-    if (rc) return rc;
-    hipLaunchKernelGGL(compact_scan_kernel, dim3(L.ntiles), dim3(SCAN_TILE), 0, s, count_l,
-                       new_count, changed, L.nheads, C, p->dev_status, p->ring_ctr, hdr, st,
-                       off, foff);
-    rc = launch_check("kvc_compact_pages/scan");
-    if (rc) return rc;
-    hipLaunchKernelGGL(compact_commit_kernel, dim3(L.nheads), dim3(256), 0, s, rows_l, count_l,
-                       new_count, changed, C, g->num_pages, layer * L.nheads, p->dev_status,
-                       p->ring_ctr, p->free_ring, p->owner, hdr, off, foff, old_rows_out,
-                       old_count_out);
-    return launch_check("kvc_compact_pages/commit");
+    return launch_compact(g, layer, p, new_count, changed, old_rows_out, old_count_out, ws,
+                          (hipStream_t)stream);
 }

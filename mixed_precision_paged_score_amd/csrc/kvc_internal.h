@@ -23,6 +23,11 @@ constexpr int PRUNE = KVC_PRUNE, LOW = KVC_LOW, HIGH = KVC_HIGH, FRESH = KVC_FRE
 
 void set_error(const char *what, hipError_t e);
 
+// one allocation round (compact.hip); arguments already validated
+int launch_compact(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                   const int32_t *new_count, const uint8_t *changed, int32_t *old_rows_out,
+                   int32_t *old_count_out, void *ws, hipStream_t s);
+
 inline int launch_check(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

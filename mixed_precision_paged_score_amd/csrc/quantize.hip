@@ -19,47 +19,93 @@
 //                    operand order, parameters and positions; empty slots are zero / -1.
 #include "kvc_internal.h"
 #include "workspace.h"
+#include "quant_row.h"
 
 #pragma clang fp contract(off)
 
 namespace kvc {
 
+// grid (ntq, B): per 256-token tile, #HIGH and #LOW per KV head of `tier` (and of `prev`)
 __global__ __launch_bounds__(256) void quant_count_kernel(
-    const uint8_t *__restrict__ tier, const int32_t *__restrict__ cu, int Hkv, int ntq,
-    int max_seqlen, const int32_t *status, int32_t *__restrict__ tile_cnt,
+    const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
+    const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen, const int32_t *status,
+    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ tile_cnt2,
     int32_t *__restrict__ entry, int nheads) {
-    __shared__ int s_cnt[512];
+    __shared__ int s_cnt[2][512];
     const int b = blockIdx.y, tq = blockIdx.x;
     if (b == 0 && tq == 0 && threadIdx.x == 0) entry[nheads] = *status;
     const int lo = cu[b], N = cu[b + 1] - lo;
     const int t0 = tq * QTILE;
     if (N > max_seqlen || t0 >= N) return;
-    for (int i = threadIdx.x; i < 2 * Hkv; i += blockDim.x) s_cnt[i] = 0;
+    for (int i = threadIdx.x; i < 2 * Hkv; i += blockDim.x) s_cnt[0][i] = s_cnt[1][i] = 0;
     __syncthreads();
     const int nt = min(QTILE, N - t0);
-    const uint8_t *tb = tier + (int64_t(lo) + t0) * Hkv;
+    const int64_t base = (int64_t(lo) + t0) * Hkv;
     for (int idx = threadIdx.x; idx < nt * Hkv; idx += blockDim.x) {
-        const int x = tb[idx];
         const int h = idx % Hkv;
-        if (x == HIGH) atomicAdd(&s_cnt[2 * h], 1);
-        else if (x == LOW) atomicAdd(&s_cnt[2 * h + 1], 1);
+        const int x = tier[base + idx];
+        if (x == HIGH) atomicAdd(&s_cnt[0][2 * h], 1);
+        else if (x == LOW) atomicAdd(&s_cnt[0][2 * h + 1], 1);
+        if (prev) {
+            const int y = prev[base + idx];
+            if (y == HIGH) atomicAdd(&s_cnt[1][2 * h], 1);
+            else if (y == LOW) atomicAdd(&s_cnt[1][2 * h + 1], 1);
+        }
     }
     __syncthreads();
-    int32_t *out = tile_cnt + (int64_t(b) * ntq + tq) * Hkv * 2;
-    for (int i = threadIdx.x; i < 2 * Hkv; i += blockDim.x) out[i] = s_cnt[i];
+    const int64_t o = (int64_t(b) * ntq + tq) * Hkv * 2;
+    for (int i = threadIdx.x; i < 2 * Hkv; i += blockDim.x) {
+        tile_cnt[o + i] = s_cnt[0][i];
+        if (prev) tile_cnt2[o + i] = s_cnt[1][i];
+    }
 }
 
-// grid (Hkv, B): exclusive scan over the request's tiles of the (HIGH, LOW) columns of one
-// head.  Thread (k, c) sums chunk c of column k; chunk sums are scanned serially in LDS.
+// exclusive scan over a request's tiles of the (HIGH, LOW) columns of one head; returns the
+// totals.  Thread (k, c) sums chunk c of column k; chunk sums are scanned serially in LDS.
+__device__ void scan_columns(const int32_t *__restrict__ cnt, int32_t *__restrict__ out,
+                             int64_t col0, int Hkv, int nt, int (&s_sum)[2][128], int (&tot)[2]) {
+    const int k = threadIdx.x >> 7, c = threadIdx.x & 127;
+    const int cs = (nt + 127) / 128;
+    const int j0 = c * cs, j1 = min(nt, j0 + cs);
+    const int64_t col = col0 + k;
+    int sum = 0;
+    for (int j = j0; j < j1; ++j) sum += cnt[col + int64_t(j) * Hkv * 2];
+    s_sum[k][c] = sum;
+    __syncthreads();
+    if (threadIdx.x < 2) {
+        int run = 0;
+        for (int q = 0; q < 128; ++q) {
+            const int v = s_sum[threadIdx.x][q];
+            s_sum[threadIdx.x][q] = run;
+            run += v;
+        }
+        tot[threadIdx.x] = run;
+    }
+    __syncthreads();
+    int run = s_sum[k][c];
+    for (int j = j0; j < j1; ++j) {
+        const int v = cnt[col + int64_t(j) * Hkv * 2];
+        out[col + int64_t(j) * Hkv * 2] = run;
+        run += v;
+    }
+    __syncthreads();
+}
+
+// grid (Hkv, B).  ok[i] = 1 when head i's pages are to be written: its tier counts match the
+// pool's (and, re-tiering, its previous counts match the snapshot and the head is rebuilt).
 __global__ __launch_bounds__(256) void quant_scan_kernel(
-    const int32_t *__restrict__ tile_cnt, const int32_t *__restrict__ cu, int Hkv, int ntq,
-    int max_seqlen, const int32_t *__restrict__ count_l, int32_t *__restrict__ tile_base,
-    int32_t *__restrict__ ok, int32_t *status) {
+    const int32_t *__restrict__ tile_cnt, const int32_t *__restrict__ tile_cnt2,
+    const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
+    const int32_t *__restrict__ count_l, const uint8_t *__restrict__ changed,
+    const int32_t *__restrict__ old_count, int32_t *__restrict__ tile_base,
+    int32_t *__restrict__ tile_base2, int32_t *__restrict__ ok, int32_t *status) {
     __shared__ int s_sum[2][128];
-    __shared__ int s_tot[2];
+    __shared__ int s_tot[2], s_tot2[2];
     const int h = blockIdx.x, b = blockIdx.y;
     const int i = b * Hkv + h;
-    if (ok[gridDim.x * gridDim.y] != 0) {      // pool status was set on entry: no-op
+    const bool rebuild = tile_cnt2 != nullptr;
+    if (ok[gridDim.x * gridDim.y] != 0 || (rebuild && !changed[i])) {
+        // pool status set on entry (no-op), or a head that keeps its pages
         if (threadIdx.x == 0) ok[i] = 0;
         return;
     }
@@ -72,42 +118,26 @@ __global__ __launch_bounds__(256) void quant_scan_kernel(
         return;
     }
     const int nt = (N + QTILE - 1) / QTILE;
-    const int k = threadIdx.x >> 7, c = threadIdx.x & 127;
-    const int cs = (nt + 127) / 128;
-    const int j0 = c * cs, j1 = min(nt, j0 + cs);
-    const int64_t col = (int64_t(b) * ntq) * Hkv * 2 + h * 2 + k;
-    int sum = 0;
-    for (int j = j0; j < j1; ++j) sum += tile_cnt[col + int64_t(j) * Hkv * 2];
-    s_sum[k][c] = sum;
-    __syncthreads();
-    if (threadIdx.x < 2) {
-        int run = 0;
-        for (int q = 0; q < 128; ++q) {
-            const int v = s_sum[threadIdx.x][q];
-            s_sum[threadIdx.x][q] = run;
-            run += v;
-        }
-        s_tot[threadIdx.x] = run;
-    }
-    __syncthreads();
-    int run = s_sum[k][c];
-    for (int j = j0; j < j1; ++j) {
-        const int v = tile_cnt[col + int64_t(j) * Hkv * 2];
-        tile_base[col + int64_t(j) * Hkv * 2] = run;
-        run += v;
-    }
+    const int64_t col0 = (int64_t(b) * ntq) * Hkv * 2 + h * 2;
+    scan_columns(tile_cnt, tile_base, col0, Hkv, nt, s_sum, s_tot);
+    if (rebuild) scan_columns(tile_cnt2, tile_base2, col0, Hkv, nt, s_sum, s_tot2);
     if (threadIdx.x == 0) {
-        const int good = s_tot[0] == count_l[2 * i] && s_tot[1] == count_l[2 * i + 1];
+        bool good = s_tot[0] == count_l[2 * i] && s_tot[1] == count_l[2 * i + 1];
+        if (rebuild) good = good && s_tot2[0] == old_count[2 * i] && s_tot2[1] == old_count[2 * i + 1];
         ok[i] = good;
         if (!good) atomicOr(status, KVC_DEV_COUNT_MISMATCH);
     }
 }
 
-// grid (ntq, B), 4 waves: wave w ranks heads w, w+4, ... over the tile's tokens
+// grid (ntq, B), 4 waves: wave w ranks heads w, w+4, ... over the tile's tokens with 64-lane
+// ballots.  poslist: HIGH ranks from the front, LOW ranks from the back (positions); oldrank
+// (re-tiering): the rank of each position among its previous tier.
 __global__ __launch_bounds__(256) void quant_select_kernel(
-    const uint8_t *__restrict__ tier, const int32_t *__restrict__ cu, int Hkv, int ntq,
-    int max_seqlen, const int32_t *__restrict__ tile_base, const int32_t *__restrict__ ok,
-    int32_t *__restrict__ poslist) {
+    const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
+    const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
+    const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_base2,
+    const int32_t *__restrict__ ok, int32_t *__restrict__ poslist,
+    int32_t *__restrict__ oldrank) {
     const int b = blockIdx.y, tq = blockIdx.x;
     const int lo = cu[b], N = cu[b + 1] - lo;
     const int t0 = tq * QTILE;
@@ -118,87 +148,96 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
     for (int h = wave; h < Hkv; h += 4) {
         const int i = b * Hkv + h;
         if (!ok[i]) continue;
-        const int32_t *base = tile_base + ((int64_t(b) * ntq + tq) * Hkv + h) * 2;
-        int rH = base[0], rL = base[1];
+        const int64_t tb = ((int64_t(b) * ntq + tq) * Hkv + h) * 2;
+        int rH = tile_base[tb], rL = tile_base[tb + 1];
+        int oH = prev ? tile_base2[tb] : 0, oL = prev ? tile_base2[tb + 1] : 0;
         int32_t *pl = poslist + int64_t(i) * max_seqlen;
+        int32_t *orank = prev ? oldrank + int64_t(i) * max_seqlen : nullptr;
         for (int c0 = 0; c0 < nt; c0 += 64) {
             const int tt = c0 + lane;
-            const int x = tt < nt ? tier[(int64_t(lo) + t0 + tt) * Hkv + h] : PRUNE;
+            const int64_t r = (int64_t(lo) + t0 + tt) * Hkv + h;
+            const int x = tt < nt ? tier[r] : PRUNE;
             const uint64_t mH = __ballot(x == HIGH);
             const uint64_t mL = __ballot(x == LOW);
             if (x == HIGH) pl[rH + __popcll(mH & lt)] = t0 + tt;
             else if (x == LOW) pl[max_seqlen - 1 - (rL + __popcll(mL & lt))] = t0 + tt;
             rH += __popcll(mH);
             rL += __popcll(mL);
+            if (prev) {
+                const int y = tt < nt ? prev[r] : PRUNE;
+                const uint64_t nH = __ballot(y == HIGH);
+                const uint64_t nL = __ballot(y == LOW);
+                if (y == HIGH) orank[t0 + tt] = oH + __popcll(nH & lt);
+                else if (y == LOW) orank[t0 + tt] = oL + __popcll(nL & lt);
+                oH += __popcll(nH);
+                oL += __popcll(nL);
+            }
         }
-    }
-}
-
-// ---- the quantizer (one 128-channel row per 16-lane group, 8 channels per lane) --------
-struct RowQ {
-    float z, inv, lq;
-    uint16_t s16, z16;
-};
-
-__device__ __forceinline__ RowQ row_params(const float (&x)[8], float lq) {
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-        mn = fminf(mn, x[e]);
-        mx = fmaxf(mx, x[e]);
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-    }
-    RowQ q;
-    const float rng = mx - mn;
-    const float s32 = rng / lq;                   // correctly rounded float32 division
-    uint16_t s16 = f2h_rn(s32);
-    if (s16 == 0 && mx > mn) s16 = 1;             // smallest fp16 subnormal, 2^-24
-    const float sf = h2f(s16);
-    q.inv = sf > 0.0f ? 1.0f / sf : 0.0f;
-    q.z = mn + 0.0f;                              // a -0 minimum is stored as +0
-    q.z16 = f2h_rn(q.z);
-    q.s16 = s16;
-    q.lq = lq;
-    return q;
-}
-
-__device__ __forceinline__ uint32_t code_of(float x, const RowQ &q) {
-    const float d = x - q.z;
-    const float y = d * q.inv;
-    return uint32_t(fminf(rintf(y), q.lq));
-}
-
-__device__ __forceinline__ void load_row8(const uint16_t *src, bool live, float (&x)[8]) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (live) u = *reinterpret_cast<const uint4 *>(src);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[2 * e] = h2f(uint16_t(w[e] & 0xffffu));
-        x[2 * e + 1] = h2f(uint16_t(w[e] >> 16));
     }
 }
 
 constexpr int QP_WAVES = 4;
 constexpr int VST_BYTES = LS * D;     // per-wave staging of value codes (LOW page size)
 
-// grid (ceil(C / 4), B*Hkv): wave w of block x handles page index 4x + w of head y
+__device__ __forceinline__ int k_nib(int e) { return (e & 1) + 2 * (e >> 2) + 4 * ((e >> 1) & 1); }
+
+// codes of the lane's 8 channels 8c..8c+7 of slot `so` in an old page of tier `t`
+__device__ __forceinline__ void old_codes(const uint8_t *pg, int t, int so, int c, uint32_t (&kc)[8],
+                                          uint32_t (&vc)[8], uint32_t &kpar, uint32_t &vpar) {
+    if (t == HIGH) {
+        const uint2 kw = *reinterpret_cast<const uint2 *>(pg + K_OFF + so * 128 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kc[e] = (kw.x >> (8 * e)) & 255u;
+            kc[4 + e] = (kw.y >> (8 * e)) & 255u;
+        }
+    } else {
+        const uint32_t kw = *reinterpret_cast<const uint32_t *>(pg + K_OFF + so * 64 + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kc[e] = (kw >> (4 * k_nib(e))) & 15u;
+    }
+    const int n = c >> 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int dl = 8 * (c & 1) + e;
+        if (t == HIGH) {
+            const int j = so >> 2, r = so & 3;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(pg + V_OFF + 16 * (16 * j + dl) + 4 * (n >> 1));
+            vc[e] = (w >> (4 * (2 * (n & 1) + (r >> 1) + 4 * (r & 1)))) & 15u;
+        } else {
+            const int f = so >> 4, j = (so & 15) >> 2, r = so & 3;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(pg + V_OFF + 16 * (16 * j + dl) + 4 * (2 * f + (n >> 2)));
+            vc[e] = (w >> (2 * (2 * (n & 3) + (r >> 1) + 8 * (r & 1)))) & 3u;
+        }
+    }
+    const uint2 par = *reinterpret_cast<const uint2 *>(pg + PARAM_OFF + 8 * so);
+    kpar = par.x;
+    vpar = par.y;
+}
+
+// fp16 rounding of a code's reconstruction code*scale + zero (one float32 rounding, then RNE)
+__device__ __forceinline__ float recon16(uint32_t code, uint32_t par) {
+    const float r = fmaf(float(code), h2f(uint16_t(par & 0xffffu)), h2f(uint16_t(par >> 16)));
+    return h2f(f2h_rn(r));
+}
+
+// grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
+// REBUILD: each token's codes come from the fp16 rows (previous tier FRESH), are copied from
+// its old page (tier unchanged), or are re-quantized from its old K8V4 codes (HIGH -> LOW).
+template <bool REBUILD>
 __global__ __launch_bounds__(256) void quant_pages_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
     const int32_t *__restrict__ ok, const int32_t *__restrict__ poslist,
-    uint8_t *__restrict__ pages) {
+    const uint8_t *__restrict__ prev, const int32_t *__restrict__ old_rows,
+    const int32_t *__restrict__ oldrank, uint8_t *__restrict__ pages, int32_t *status) {
     __shared__ uint8_t s_v[QP_WAVES][VST_BYTES];
     __shared__ uint16_t s_par[QP_WAVES][LS][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = blockIdx.y;
     const int nheads = gridDim.y;
-    if (ok[nheads] != 0 || !ok[i]) return;     // pool failed earlier, or head mismatched
+    if (ok[nheads] != 0 || !ok[i]) return;     // pool failed earlier, head mismatched or kept
     const int b = i / Hkv, h = i - b * Hkv;
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     const int qH = ceil_div(nh, HS), qL = ceil_div(nl, LS);
@@ -219,56 +258,105 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     } else {
         return;
     }
+    const int T = high ? HIGH : LOW;
     uint8_t *pg = pages + int64_t(page) * PAGE;
     const int32_t *pl = poslist + int64_t(i) * max_seqlen;
     const int lo = cu[b];
     const int rg = lane >> 4, c = lane & 15;
     const int nslots = high ? HS : LS;
     uint8_t *sv = s_v[wave];
-    // positions of this page's tokens: HIGH ranks from the front, LOW ranks from the back
     for (int pass = 0; pass < nslots / 4; ++pass) {
         const int s = pass * 4 + rg;
         const bool live = s < m;
         int pos = 0;
         if (live) pos = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
-        const int64_t roff = ((int64_t(lo) + pos) * Hkv + h) * D + 8 * c;
-        // key row
-        float x[8];
-        load_row8(K + roff, live, x);
-        RowQ q = row_params(x, high ? 255.0f : 15.0f);
-        if (high) {
-            uint32_t w0 = 0, w1 = 0;
+        const int64_t grow = int64_t(lo) + pos;
+        int src = FRESH;
+        bool valid = live;
+        if (REBUILD && live) {
+            src = prev[grow * Hkv + h];
+            // a tier never rises, and a fresh token needs its fp16 rows
+            valid = src == T || (src == HIGH && T == LOW) || (src == FRESH && K != nullptr);
+            if (!valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
+        }
+        uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;   // key code words, value code bytes
+        uint16_t ks = 0, kz = 0, vs = 0, vz = 0;
+        if (!valid) {
+            // leave the slot zero
+        } else if (src == T) {
+            // unchanged tier: copy the token's codes and parameters from its old page
+            const int so = oldrank[int64_t(i) * max_seqlen + pos];
+            const int opage = T == HIGH ? old_rows[int64_t(i) * C + (so >> 4)]
+                                        : old_rows[int64_t(i) * C + C - 1 - (so >> 5)];
+            const int sop = T == HIGH ? (so & 15) : (so & 31);
+            uint32_t kc[8], vc[8], kp, vp;
+            old_codes(pages + int64_t(opage) * PAGE, T, sop, c, kc, vc, kp, vp);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w0 |= code_of(x[e], q) << (8 * e);
+            for (int e = 0; e < 4; ++e) {
+                vw0 |= vc[e] << (8 * e);
+                vw1 |= vc[4 + e] << (8 * e);
+            }
+            if (high) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w1 |= code_of(x[4 + e], q) << (8 * e);
-            if (!live) w0 = w1 = 0;
-            *reinterpret_cast<uint2 *>(pg + K_OFF + s * 128 + 8 * c) = make_uint2(w0, w1);
+                for (int e = 0; e < 4; ++e) {
+                    kw0 |= kc[e] << (8 * e);
+                    kw1 |= kc[4 + e] << (8 * e);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kw0 |= kc[e] << (4 * k_nib(e));
+            }
+            ks = uint16_t(kp & 0xffffu);
+            kz = uint16_t(kp >> 16);
+            vs = uint16_t(vp & 0xffffu);
+            vz = uint16_t(vp >> 16);
         } else {
-            uint32_t w = 0;
+            // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
+            float xk[8], xv[8];
+            if (!REBUILD || src == FRESH) {
+                const int64_t roff = (grow * Hkv + h) * D + 8 * c;
+                load_row8(K + roff, live, xk);
+                load_row8(V + roff, live, xv);
+            } else {
+                const int so = oldrank[int64_t(i) * max_seqlen + pos];   // old HIGH rank
+                const int opage = old_rows[int64_t(i) * C + (so >> 4)];
+                uint32_t kc[8], vc[8], kp, vp;
+                old_codes(pages + int64_t(opage) * PAGE, HIGH, so & 15, c, kc, vc, kp, vp);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                w |= code_of(x[e], q) << (4 * ((e & 1) + 2 * (e >> 2) + 4 * ((e >> 1) & 1)));
-            if (!live) w = 0;
-            *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = w;
+                for (int e = 0; e < 8; ++e) {
+                    xk[e] = recon16(kc[e], kp);
+                    xv[e] = recon16(vc[e], vp);
+                }
+            }
+            const RowQ qk = row_params(xk, high ? 255.0f : 15.0f);
+            if (high) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kw0 |= code_of(xk[e], qk) << (8 * e);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kw1 |= code_of(xk[4 + e], qk) << (8 * e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kw0 |= code_of(xk[e], qk) << (4 * k_nib(e));
+            }
+            const RowQ qv = row_params(xv, high ? 15.0f : 3.0f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vw0 |= code_of(xv[e], qv) << (8 * e);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vw1 |= code_of(xv[4 + e], qv) << (8 * e);
+            ks = qk.s16;
+            kz = qk.z16;
+            vs = qv.s16;
+            vz = qv.z16;
         }
+        if (!live) kw0 = kw1 = vw0 = vw1 = 0;
+        if (high) *reinterpret_cast<uint2 *>(pg + K_OFF + s * 128 + 8 * c) = make_uint2(kw0, kw1);
+        else *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = kw0;
+        *reinterpret_cast<uint2 *>(sv + s * D + 8 * c) = make_uint2(vw0, vw1);
         if (c == 0) {
-            s_par[wave][s][0] = live ? q.s16 : 0;
-            s_par[wave][s][1] = live ? q.z16 : 0;
-        }
-        // value row: codes staged in LDS as bytes [slot][channel]
-        load_row8(V + roff, live, x);
-        q = row_params(x, high ? 15.0f : 3.0f);
-        uint32_t v0 = 0, v1 = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v0 |= code_of(x[e], q) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v1 |= code_of(x[4 + e], q) << (8 * e);
-        if (!live) v0 = v1 = 0;
-        *reinterpret_cast<uint2 *>(sv + s * D + 8 * c) = make_uint2(v0, v1);
-        if (c == 0) {
-            s_par[wave][s][2] = live ? q.s16 : 0;
-            s_par[wave][s][3] = live ? q.z16 : 0;
+            s_par[wave][s][0] = live ? ks : 0;
+            s_par[wave][s][1] = live ? kz : 0;
+            s_par[wave][s][2] = live ? vs : 0;
+            s_par[wave][s][3] = live ? vz : 0;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -316,7 +404,6 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * s) = make_uint2(a, bb);
         *reinterpret_cast<int32_t *>(pg + POS_OFF + 4 * s) = pos;
     }
-    // a HIGH page's key area beyond slot 15 does not exist; its value area is complete
 }
 
 }  // namespace kvc
@@ -334,9 +421,12 @@ extern "C" int kvc_quantize_and_place(const kvc_geom *g, int32_t layer, const kv
     if (rc) return rc;
     rc = check_pool(p);
     if (rc) return rc;
-    if (prev_tier || changed || old_rows || old_count) return KVC_E_UNSUPPORTED;
+    const bool rebuild = prev_tier != nullptr;
+    if (rebuild && (!changed || !old_rows || !old_count)) return KVC_E_NULL;
+    if (!rebuild && (changed || old_rows || old_count)) return KVC_E_UNSUPPORTED;
     if (!cu) return KVC_E_NULL;
-    if (total_tokens > 0 && (!k || !v || !tier)) return KVC_E_NULL;
+    if (total_tokens > 0 && !tier) return KVC_E_NULL;
+    if (!rebuild && total_tokens > 0 && (!k || !v)) return KVC_E_NULL;
     if (layer < 0 || layer >= g->num_layers || max_seqlen < 0 || total_tokens < 0)
         return KVC_E_SHAPE;
     if (g->num_kv_heads > 256) return KVC_E_SHAPE;
@@ -347,27 +437,37 @@ extern "C" int kvc_quantize_and_place(const kvc_geom *g, int32_t layer, const kv
     char *w = static_cast<char *>(ws);
     int32_t *tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     int32_t *tile_base = reinterpret_cast<int32_t *>(w + L.tile_base);
+    int32_t *tile_cnt2 = rebuild ? reinterpret_cast<int32_t *>(w + L.tile_cnt2) : nullptr;
+    int32_t *tile_base2 = rebuild ? reinterpret_cast<int32_t *>(w + L.tile_base2) : nullptr;
     int32_t *ok = reinterpret_cast<int32_t *>(w + L.ok);
     int32_t *poslist = reinterpret_cast<int32_t *>(w + L.poslist);
+    int32_t *oldrank = rebuild ? reinterpret_cast<int32_t *>(w + L.oldrank) : nullptr;
     const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
     const int nheads = B * Hkv;
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(quant_count_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, cu, Hkv,
-                       L.ntq, max_seqlen, p->dev_status, tile_cnt, ok, nheads);
+    hipLaunchKernelGGL(quant_count_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
+                       Hkv, L.ntq, max_seqlen, p->dev_status, tile_cnt, tile_cnt2, ok, nheads);
     rc = launch_check("kvc_quantize_and_place/count");
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_scan_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, cu, Hkv,
-                       L.ntq, max_seqlen, count_l, tile_base, ok, p->dev_status);
+    hipLaunchKernelGGL(quant_scan_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, tile_cnt2, cu,
+                       Hkv, L.ntq, max_seqlen, count_l, changed, old_count, tile_base,
+                       tile_base2, ok, p->dev_status);
     rc = launch_check("kvc_quantize_and_place/scan");
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, cu, Hkv,
-                       L.ntq, max_seqlen, tile_base, ok, poslist);
+    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
+                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, poslist, oldrank);
     rc = launch_check("kvc_quantize_and_place/select");
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_pages_kernel, dim3((C + QP_WAVES - 1) / QP_WAVES, nheads),
-                       dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv, C, max_seqlen, rows_l,
-                       count_l, ok, poslist, p->pages);
+    const dim3 grid((C + QP_WAVES - 1) / QP_WAVES, nheads);
+    if (rebuild)
+        hipLaunchKernelGGL(quant_pages_kernel<true>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv,
+                           C, max_seqlen, rows_l, count_l, ok, poslist, prev_tier, old_rows,
+                           oldrank, p->pages, p->dev_status);
+    else
+        hipLaunchKernelGGL(quant_pages_kernel<false>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu,
+                           Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, nullptr, nullptr,
+                           nullptr, p->pages, p->dev_status);
     return launch_check("kvc_quantize_and_place/pages");
 }

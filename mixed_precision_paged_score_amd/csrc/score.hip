@@ -77,6 +77,8 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
             if (p != FRESH) {
                 if (x < p) s_chg[h] = 1;
                 x = min(x, p);
+            } else if (x != PRUNE) {
+                s_chg[h] = 1;                  // a fresh token joins the head's pages
             }
         }
         tier[r * Hkv + h] = uint8_t(x);

@@ -34,23 +34,38 @@ struct CompactWs {
     }
 };
 
+// ---- append_tokens ----------------------------------------------------------------------
+struct AppendWs {
+    size_t compact, new_count, changed, bytes;
+    explicit AppendWs(const kvc_geom *g) {
+        const size_t heads = size_t(g->batch) * g->num_kv_heads;
+        compact = 0;
+        new_count = CompactWs(g).bytes;
+        changed = new_count + align256(sizeof(int32_t) * 2 * heads);
+        bytes = changed + align256(heads);
+    }
+};
+
 // ---- quantize_and_place ----------------------------------------------------------------
 constexpr int QTILE = 256;        // tokens per rank tile
 
 struct QuantWs {
     int ntq;
-    size_t tile_cnt, tile_base, ok, poslist, bytes;
+    size_t tile_cnt, tile_base, tile_cnt2, tile_base2, ok, poslist, oldrank, bytes;
     QuantWs(const kvc_geom *g, int max_seqlen) {
         ntq = (max_seqlen + QTILE - 1) / QTILE;
         if (ntq < 1) ntq = 1;
-        size_t cnt = sizeof(int32_t) * size_t(g->batch) * ntq * g->num_kv_heads * 2;
-        tile_cnt = 0;
-        tile_base = align256(cnt);
-        ok = tile_base + align256(cnt);
-        poslist = ok + align256(sizeof(int32_t) * (size_t(g->batch) * g->num_kv_heads + 1));
-        size_t pl = sizeof(int32_t) * size_t(g->batch) * g->num_kv_heads *
-                    size_t(max_seqlen > 0 ? max_seqlen : 1);
-        bytes = poslist + align256(pl);
+        const size_t cnt = align256(sizeof(int32_t) * size_t(g->batch) * ntq * g->num_kv_heads * 2);
+        const size_t heads = size_t(g->batch) * g->num_kv_heads;
+        const size_t pl = align256(sizeof(int32_t) * heads * size_t(max_seqlen > 0 ? max_seqlen : 1));
+        tile_cnt = 0;                       // per tile (HIGH, LOW) counts of the new tiers
+        tile_base = tile_cnt + cnt;         // their exclusive prefix over tiles
+        tile_cnt2 = tile_base + cnt;        // the same for the previous tiers (re-tiering)
+        tile_base2 = tile_cnt2 + cnt;
+        ok = tile_base2 + cnt;              // per head: write its pages; [heads] = entry status
+        poslist = ok + align256(sizeof(int32_t) * (heads + 1));
+        oldrank = poslist + pl;             // per head and position: rank in its old tier
+        bytes = oldrank + pl;
     }
 };
 

@@ -57,3 +57,70 @@ class PromptPath:
     def decode(self, layer, q, out):
         kvc.paged_decode_attention(self.geom, layer, self.pool, q, self.scale, out,
                                    self.ws_decode)
+
+
+class GenerationPath(PromptPath):
+    """Prompt, then per decode step one appended token per (request, KV head), and every
+    `round` steps a re-tier round: score with the previous tiers as ceiling, compact with the
+    rebuilt heads' flags, quantize/place in re-tier mode.  The per-position tier state is the
+    caller's bookkeeping: it is kept here as [B][max_len][Hkv] and packed to the ragged layout
+    the library reads (a device copy, outside the library calls)."""
+
+    def __init__(self, w, max_len, device="cuda", num_pages=None):
+        import dataclasses
+        # size workspaces and row capacity for the longest sequence the run reaches
+        wl = dataclasses.replace(w, seqlens=[max_len] * w.batch)
+        super().__init__(wl, device, num_pages)
+        self.w = w
+        self.lens = list(w.seqlens)
+        H = w.num_kv_heads
+        self.state = torch.full((w.batch, max_len, H), kvc.PRUNE, dtype=torch.uint8, device=device)
+        self.ws_append = kvc.workspace(self.geom, kvc.OP_APPEND, device=device)
+        self.changed = torch.empty((w.batch, H), dtype=torch.uint8, device=device)
+        self.old_rows = torch.empty((w.batch, H, self.geom.row_capacity), dtype=torch.int32,
+                                    device=device)
+        self.old_count = torch.empty((w.batch, H, 2), dtype=torch.int32, device=device)
+        self._set_layout()
+
+    def _set_layout(self):
+        import numpy as np
+        cu = np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int32)
+        self.cu = torch.tensor(cu, dtype=torch.int32, device=self.device)
+        self.T = int(cu[-1])
+        self.max_seqlen = max(self.lens)
+
+    def packed_state(self):
+        return torch.cat([self.state[b, :n] for b, n in enumerate(self.lens)]).contiguous()
+
+    def unpack_state(self, tier):
+        o = 0
+        for b, n in enumerate(self.lens):
+            self.state[b, :n] = tier[o:o + n]
+            o += n
+
+    def prompt(self, layer, acc, k, v):
+        self._set_layout()
+        super().prompt(layer, acc, k, v)
+        self.unpack_state(self.tier[:self.T])
+
+    def append(self, layer, k_new, v_new):
+        pos = torch.tensor(self.lens, dtype=torch.int32, device=self.device)
+        kvc.append_tokens(self.geom, layer, self.pool, k_new, v_new, pos, self.ws_append)
+        for b, n in enumerate(self.lens):
+            self.state[b, n] = kvc.HIGH
+        self.lens = [n + 1 for n in self.lens]
+        self._set_layout()
+
+    def retier(self, layer, acc):
+        w = self.w
+        prev = self.packed_state()
+        kvc.score_tokens(self.geom, acc, self.cu, self.T, self.max_seqlen, w.alpha_h, w.alpha_l,
+                         w.window, self.tier, self.new_count, prev_tier=prev,
+                         changed=self.changed, dev_status=self.score_status)
+        kvc.compact_pages(self.geom, layer, self.pool, self.new_count, self.ws_compact,
+                          changed=self.changed, old_rows=self.old_rows, old_count=self.old_count)
+        kvc.quantize_and_place(self.geom, layer, self.pool, None, None, self.cu, self.T,
+                               self.max_seqlen, self.tier, self.ws_quant, prev_tier=prev,
+                               changed=self.changed, old_rows=self.old_rows,
+                               old_count=self.old_count)
+        self.unpack_state(self.tier[:self.T])

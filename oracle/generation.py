@@ -1,0 +1,148 @@
+"""Oracle: the generation phase -- appends, re-tier rounds and rebuilt heads (test infra only).
+
+Source: DiffKV review page.  Free-parameter ledger: the most recent W tokens are always kept
+at high precision, so a generated token enters the HIGH tier.  Referee major comment 3: a
+token that leaves the window is irreversibly demoted or pruned (tiers never rise).  "What
+carries the argument": pages are re-assigned by prefix sum over the circular free list.
+
+Readings taken: every decode step appends one token per (request, KV head) as
+K8V4 in the next HIGH slot; every `round` steps the tokens are re-scored with the previous
+tier as a ceiling; a head with any demotion, prune or kept fresh token is rebuilt (fresh
+row, old pages returned).  A token keeps its codes while its tier is unchanged; a HIGH
+token demoted to LOW is re-quantized from the fp16 rounding of its K8V4 reconstruction.
+
+The state is a per-(request, KV head) record of every live token: position -> (tier, key
+codes, key scale, key zero, value codes, value scale, value zero).  Page images are a pure
+function of these records.
+"""
+import numpy as np
+
+from . import layout, quant, score as osc
+from .pool import Pool
+
+HIGH, LOW, PRUNE, FRESH = 2, 1, 0, 3
+
+
+class Generation:
+    def __init__(self, batch, num_kv_heads, row_capacity, num_pages, layer=0):
+        self.B, self.H = batch, num_kv_heads
+        self.layer = layer
+        self.pool = Pool(1, batch, num_kv_heads, row_capacity, num_pages)
+        self.rec = [[dict() for _ in range(num_kv_heads)] for _ in range(batch)]
+        self.tiers = [np.zeros((0, num_kv_heads), np.uint8) for _ in range(batch)]
+
+    # ---- helpers ---------------------------------------------------------------------
+    @staticmethod
+    def _record(tier, k_row, v_row):
+        kc, ks, kz = quant.quantize_rows(k_row[None], quant.K_BITS[tier])
+        vc, vs, vz = quant.quantize_rows(v_row[None], quant.V_BITS[tier])
+        return (tier, kc[0], ks[0], kz[0], vc[0], vs[0], vz[0])
+
+    @staticmethod
+    def _demote(r):
+        _, kc, ks, kz, vc, vs, vz = r
+        k2 = quant.requantize_from(kc[None], np.array([ks]), np.array([kz]), quant.K_BITS[LOW])
+        v2 = quant.requantize_from(vc[None], np.array([vs]), np.array([vz]), quant.V_BITS[LOW])
+        return (LOW, k2[0][0], k2[1][0], k2[2][0], v2[0][0], v2[1][0], v2[2][0])
+
+    def counts(self):
+        c = np.zeros((self.B, self.H, 2), np.int64)
+        for b in range(self.B):
+            for h in range(self.H):
+                for (t, *_rest) in self.rec[b][h].values():
+                    c[b, h, 0 if t == HIGH else 1] += 1
+        return c
+
+    # ---- the three operations ----------------------------------------------------------
+    def prompt(self, k, v, tier, cu):
+        """Prompt placement of all requests (prompt mode: every head rebuilt)."""
+        count = np.zeros((self.B, self.H, 2), np.int64)
+        for b in range(self.B):
+            lo, hi = int(cu[b]), int(cu[b + 1])
+            self.tiers[b] = tier[lo:hi].copy()
+            for h in range(self.H):
+                count[b, h, 0] = int(np.sum(tier[lo:hi, h] == HIGH))
+                count[b, h, 1] = int(np.sum(tier[lo:hi, h] == LOW))
+        self.pool.compact(self.layer, count)
+        if self.pool.status:
+            return
+        for b in range(self.B):
+            lo, hi = int(cu[b]), int(cu[b + 1])
+            for h in range(self.H):
+                self.rec[b][h] = {}
+                for t in range(hi - lo):
+                    x = int(tier[lo + t, h])
+                    if x in (HIGH, LOW):
+                        self.rec[b][h][t] = self._record(x, k[lo + t, h], v[lo + t, h])
+
+    def append(self, k_new, v_new):
+        """One new token per request and KV head at position len(request), tier HIGH."""
+        count = self.counts()
+        count[..., 0] += 1
+        self.pool.compact(self.layer, count, changed=np.zeros((self.B, self.H), np.uint8))
+        if self.pool.status:
+            return
+        for b in range(self.B):
+            pos = len(self.tiers[b])
+            self.tiers[b] = np.concatenate([self.tiers[b], np.full((1, self.H), HIGH, np.uint8)])
+            for h in range(self.H):
+                self.rec[b][h][pos] = self._record(HIGH, k_new[b, h], v_new[b, h])
+
+    def retier(self, acc, alpha_h, alpha_l, window):
+        """One round: score with the previous tiers as ceiling, rebuild changed heads."""
+        prev = np.concatenate(self.tiers)
+        cu = np.concatenate([[0], np.cumsum([len(t) for t in self.tiers])])
+        tier, count, changed = osc.score_tokens(acc, cu, self.H, alpha_h, alpha_l, window, prev)
+        self.pool.compact(self.layer, count, changed)
+        if self.pool.status:
+            return tier, count, changed
+        for b in range(self.B):
+            lo, hi = int(cu[b]), int(cu[b + 1])
+            self.tiers[b] = tier[lo:hi].copy()
+            for h in range(self.H):
+                if not changed[b, h]:
+                    continue
+                new = {}
+                for pos, r in self.rec[b][h].items():
+                    x = int(tier[lo + pos, h])
+                    if x == PRUNE:
+                        continue
+                    new[pos] = r if x == r[0] else self._demote(r)
+                self.rec[b][h] = new
+        return tier, count, changed
+
+    # ---- views -------------------------------------------------------------------------
+    def head_pages(self, b, h):
+        """Page images of one head: {HIGH: [...], LOW: [...]} in row order."""
+        out = {}
+        for t in (HIGH, LOW):
+            items = sorted((p, r) for p, r in self.rec[b][h].items() if r[0] == t)
+            per = layout.SLOTS[t]
+            pages = []
+            for p0 in range(0, len(items), per):
+                chunk = items[p0:p0 + per]
+                pages.append(layout.build_page(
+                    t, np.stack([r[1] for _, r in chunk]), np.stack([r[4] for _, r in chunk]),
+                    [r[2] for _, r in chunk], [r[3] for _, r in chunk],
+                    [r[5] for _, r in chunk], [r[6] for _, r in chunk],
+                    [p for p, _ in chunk]))
+            out[t] = pages
+        return out
+
+    def head_dequantized(self, b, h):
+        """float32 keys and values of the head's live tokens (HIGH first, then LOW)."""
+        ks, vs = [], []
+        for t in (HIGH, LOW):
+            items = sorted((p, r) for p, r in self.rec[b][h].items() if r[0] == t)
+            if not items:
+                continue
+            kc = np.stack([r[1] for _, r in items])
+            vc = np.stack([r[4] for _, r in items])
+            ks.append(quant.dequantize_rows(kc, np.array([r[2] for _, r in items]),
+                                            np.array([r[3] for _, r in items])))
+            vs.append(quant.dequantize_rows(vc, np.array([r[5] for _, r in items]),
+                                            np.array([r[6] for _, r in items])))
+        if not ks:
+            z = np.zeros((0, layout.D), np.float32)
+            return z, z
+        return np.concatenate(ks), np.concatenate(vs)

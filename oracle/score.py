@@ -33,7 +33,8 @@ def score_tokens(acc_sum, cu_seqlens, num_kv_heads, alpha_h, alpha_l, window,
     prev_tier  uint8 [T][Hkv] or None; FRESH (3) marks a token that has no tier yet
 
     Returns (tier uint8 [T][Hkv], count int32 [B][Hkv][2] = (#HIGH, #LOW),
-             changed uint8 [B][Hkv] = 1 where some already-tiered token dropped a tier).
+             changed uint8 [B][Hkv] = 1 where some already-tiered token dropped a tier or a
+             fresh token was kept, i.e. where the head's pages are rebuilt).
     """
     acc_sum = np.asarray(acc_sum, dtype=np.float32)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
@@ -68,7 +69,8 @@ def score_tokens(acc_sum, cu_seqlens, num_kv_heads, alpha_h, alpha_l, window,
             if prev_tier is not None:
                 p = np.asarray(prev_tier[lo:hi, h], dtype=np.uint8)
                 tiered = p != FRESH
-                if np.any(tiered & (x < p)):
+                # the head must be rebuilt if a tiered token drops or a fresh one is kept
+                if np.any(tiered & (x < p)) or np.any(~tiered & (x != PRUNE)):
                     changed[b, h] = 1
                 x = np.where(tiered, np.minimum(x, p), x).astype(np.uint8)   # never promote
             tier[lo:hi, h] = x

@@ -53,10 +53,18 @@ def test_synchronous_errors_enqueue_nothing():
                                  256, 1 << 20, None) == kvc.E_SHAPE
     assert lib.kvc_compact_pages(ctypes.byref(g), 0, ctypes.byref(p), 16, None, None, None,
                                  256, 8, None) == kvc.E_WORKSPACE
-    # quantize: re-tier inputs not implemented yet
+    # quantize: re-tier mode needs all four of prev_tier, changed, old_rows, old_count
     assert lib.kvc_quantize_and_place(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, 10, 5,
                                       16, 16, None, None, None, 256, 1 << 20,
+                                      None) == kvc.E_NULL
+    assert lib.kvc_quantize_and_place(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, 10, 5,
+                                      16, None, 16, None, None, 256, 1 << 20,
                                       None) == kvc.E_UNSUPPORTED
+    # append: missing positions, misaligned keys
+    assert lib.kvc_append_tokens(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, None, 256,
+                                 1 << 20, None) == kvc.E_NULL
+    assert lib.kvc_append_tokens(ctypes.byref(g), 0, ctypes.byref(p), 18, 16, 16, 256,
+                                 1 << 20, None) == kvc.E_ALIGN
     # decode: misaligned query
     assert lib.kvc_paged_decode_attention(ctypes.byref(g), 0, ctypes.byref(p), 18, 1.0, 16, 1,
                                           256, 1 << 20, None) == kvc.E_ALIGN

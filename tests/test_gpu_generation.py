@@ -1,0 +1,102 @@
+"""Generation phase on the GPU vs the oracle's record simulation (MI355X only): per-step
+appends (kvc_append_tokens) and re-tier rounds (score with previous tiers, compact with the
+rebuilt heads, quantize/place in re-tier mode), compared bit-exactly after every round."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(__file__))
+import parity  # noqa: E402
+from oracle import attention as oatt, generation as ogen  # noqa: E402
+from mixed_precision_paged_score_amd import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _compare_heads(w, path, gen, heads=None):
+    C = path.geom.row_capacity
+    heads = heads if heads is not None else [(b, h) for b in range(w.batch)
+                                             for h in range(w.num_kv_heads)]
+    for (b, h) in heads:
+        want = gen.head_pages(b, h)
+        row = parity.np_(path.pool.page_table[0, b, h])
+        ids = [int(row[p]) for p in range(len(want[ogen.HIGH]))] + \
+              [int(row[C - 1 - p]) for p in range(len(want[ogen.LOW]))]
+        imgs = want[ogen.HIGH] + want[ogen.LOW]
+        if not ids:
+            continue
+        got = parity.np_(path.pool.pages[torch.tensor(ids, device=DEV)])
+        for n, (gp, e) in enumerate(zip(got, imgs)):
+            if not np.array_equal(gp, e):
+                bad = np.nonzero(gp != e)[0]
+                raise AssertionError(f"head ({b},{h}) page #{n}: {len(bad)} bytes differ, "
+                                     f"first {bad[:6].tolist()}")
+
+
+def run_generation(w, steps, round_every, sample_heads=None, check_every_round=True):
+    from mixed_precision_paged_score_amd import pipeline
+    print(f"[generation] B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+          f"prompt={w.seqlens} steps={steps} round={round_every} P={w.num_pages}", flush=True)
+    k, v = workloads.make_kv(w)
+    acc = workloads.make_acc(w, k)
+    max_len = max(w.seqlens) + steps
+    path = pipeline.GenerationPath(w, max_len, DEV)
+    path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
+    tier0, _, _ = parity.oracle_score(w, acc)
+    gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages)
+    gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
+    g = torch.Generator().manual_seed(w.seed + 99)
+    rounds = 0
+    for s in range(steps):
+        kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        path.append(0, kn.to(DEV), vn.to(DEV))
+        gen.append(kn.numpy(), vn.numpy())
+        if (s + 1) % round_every == 0:
+            import dataclasses
+            wr = dataclasses.replace(w, seqlens=list(path.lens), seed=w.seed + 1000 * (s + 1))
+            acc_r = workloads.make_acc_zipf(wr)
+            path.retier(0, acc_r.to(DEV))
+            tier_o, _, changed_o = gen.retier(acc_r.numpy(), w.alpha_h, w.alpha_l, w.window)
+            rounds += 1
+            if check_every_round:
+                torch.cuda.synchronize()
+                assert np.array_equal(parity.np_(path.changed), changed_o)
+                assert np.array_equal(parity.np_(path.tier[:path.T]), tier_o)
+                parity.compare_pool(path.pool, gen.pool)
+                _compare_heads(w, path, gen, sample_heads)
+    torch.cuda.synchronize()
+    assert path.pool.status() == 0
+    parity.compare_pool(path.pool, gen.pool)
+    _compare_heads(w, path, gen, sample_heads)
+    # decode attention over the final state
+    q = workloads.make_queries(w, "cpu", 7)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    path.decode(0, q.to(DEV), out)
+    torch.cuda.synchronize()
+    G = w.group
+    heads = sample_heads or [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    for (b, h) in heads:
+        kd, vd = gen.head_dequantized(b, h)
+        want = oatt.decode_group(q.numpy()[b, h * G:(h + 1) * G], kd, vd, path.scale)
+        parity.assert_close_attention(parity.np_(out[b, h * G:(h + 1) * G]), want)
+    n_demoted = sum(int((t == ogen.LOW).sum()) for t in gen.tiers)
+    print(f"[generation] ok: {rounds} rounds, {n_demoted} LOW tokens, ring head {gen.pool.head}",
+          flush=True)
+    return path, gen
+
+
+def test_generation_small_ragged():
+    w = workloads.Workload("gen-small", 1, 3, 16, 4, [300, 160, 500], 1.0, 0.2, 16, 2048, "zipf",
+                           seed=31)
+    run_generation(w, steps=96, round_every=32)
+
+
+def test_generation_group8_with_pruning_and_page_boundaries():
+    # appends cross HIGH page boundaries (16 slots) many times; alpha_l prunes
+    w = workloads.Workload("gen-g8", 1, 2, 16, 2, [129, 77], 1.0, 0.5, 8, 1024, "zipf", seed=32)
+    run_generation(w, steps=70, round_every=20)
