@@ -88,6 +88,9 @@ class GenerationPath(PromptPath):
         self.cu = torch.tensor(cu, dtype=torch.int32, device=self.device)
         self.T = int(cu[-1])
         self.max_seqlen = max(self.lens)
+        self.lens_dev = torch.tensor(self.lens, dtype=torch.int32, device=self.device)
+        self._bidx = torch.arange(self.w.batch, device=self.device)
+        self._cu_step = torch.arange(self.w.batch + 1, dtype=torch.int32, device=self.device)
 
     def packed_state(self):
         return torch.cat([self.state[b, :n] for b, n in enumerate(self.lens)]).contiguous()
@@ -104,12 +107,15 @@ class GenerationPath(PromptPath):
         self.unpack_state(self.tier[:self.T])
 
     def append(self, layer, k_new, v_new):
-        pos = torch.tensor(self.lens, dtype=torch.int32, device=self.device)
-        kvc.append_tokens(self.geom, layer, self.pool, k_new, v_new, pos, self.ws_append)
-        for b, n in enumerate(self.lens):
-            self.state[b, n] = kvc.HIGH
+        kvc.append_tokens(self.geom, layer, self.pool, k_new, v_new, self.lens_dev,
+                          self.ws_append)
+        # bookkeeping: the new positions are HIGH, every request is one token longer
+        self.state[self._bidx, self.lens_dev.long()] = kvc.HIGH
+        self.lens_dev.add_(1)
+        self.cu.add_(self._cu_step)
         self.lens = [n + 1 for n in self.lens]
-        self._set_layout()
+        self.T += self.w.batch
+        self.max_seqlen += 1
 
     def retier(self, layer, acc):
         w = self.w

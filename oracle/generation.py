@@ -24,12 +24,19 @@ HIGH, LOW, PRUNE, FRESH = 2, 1, 0, 3
 
 
 class Generation:
-    def __init__(self, batch, num_kv_heads, row_capacity, num_pages, layer=0):
+    """`track`: the (request, KV head) pairs whose code records are kept (default: all).
+    Tiers, counts and the allocator are always simulated for every head."""
+
+    def __init__(self, batch, num_kv_heads, row_capacity, num_pages, layer=0, track=None):
         self.B, self.H = batch, num_kv_heads
         self.layer = layer
         self.pool = Pool(1, batch, num_kv_heads, row_capacity, num_pages)
         self.rec = [[dict() for _ in range(num_kv_heads)] for _ in range(batch)]
-        self.tiers = [np.zeros((0, num_kv_heads), np.uint8) for _ in range(batch)]
+        self._tb = [np.zeros((0, num_kv_heads), np.uint8) for _ in range(batch)]   # capacity
+        self.lens = [0] * batch
+        self.count = np.zeros((batch, num_kv_heads, 2), np.int64)
+        self.track = set(track) if track is not None else {(b, h) for b in range(batch)
+                                                           for h in range(num_kv_heads)}
 
     # ---- helpers ---------------------------------------------------------------------
     @staticmethod
@@ -46,12 +53,18 @@ class Generation:
         return (LOW, k2[0][0], k2[1][0], k2[2][0], v2[0][0], v2[1][0], v2[2][0])
 
     def counts(self):
-        c = np.zeros((self.B, self.H, 2), np.int64)
-        for b in range(self.B):
-            for h in range(self.H):
-                for (t, *_rest) in self.rec[b][h].values():
-                    c[b, h, 0 if t == HIGH else 1] += 1
-        return c
+        return self.count.copy()
+
+    @property
+    def tiers(self):
+        """Current tier of every position of every request (views)."""
+        return [self._tb[b][:self.lens[b]] for b in range(self.B)]
+
+    def _set_tiers(self, b, t):
+        if len(t) > len(self._tb[b]):
+            self._tb[b] = np.zeros((max(len(t), 2 * len(self._tb[b])), self.H), np.uint8)
+        self._tb[b][:len(t)] = t
+        self.lens[b] = len(t)
 
     # ---- the three operations ----------------------------------------------------------
     def prompt(self, k, v, tier, cu):
@@ -59,21 +72,28 @@ class Generation:
         count = np.zeros((self.B, self.H, 2), np.int64)
         for b in range(self.B):
             lo, hi = int(cu[b]), int(cu[b + 1])
-            self.tiers[b] = tier[lo:hi].copy()
+            self._set_tiers(b, tier[lo:hi])
             for h in range(self.H):
                 count[b, h, 0] = int(np.sum(tier[lo:hi, h] == HIGH))
                 count[b, h, 1] = int(np.sum(tier[lo:hi, h] == LOW))
         self.pool.compact(self.layer, count)
         if self.pool.status:
             return
+        self.count = count
         for b in range(self.B):
             lo, hi = int(cu[b]), int(cu[b + 1])
             for h in range(self.H):
                 self.rec[b][h] = {}
-                for t in range(hi - lo):
-                    x = int(tier[lo + t, h])
-                    if x in (HIGH, LOW):
-                        self.rec[b][h][t] = self._record(x, k[lo + t, h], v[lo + t, h])
+                if (b, h) not in self.track:
+                    continue
+                for x in (HIGH, LOW):
+                    pos = np.nonzero(tier[lo:hi, h] == x)[0]
+                    if len(pos) == 0:
+                        continue
+                    kc, ks, kz = quant.quantize_rows(k[lo + pos, h], quant.K_BITS[x])
+                    vc, vs, vz = quant.quantize_rows(v[lo + pos, h], quant.V_BITS[x])
+                    for n, t in enumerate(pos):
+                        self.rec[b][h][int(t)] = (x, kc[n], ks[n], kz[n], vc[n], vs[n], vz[n])
 
     def append(self, k_new, v_new):
         """One new token per request and KV head at position len(request), tier HIGH."""
@@ -82,11 +102,17 @@ class Generation:
         self.pool.compact(self.layer, count, changed=np.zeros((self.B, self.H), np.uint8))
         if self.pool.status:
             return
+        self.count = count
         for b in range(self.B):
-            pos = len(self.tiers[b])
-            self.tiers[b] = np.concatenate([self.tiers[b], np.full((1, self.H), HIGH, np.uint8)])
+            pos = self.lens[b]
+            if pos == len(self._tb[b]):
+                self._set_tiers(b, np.concatenate([self.tiers[b], np.zeros((pos + 1, self.H), np.uint8)]))
+                self.lens[b] = pos
+            self._tb[b][pos] = HIGH
+            self.lens[b] = pos + 1
             for h in range(self.H):
-                self.rec[b][h][pos] = self._record(HIGH, k_new[b, h], v_new[b, h])
+                if (b, h) in self.track:
+                    self.rec[b][h][pos] = self._record(HIGH, k_new[b, h], v_new[b, h])
 
     def retier(self, acc, alpha_h, alpha_l, window):
         """One round: score with the previous tiers as ceiling, rebuild changed heads."""
@@ -96,11 +122,12 @@ class Generation:
         self.pool.compact(self.layer, count, changed)
         if self.pool.status:
             return tier, count, changed
+        self.count = count.astype(np.int64)
         for b in range(self.B):
             lo, hi = int(cu[b]), int(cu[b + 1])
-            self.tiers[b] = tier[lo:hi].copy()
+            self._set_tiers(b, tier[lo:hi])
             for h in range(self.H):
-                if not changed[b, h]:
+                if not changed[b, h] or (b, h) not in self.track:
                     continue
                 new = {}
                 for pos, r in self.rec[b][h].items():

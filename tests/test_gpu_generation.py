@@ -47,7 +47,12 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
     path = pipeline.GenerationPath(w, max_len, DEV)
     path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
     tier0, _, _ = parity.oracle_score(w, acc)
-    gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages)
+    if isinstance(sample_heads, int):
+        rng = np.random.default_rng(w.seed)
+        allh = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+        sample_heads = [allh[i] for i in rng.choice(len(allh), sample_heads, replace=False)]
+    gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages,
+                          track=sample_heads)
     gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
     g = torch.Generator().manual_seed(w.seed + 99)
     rounds = 0
@@ -100,3 +105,11 @@ def test_generation_group8_with_pruning_and_page_boundaries():
     # appends cross HIGH page boundaries (16 slots) many times; alpha_l prunes
     w = workloads.Workload("gen-g8", 1, 2, 16, 2, [129, 77], 1.0, 0.5, 8, 1024, "zipf", seed=32)
     run_generation(w, steps=70, round_every=20)
+
+
+def test_workload4_shape_sampled():
+    # 16 requests x (4096-token prompt + 512 generated tokens), 64 query / 8 KV heads, a
+    # re-tier round every 128 steps, 2^18 pages; codes and attention on 6 sampled heads,
+    # tiers and allocator state for all heads after every round
+    w = workloads.workload(4)
+    run_generation(w, steps=512, round_every=128, sample_heads=6)
