@@ -38,7 +38,31 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch, 4 launches.
+    Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its per-dispatch counters give the factor
+    that turns those counters into bytes."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    evs = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n},
+                      "launches": 4, "median_ms": ms[len(ms) // 2],
+                      "copy_GBps_read_plus_write": 2 * n / (ms[len(ms) // 2] / 1e3) / 1e9}),
+          flush=True)
 
 
 def decode_algorithmic_bytes(count, B, Hq):
@@ -90,8 +114,11 @@ def cpu_baseline(w, k, v, acc, qs, nreq):
 
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration()
+        return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+        print(json.dumps({"error": "the benchmark measures one GPU; --gpus above 1 is not supported (the path would shard requests and KV heads across GPUs, each running this same single-GPU step)",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     from mixed_precision_paged_score_amd import kvc, pipeline, workloads

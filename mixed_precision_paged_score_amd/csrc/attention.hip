@@ -34,7 +34,13 @@ namespace kvc {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_MARGIN = 8.0f;      // log2 units
 constexpr float M_INIT = -1.0e30f;          // finite "minus infinity" for the running max
-constexpr int DEC_WAVES = 4;
+#ifndef KVC_DEC_WAVES
+#define KVC_DEC_WAVES 4
+#endif
+#ifndef KVC_DEC_OCC
+#define KVC_DEC_OCC 3
+#endif
+constexpr int DEC_WAVES = KVC_DEC_WAVES;    // waves per workgroup (slices of one head)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -67,28 +73,32 @@ constexpr uint32_t CRB = 0x00C000C0u;    // bits 6..7 of both halves
 constexpr float KOFF_HIGH = 1024.0f;     // 8-bit key codes: byte -> 1024 + code
 constexpr float COFF = 16.0f;            // 4/2-bit codes: 16 + code
 
-// Per-lane bytes of a pair of 16-token tiles (A, B) of one tier.  A HIGH tile is one HIGH
-// page; a LOW tile is one half (16 slots) of a LOW page.  Keys and values of both tiles are
-// needed by every lane (matrix operands); parameters only for the lane's own tile.
-template <bool HIGH> struct Pair;
-template <> struct Pair<true> {
+// Per-lane bytes of a pair of 16-token tiles (A, B) of one tier, in two parts so the next
+// pair's value/parameter loads can reuse the registers of the current pair's keys.  A HIGH
+// tile is one HIGH page; a LOW tile is one half (16 slots) of a LOW page.  Keys and values of
+// both tiles are needed by every lane (matrix operands); parameters only for its own tile.
+template <bool HIGH> struct Keys;
+template <> struct Keys<true> {
     uint4 ka0, ka1, kb0, kb1;   // channels 32j..32j+31 of token (lane & 15), 8-bit codes
+};
+template <> struct Keys<false> {
+    uint4 ka, kb;               // channels 32j..32j+31 of token (lane & 15), 4-bit codes
+};
+template <bool HIGH> struct Vals;
+template <> struct Vals<true> {
     uint4 va, vb;               // value unit 16j + (lane & 15): tokens 4j..4j+3, 8 channels
     uint4 p0, p1;               // parameters of tokens 4j..4j+3 of the lane's tile
 };
-template <> struct Pair<false> {
-    uint4 ka, kb;               // channels 32j..32j+31 of token (lane & 15), 4-bit codes
+template <> struct Vals<false> {
     uint2 va, vb;               // the tiles' halves of value unit 16j + (lane & 15)
     uint4 p0, p1;
 };
 
 template <bool HIGH>
-__device__ __forceinline__ Pair<HIGH> load_pair(const uint8_t *pga, const uint8_t *pgb, int fa,
-                                                int fb, int lane, bool own_b) {
+__device__ __forceinline__ Keys<HIGH> load_keys(const uint8_t *pga, const uint8_t *pgb, int fa,
+                                                int fb, int lane) {
     const int j = lane >> 4, tok = lane & 15;
-    Pair<HIGH> d;
-    const uint8_t *pgo = own_b ? pgb : pga;
-    const int fo = own_b ? fb : fa;
+    Keys<HIGH> d;
     if constexpr (HIGH) {
         const uint4 *a = reinterpret_cast<const uint4 *>(pga + K_OFF + tok * 128 + 32 * j);
         const uint4 *b = reinterpret_cast<const uint4 *>(pgb + K_OFF + tok * 128 + 32 * j);
@@ -96,14 +106,27 @@ __device__ __forceinline__ Pair<HIGH> load_pair(const uint8_t *pga, const uint8_
         d.ka1 = a[1];
         d.kb0 = b[0];
         d.kb1 = b[1];
+    } else {
+        d.ka = *reinterpret_cast<const uint4 *>(pga + K_OFF + (16 * fa + tok) * 64 + 16 * j);
+        d.kb = *reinterpret_cast<const uint4 *>(pgb + K_OFF + (16 * fb + tok) * 64 + 16 * j);
+    }
+    return d;
+}
+
+template <bool HIGH>
+__device__ __forceinline__ Vals<HIGH> load_vals(const uint8_t *pga, const uint8_t *pgb, int fa,
+                                                int fb, int lane, bool own_b) {
+    const int j = lane >> 4;
+    Vals<HIGH> d;
+    const uint8_t *pgo = own_b ? pgb : pga;
+    const int fo = own_b ? fb : fa;
+    if constexpr (HIGH) {
         d.va = *reinterpret_cast<const uint4 *>(pga + V_OFF + 16 * lane);
         d.vb = *reinterpret_cast<const uint4 *>(pgb + V_OFF + 16 * lane);
         const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 32 * j);
         d.p0 = pp[0];
         d.p1 = pp[1];
     } else {
-        d.ka = *reinterpret_cast<const uint4 *>(pga + K_OFF + (16 * fa + tok) * 64 + 16 * j);
-        d.kb = *reinterpret_cast<const uint4 *>(pgb + K_OFF + (16 * fb + tok) * 64 + 16 * j);
         d.va = *reinterpret_cast<const uint2 *>(pga + V_OFF + 16 * lane + 8 * fa);
         d.vb = *reinterpret_cast<const uint2 *>(pgb + V_OFF + 16 * lane + 8 * fb);
         const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 8 * (16 * fo + 4 * j));
@@ -173,29 +196,39 @@ struct Magic {
     uint32_t c16;    // 0x4C004C00 (4/2-bit codes -> 16 + code)
 };
 
-// One pair of tiles.  The query operand repeats the 8 query heads in columns 0..7 and
-// 8..15; lane column c = lane & 15 keeps tile A's scores when c < 8 and tile B's when c >= 8,
-// so every lane's softmax work is useful although G <= 8.
+// S^T for a pair of tiles.  The query operands live in LDS (shared by the workgroup's waves):
+// qa holds the 8 query heads in columns 0..7 (zero in 8..15), qb in columns 8..15, so lane
+// column c = lane & 15 gets tile A's scores when c < 8 and tile B's when c >= 8 and every
+// lane's softmax work is useful although G <= 8.
 template <bool HIGH>
-__device__ __forceinline__ void attend_pair(const Pair<HIGH> &d, int live_own,
-                                            const h8 (&qo)[4], float sumq, float scale_log2,
-                                            int lane, const Magic &mg, WaveState &st) {
-    const int j = lane >> 4, c = lane & 15;
-    const bool own_b = c >= 8;
-    f4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_qa)[64],
+                                          const uint4 (*s_qb)[64], int lane, const Magic &mg) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    // an opaque lane index keeps the compiler from hoisting the LDS reads out of the loop
+    // (which would pin 32 registers for the operands)
+    int li = lane;
+    asm volatile("" : "+v"(li));
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+        const h8 qa = __builtin_bit_cast(h8, s_qa[m][li]);
+        const h8 qb = __builtin_bit_cast(h8, s_qb[m][li]);
         if constexpr (HIGH) {
-            acc_a = mfma32(key_op_high(d.ka0, d.ka1, m, mg.k8), qo[m], acc_a);
-            acc_b = mfma32(key_op_high(d.kb0, d.kb1, m, mg.k8), qo[m], acc_b);
+            acc = mfma32(key_op_high(d.ka0, d.ka1, m, mg.k8), qa, acc);
+            acc = mfma32(key_op_high(d.kb0, d.kb1, m, mg.k8), qb, acc);
         } else {
-            acc_a = mfma32(key_op_low(d.ka, m, mg.c16), qo[m], acc_a);
-            acc_b = mfma32(key_op_low(d.kb, m, mg.c16), qo[m], acc_b);
+            acc = mfma32(key_op_low(d.ka, m, mg.c16), qa, acc);
+            acc = mfma32(key_op_low(d.kb, m, mg.c16), qb, acc);
         }
     }
-    f4 acc;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = own_b ? acc_b[r] : acc_a[r];
+    return acc;
+}
+
+template <bool HIGH>
+__device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> &d, int live_own,
+                                                float sumq, float scale_log2, int lane,
+                                                const Magic &mg, WaveState &st) {
+    const int j = lane >> 4, c = lane & 15;
+    const bool own_b = c >= 8;
     constexpr float KOFF = HIGH ? KOFF_HIGH : COFF;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
     float L[4], vs[4], vz[4];
@@ -269,10 +302,13 @@ __device__ __forceinline__ void attend_pair(const Pair<HIGH> &d, int live_own,
 }
 
 // tiles [t0, t1) of one tier of a head, two at a time; page ids of up to 64 pages come from
-// one lane-indexed register, so no load waits on another load; one pair in flight ahead
+// one lane-indexed register, so no load waits on another load.  The next pair's keys are
+// requested before this pair's scores, its values and parameters before this pair's softmax
+// (reusing the registers of the keys just consumed).
 template <bool HIGH>
 __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
-                                             int C, const uint8_t *pages, const h8 (&qo)[4],
+                                             int C, const uint8_t *pages,
+                                             const uint4 (*s_qa)[64], const uint4 (*s_qb)[64],
                                              float sumq, float scale_log2, int lane,
                                              const Magic &mg, WaveState &st) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
@@ -289,31 +325,52 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         auto live_of = [&](int t) -> int {
             return t >= c1 ? 0 : (HIGH ? min(HS, n_tier - HS * t) : min(16, n_tier - 16 * t));
         };
-        auto load = [&](int t) -> Pair<HIGH> {
-            const int tb = t + 1 < c1 ? t + 1 : t;    // a missing tile B re-reads tile A
-            return load_pair<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane, own_b);
+        auto tb_of = [&](int t) -> int { return t + 1 < c1 ? t + 1 : t; };  // missing B: reuse A
+        // pair starting at tile t; past the last pair the loads repeat the last pair (cache
+        // hits), which keeps the loop free of branches around loads and of register copies
+        const int tlast = c0 + ((c1 - 1 - c0) & ~1);
+        auto keys_at = [&](int t) {
+            t = min(t, tlast);
+            const int tb = tb_of(t);
+            return load_keys<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane);
         };
-        Pair<HIGH> cur = load(c0);
-        for (int t = c0; t < c1; t += 2) {
-            Pair<HIGH> nxt = cur;
-            if (t + 2 < c1) nxt = load(t + 2);
-            const int live_own = own_b ? live_of(t + 1) : live_of(t);
-            attend_pair<HIGH>(cur, live_own, qo, sumq, scale_log2, lane, mg, st);
-            cur = nxt;
+        auto vals_at = [&](int t) {
+            t = min(t, tlast);
+            const int tb = tb_of(t);
+            return load_vals<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane, own_b);
+        };
+        Keys<HIGH> ka = keys_at(c0), kb;
+        Vals<HIGH> va = vals_at(c0), vb;
+        for (int t = c0;;) {
+            kb = keys_at(t + 2);
+            f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg);
+            vb = vals_at(t + 2);
+            pair_softmax_pv<HIGH>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq, scale_log2,
+                                  lane, mg, st);
+            t += 2;
+            if (t >= c1) break;
+            ka = keys_at(t + 2);
+            acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg);
+            va = vals_at(t + 2);
+            pair_softmax_pv<HIGH>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq, scale_log2,
+                                  lane, mg, st);
+            t += 2;
+            if (t >= c1) break;
         }
     }
 }
 
 // grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
 // take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
-__global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(KVC_DEC_OCC)))
 void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
                         const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
                         const int32_t *__restrict__ count_l, int Hkv, int GT, int C, int S,
                         float *__restrict__ part) {
-    __shared__ float s_o[DEC_WAVES][32][64];
+    __shared__ float s_o[DEC_WAVES][8][D];      // [wave][query head][channel]
     __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16],
         s_lp[DEC_WAVES][16];
+    __shared__ uint4 s_qa[4][64], s_qb[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & 15, j = lane >> 4, gq = c & 7;
     const int NGP = (GT + 7) >> 3;             // groups of 8 query heads per KV head
@@ -338,8 +395,9 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     };
     const int u0 = tile_of(W * cc / NC), u1 = tile_of(W * (cc + 1) / NC);
 
-    // query operand: lane (c, j) holds q[gq][32j + 8m + {0,2,1,3,4,6,5,7}], gq = c & 7
-    h8 qo[4];
+    // query operands: lane (c, j) holds q[gq][32j + 8m + {0,2,1,3,4,6,5,7}], gq = c & 7,
+    // kept in LDS for the whole workgroup (all its waves serve the same head): qa in columns
+    // 0..7, qb in columns 8..15
     float sumq = 0.0f;
     {
         uint4 qv[4] = {};
@@ -350,13 +408,22 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const h2 x0 = as_h2(qv[m].x), x1 = as_h2(qv[m].y), x2 = as_h2(qv[m].z), x3 = as_h2(qv[m].w);
-            qo[m] = h8{x0[0], x1[0], x0[1], x1[1], x2[0], x3[0], x2[1], x3[1]};
+            const h8 o = {x0[0], x1[0], x0[1], x1[1], x2[0], x3[0], x2[1], x3[1]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sumq += float(qo[m][e]);
+            for (int e = 0; e < 8; ++e) sumq += float(o[e]);
+            if (wave == 0) {
+                const uint4 ov = __builtin_bit_cast(uint4, o);
+                const bool lo_half = c < 8;
+                s_qa[m][lane] = make_uint4(lo_half ? ov.x : 0u, lo_half ? ov.y : 0u,
+                                           lo_half ? ov.z : 0u, lo_half ? ov.w : 0u);
+                s_qb[m][lane] = make_uint4(lo_half ? 0u : ov.x, lo_half ? 0u : ov.y,
+                                           lo_half ? 0u : ov.z, lo_half ? 0u : ov.w);
+            }
         }
         sumq += __shfl_xor(sumq, 16, 64);
         sumq += __shfl_xor(sumq, 32, 64);
     }
+    __syncthreads();
 
     WaveState st;
 #pragma unroll
@@ -367,9 +434,10 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
     const int32_t *row = rows_l + int64_t(i) * C;
-    attend_range<true>(u0, min(u1, qH), nh, row, C, pages, qo, sumq, scale_log2, lane, mg, st);
-    attend_range<false>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, qo, sumq, scale_log2, lane,
-                        mg, st);
+    attend_range<true>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2, lane,
+                       mg, st);
+    attend_range<false>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
+                        scale_log2, lane, mg, st);
     // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
     for (int o = 8; o <= 32; o <<= 1) {
@@ -380,10 +448,18 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
         }
     }
     // ---- merge the four waves in LDS and write this workgroup's partial --------------------
+    // rows gg (tile A half, lanes 0..31) and gg + 8 (tile B half, lanes 32..63) of the
+    // accumulator belong to the same query head
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_o[wave][4 * n + r][lane] = st.o[n][r];
+        for (int r = 0; r < 4; ++r) st.o[n][r] += __shfl_xor(st.o[n][r], 32, 64);
+    if (lane < 32) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_o[wave][4 * j + r][16 * n + c] = st.o[n][r];
+    }
     if (lane < 8) {
         s_m[wave][lane] = st.m;
         s_l[wave][lane] = st.l;
@@ -398,15 +474,10 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, s_m[w][gg]);
         float Ls = 0.0f, O = 0.0f;
-        const int n = d >> 4, dl = d & 15;
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) {
             const float f = __builtin_amdgcn_exp2f(s_m[w][gg] - M);
-            // rows gg (tile-A half) and gg + 8 (tile-B half) of the wave's accumulator
-            const int ra = gg, rb = gg + 8;
-            const float oa = s_o[w][4 * n + (ra & 3)][16 * (ra >> 2) + dl];
-            const float ob = s_o[w][4 * n + (rb & 3)][16 * (rb >> 2) + dl];
-            O += (oa + ob - COFF * s_lp[w][gg] + s_lz[w][gg]) * f;
+            O += (s_o[w][gg][d] - COFF * s_lp[w][gg] + s_lz[w][gg]) * f;
             Ls += s_l[w][gg] * f;
         }
         float *pp = hp + (int64_t(s) * GT + g0 + gg) * PART_STRIDE;

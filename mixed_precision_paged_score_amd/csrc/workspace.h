@@ -72,9 +72,13 @@ struct QuantWs {
 // ---- paged_decode_attention ------------------------------------------------------------
 constexpr int PART_STRIDE = 132;  // floats per partial: m, l, pad, pad, o[128]
 
+#ifndef KVC_DEC_SPLIT_TARGET
+#define KVC_DEC_SPLIT_TARGET 2048      // workgroups per decode launch to aim for
+#endif
+
 inline int decode_splits(const kvc_geom *g) {
     int heads = g->batch * g->num_kv_heads;
-    int s = (2048 + heads - 1) / heads;
+    int s = (KVC_DEC_SPLIT_TARGET + heads - 1) / heads;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return s;

@@ -9,7 +9,7 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvc.so")
+LIB_PATH = os.environ.get("KVC_LIB_PATH") or os.path.join(HERE, "libkvc.so")
 
 OK, E_NULL, E_ALIGN, E_SHAPE, E_WORKSPACE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 DEV_POOL_EXHAUSTED, DEV_ROW_OVERFLOW, DEV_SHRINK, DEV_COUNT_MISMATCH, DEV_SEQLEN = 1, 2, 4, 8, 16
