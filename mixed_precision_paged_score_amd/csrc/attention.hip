@@ -246,7 +246,12 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));      // both tiles of the pair
-    if (__ballot(tmax > st.m + RESCALE_MARGIN) != 0ull) {
+    // the branch is uniform, but written as a per-lane condition (an opaque lane value that
+    // is always 1) the compiler predicates it instead of splitting the accumulators' live
+    // ranges, which would copy all 32 of them on the common path
+    int one = 1;
+    asm volatile("" : "+v"(one));
+    if (one && __ballot(tmax > st.m + RESCALE_MARGIN) != 0ull) {
         const float mn = fmaxf(st.m, tmax);
         const float corr = __builtin_amdgcn_exp2f(st.m - mn);
         st.l *= corr;
@@ -371,7 +376,10 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16],
         s_lp[DEC_WAVES][16];
     __shared__ uint4 s_qa[4][64], s_qb[4][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the wave index is the same in all lanes: reading it from lane 0 tells the compiler so,
+    // which keeps the tile ranges, the loop control and page-id lookups in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, j = lane >> 4, gq = c & 7;
     const int NGP = (GT + 7) >> 3;             // groups of 8 query heads per KV head
     const int s = blockIdx.x % S;
@@ -491,6 +499,9 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 
 // merge the S partials of one (request, query head): one wave per query head; lane s < S
 // holds split s's max, the weights are broadcast, each lane accumulates 2 channels
+// one wave per (request, query head): lanes first hold the splits' (m, l) (S <= 64), then
+// two output channels each; the splits' partial rows are loaded eight at a time, all
+// independent, and weighted with exp2(m_s - M) read from the owning lane
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
                                                              int Hq, int G, int S, int nqh,
                                                              void *out, int out_fp32) {
@@ -500,51 +511,44 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     const int b = qh / Hq, hq = qh - b * Hq;
     const int h = hq / G, gg = hq - h * G;
     const int Hkv = Hq / G;
-    const float *hp = part + (int64_t(b) * Hkv + h) * S * G * PART_STRIDE;
+    const int64_t sstride = int64_t(G) * PART_STRIDE;
+    const float *hp = part + ((int64_t(b) * Hkv + h) * S * G + gg) * PART_STRIDE;
+    float ms = M_INIT, ls = 0.0f;
+    if (lane < S) {
+        ms = hp[lane * sstride];
+        ls = hp[lane * sstride + 1];
+    }
+    float M = ms;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float w = lane < S ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+    float Ls = ls * w;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
     float r0 = 0.0f, r1 = 0.0f;
-    float M = M_INIT, Ls = 0.0f;
-    for (int s0 = 0; s0 < S; s0 += 64) {
-        const int s = s0 + lane;
-        float ms = M_INIT, ls = 0.0f;
-        if (s < S) {
-            ms = hp[(int64_t(s) * G + gg) * PART_STRIDE];
-            ls = hp[(int64_t(s) * G + gg) * PART_STRIDE + 1];
+    for (int k0 = 0; k0 < S; k0 += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = min(k0 + u, S - 1);          // past the end: reload, weight 0
+            v[u] = *reinterpret_cast<const float2 *>(hp + k * sstride + 4 + 2 * lane);
         }
-        float cm = ms;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
-        const float Mn = fmaxf(M, cm);
-        const float corr = __builtin_amdgcn_exp2f(M - Mn);
-        r0 *= corr;
-        r1 *= corr;
-        Ls *= corr;
-        M = Mn;
-        const float w = __builtin_amdgcn_exp2f(ms - M);
-        float lw = ls * w;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) lw += __shfl_xor(lw, o, 64);
-        Ls += lw;
-        const int n = min(64, S - s0);
-        for (int k = 0; k < n; ++k) {
-            const float wk = __shfl(w, k, 64);
-            if (wk == 0.0f) continue;
-            const float2 o2 = *reinterpret_cast<const float2 *>(
-                hp + (int64_t(s0 + k) * G + gg) * PART_STRIDE + 4 + 2 * lane);
-            r0 += o2.x * wk;
-            r1 += o2.y * wk;
+        for (int u = 0; u < 8; ++u) {
+            const int wk = __builtin_amdgcn_readlane(__float_as_int(w), min(k0 + u, 63));
+            const float wf = k0 + u < S ? __int_as_float(wk) : 0.0f;
+            r0 += v[u].x * wf;
+            r1 += v[u].y * wf;
         }
     }
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     const int64_t idx = int64_t(qh) * D + 2 * lane;
+    const float o0 = Ls > 0.0f ? r0 / Ls : 0.0f, o1 = Ls > 0.0f ? r1 / Ls : 0.0f;
     if (out_fp32) {
-        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) =
-            make_float2(Ls > 0.0f ? r0 / Ls : 0.0f, Ls > 0.0f ? r1 / Ls : 0.0f);
+        *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(o0, o1);
     } else {
-        const uint32_t v = uint32_t(f2h_rn(Ls > 0.0f ? r0 / Ls : 0.0f)) |
-                           (uint32_t(f2h_rn(Ls > 0.0f ? r1 / Ls : 0.0f)) << 16);
+        const uint32_t v = uint32_t(f2h_rn(o0)) | (uint32_t(f2h_rn(o1)) << 16);
         *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(out) + idx) = v;
     }
-    (void)inv;
 }
 
 }  // namespace kvc
