@@ -2,18 +2,23 @@
 MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input resident in HBM:
-release the layer's pages, score_tokens -> compact_pages -> quantize_and_place for the
-full prompt, then the workload's decode steps of paged_decode_attention (fresh queries).
-Default workload: one layer, 16 requests x 32,768 tokens, 64 query / 8 KV heads, Zipf(1.1)
-accumulators, 2^18 pages, 64 decode steps.
+score_tokens -> compact_pages (prompt mode: the layer's previous pages go back to the ring,
+new ones are assigned) -> quantize_and_place for the full prompt, then the workload's decode
+steps of paged_decode_attention (fresh queries).  Default workload: one layer, 16 requests x
+32,768 tokens, 64 query / 8 KV heads, Zipf(1.1) accumulators, 64 decode steps; the pool has
+room for two layouts of the layer (2 x 2^18 pages).  The step's library calls are captured
+into two HIP graphs (prompt round, decode steps) and replayed; --eager launches them from
+Python instead.
 
-Prints one JSON line (rank 0).  `value` = KV token-heads compacted per second over the
-compaction part of the step; `decode_GBps` = algorithmic bytes of paged decode attention
-per second; `roofline` is for the dominant kernel (decode attention main kernel, timed per
-launch with HIP events on the stream it runs on); `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line.  `value` = KV token-heads compacted per second over the compaction
+part of the step; `decode_GBps` = algorithmic bytes of paged decode attention per second;
+`roofline` is for the dominant work, the decode-attention call (main + combine kernel),
+timed with HIP events around the replayed decode steps on the stream they run on, divided
+by the number of calls; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
 """
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -38,6 +43,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every library call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM counters)")
     return ap.parse_args()
@@ -124,7 +131,11 @@ def main():
     from mixed_precision_paged_score_amd import kvc, pipeline, workloads
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    # the pool holds two layouts of the layer: every step's prompt-mode compaction returns the
+    # previous step's pages to the ring tail and takes the new ones from the ring head, and
+    # an all-or-nothing round may only hand out pages that are free when it starts
     w = workloads.workload(a.workload)
+    w = dataclasses.replace(w, num_pages=2 * w.num_pages)
     nsteps_dec = a.decode_steps if a.decode_steps is not None else w.decode_steps
     k, v = workloads.make_kv(w, dev)
     acc = workloads.make_acc(w, k, dev)
@@ -134,21 +145,31 @@ def main():
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    def step(record):
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        path.release(0)
+    if not a.eager:
+        # the step's library calls are captured once into two HIP graphs (prompt round,
+        # decode steps); every replay redoes all of the work on the resident inputs
         path.prompt(0, acc, k, v)
+        torch.cuda.synchronize()
+        g_prompt = path.capture_prompt(0, acc, k, v)
+        g_dec = path.capture_decode(0, qs, out)
+        torch.cuda.synchronize()
+
+    def step(record):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        if a.eager:
+            path.prompt(0, acc, k, v)
+        else:
+            g_prompt.replay()
         e1.record(stream)
-        dec = []
-        for s in range(nsteps_dec):
-            d0, d1 = ev(), ev()
-            d0.record(stream)
-            path.decode(0, qs[s], out)
-            d1.record(stream)
-            dec.append((d0, d1))
+        if a.eager:
+            for s in range(nsteps_dec):
+                path.decode(0, qs[s], out)
+        else:
+            g_dec.replay()
+        e2.record(stream)
         if record is not None:
-            record.append(((e0, e1), dec))
+            record.append((e0, e1, e2))
 
     for _ in range(a.warmup):
         step(None)
@@ -161,8 +182,8 @@ def main():
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    comp_ms = [r[0][0].elapsed_time(r[0][1]) for r in recs]
-    dec_ms = [d0.elapsed_time(d1) for r in recs for (d0, d1) in r[1]]
+    comp_ms = [e0.elapsed_time(e1) for (e0, e1, e2) in recs]
+    dec_ms = [e1.elapsed_time(e2) / max(nsteps_dec, 1) for (e0, e1, e2) in recs]
     count = path.new_count.cpu().numpy()
     T, Hkv, Hq, B = w.total_tokens, w.num_kv_heads, w.num_q_heads, w.batch
     token_heads = T * Hkv

@@ -221,6 +221,51 @@ __device__ __forceinline__ float recon16(uint32_t code, uint32_t par) {
     return h2f(f2h_rn(r));
 }
 
+// one slot's outputs: key codes straight to the page (an empty slot writes zeros), value
+// codes and the four fp16 parameters to the wave's LDS staging
+__device__ __forceinline__ void store_slot(uint8_t *pg, uint8_t *sv, uint16_t (*par)[4], bool high,
+                                           int s, int c, bool live, uint32_t kw0, uint32_t kw1,
+                                           uint32_t vw0, uint32_t vw1, uint16_t ks, uint16_t kz,
+                                           uint16_t vs, uint16_t vz) {
+    if (!live) kw0 = kw1 = vw0 = vw1 = 0;
+    if (high) *reinterpret_cast<uint2 *>(pg + K_OFF + s * 128 + 8 * c) = make_uint2(kw0, kw1);
+    else *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = kw0;
+    *reinterpret_cast<uint2 *>(sv + s * D + 8 * c) = make_uint2(vw0, vw1);
+    if (c == 0) {
+        par[s][0] = live ? ks : 0;
+        par[s][1] = live ? kz : 0;
+        par[s][2] = live ? vs : 0;
+        par[s][3] = live ? vz : 0;
+    }
+}
+
+// prompt placement of one page: NP passes of 4 slots (one 16-lane group per slot).  The
+// slots' positions are all loaded first, so each pass waits for one round trip (its K/V
+// rows, 16 bytes of each per lane) instead of two.
+template <int NP, typename Emit>
+__device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
+                                            const uint16_t *__restrict__ V,
+                                            const int32_t *__restrict__ pl, int lo, int Hkv, int h,
+                                            int max_seqlen, int first, int m, bool high, int rg,
+                                            int c, Emit &emit) {
+    int pos[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int s = 4 * p + rg;
+        pos[p] = 0;
+        if (s < m) pos[p] = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const bool live = 4 * p + rg < m;
+        const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
+        float xk[8], xv[8];
+        load_row8(K + roff, live, xk);
+        load_row8(V + roff, live, xv);
+        emit(4 * p + rg, live, xk, xv);
+    }
+}
+
 // grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
 // REBUILD: each token's codes come from the fp16 rows (previous tier FRESH), are copied from
 // its old page (tier unchanged), or are re-quantized from its old K8V4 codes (HIGH -> LOW).
@@ -265,26 +310,51 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     const int rg = lane >> 4, c = lane & 15;
     const int nslots = high ? HS : LS;
     uint8_t *sv = s_v[wave];
+    // quantize the lane's 8 channels of slot s from float rows (or store a zero slot), write
+    // the key codes to the page and stage value codes and parameters in LDS
+    auto emit_fresh = [&](int s, bool live, const float (&xk)[8], const float (&xv)[8]) {
+        uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
+        const RowQ qk = row_params(xk, high ? 255.0f : 15.0f);
+        if (high) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kw0 |= code_of(xk[e], qk) << (8 * e);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kw1 |= code_of(xk[4 + e], qk) << (8 * e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kw0 |= code_of(xk[e], qk) << (4 * k_nib(e));
+        }
+        const RowQ qv = row_params(xv, high ? 15.0f : 3.0f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vw0 |= code_of(xv[e], qv) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vw1 |= code_of(xv[4 + e], qv) << (8 * e);
+        store_slot(pg, sv, s_par[wave], high, s, c, live, kw0, kw1, vw0, vw1, qk.s16, qk.z16,
+                   qv.s16, qv.z16);
+    };
+    if constexpr (!REBUILD) {
+        // every row of the page is requested before the first one is quantized
+        if (high) fresh_slots<HS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, true, rg, c, emit_fresh);
+        else fresh_slots<LS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, false, rg, c, emit_fresh);
+    } else {
     for (int pass = 0; pass < nslots / 4; ++pass) {
         const int s = pass * 4 + rg;
         const bool live = s < m;
         int pos = 0;
         if (live) pos = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
         const int64_t grow = int64_t(lo) + pos;
-        int src = FRESH;
+        const int src = live ? int(prev[grow * Hkv + h]) : int(FRESH);
         bool valid = live;
-        if (REBUILD && live) {
-            src = prev[grow * Hkv + h];
+        if (live) {
             // a tier never rises, and a fresh token needs its fp16 rows
             valid = src == T || (src == HIGH && T == LOW) || (src == FRESH && K != nullptr);
             if (!valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
         }
-        uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;   // key code words, value code bytes
-        uint16_t ks = 0, kz = 0, vs = 0, vz = 0;
         if (!valid) {
-            // leave the slot zero
+            store_slot(pg, sv, s_par[wave], high, s, c, false, 0, 0, 0, 0, 0, 0, 0, 0);
         } else if (src == T) {
             // unchanged tier: copy the token's codes and parameters from its old page
+            uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
             const int so = oldrank[int64_t(i) * max_seqlen + pos];
             const int opage = T == HIGH ? old_rows[int64_t(i) * C + (so >> 4)]
                                         : old_rows[int64_t(i) * C + C - 1 - (so >> 5)];
@@ -306,17 +376,16 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kw0 |= kc[e] << (4 * k_nib(e));
             }
-            ks = uint16_t(kp & 0xffffu);
-            kz = uint16_t(kp >> 16);
-            vs = uint16_t(vp & 0xffffu);
-            vz = uint16_t(vp >> 16);
+            store_slot(pg, sv, s_par[wave], high, s, c, true, kw0, kw1, vw0, vw1,
+                       uint16_t(kp & 0xffffu), uint16_t(kp >> 16), uint16_t(vp & 0xffffu),
+                       uint16_t(vp >> 16));
         } else {
             // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
             float xk[8], xv[8];
-            if (!REBUILD || src == FRESH) {
+            if (src == FRESH) {
                 const int64_t roff = (grow * Hkv + h) * D + 8 * c;
-                load_row8(K + roff, live, xk);
-                load_row8(V + roff, live, xv);
+                load_row8(K + roff, true, xk);
+                load_row8(V + roff, true, xv);
             } else {
                 const int so = oldrank[int64_t(i) * max_seqlen + pos];   // old HIGH rank
                 const int opage = old_rows[int64_t(i) * C + (so >> 4)];
@@ -328,36 +397,9 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                     xv[e] = recon16(vc[e], vp);
                 }
             }
-            const RowQ qk = row_params(xk, high ? 255.0f : 15.0f);
-            if (high) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kw0 |= code_of(xk[e], qk) << (8 * e);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kw1 |= code_of(xk[4 + e], qk) << (8 * e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kw0 |= code_of(xk[e], qk) << (4 * k_nib(e));
-            }
-            const RowQ qv = row_params(xv, high ? 15.0f : 3.0f);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vw0 |= code_of(xv[e], qv) << (8 * e);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vw1 |= code_of(xv[4 + e], qv) << (8 * e);
-            ks = qk.s16;
-            kz = qk.z16;
-            vs = qv.s16;
-            vz = qv.z16;
+            emit_fresh(s, true, xk, xv);
         }
-        if (!live) kw0 = kw1 = vw0 = vw1 = 0;
-        if (high) *reinterpret_cast<uint2 *>(pg + K_OFF + s * 128 + 8 * c) = make_uint2(kw0, kw1);
-        else *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = kw0;
-        *reinterpret_cast<uint2 *>(sv + s * D + 8 * c) = make_uint2(vw0, vw1);
-        if (c == 0) {
-            s_par[wave][s][0] = live ? ks : 0;
-            s_par[wave][s][1] = live ? kz : 0;
-            s_par[wave][s][2] = live ? vs : 0;
-            s_par[wave][s][3] = live ? vz : 0;
-        }
+    }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

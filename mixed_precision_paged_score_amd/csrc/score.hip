@@ -14,7 +14,10 @@
 
 namespace kvc {
 
-constexpr int SCORE_TILE = 64;   // tokens per workgroup
+#ifndef KVC_SCORE_TILE
+#define KVC_SCORE_TILE 256
+#endif
+constexpr int SCORE_TILE = KVC_SCORE_TILE;   // tokens per workgroup
 constexpr int SCORE_THREADS = 256;
 constexpr int MAX_HKV_LDS = 256;
 

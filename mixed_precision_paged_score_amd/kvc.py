@@ -93,8 +93,7 @@ def workspace_bytes(geom, op, max_seqlen=0):
 
 
 def workspace(geom, op, max_seqlen=0, device="cuda"):
-    """Workspace for one call type.  Zero-filled: the decode workspace's arrival counters
-    must start at zero (the library leaves them zero after every call)."""
+    """Workspace for one call type (zero-filled; every call initialises what it reads)."""
     n = max(workspace_bytes(geom, op, max_seqlen), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 

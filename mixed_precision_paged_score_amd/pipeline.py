@@ -58,6 +58,26 @@ class PromptPath:
         kvc.paged_decode_attention(self.geom, layer, self.pool, q, self.scale, out,
                                    self.ws_decode)
 
+    # -- HIP graphs -------------------------------------------------------------------------
+    # Every library call is asynchronous on the current stream, reads its sizes from device
+    # memory and clears its own scratch with kernels (no memset nodes), so a sequence of calls
+    # can be captured once and replayed; each replay redoes all the work on the current data.
+    def capture_prompt(self, layer, acc, k, v):
+        """Graph of one prompt round of a layer: score, compact (prompt mode: the layer's
+        current pages go back to the ring, new ones are assigned) and quantize/place."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.prompt(layer, acc, k, v)
+        return g
+
+    def capture_decode(self, layer, qs, out):
+        """Graph of len(qs) decode steps (one per query tensor, all writing `out`)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for q in qs:
+                self.decode(layer, q, out)
+        return g
+
 
 class GenerationPath(PromptPath):
     """Prompt, then per decode step one appended token per (request, KV head), and every
