@@ -94,44 +94,69 @@ template <> struct Vals<false> {
     uint4 p0, p1;
 };
 
+// Page reads are buffer loads: one descriptor per page (wave-uniform, scalar registers:
+// page address and its size as the range) and a 32-bit per-lane offset, so no lane does
+// 64-bit address arithmetic, and an offset outside the page would read zeros.
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+constexpr int BUF_FLAGS = 0x00020000;      // raw (untyped) 32-bit access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(page), 0, PAGE, BUF_FLAGS);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u4v x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u2v x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(x[0], x[1]);
+}
+
 template <bool HIGH>
-__device__ __forceinline__ Keys<HIGH> load_keys(const uint8_t *pga, const uint8_t *pgb, int fa,
-                                                int fb, int lane) {
-    const int j = lane >> 4, tok = lane & 15;
+__device__ __forceinline__ Keys<HIGH> load_keys(__amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, int fa, int fb,
+                                                int lane) {
+    const uint32_t j = lane >> 4, tok = lane & 15;
     Keys<HIGH> d;
     if constexpr (HIGH) {
-        const uint4 *a = reinterpret_cast<const uint4 *>(pga + K_OFF + tok * 128 + 32 * j);
-        const uint4 *b = reinterpret_cast<const uint4 *>(pgb + K_OFF + tok * 128 + 32 * j);
-        d.ka0 = a[0];
-        d.ka1 = a[1];
-        d.kb0 = b[0];
-        d.kb1 = b[1];
+        const uint32_t o = K_OFF + tok * 128 + 32 * j;
+        d.ka0 = ld16(ra, o);
+        d.ka1 = ld16(ra, o + 16);
+        d.kb0 = ld16(rb, o);
+        d.kb1 = ld16(rb, o + 16);
     } else {
-        d.ka = *reinterpret_cast<const uint4 *>(pga + K_OFF + (16 * fa + tok) * 64 + 16 * j);
-        d.kb = *reinterpret_cast<const uint4 *>(pgb + K_OFF + (16 * fb + tok) * 64 + 16 * j);
+        d.ka = ld16(ra, K_OFF + (16 * uint32_t(fa) + tok) * 64 + 16 * j);
+        d.kb = ld16(rb, K_OFF + (16 * uint32_t(fb) + tok) * 64 + 16 * j);
     }
     return d;
 }
 
 template <bool HIGH>
-__device__ __forceinline__ Vals<HIGH> load_vals(const uint8_t *pga, const uint8_t *pgb, int fa,
-                                                int fb, int lane, bool own_b) {
-    const int j = lane >> 4;
+__device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, int fa, int fb,
+                                                int lane, bool own_b) {
+    const uint32_t j = lane >> 4;
     Vals<HIGH> d;
-    const uint8_t *pgo = own_b ? pgb : pga;
-    const int fo = own_b ? fb : fa;
     if constexpr (HIGH) {
-        d.va = *reinterpret_cast<const uint4 *>(pga + V_OFF + 16 * lane);
-        d.vb = *reinterpret_cast<const uint4 *>(pgb + V_OFF + 16 * lane);
-        const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 32 * j);
-        d.p0 = pp[0];
-        d.p1 = pp[1];
+        d.va = ld16(ra, V_OFF + 16 * uint32_t(lane));
+        d.vb = ld16(rb, V_OFF + 16 * uint32_t(lane));
+        // parameters of the lane's own tile: each half-wave reads its tile's page
+        const uint32_t o = PARAM_OFF + 32 * j;
+        if (own_b) {
+            d.p0 = ld16(rb, o);
+            d.p1 = ld16(rb, o + 16);
+        } else {
+            d.p0 = ld16(ra, o);
+            d.p1 = ld16(ra, o + 16);
+        }
     } else {
-        d.va = *reinterpret_cast<const uint2 *>(pga + V_OFF + 16 * lane + 8 * fa);
-        d.vb = *reinterpret_cast<const uint2 *>(pgb + V_OFF + 16 * lane + 8 * fb);
-        const uint4 *pp = reinterpret_cast<const uint4 *>(pgo + PARAM_OFF + 8 * (16 * fo + 4 * j));
-        d.p0 = pp[0];
-        d.p1 = pp[1];
+        // the two LOW tiles of a pair are the halves of one page (ra and rb are the same)
+        d.va = ld8(ra, V_OFF + 16 * uint32_t(lane) + 8 * uint32_t(fa));
+        d.vb = ld8(rb, V_OFF + 16 * uint32_t(lane) + 8 * uint32_t(fb));
+        const uint32_t o = PARAM_OFF + 8 * (16 * uint32_t(own_b ? fb : fa) + 4 * j);
+        d.p0 = ld16(ra, o);
+        d.p1 = ld16(ra, o + 16);
     }
     return d;
 }
@@ -337,12 +362,14 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         auto keys_at = [&](int t) {
             t = min(t, tlast);
             const int tb = tb_of(t);
-            return load_keys<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane);
+            return load_keys<HIGH>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1, tb & 1,
+                                   lane);
         };
         auto vals_at = [&](int t) {
             t = min(t, tlast);
             const int tb = tb_of(t);
-            return load_vals<HIGH>(page_of(t), page_of(tb), t & 1, tb & 1, lane, own_b);
+            return load_vals<HIGH>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1, tb & 1,
+                                   lane, own_b);
         };
         Keys<HIGH> ka = keys_at(c0), kb;
         Vals<HIGH> va = vals_at(c0), vb;
