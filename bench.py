@@ -72,6 +72,37 @@ def copy_calibration():
           flush=True)
 
 
+def traffic_record(workload):
+    """HBM bytes per decode call and per compaction round from the committed rocprofv3
+    counter summary (profiles/traffic_<workload>.md), each kept only while the kernel sources
+    it was measured on are unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None, None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None, None
+    csrc = os.path.join(ROOT, "mixed_precision_paged_score_amd", "csrc")
+
+    def same(names):
+        for n in names:
+            f = os.path.join(csrc, n)
+            if not os.path.exists(f) or n not in rec["kernel_sources_sha256"]:
+                return False
+            if hashlib.sha256(open(f, "rb").read()).hexdigest() != rec["kernel_sources_sha256"][n]:
+                return False
+        return True
+    dec = rec["decode_call_bytes"]["total"] if same(["attention.hip", "workspace.h",
+                                                      "kvc_internal.h"]) else None
+    comp = rec["compaction_round_bytes"]["total"] if same(
+        ["score.hip", "compact.hip", "quantize.hip", "quant_row.h", "workspace.h",
+         "kvc_internal.h"]) else None
+    return dec, comp
+
+
 def decode_algorithmic_bytes(count, B, Hq):
     """Bytes the decode must read/write: per live HIGH token 128 + 64 code bytes + 8 bytes of
     scale/zero, per live LOW token 64 + 32 + 8, 4 bytes per page id, q and fp32 output."""
@@ -195,6 +226,7 @@ def main():
     comp_gbps = cbytes / comp_s / 1e9
     ms_per_step = wall / a.steps * 1e3
     nh, nl = int(count[..., 0].sum()), int(count[..., 1].sum())
+    dec_traffic, comp_traffic = traffic_record(w.name)
     res = {
         "metric": "KV tokens compacted/s + paged decode attn GB/s (fraction of HBM peak)",
         "value": token_heads / comp_s,
@@ -215,13 +247,14 @@ def main():
                    "window": w.window},
         "compaction": {"ms": comp_s * 1e3, "GBps": comp_gbps, "frac_hbm": comp_gbps / HBM_PEAK_GBPS,
                        "algorithmic_bytes": cbytes, "token_heads": token_heads,
-                       "high": nh, "low": nl, "pruned": token_heads - nh - nl},
+                       "high": nh, "low": nl, "pruned": token_heads - nh - nl,
+                       "traffic": comp_traffic},
         "decode_GBps": dec_gbps,
         "decode": {"us_per_call": dec_s * 1e6, "GBps": dec_gbps,
                    "frac_hbm": dec_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},
         "pool_status": status,
     }
     if not a.no_cpu_baseline:

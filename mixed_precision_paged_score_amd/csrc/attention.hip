@@ -216,6 +216,25 @@ struct WaveState {
     float l, lz, lp; // partial sums of the lane's own scores: p, p*zero_v, P' (offset removal)
 };
 
+__device__ __forceinline__ float fmax_raw(float a, float b) {   // no NaNs here: plain v_max
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// max over the lanes of one score column: the four 16-lane groups (xor 16, xor 32) and the
+// two tile halves (xor 8), with lane swaps and a row rotation instead of LDS permutes
+__device__ __forceinline__ float max_over_column(float x) {
+    uint32_t u = __float_as_uint(x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmax_raw(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    u = __float_as_uint(x);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmax_raw(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf,
+                                                             false));   // row_ror:8
+    return fmax_raw(x, y);
+}
+
 struct Magic {
     uint32_t k8;     // 0x64646464 (key bytes -> 1024 + code)
     uint32_t c16;    // 0x4C004C00 (4/2-bit codes -> 16 + code)
@@ -227,8 +246,9 @@ struct Magic {
 // lane's softmax work is useful although G <= 8.
 template <bool HIGH>
 __device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_qa)[64],
-                                          const uint4 (*s_qb)[64], int lane, const Magic &mg) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+                                          const uint4 (*s_qb)[64], int lane, const Magic &mg,
+                                          float acc0) {
+    f4 acc = {acc0, acc0, acc0, acc0};      // -code offset * sum(q): removes the offset
     // an opaque lane index keeps the compiler from hoisting the LDS reads out of the loop
     // (which would pin 32 registers for the operands)
     int li = lane;
@@ -254,23 +274,20 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
                                                 const Magic &mg, WaveState &st) {
     const int j = lane >> 4, c = lane & 15;
     const bool own_b = c >= 8;
-    constexpr float KOFF = HIGH ? KOFF_HIGH : COFF;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
     float L[4], vs[4], vz[4];
     float tmax = M_INIT;
-    const float koff_sum = KOFF * sumq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float ks = half_lo(pw[2 * r]), kz = half_hi(pw[2 * r]);
         vs[r] = half_lo(pw[2 * r + 1]);
         vz[r] = half_hi(pw[2 * r + 1]);
-        const float x = (ks * (acc[r] - koff_sum) + kz * sumq) * scale_log2;   // q.k_hat
+        // q.k_hat * scale * log2(e); sumq is already scaled by scale * log2(e)
+        const float x = ks * (acc[r] * scale_log2) + kz * sumq;
         L[r] = (4 * j + r < live_own) ? x : -__builtin_inff();
         tmax = fmaxf(tmax, L[r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));      // both tiles of the pair
+    tmax = max_over_column(tmax);
     // the branch is uniform, but written as a per-lane condition (an opaque lane value that
     // is always 1) the compiler predicates it instead of splitting the accumulators' live
     // ranges, which would copy all 32 of them on the common path
@@ -343,6 +360,8 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
                                              const Magic &mg, WaveState &st) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
     const bool own_b = (lane & 15) >= 8;
+    const float acc0 = -(HIGH ? KOFF_HIGH : COFF) * sumq;   // the key codes' offset
+    const float sumq_s = sumq * scale_log2;
     for (int c0 = t0; c0 < t1; c0 += 64 * TPP) {
         const int c1 = min(t1, c0 + 64 * TPP);
         const int p0 = c0 / TPP;
@@ -375,16 +394,16 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         Vals<HIGH> va = vals_at(c0), vb;
         for (int t = c0;;) {
             kb = keys_at(t + 2);
-            f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg);
+            f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg, acc0);
             vb = vals_at(t + 2);
-            pair_softmax_pv<HIGH>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq, scale_log2,
+            pair_softmax_pv<HIGH>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s, scale_log2,
                                   lane, mg, st);
             t += 2;
             if (t >= c1) break;
             ka = keys_at(t + 2);
-            acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg);
+            acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg, acc0);
             va = vals_at(t + 2);
-            pair_softmax_pv<HIGH>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq, scale_log2,
+            pair_softmax_pv<HIGH>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s, scale_log2,
                                   lane, mg, st);
             t += 2;
             if (t >= c1) break;
