@@ -104,20 +104,23 @@ def traffic_record(workload):
 
 
 def decode_algorithmic_bytes(count, B, Hq):
-    """Bytes the decode must read/write: per live HIGH token 128 + 64 code bytes + 8 bytes of
-    scale/zero, per live LOW token 64 + 32 + 8, 4 bytes per page id, q and fp32 output."""
+    """Bytes the decode must move per call, per live token-head 204 (HIGH: 128 + 64 code bytes,
+    8 bytes of scale/zero, 4 of position) or 108 (LOW: 64 + 32 + 8 + 4), 4 per page id, the
+    fp16 query and the fp32 output."""
     nh = count[..., 0].astype(np.int64)
     nl = count[..., 1].astype(np.int64)
     pages = -(-nh // 16) + -(-nl // 32)
-    return int((nh * 200 + nl * 104 + pages * 4).sum() + B * Hq * 128 * (2 + 4))
+    return int((nh * 204 + nl * 108 + pages * 4).sum() + B * Hq * 128 * (2 + 4))
 
 
 def compaction_algorithmic_bytes(count, T, Hkv, Hq):
-    """Read K+V fp16 (512 B) and accumulators (4 B per query head) of every token-head; write
-    200 B per HIGH and 104 B per LOW token-head (codes + scale/zero) + 4 B position, tier byte."""
-    nh = count[..., 0].astype(np.int64).sum()
-    nl = count[..., 1].astype(np.int64).sum()
-    return int(T * Hkv * 512 + T * Hq * 4 + T * Hkv + nh * 204 + nl * 108)
+    """Per token-head: read K+V fp16 (512 B) and the accumulators (4 B per query head); write
+    204 B per HIGH and 108 B per LOW token-head (codes, scale/zero, position); 4 B per page of
+    page-table, ring and reverse-map traffic."""
+    nh = count[..., 0].astype(np.int64)
+    nl = count[..., 1].astype(np.int64)
+    pages = int((-(-nh // 16) + -(-nl // 32)).sum())
+    return int(T * Hkv * 512 + T * Hq * 4 + nh.sum() * 204 + nl.sum() * 108 + pages * 4)
 
 
 def cpu_baseline(w, k, v, acc, qs, nreq):

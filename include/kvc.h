@@ -68,7 +68,12 @@ enum { KVC_PRUNE = 0, KVC_LOW = 1, KVC_HIGH = 2, KVC_FRESH = 3 };
 /* unified page format (both tiers share one 3456-byte page):
  *   [   0, 2048)  key codes: HIGH 16 slots x 128 B (8-bit), LOW 32 slots x 64 B (4-bit)
  *   [2048, 3072)  value codes, 64 units of 16 B laid out for the decode kernel's matrix
- *                 operands: HIGH 4-bit, LOW 2-bit (exact bit positions: the design doc)
+ *                 operands: unit 16j + l (j < 4, l < 16) holds channels l, l+16, ..., l+112;
+ *                 HIGH (4-bit): slot 4j + r, channel 16n + l in word n >> 1, nibble
+ *                 2(n & 1) + (r >> 1) + 4(r & 1); LOW (2-bit): slot 16f + 4j + r in word
+ *                 2f + (n >> 2), 2-bit field 2(n & 3) + (r >> 1) + 8(r & 1)
+ *   key codes of a LOW slot: word w (little-endian) holds channels 8w..8w+7, channel
+ *                 8w + e in nibble (e & 1) + 2(e >> 2) + 4((e >> 1) & 1)
  *   [3072, 3328)  per slot: key scale, key zero, value scale, value zero (fp16)
  *   [3328, 3456)  per slot: token position (int32), -1 for an empty slot            */
 #define KVC_HEAD_DIM 128

@@ -2,7 +2,7 @@
 
 Source: DiffKV review page -- the abstract's memory manager serves attention over the
 compressed, paged KV cache, and "Assumptions" lists standard causal multi-head attention
-(the page's Eq. 1).  Reading taken (DESIGN.md): one new query per request attends to every
+(the page's Eq. 1).  Reading taken: one new query per request attends to every
 live cached token of its KV head (all of them precede it, so there is no mask), with
 softmax scale 1/sqrt(128); query head hq reads KV head hq // G.  Keys and values are the
 float32 reconstructions code*scale + zero.  Accumulation is float64; a head with no live

@@ -5,7 +5,7 @@ at high precision, so a generated token enters the HIGH tier.  Referee major com
 token that leaves the window is irreversibly demoted or pruned (tiers never rise).  "What
 carries the argument": pages are re-assigned by prefix sum over the circular free list.
 
-Readings taken (DESIGN.md): every decode step appends one token per (request, KV head) as
+Readings taken: every decode step appends one token per (request, KV head) as
 K8V4 in the next HIGH slot; every `round` steps the tokens are re-scored with the previous
 tier as a ceiling; a head with any demotion, prune or kept fresh token is rebuilt (fresh
 row, old pages returned).  A token keeps its codes while its tier is unchanged; a HIGH

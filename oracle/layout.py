@@ -2,7 +2,7 @@
 
 Source: DiffKV review page, "Core claim" -- one GPU-resident manager with *unified* pages
 shared by both precision tiers.  The page prints no byte layout; this module is the
-layout this project defines ("Unified page"), written out independently of the
+layout this project defines, written out independently of the
 GPU code so that page images can be compared byte for byte.
 
 One page is 3456 bytes and holds either 16 HIGH (K8V4) tokens or 32 LOW (K4V2) tokens:

@@ -4,7 +4,7 @@ Test infrastructure only.
 
 Source: DiffKV review page, "Core claim" (K8V4 for important tokens, K4V2 for moderately
 important ones, unified pages) and "What carries the argument" (each head owns its own
-high- and low-precision pages).  Reading taken (DESIGN.md): within one head and one tier,
+high- and low-precision pages).  Reading taken: within one head and one tier,
 tokens take slots in ascending position order, so HIGH token number s (counting from 0 in
 position order) sits in slot s % 16 of the head's HIGH page s // 16 (row position s // 16),
 and LOW token number s in slot s % 32 of LOW page s // 32 (row position C-1 - s // 32).

@@ -8,7 +8,7 @@ circular free page list gives every head a disjoint contiguous region of page ID
 allocation and recycling happen on the GPU in one coordinated step.  "Core claim": unified
 pages, a circular free page list and a bidirectional page table.
 
-Readings taken (the design doc lists them):
+Readings taken:
   * the ring holds page ids; the free pages are ring[(head + k) mod P] for k < tail - head;
     head and tail only grow.  Pages are taken at head and returned at tail.
   * one row of C slots per (layer, request, KV head): HIGH pages fill positions 0,1,2,...

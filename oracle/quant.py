@@ -2,7 +2,7 @@
 
 Source: DiffKV review page, "Core claim" and the free-parameter ledger -- important tokens
 are stored as K8V4 (8-bit keys, 4-bit values), moderately important ones as K4V2.  The page
-does not print the quantizer; the reading taken (listed in the design doc) is the plain
+does not print the quantizer; the reading taken is the plain
 per-token, per-head asymmetric min/max scheme over the 128 channels of one key or value row:
 
     mn, mx  = min and max of the row's fp16 values (exact in float32)

@@ -9,7 +9,7 @@ sequence length.  Free-parameter ledger: the most recent W = 64 tokens are alway
 high precision.  Referee major comment 3: a token leaving the window is irreversibly
 demoted or pruned, so a re-tier never promotes.
 
-Readings taken where the page is silent (each listed in the design doc):
+Readings taken where the page is silent:
   * "subsequent tokens" = strictly later query positions, so token t of a length-N request
     is averaged over cnt = N-1-t queries; the caller supplies the sum (acc_sum), the
     division happens here.
