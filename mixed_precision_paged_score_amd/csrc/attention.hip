@@ -41,6 +41,13 @@ constexpr float M_INIT = -1.0e30f;          // finite "minus infinity" for the r
 #define KVC_DEC_OCC 3
 #endif
 constexpr int DEC_WAVES = KVC_DEC_WAVES;    // waves per workgroup (slices of one head)
+#ifndef KVC_DEC_UH
+#define KVC_DEC_UH 3
+#endif
+#ifndef KVC_DEC_UL
+#define KVC_DEC_UL 2
+#endif
+constexpr int DEC_UH = KVC_DEC_UH, DEC_UL = KVC_DEC_UL;   // slice weights of HIGH / LOW tiles
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -438,12 +445,15 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     const int qH = ceil_div(nh, HS);
     const int tL = ceil_div(nl, 16);
-    // work units: HIGH tile 2, LOW tile 1; slices start on even tiles (pairs stay in a page)
-    const int64_t W = 2 * int64_t(qH) + tL;
+    // work units: a HIGH tile (one page) weighs DEC_UH, a LOW tile (half a page) DEC_UL;
+    // slices start on even LOW tiles (pairs stay in a page)
+    const int64_t WH = int64_t(DEC_UH) * qH;
+    const int64_t W = WH + int64_t(DEC_UL) * tL;
     const int NC = S * DEC_WAVES;
     const int cc = s * DEC_WAVES + wave;
     auto tile_of = [&](int64_t x) -> int {
-        int t = x <= 2 * int64_t(qH) ? int((x + 1) >> 1) : qH + int(x - 2 * int64_t(qH));
+        int t = x <= WH ? int((x + DEC_UH - 1) / DEC_UH)
+                        : qH + int((x - WH + DEC_UL - 1) / DEC_UL);
         if (t > qH) t = qH + ((t - qH + 1) & ~1);     // LOW pairs start on even LOW tiles
         return min(t, qH + tL);
     };
