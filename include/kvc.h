@@ -104,7 +104,8 @@ typedef struct {
 } kvc_pool;
 
 /* Operation ids for kvc_workspace_bytes */
-enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4 };
+enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4,
+       KVC_OP_DECODE_ACC = 5 };
 
 /* Version string of the library. */
 const char *kvc_version(void);
@@ -215,6 +216,25 @@ int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_po
                                const uint16_t *q, float softmax_scale, void *out,
                                int32_t out_is_fp32, void *workspace, size_t workspace_bytes,
                                kvc_stream_t stream);
+
+/* The same decode attention, and it adds each cached token's attention weight from this
+ * query into the significance accumulators: the query is a later token for every cached
+ * token, so acc_sum[cu_seqlens[b] + pos][hq] += softmax weight of (b, hq) on the live token at
+ * position pos (DiffKV review page, "What carries the argument": a token's score is the mean
+ * of the attention it receives from subsequent tokens).  The weights are the ones the output
+ * uses: exp(s*q.k_hat - max) / sum over the head's live tokens.  Pruned tokens get nothing.
+ *   acc_sum     float32 [T][Hq], the layout kvc_score_tokens reads; updated in place
+ *   cu_seqlens  int32 [B+1] of the same requests (N_b = cu_seqlens[b+1] - cu_seqlens[b]); a
+ *               live token with position >= N_b is skipped and sets KVC_DEV_SEQLEN
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE_ACC, 0) bytes, 256-B aligned (split
+ *        partials, softmax max/sum per query head, logits of every live token).
+ * Every (token, query head) is written by one thread: no atomics, deterministic.
+ * Errors: as kvc_paged_decode_attention; KVC_E_NULL if acc_sum or cu_seqlens is NULL. */
+int kvc_paged_decode_attention_acc(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                                   const uint16_t *q, float softmax_scale, void *out,
+                                   int32_t out_is_fp32, float *acc_sum,
+                                   const int32_t *cu_seqlens, void *workspace,
+                                   size_t workspace_bytes, kvc_stream_t stream);
 
 #ifdef __cplusplus
 }

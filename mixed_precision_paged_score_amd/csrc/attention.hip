@@ -275,10 +275,12 @@ __device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_q
     return acc;
 }
 
-template <bool HIGH>
+// LG: the lane also stores its four logits (log2 units, -inf for empty slots) at lg, 16
+// bytes, when lg is not null (the score-accumulating variant)
+template <bool HIGH, bool LG>
 __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> &d, int live_own,
                                                 float sumq, float scale_log2, int lane,
-                                                const Magic &mg, WaveState &st) {
+                                                const Magic &mg, WaveState &st, float *lg) {
     const int j = lane >> 4, c = lane & 15;
     const bool own_b = c >= 8;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
@@ -293,6 +295,9 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
         const float x = ks * (acc[r] * scale_log2) + kz * sumq;
         L[r] = (4 * j + r < live_own) ? x : -__builtin_inff();
         tmax = fmaxf(tmax, L[r]);
+    }
+    if constexpr (LG) {
+        if (lg) *reinterpret_cast<float4 *>(lg) = make_float4(L[0], L[1], L[2], L[3]);
     }
     tmax = max_over_column(tmax);
     // the branch is uniform, but written as a per-lane condition (an opaque lane value that
@@ -359,12 +364,15 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
 // one lane-indexed register, so no load waits on another load.  The next pair's keys are
 // requested before this pair's scores, its values and parameters before this pair's softmax
 // (reusing the registers of the keys just consumed).
-template <bool HIGH>
+// lgh (LG only): the head's logit rows [tile][GT][16] offset to this tier's first tile and
+// to the lane's query head and token group (null for lanes without a query head)
+template <bool HIGH, bool LG>
 __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
                                              int C, const uint8_t *pages,
                                              const uint4 (*s_qa)[64], const uint4 (*s_qb)[64],
                                              float sumq, float scale_log2, int lane,
-                                             const Magic &mg, WaveState &st) {
+                                             const Magic &mg, WaveState &st, float *lgh,
+                                             int lg_tile_stride) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
     const bool own_b = (lane & 15) >= 8;
     const float acc0 = -(HIGH ? KOFF_HIGH : COFF) * sumq;   // the key codes' offset
@@ -397,21 +405,30 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
             return load_vals<HIGH>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1, tb & 1,
                                    lane, own_b);
         };
+        // the lane's logit slot for the pair starting at tile t (its own tile of the pair)
+        auto lg_at = [&](int t) -> float * {
+            if constexpr (!LG) {
+                return nullptr;
+            } else {
+                const int own = own_b ? t + 1 : t;
+                return (lgh && own < c1) ? lgh + int64_t(own) * lg_tile_stride : nullptr;
+            }
+        };
         Keys<HIGH> ka = keys_at(c0), kb;
         Vals<HIGH> va = vals_at(c0), vb;
         for (int t = c0;;) {
             kb = keys_at(t + 2);
             f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg, acc0);
             vb = vals_at(t + 2);
-            pair_softmax_pv<HIGH>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s, scale_log2,
-                                  lane, mg, st);
+            pair_softmax_pv<HIGH, LG>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s,
+                                      scale_log2, lane, mg, st, lg_at(t));
             t += 2;
             if (t >= c1) break;
             ka = keys_at(t + 2);
             acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg, acc0);
             va = vals_at(t + 2);
-            pair_softmax_pv<HIGH>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s, scale_log2,
-                                  lane, mg, st);
+            pair_softmax_pv<HIGH, LG>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s,
+                                      scale_log2, lane, mg, st, lg_at(t));
             t += 2;
             if (t >= c1) break;
         }
@@ -420,11 +437,14 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
 
 // grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
 // take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
+// LG: also store every live token's logit per query head into lg [head][tile][GT][16]
+// (tiles in the head's order: HIGH tiles, then LOW tiles), for the score accumulation
+template <bool LG>
 __global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(KVC_DEC_OCC)))
 void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
                         const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
                         const int32_t *__restrict__ count_l, int Hkv, int GT, int C, int S,
-                        float *__restrict__ part) {
+                        float *__restrict__ part, float *__restrict__ lg, int64_t tiles_cap) {
     __shared__ float s_o[DEC_WAVES][8][D];      // [wave][query head][channel]
     __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16],
         s_lp[DEC_WAVES][16];
@@ -498,10 +518,16 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
     const int32_t *row = rows_l + int64_t(i) * C;
-    attend_range<true>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2, lane,
-                       mg, st);
-    attend_range<false>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
-                        scale_log2, lane, mg, st);
+    float *lgh = nullptr;       // the lane's query head and token group in tile 0 of the head
+    if constexpr (LG) {
+        if (gq < G) lgh = lg + ((int64_t(i) * tiles_cap) * GT + g0 + gq) * 16 + 4 * j;
+    }
+    const int lg_stride = GT * 16;
+    attend_range<true, LG>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2,
+                           lane, mg, st, lgh, lg_stride);
+    attend_range<false, LG>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
+                            scale_log2, lane, mg, st,
+                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride);
     // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
     for (int o = 8; o <= 32; o <<= 1) {
@@ -560,7 +586,8 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 // independent, and weighted with exp2(m_s - M) read from the owning lane
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
                                                              int Hq, int G, int S, int nqh,
-                                                             void *out, int out_fp32) {
+                                                             void *out, int out_fp32,
+                                                             float *__restrict__ mls) {
     const int lane = threadIdx.x & 63;
     const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);    // b*Hq + hq
     if (qh >= nqh) return;
@@ -599,6 +626,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
     const int64_t idx = int64_t(qh) * D + 2 * lane;
     const float o0 = Ls > 0.0f ? r0 / Ls : 0.0f, o1 = Ls > 0.0f ? r1 / Ls : 0.0f;
+    if (mls && lane == 0) *reinterpret_cast<float2 *>(mls + 2 * int64_t(qh)) = make_float2(M, Ls);
     if (out_fp32) {
         *reinterpret_cast<float2 *>(static_cast<float *>(out) + idx) = make_float2(o0, o1);
     } else {
@@ -607,40 +635,125 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
 }
 
+// grid (B*Hkv, ceil(tiles_cap / 4)), 4 waves, one tile each: acc_sum[cu[b] + pos][hq] +=
+// exp2(logit - M) / L for the tile's live tokens and the head's GT query heads, where M and L
+// are the query head's softmax max and sum over all splits.  Each (token, query head) is
+// written by one lane, so no atomics are needed.
+__global__ __launch_bounds__(256) void decode_acc_kernel(
+    const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int GT, int C,
+    const float *__restrict__ lg, int64_t tiles_cap, const float *__restrict__ mls,
+    float *__restrict__ acc, int32_t *status) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x;
+    const int tile = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
+    if (tile >= qH + tL || tile >= tiles_cap) return;
+    const int b = i / Hkv, h = i - b * Hkv;
+    const int Hq = Hkv * GT;
+    int page, slot0, live;
+    if (tile < qH) {
+        page = rows_l[int64_t(i) * C + tile];
+        slot0 = 0;
+        live = min(HS, nh - HS * tile);
+    } else {
+        const int t = tile - qH;
+        page = rows_l[int64_t(i) * C + C - 1 - (t >> 1)];
+        slot0 = 16 * (t & 1);
+        live = min(16, nl - 16 * t);
+    }
+    const int lo = cu[b], N = cu[b + 1] - lo;
+    const int32_t *pos = reinterpret_cast<const int32_t *>(pages + int64_t(page) * PAGE + POS_OFF);
+    const float *lt = lg + (int64_t(i) * tiles_cap + tile) * GT * 16;
+    for (int k = lane; k < 16 * GT; k += 64) {
+        const int tok = k & 15, g = k >> 4;
+        if (tok >= live) continue;
+        const int p = pos[slot0 + tok];
+        if (p < 0 || p >= N) {
+            atomicOr(status, KVC_DEV_SEQLEN);
+            continue;
+        }
+        const int hq = h * GT + g;
+        const float2 ml = *reinterpret_cast<const float2 *>(mls + 2 * (int64_t(b) * Hq + hq));
+        if (!(ml.y > 0.0f)) continue;
+        const float w = __builtin_amdgcn_exp2f(lt[g * 16 + tok] - ml.x) / ml.y;
+        float *a = acc + (int64_t(lo) + p) * Hq + hq;
+        *a = *a + w;
+    }
+}
+
 }  // namespace kvc
 
 using namespace kvc;
 
-extern "C" int kvc_paged_decode_attention(const kvc_geom *g, int32_t layer, const kvc_pool *p,
-                                          const uint16_t *q, float softmax_scale, void *out,
-                                          int32_t out_is_fp32, void *ws, size_t ws_bytes,
-                                          kvc_stream_t stream) {
+namespace {
+
+int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint16_t *q,
+                float softmax_scale, void *out, int32_t out_is_fp32, float *acc_sum,
+                const int32_t *cu, void *ws, size_t ws_bytes, kvc_stream_t stream) {
     int rc = check_geom(g);
     if (rc) return rc;
     rc = check_pool(p);
     if (rc) return rc;
     if (!q || !out) return KVC_E_NULL;
+    const bool accum = acc_sum != nullptr || cu != nullptr;
+    if (accum && (!acc_sum || !cu)) return KVC_E_NULL;
     if (!aligned16(q) || !aligned16(out)) return KVC_E_ALIGN;
     if (layer < 0 || layer >= g->num_layers) return KVC_E_SHAPE;
     const int G = g->num_q_heads / g->num_kv_heads;
     if (G > 16) return KVC_E_SHAPE;
-    DecodeWs L(g);
+    DecodeWs L(g, accum);
     if (!ws || ws_bytes < L.bytes) return KVC_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part);
+    char *w = static_cast<char *>(ws);
+    float *part = reinterpret_cast<float *>(w + L.part);
+    float *mls = accum ? reinterpret_cast<float *>(w + L.mls) : nullptr;
+    float *lg = accum ? reinterpret_cast<float *>(w + L.lg) : nullptr;
     const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
     const int nheads = B * Hkv;
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
     const int ngp = (G + 7) / 8;
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3(L.splits * nheads * ngp), dim3(64 * DEC_WAVES), 0, s,
-                       q, softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
-                       part);
+    const dim3 grid(L.splits * nheads * ngp), block(64 * DEC_WAVES);
+    if (accum)
+        hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, block, 0, s, q,
+                           softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
+                           part, lg, L.tiles_cap);
+    else
+        hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, block, 0, s, q,
+                           softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
+                           part, nullptr, int64_t(0));
     rc = launch_check("kvc_paged_decode_attention/main");
     if (rc) return rc;
     const int nqh = B * g->num_q_heads;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((nqh + 3) / 4), dim3(256), 0, s, part,
-                       g->num_q_heads, G, L.splits, nqh, out, out_is_fp32);
-    return launch_check("kvc_paged_decode_attention/combine");
+                       g->num_q_heads, G, L.splits, nqh, out, out_is_fp32, mls);
+    rc = launch_check("kvc_paged_decode_attention/combine");
+    if (rc || !accum) return rc;
+    const dim3 agrid(nheads, unsigned((L.tiles_cap + 3) / 4));
+    hipLaunchKernelGGL(decode_acc_kernel, agrid, dim3(256), 0, s, p->pages, rows_l, count_l, cu,
+                       Hkv, G, C, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
+    return launch_check("kvc_paged_decode_attention_acc/accumulate");
+}
+
+}  // namespace
+
+extern "C" int kvc_paged_decode_attention(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                                          const uint16_t *q, float softmax_scale, void *out,
+                                          int32_t out_is_fp32, void *ws, size_t ws_bytes,
+                                          kvc_stream_t stream) {
+    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, nullptr, nullptr, ws,
+                       ws_bytes, stream);
+}
+
+extern "C" int kvc_paged_decode_attention_acc(const kvc_geom *g, int32_t layer,
+                                              const kvc_pool *p, const uint16_t *q,
+                                              float softmax_scale, void *out, int32_t out_is_fp32,
+                                              float *acc_sum, const int32_t *cu_seqlens,
+                                              void *ws, size_t ws_bytes, kvc_stream_t stream) {
+    if (!acc_sum || !cu_seqlens) return KVC_E_NULL;
+    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, acc_sum, cu_seqlens, ws,
+                       ws_bytes, stream);
 }

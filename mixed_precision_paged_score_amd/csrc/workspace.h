@@ -86,12 +86,22 @@ inline int decode_splits(const kvc_geom *g) {
 
 struct DecodeWs {
     int splits;
-    size_t part, bytes;
-    explicit DecodeWs(const kvc_geom *g) {
+    int64_t tiles_cap;     // tiles per head the logit buffer holds (HIGH pages + 2 x LOW pages)
+    size_t part, mls, lg, bytes;
+    // acc: also the buffers of the score-accumulating variant
+    DecodeWs(const kvc_geom *g, bool acc) {
         splits = decode_splits(g);
+        tiles_cap = 2 * int64_t(g->row_capacity);
         part = 0;          // float [B][Hkv][S][G][PART_STRIDE]
         bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
                          splits);
+        mls = bytes;       // float [B][Hq][2]: the softmax's max and sum per query head
+        lg = mls;          // float [B*Hkv][tiles_cap][G][16]: logits in the heads' tile order
+        if (acc) {
+            lg = mls + align256(sizeof(float) * 2 * size_t(g->batch) * g->num_q_heads);
+            bytes = lg + align256(sizeof(float) * size_t(g->batch) * g->num_q_heads *
+                                  size_t(tiles_cap) * 16);
+        }
     }
 };
 

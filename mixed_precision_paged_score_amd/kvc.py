@@ -15,12 +15,12 @@ OK, E_NULL, E_ALIGN, E_SHAPE, E_WORKSPACE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3,
 DEV_POOL_EXHAUSTED, DEV_ROW_OVERFLOW, DEV_SHRINK, DEV_COUNT_MISMATCH, DEV_SEQLEN = 1, 2, 4, 8, 16
 DEV_INTERNAL, DEV_BAD_TIER = 32, 64
 PRUNE, LOW, HIGH, FRESH = 0, 1, 2, 3
-OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND = 1, 2, 3, 4
+OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC = 1, 2, 3, 4, 5
 HEAD_DIM, HIGH_SLOTS, LOW_SLOTS, PAGE_BYTES = 128, 16, 32, 3456
 
 EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_init",
            "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
-           "kvc_paged_decode_attention", "kvc_append_tokens"]
+           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -55,9 +55,11 @@ _lib.kvc_compact_pages.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _vp, _sz, _
 _lib.kvc_quantize_and_place.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _sz, _vp]
+_lib.kvc_paged_decode_attention_acc.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _vp,
+                                                _vp, _sz, _vp]
 _lib.kvc_append_tokens.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
-           "kvc_paged_decode_attention", "kvc_append_tokens"):
+           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -161,6 +163,16 @@ def paged_decode_attention(geom, layer, pool, q, softmax_scale, out, ws, stream=
                                            _ptr(q), float(softmax_scale), _ptr(out),
                                            int(out.dtype == torch.float32), _ptr(ws), ws.numel(),
                                            _stream(stream)), "kvc_paged_decode_attention")
+
+
+def paged_decode_attention_acc(geom, layer, pool, q, softmax_scale, out, acc_sum, cu_seqlens, ws,
+                               stream=None):
+    _check(_lib.kvc_paged_decode_attention_acc(ctypes.byref(geom), int(layer),
+                                               ctypes.byref(pool.c), _ptr(q), float(softmax_scale),
+                                               _ptr(out), int(out.dtype == torch.float32),
+                                               _ptr(acc_sum), _ptr(cu_seqlens), _ptr(ws),
+                                               ws.numel(), _stream(stream)),
+           "kvc_paged_decode_attention_acc")
 
 
 def append_tokens(geom, layer, pool, k_new, v_new, positions, ws, stream=None):
