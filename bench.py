@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-acc", action="store_true",
+                    help="skip the extra timing of decode attention with score accumulation")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
     ap.add_argument("--eager", action="store_true",
                     help="launch every library call from Python instead of replaying HIP graphs")
@@ -70,6 +72,34 @@ def copy_calibration():
                       "launches": 4, "median_ms": ms[len(ms) // 2],
                       "copy_GBps_read_plus_write": 2 * n / (ms[len(ms) // 2] / 1e3) / 1e9}),
           flush=True)
+
+
+def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
+    """Decode attention with score accumulation (every cached token's weight added into fp32
+    accumulators), the same decode steps, replayed as one graph outside the timed steps;
+    returns microseconds per call."""
+    acc = torch.zeros((path.T, path.w.num_q_heads), dtype=torch.float32, device=out.device)
+    if a.eager:
+        def run():
+            for q in qs:
+                path.decode_acc(0, q, out, acc)
+    else:
+        path.decode_acc(0, qs[0], out, acc)          # workspace made before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for q in qs:
+                path.decode_acc(0, q, out, acc)
+        run = g.replay
+    for _ in range(max(a.warmup, 1)):
+        run()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(a.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (a.steps * nsteps_dec)
 
 
 def traffic_record(workload):
@@ -216,6 +246,9 @@ def main():
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    acc_us = None
+    if not a.no_acc and nsteps_dec > 0:
+        acc_us = time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream)
     comp_ms = [e0.elapsed_time(e1) for (e0, e1, e2) in recs]
     dec_ms = [e1.elapsed_time(e2) / max(nsteps_dec, 1) for (e0, e1, e2) in recs]
     count = path.new_count.cpu().numpy()
@@ -224,6 +257,9 @@ def main():
     comp_s = float(np.mean(comp_ms)) / 1e3
     dec_s = float(np.mean(dec_ms)) / 1e3
     dbytes = decode_algorithmic_bytes(count, B, Hq)
+    # the accumulating decode also reads and writes one fp32 accumulator per live token and
+    # query head
+    acc_bytes = int(count.sum()) * (Hq // Hkv) * 8
     cbytes = compaction_algorithmic_bytes(count, T, Hkv, Hq)
     dec_gbps = dbytes / dec_s / 1e9
     comp_gbps = cbytes / comp_s / 1e9
@@ -255,6 +291,11 @@ def main():
         "decode_GBps": dec_gbps,
         "decode": {"us_per_call": dec_s * 1e6, "GBps": dec_gbps,
                    "frac_hbm": dec_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes},
+        "decode_with_score_accumulation": None if acc_us is None else {
+            "us_per_call": acc_us,
+            "GBps": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9,
+            "frac_hbm": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes": dbytes + acc_bytes},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},

@@ -223,13 +223,15 @@ int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_po
  * position pos (DiffKV review page, "What carries the argument": a token's score is the mean
  * of the attention it receives from subsequent tokens).  The weights are the ones the output
  * uses: exp(s*q.k_hat - max) / sum over the head's live tokens.  Pruned tokens get nothing.
- *   acc_sum     float32 [T][Hq], the layout kvc_score_tokens reads; updated in place
+ *   acc_sum     float32 [T][Hq], the layout kvc_score_tokens reads, 16-byte aligned;
+ *               updated in place
  *   cu_seqlens  int32 [B+1] of the same requests (N_b = cu_seqlens[b+1] - cu_seqlens[b]); a
  *               live token with position >= N_b is skipped and sets KVC_DEV_SEQLEN
  *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE_ACC, 0) bytes, 256-B aligned (split
  *        partials, softmax max/sum per query head, logits of every live token).
  * Every (token, query head) is written by one thread: no atomics, deterministic.
- * Errors: as kvc_paged_decode_attention; KVC_E_NULL if acc_sum or cu_seqlens is NULL. */
+ * Errors: as kvc_paged_decode_attention; KVC_E_NULL if acc_sum or cu_seqlens is NULL,
+ * KVC_E_ALIGN if acc_sum is not 16-byte aligned. */
 int kvc_paged_decode_attention_acc(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                                    const uint16_t *q, float softmax_scale, void *out,
                                    int32_t out_is_fp32, float *acc_sum,

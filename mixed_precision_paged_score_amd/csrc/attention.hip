@@ -275,12 +275,13 @@ __device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_q
     return acc;
 }
 
-// LG: the lane also stores its four logits (log2 units, -inf for empty slots) at lg, 16
-// bytes, when lg is not null (the score-accumulating variant)
+// LG: the lane also stores its four logits (log2 units, -inf for empty slots) at lg,
+// lg + lg_gt, ..., when lg is not null (the score-accumulating variant)
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> &d, int live_own,
                                                 float sumq, float scale_log2, int lane,
-                                                const Magic &mg, WaveState &st, float *lg) {
+                                                const Magic &mg, WaveState &st, float *lg,
+                                                int lg_gt) {
     const int j = lane >> 4, c = lane & 15;
     const bool own_b = c >= 8;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
@@ -297,7 +298,10 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
         tmax = fmaxf(tmax, L[r]);
     }
     if constexpr (LG) {
-        if (lg) *reinterpret_cast<float4 *>(lg) = make_float4(L[0], L[1], L[2], L[3]);
+        if (lg) {          // tokens 4j..4j+3 of the lane's tile, GT words apart
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lg[r * lg_gt] = L[r];
+        }
     }
     tmax = max_over_column(tmax);
     // the branch is uniform, but written as a per-lane condition (an opaque lane value that
@@ -364,8 +368,8 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
 // one lane-indexed register, so no load waits on another load.  The next pair's keys are
 // requested before this pair's scores, its values and parameters before this pair's softmax
 // (reusing the registers of the keys just consumed).
-// lgh (LG only): the head's logit rows [tile][GT][16] offset to this tier's first tile and
-// to the lane's query head and token group (null for lanes without a query head)
+// lgh (LG only): the head's logits [tile][16 tokens][GT] offset to this tier's first tile,
+// the lane's first token (4j) and its query head (null for lanes without a query head)
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
                                              int C, const uint8_t *pages,
@@ -421,14 +425,14 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
             f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg, acc0);
             vb = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t));
+                                      scale_log2, lane, mg, st, lg_at(t), lg_tile_stride / 16);
             t += 2;
             if (t >= c1) break;
             ka = keys_at(t + 2);
             acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg, acc0);
             va = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t));
+                                      scale_log2, lane, mg, st, lg_at(t), lg_tile_stride / 16);
             t += 2;
             if (t >= c1) break;
         }
@@ -437,7 +441,7 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
 
 // grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
 // take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
-// LG: also store every live token's logit per query head into lg [head][tile][GT][16]
+// LG: also store every live token's logit per query head into lg [head][tile][16][GT]
 // (tiles in the head's order: HIGH tiles, then LOW tiles), for the score accumulation
 template <bool LG>
 __global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(KVC_DEC_OCC)))
@@ -518,9 +522,9 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
     const int32_t *row = rows_l + int64_t(i) * C;
-    float *lgh = nullptr;       // the lane's query head and token group in tile 0 of the head
+    float *lgh = nullptr;       // the lane's query head and first token in tile 0 of the head
     if constexpr (LG) {
-        if (gq < G) lgh = lg + ((int64_t(i) * tiles_cap) * GT + g0 + gq) * 16 + 4 * j;
+        if (gq < G) lgh = lg + (int64_t(i) * tiles_cap * 16 + 4 * j) * GT + g0 + gq;
     }
     const int lg_stride = GT * 16;
     attend_range<true, LG>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2,
@@ -635,10 +639,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
 }
 
-// grid (B*Hkv, ceil(tiles_cap / 4)), 4 waves, one tile each: acc_sum[cu[b] + pos][hq] +=
-// exp2(logit - M) / L for the tile's live tokens and the head's GT query heads, where M and L
+// grid (B*Hkv, ACC_BLOCKS), 4 waves; wave w of block y takes tiles 4y + w, 4y + w +
+// 4*ACC_BLOCKS, ... of its head: acc_sum[cu[b] + pos][hq] += exp2(logit - M) / L for the
+// tile's live tokens and the head's GT query heads (lane k: token k / GT, query head k % GT,
+// so one token's query heads are neighbouring floats of one accumulator row), where M and L
 // are the query head's softmax max and sum over all splits.  Each (token, query head) is
-// written by one lane, so no atomics are needed.
+// written by one lane: no atomics, deterministic.
+constexpr int ACC_BLOCKS = 64;
 __global__ __launch_bounds__(256) void decode_acc_kernel(
     const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
     const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int GT, int C,
@@ -646,40 +653,41 @@ __global__ __launch_bounds__(256) void decode_acc_kernel(
     float *__restrict__ acc, int32_t *status) {
     const int lane = threadIdx.x & 63;
     const int i = blockIdx.x;
-    const int tile = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
-    if (tile >= qH + tL || tile >= tiles_cap) return;
+    const int ntiles = int(min(int64_t(qH + tL), tiles_cap));
     const int b = i / Hkv, h = i - b * Hkv;
     const int Hq = Hkv * GT;
-    int page, slot0, live;
-    if (tile < qH) {
-        page = rows_l[int64_t(i) * C + tile];
-        slot0 = 0;
-        live = min(HS, nh - HS * tile);
-    } else {
-        const int t = tile - qH;
-        page = rows_l[int64_t(i) * C + C - 1 - (t >> 1)];
-        slot0 = 16 * (t & 1);
-        live = min(16, nl - 16 * t);
-    }
     const int lo = cu[b], N = cu[b + 1] - lo;
-    const int32_t *pos = reinterpret_cast<const int32_t *>(pages + int64_t(page) * PAGE + POS_OFF);
-    const float *lt = lg + (int64_t(i) * tiles_cap + tile) * GT * 16;
-    for (int k = lane; k < 16 * GT; k += 64) {
-        const int tok = k & 15, g = k >> 4;
-        if (tok >= live) continue;
-        const int p = pos[slot0 + tok];
-        if (p < 0 || p >= N) {
-            atomicOr(status, KVC_DEV_SEQLEN);
-            continue;
+    const float *mlh = mls + 2 * (int64_t(b) * Hq + int64_t(h) * GT);
+    for (int tile = blockIdx.y * 4 + (threadIdx.x >> 6); tile < ntiles; tile += ACC_BLOCKS * 4) {
+        int page, slot0, live;
+        if (tile < qH) {
+            page = rows_l[int64_t(i) * C + tile];
+            slot0 = 0;
+            live = min(HS, nh - HS * tile);
+        } else {
+            const int t = tile - qH;
+            page = rows_l[int64_t(i) * C + C - 1 - (t >> 1)];
+            slot0 = 16 * (t & 1);
+            live = min(16, nl - 16 * t);
         }
-        const int hq = h * GT + g;
-        const float2 ml = *reinterpret_cast<const float2 *>(mls + 2 * (int64_t(b) * Hq + hq));
-        if (!(ml.y > 0.0f)) continue;
-        const float w = __builtin_amdgcn_exp2f(lt[g * 16 + tok] - ml.x) / ml.y;
-        float *a = acc + (int64_t(lo) + p) * Hq + hq;
-        *a = *a + w;
+        const int32_t *pos =
+            reinterpret_cast<const int32_t *>(pages + int64_t(page) * PAGE + POS_OFF) + slot0;
+        const float *lt = lg + (int64_t(i) * tiles_cap + tile) * 16 * GT;
+        for (int k = lane; k < live * GT; k += 64) {
+            const int tok = k / GT, g = k - tok * GT;
+            const int p = pos[tok];
+            if (p < 0 || p >= N) {
+                atomicOr(status, KVC_DEV_SEQLEN);
+                continue;
+            }
+            const float2 ml = *reinterpret_cast<const float2 *>(mlh + 2 * g);
+            if (!(ml.y > 0.0f)) continue;
+            const float w = __builtin_amdgcn_exp2f(lt[k] - ml.x) / ml.y;
+            float *a = acc + (int64_t(lo) + p) * Hq + int64_t(h) * GT + g;
+            *a = *a + w;
+        }
     }
 }
 
@@ -700,6 +708,7 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
     const bool accum = acc_sum != nullptr || cu != nullptr;
     if (accum && (!acc_sum || !cu)) return KVC_E_NULL;
     if (!aligned16(q) || !aligned16(out)) return KVC_E_ALIGN;
+    if (accum && !aligned16(acc_sum)) return KVC_E_ALIGN;
     if (layer < 0 || layer >= g->num_layers) return KVC_E_SHAPE;
     const int G = g->num_q_heads / g->num_kv_heads;
     if (G > 16) return KVC_E_SHAPE;
@@ -732,7 +741,7 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
                        g->num_q_heads, G, L.splits, nqh, out, out_is_fp32, mls);
     rc = launch_check("kvc_paged_decode_attention/combine");
     if (rc || !accum) return rc;
-    const dim3 agrid(nheads, unsigned((L.tiles_cap + 3) / 4));
+    const dim3 agrid(nheads, ACC_BLOCKS);
     hipLaunchKernelGGL(decode_acc_kernel, agrid, dim3(256), 0, s, p->pages, rows_l, count_l, cu,
                        Hkv, G, C, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
     return launch_check("kvc_paged_decode_attention_acc/accumulate");

@@ -96,7 +96,7 @@ struct DecodeWs {
         bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
                          splits);
         mls = bytes;       // float [B][Hq][2]: the softmax's max and sum per query head
-        lg = mls;          // float [B*Hkv][tiles_cap][G][16]: logits in the heads' tile order
+        lg = mls;          // float [B*Hkv][tiles_cap][16][G]: logits in the heads' tile order
         if (acc) {
             lg = mls + align256(sizeof(float) * 2 * size_t(g->batch) * g->num_q_heads);
             bytes = lg + align256(sizeof(float) * size_t(g->batch) * g->num_q_heads *
