@@ -368,6 +368,19 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
 // one lane-indexed register, so no load waits on another load.  The next pair's keys are
 // requested before this pair's scores, its values and parameters before this pair's softmax
 // (reusing the registers of the keys just consumed).
+// page ids of the first chunk (up to 64 pages) of tiles [t0, t1) of one tier: lane k holds
+// the id of page t0 / TPP + k (0 beyond the chunk)
+template <bool HIGH>
+__device__ __forceinline__ int first_chunk_pids(int t0, int t1, const int32_t *row, int C,
+                                                int lane) {
+    constexpr int TPP = HIGH ? 1 : 2;
+    if (t0 >= t1) return 0;
+    const int c1 = min(t1, t0 + 64 * TPP);
+    const int p0 = t0 / TPP;
+    const int np = (c1 - 1) / TPP - p0 + 1;
+    return lane < np ? (HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)]) : 0;
+}
+
 // lgh (LG only): the head's logits [tile][16 tokens][GT] offset to this tier's first tile,
 // the lane's first token (4j) and its query head (null for lanes without a query head)
 template <bool HIGH, bool LG>
@@ -376,7 +389,7 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
                                              const uint4 (*s_qa)[64], const uint4 (*s_qb)[64],
                                              float sumq, float scale_log2, int lane,
                                              const Magic &mg, WaveState &st, float *lgh,
-                                             int lg_tile_stride) {
+                                             int lg_tile_stride, int pid_first) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
     const bool own_b = (lane & 15) >= 8;
     const float acc0 = -(HIGH ? KOFF_HIGH : COFF) * sumq;   // the key codes' offset
@@ -385,8 +398,8 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         const int c1 = min(t1, c0 + 64 * TPP);
         const int p0 = c0 / TPP;
         const int np = (c1 - 1) / TPP - p0 + 1;
-        int pid = 0;
-        if (lane < np) pid = HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)];
+        int pid = pid_first;     // the first chunk's ids were requested by the caller early
+        if (c0 != t0) pid = lane < np ? (HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)]) : 0;
         auto page_of = [&](int t) -> const uint8_t * {
             return pages + int64_t(__builtin_amdgcn_readlane(pid, t / TPP - p0)) * PAGE;
         };
@@ -466,6 +479,12 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     const int Hq = Hkv * GT;
     const int G = min(8, GT - 8 * gp);         // query heads of this group
     const int g0 = 8 * gp;
+    // the query rows and the head's counts are requested together, before either is used
+    uint4 qv[4] = {};
+    if (gq < G) {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(q + (int64_t(b) * Hq + h * GT + g0 + gq) * D + 32 * j);
+        qv[0] = qp[0]; qv[1] = qp[1]; qv[2] = qp[2]; qv[3] = qp[3];
+    }
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     const int qH = ceil_div(nh, HS);
     const int tL = ceil_div(nl, 16);
@@ -486,13 +505,12 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     // query operands: lane (c, j) holds q[gq][32j + 8m + {0,2,1,3,4,6,5,7}], gq = c & 7,
     // kept in LDS for the whole workgroup (all its waves serve the same head): qa in columns
     // 0..7, qb in columns 8..15
+    // the first page ids of both tiers are requested before the workgroup waits on its barrier
+    const int32_t *row = rows_l + int64_t(i) * C;
+    const int pid_h = first_chunk_pids<true>(u0, min(u1, qH), row, C, lane);
+    const int pid_l = first_chunk_pids<false>(max(u0, qH) - qH, u1 - qH, row, C, lane);
     float sumq = 0.0f;
     {
-        uint4 qv[4] = {};
-        if (gq < G) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (int64_t(b) * Hq + h * GT + g0 + gq) * D + 32 * j);
-            qv[0] = qp[0]; qv[1] = qp[1]; qv[2] = qp[2]; qv[3] = qp[3];
-        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const h2 x0 = as_h2(qv[m].x), x1 = as_h2(qv[m].y), x2 = as_h2(qv[m].z), x3 = as_h2(qv[m].w);
@@ -521,17 +539,16 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
-    const int32_t *row = rows_l + int64_t(i) * C;
     float *lgh = nullptr;       // the lane's query head and first token in tile 0 of the head
     if constexpr (LG) {
         if (gq < G) lgh = lg + (int64_t(i) * tiles_cap * 16 + 4 * j) * GT + g0 + gq;
     }
     const int lg_stride = GT * 16;
     attend_range<true, LG>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2,
-                           lane, mg, st, lgh, lg_stride);
+                           lane, mg, st, lgh, lg_stride, pid_h);
     attend_range<false, LG>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
                             scale_log2, lane, mg, st,
-                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride);
+                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride, pid_l);
     // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
     for (int o = 8; o <= 32; o <<= 1) {
