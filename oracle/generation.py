@@ -138,6 +138,64 @@ class Generation:
                 self.rec[b][h] = new
         return tier, count, changed
 
+    def step(self, k_new, v_new, acc, alpha_h, alpha_l, window):
+        """One decode step under the per-step policy.  DiffKV review page: Algorithm 1 (as the
+        referee report describes it, major comment 2 and minor comment 4) scores the
+        candidate token t_c that has just left the recent window against alpha_h/N and
+        alpha_l/N; the free-parameter ledger keeps the most recent W tokens at high precision;
+        "What carries the argument": the score is the mean attention received from later
+        tokens.  Readings: the new token enters HIGH at position N-1 (N = length after it);
+        t_c = N-1-W; its score is max over the group of acc[t_c] / (N-1-t_c) and the
+        thresholds alpha/N, each a float32 division; HIGH keeps it, LOW re-quantizes it from
+        its K8V4 reconstruction, PRUNE drops it.  acc float32 [T][Hq] over the lengths after
+        the new token.  Returns uint8 [B][Hkv]: the tier given to t_c (255: none left)."""
+        count = self.counts()
+        G = acc.shape[1] // self.H
+        cu = np.concatenate([[0], np.cumsum([n + 1 for n in self.lens])])
+        decided = np.full((self.B, self.H), 255, np.uint8)
+        a_h, a_l = np.float32(alpha_h), np.float32(alpha_l)
+        for b in range(self.B):
+            N = self.lens[b] + 1
+            t_c = N - 1 - int(window)
+            for h in range(self.H):
+                count[b, h, 0] += 1                      # the new token
+                if t_c < 0:
+                    continue
+                cnt = np.float32(N - 1 - t_c)
+                score = max(np.float32(acc[cu[b] + t_c, h * G + g]) / cnt for g in range(G))
+                N32 = np.float32(N)
+                x = HIGH if score >= a_h / N32 else (LOW if score >= a_l / N32 else PRUNE)
+                decided[b, h] = x
+                if x != HIGH:
+                    count[b, h, 0] -= 1
+                if x == LOW:
+                    count[b, h, 1] += 1
+        self.pool.compact(self.layer, count, changed=np.zeros((self.B, self.H), np.uint8))
+        if self.pool.status:
+            return decided
+        self.count = count
+        for b in range(self.B):
+            pos = self.lens[b]
+            if pos == len(self._tb[b]):
+                grown = np.concatenate([self.tiers[b], np.zeros((pos + 1, self.H), np.uint8)])
+                self._set_tiers(b, grown)
+                self.lens[b] = pos
+            self._tb[b][pos] = HIGH
+            self.lens[b] = pos + 1
+            t_c = pos - int(window)
+            for h in range(self.H):
+                x = int(decided[b, h])
+                if x != 255:
+                    self._tb[b][t_c, h] = x
+                if (b, h) not in self.track:
+                    continue
+                self.rec[b][h][pos] = self._record(HIGH, k_new[b, h], v_new[b, h])
+                if x == LOW:
+                    self.rec[b][h][t_c] = self._demote(self.rec[b][h][t_c])
+                elif x == PRUNE:
+                    del self.rec[b][h][t_c]
+        return decided
+
     # ---- views -------------------------------------------------------------------------
     def head_pages(self, b, h):
         """Page images of one head: {HIGH: [...], LOW: [...]} in row order."""

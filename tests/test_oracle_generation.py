@@ -80,3 +80,107 @@ def test_rounds_are_monotone_survivors_keep_codes_demotions_requantize():
                 for pos in range(len(g.tiers[b])):
                     kept = int(g.tiers[b][pos, h]) in (ogen.HIGH, ogen.LOW)
                     assert kept == (pos in g.rec[b][h])
+
+
+# ---- the per-step policy ---------------------------------------------------------------
+
+def _prompted(rng, B, H, G, n0, W, alpha=(1.0, 0.2)):
+    k0, v0 = _data(rng, B, H, B * n0)
+    acc0 = (rng.random((B * n0, H * G)) * np.arange(B * n0)[::-1, None] * 0.05).astype(np.float32)
+    cu = np.array([n0 * b for b in range(B + 1)])
+    tier0, _, _ = osc.score_tokens(acc0, cu, H, alpha[0], alpha[1], W)
+    g = ogen.Generation(B, H, 64, 4000)
+    g.prompt(k0, v0, tier0, cu)
+    return g, tier0
+
+
+def _acc_rows(rng, g, G):
+    n = sum(g.lens) + g.B                                  # rows after the new tokens
+    return (rng.random((n, g.H * G)) * 2.0).astype(np.float32)
+
+
+def test_step_with_zero_thresholds_is_an_append():
+    # every leaving token scores >= 0 = alpha/N: it stays HIGH and the step is an append
+    rng = np.random.default_rng(7)
+    B, H, G, n0, W = 2, 2, 2, 50, 8
+    a, _ = _prompted(rng, B, H, G, n0, W)
+    b_, _ = _prompted(np.random.default_rng(7), B, H, G, n0, W)
+    for s in range(40):
+        kn, vn = _data(rng, B, H, B)
+        dec = a.step(kn, vn, _acc_rows(rng, a, G), 0.0, 0.0, W)
+        b_.append(kn, vn)
+        assert np.all(dec == ogen.HIGH)
+    for b in range(B):
+        assert np.array_equal(a.tiers[b], b_.tiers[b])
+        for h in range(H):
+            pa, pb = a.head_pages(b, h), b_.head_pages(b, h)
+            for t in (ogen.HIGH, ogen.LOW):
+                assert len(pa[t]) == len(pb[t])
+                for x, y in zip(pa[t], pb[t]):
+                    assert np.array_equal(x, y)
+    assert a.pool.head == b_.pool.head and a.pool.tail == b_.pool.tail
+
+
+def test_step_with_infinite_thresholds_keeps_only_old_tiers_and_the_window():
+    # nothing reaches alpha/N = inf: every token leaving the window is pruned; the head keeps
+    # its prompt tokens that were outside the prompt's window and the last W tokens
+    rng = np.random.default_rng(8)
+    B, H, G, n0, W, steps = 2, 3, 2, 40, 6, 25
+    g, tier0 = _prompted(rng, B, H, G, n0, W)
+    for s in range(steps):
+        kn, vn = _data(rng, B, H, B)
+        dec = g.step(kn, vn, _acc_rows(rng, g, G), np.inf, np.inf, W)
+        assert np.all(dec == ogen.PRUNE)
+    N = n0 + steps
+    for b in range(B):
+        for h in range(H):
+            live = sorted(g.rec[b][h])
+            old = [t for t in range(n0 - W) if tier0[b * n0 + t, h] != ogen.PRUNE]
+            assert live == old + list(range(N - W, N))
+            assert g.count[b, h, 0] == sum(tier0[b * n0 + t, h] == ogen.HIGH
+                                           for t in range(n0 - W)) + W
+    g.pool.check_invariants()
+
+
+def test_step_demotion_requantizes_the_k8v4_codes():
+    # alpha_h = inf, alpha_l = 0: every leaving token goes LOW, with the codes a demotion of
+    # its stored K8V4 codes gives
+    rng = np.random.default_rng(9)
+    B, H, G, n0, W = 1, 2, 2, 30, 5
+    g, _ = _prompted(rng, B, H, G, n0, W)
+    before = {h: dict(g.rec[0][h]) for h in range(H)}
+    for s in range(12):
+        kn, vn = _data(rng, B, H, B)
+        dec = g.step(kn, vn, _acc_rows(rng, g, G), np.inf, 0.0, W)
+        assert np.all(dec == ogen.LOW)
+        for h in range(H):
+            before[h][n0 + s] = g.rec[0][h][n0 + s]
+    for h in range(H):
+        for t in range(n0 - W, n0 - W + 12):
+            r0, r1 = before[h][t], g.rec[0][h][t]
+            assert r0[0] == ogen.HIGH and r1[0] == ogen.LOW
+            k2 = quant.requantize_from(r0[1][None], np.array([r0[2]]), np.array([r0[3]]), 4)
+            v2 = quant.requantize_from(r0[4][None], np.array([r0[5]]), np.array([r0[6]]), 2)
+            assert np.array_equal(r1[1], k2[0][0]) and r1[2] == k2[1][0] and r1[3] == k2[2][0]
+            assert np.array_equal(r1[4], v2[0][0]) and r1[5] == v2[1][0] and r1[6] == v2[2][0]
+
+
+def test_step_decisions_follow_the_prompt_scoring_rule():
+    # the tier given to t_c is the one score_tokens gives that token for the same
+    # accumulators (t_c is just outside the window there)
+    rng = np.random.default_rng(10)
+    B, H, G, n0, W = 2, 2, 4, 64, 8
+    g, _ = _prompted(rng, B, H, G, n0, W)
+    seen = set()
+    for s in range(30):
+        kn, vn = _data(rng, B, H, B)
+        acc = _acc_rows(rng, g, G) * np.float32(0.06)
+        cu = np.concatenate([[0], np.cumsum([n + 1 for n in g.lens])])
+        want, _, _ = osc.score_tokens(acc, cu, H, 1.0, 0.5, W)
+        dec = g.step(kn, vn, acc, 1.0, 0.5, W)
+        for b in range(B):
+            t_c = g.lens[b] - 1 - W
+            assert np.array_equal(dec[b], want[cu[b] + t_c])
+        seen |= set(dec.ravel().tolist())
+    assert seen == {ogen.PRUNE, ogen.LOW, ogen.HIGH}
+    g.pool.check_invariants()
