@@ -80,6 +80,7 @@ enum { KVC_PRUNE = 0, KVC_LOW = 1, KVC_HIGH = 2, KVC_FRESH = 3 };
 #define KVC_HIGH_SLOTS 16
 #define KVC_LOW_SLOTS 32
 #define KVC_PAGE_BYTES 3456
+#define KVC_GEN_MAX_WINDOW 112  /* largest recent window kvc_generation_step accepts      */
 
 typedef struct {
     int32_t num_layers;   /* L: layers sharing the pool                                   */
@@ -105,7 +106,7 @@ typedef struct {
 
 /* Operation ids for kvc_workspace_bytes */
 enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4,
-       KVC_OP_DECODE_ACC = 5 };
+       KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6 };
 
 /* Version string of the library. */
 const char *kvc_version(void);
@@ -237,6 +238,36 @@ int kvc_paged_decode_attention_acc(const kvc_geom *geom, int32_t layer, const kv
                                    int32_t out_is_fp32, float *acc_sum,
                                    const int32_t *cu_seqlens, void *workspace,
                                    size_t workspace_bytes, kvc_stream_t stream);
+
+/* One decode step under the per-step tier policy (DiffKV review page: Algorithm 1 as the
+ * referee report describes it, major comment 2 and minor comment 4; free-parameter ledger
+ * for the window; "What carries the argument" for the score and the allocation round).
+ * For each request b the new token (position positions[b], so N = positions[b] + 1 tokens
+ * after it) enters every KV head's HIGH tier as K8V4, like kvc_append_tokens.  The token
+ * t_c = N-1-window, which leaves the recent window in this step, is scored when t_c >= 0:
+ * score = max over the G query heads of fl32(acc_sum[cu[b] + t_c][hq] / (N-1-t_c)); it stays
+ * HIGH if score >= fl32(alpha_h/N), goes to LOW if score >= fl32(alpha_l/N), else it is
+ * dropped.  A token moved to LOW is re-quantized as K4V2 from the fp16 rounding of its K8V4
+ * reconstruction and takes the next LOW slot (every older LOW token has a smaller position);
+ * the HIGH slots after it move down by one so that slot order stays ascending.  Pages come
+ * from one allocation round of the kvc_compact_pages kind (no head is rebuilt; a HIGH count
+ * never shrinks in a step).
+ *   k_new, v_new  fp16 [B][Hkv][128], 16-byte aligned;  positions int32 [B]
+ *   acc_sum       float32 [T][Hq] over the lengths after the new token (T = cu_seqlens[B]),
+ *                 e.g. filled by kvc_paged_decode_attention_acc; read only
+ *   cu_seqlens    int32 [B+1]; cu[b+1] - cu[b] must be N (else KVC_DEV_SEQLEN)
+ *   window        1 .. KVC_GEN_MAX_WINDOW; the head's last `window` HIGH slots must hold
+ *                 positions t_c .. N-2 (else KVC_DEV_COUNT_MISMATCH)
+ *   tier_out      uint8 [B][Hkv]: the tier given to t_c, 255 where no token left the window
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_GENERATE, 0) bytes, 256-B aligned
+ * All or nothing: when any KVC_DEV_* bit is set (before the call, by the checks above, or by
+ * the allocation round on exhaustion or row overflow) no page, count or table entry changes.
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE (layer, window), KVC_E_WORKSPACE. */
+int kvc_generation_step(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                        const uint16_t *k_new, const uint16_t *v_new, const int32_t *positions,
+                        const float *acc_sum, const int32_t *cu_seqlens, float alpha_h,
+                        float alpha_l, int32_t window, uint8_t *tier_out, void *workspace,
+                        size_t workspace_bytes, kvc_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -46,6 +46,22 @@ struct AppendWs {
     }
 };
 
+// ---- generation_step ---------------------------------------------------------------------
+constexpr int GEN_MAX_WINDOW = KVC_GEN_MAX_WINDOW;
+
+struct GenWs {
+    size_t compact, new_count, old_count, changed, decided, bytes;
+    explicit GenWs(const kvc_geom *g) {
+        const size_t heads = size_t(g->batch) * g->num_kv_heads;
+        compact = 0;
+        new_count = CompactWs(g).bytes;
+        old_count = new_count + align256(sizeof(int32_t) * 2 * heads);
+        changed = old_count + align256(sizeof(int32_t) * 2 * heads);
+        decided = changed + align256(heads);
+        bytes = decided + align256(heads);
+    }
+};
+
 // ---- quantize_and_place ----------------------------------------------------------------
 constexpr int QTILE = 256;        // tokens per rank tile
 

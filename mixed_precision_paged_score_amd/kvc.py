@@ -15,12 +15,15 @@ OK, E_NULL, E_ALIGN, E_SHAPE, E_WORKSPACE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3,
 DEV_POOL_EXHAUSTED, DEV_ROW_OVERFLOW, DEV_SHRINK, DEV_COUNT_MISMATCH, DEV_SEQLEN = 1, 2, 4, 8, 16
 DEV_INTERNAL, DEV_BAD_TIER = 32, 64
 PRUNE, LOW, HIGH, FRESH = 0, 1, 2, 3
-OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC = 1, 2, 3, 4, 5
+OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC, OP_GENERATE = 1, 2, 3, 4, 5, 6
 HEAD_DIM, HIGH_SLOTS, LOW_SLOTS, PAGE_BYTES = 128, 16, 32, 3456
+GEN_MAX_WINDOW = 112
+NO_TOKEN = 255      # generation step: no token left the window
 
 EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_init",
            "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
-           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens"]
+           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
+           "kvc_generation_step"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -58,8 +61,11 @@ _lib.kvc_paged_decode_attention.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, 
 _lib.kvc_paged_decode_attention_acc.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _vp,
                                                 _vp, _sz, _vp]
 _lib.kvc_append_tokens.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.kvc_generation_step.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i32,
+                                     _vp, _vp, _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
-           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens"):
+           "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
+           "kvc_generation_step"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -179,3 +185,12 @@ def append_tokens(geom, layer, pool, k_new, v_new, positions, ws, stream=None):
     _check(_lib.kvc_append_tokens(ctypes.byref(geom), int(layer), ctypes.byref(pool.c),
                                   _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(ws),
                                   ws.numel(), _stream(stream)), "kvc_append_tokens")
+
+
+def generation_step(geom, layer, pool, k_new, v_new, positions, acc_sum, cu_seqlens, alpha_h,
+                    alpha_l, window, tier_out, ws, stream=None):
+    _check(_lib.kvc_generation_step(ctypes.byref(geom), int(layer), ctypes.byref(pool.c),
+                                    _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(acc_sum),
+                                    _ptr(cu_seqlens), float(alpha_h), float(alpha_l),
+                                    int(window), _ptr(tier_out), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "kvc_generation_step")

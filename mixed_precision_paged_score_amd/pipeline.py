@@ -105,6 +105,8 @@ class GenerationPath(PromptPath):
         H = w.num_kv_heads
         self.state = torch.full((w.batch, max_len, H), kvc.PRUNE, dtype=torch.uint8, device=device)
         self.ws_append = kvc.workspace(self.geom, kvc.OP_APPEND, device=device)
+        self.ws_gen = None
+        self.decided = torch.empty((w.batch, H), dtype=torch.uint8, device=device)
         self.changed = torch.empty((w.batch, H), dtype=torch.uint8, device=device)
         self.old_rows = torch.empty((w.batch, H, self.geom.row_capacity), dtype=torch.int32,
                                     device=device)
@@ -142,6 +144,29 @@ class GenerationPath(PromptPath):
         self.state[self._bidx, self.lens_dev.long()] = kvc.HIGH
         self.lens_dev.add_(1)
         self.cu.add_(self._cu_step)
+        self.lens = [n + 1 for n in self.lens]
+        self.T += self.w.batch
+        self.max_seqlen += 1
+
+    def step(self, layer, k_new, v_new, acc):
+        """One decode step under the per-step policy: append the new tokens and give the
+        token leaving the window its tier.  acc float32 [T + B][Hq] over the lengths after
+        the new tokens (the layout of cu_next)."""
+        w = self.w
+        if self.ws_gen is None:
+            self.ws_gen = kvc.workspace(self.geom, kvc.OP_GENERATE, device=self.device)
+        cu_next = self.cu + self._cu_step
+        kvc.generation_step(self.geom, layer, self.pool, k_new, v_new, self.lens_dev, acc,
+                            cu_next, w.alpha_h, w.alpha_l, w.window, self.decided, self.ws_gen)
+        # bookkeeping: the new positions are HIGH, the leaving token takes its tier
+        pos = self.lens_dev.long()
+        self.state[self._bidx, pos] = kvc.HIGH
+        t_c = (pos - w.window).clamp(min=0)
+        left = self.decided != kvc.NO_TOKEN
+        cur = self.state[self._bidx, t_c]
+        self.state[self._bidx, t_c] = torch.where(left, self.decided, cur)
+        self.lens_dev.add_(1)
+        self.cu = cu_next
         self.lens = [n + 1 for n in self.lens]
         self.T += self.w.batch
         self.max_seqlen += 1

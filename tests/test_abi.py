@@ -34,6 +34,7 @@ def test_version_and_workspace_sizes():
     # the accumulating decode also holds one logit per live token and query head
     assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC) >= \
         kvc.workspace_bytes(g, kvc.OP_DECODE) + 16 * 64 * 2 * 2049 * 16 * 4
+    assert kvc.workspace_bytes(g, kvc.OP_GENERATE) > kvc.workspace_bytes(g, kvc.OP_COMPACT)
     assert kvc.workspace_bytes(g, 99) == 0
     bad = kvc.make_geom(1, 16, 60, 8, 2049, 1 << 18)        # Hq % Hkv != 0
     assert kvc.workspace_bytes(bad, kvc.OP_COMPACT) == 0
@@ -76,6 +77,17 @@ def test_synchronous_errors_enqueue_nothing():
                                               1, 256, None, 256, 1 << 30, None) == kvc.E_NULL
     assert lib.kvc_paged_decode_attention_acc(ctypes.byref(g), 0, ctypes.byref(p), 16, 1.0, 16,
                                               1, 256, 256, 256, 64, None) == kvc.E_WORKSPACE
+    # generation step: no accumulators; window outside 1..KVC_GEN_MAX_WINDOW; small workspace
+    f1, f0 = ctypes.c_float(1.0), ctypes.c_float(0.2)
+    assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, None, 16,
+                                   f1, f0, 8, 16, 256, 1 << 20, None) == kvc.E_NULL
+    for win in (0, kvc.GEN_MAX_WINDOW + 1):
+        assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, 16, 16,
+                                       f1, f0, win, 16, 256, 1 << 20, None) == kvc.E_SHAPE
+    assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, 16, 16,
+                                   f1, f0, 8, 16, 256, 64, None) == kvc.E_WORKSPACE
+    assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 18, 16, 16, 16,
+                                   f1, f0, 8, 16, 256, 1 << 20, None) == kvc.E_ALIGN
     # score: negative window
     assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
                                 ctypes.c_float(0.1), -1, None, 16, 16, None, None,

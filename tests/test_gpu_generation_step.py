@@ -1,0 +1,142 @@
+"""Per-step generation policy on the GPU (kvc_generation_step) vs the oracle's Generation.step
+(MI355X only): every step appends one token per (request, KV head) and gives the token that
+leaves the recent window its tier from that step's accumulators.  The decisions are compared
+every step; the allocator state and the page images of the tracked heads bit-exactly every
+`check_every` steps and at the end; decode attention over the final state within the
+attention tolerance (2e-3 max-abs, 1e-3 relative L2)."""
+import dataclasses
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(__file__))
+import parity  # noqa: E402
+from oracle import attention as oatt, generation as ogen  # noqa: E402
+from mixed_precision_paged_score_amd import workloads  # noqa: E402
+from test_gpu_generation import _compare_heads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_steps(w, steps, sample_heads=None, check_every=1, acc_device="cpu"):
+    from mixed_precision_paged_score_amd import pipeline, kvc
+    print(f"[step] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+          f"prompt={w.seqlens[:6]} W={w.window} alpha=({w.alpha_h},{w.alpha_l}) steps={steps} "
+          f"P={w.num_pages}", flush=True)
+    k, v = workloads.make_kv(w)
+    acc = workloads.make_acc(w, k)
+    path = pipeline.GenerationPath(w, max(w.seqlens) + steps, DEV)
+    path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
+    tier0, _, _ = parity.oracle_score(w, acc)
+    if isinstance(sample_heads, int):
+        rng = np.random.default_rng(w.seed)
+        allh = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+        sample_heads = [allh[i] for i in rng.choice(len(allh), sample_heads, replace=False)]
+    gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages,
+                          track=sample_heads)
+    gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
+    g = torch.Generator().manual_seed(w.seed + 77)
+    seen = np.zeros(256, np.int64)
+    for s in range(steps):
+        kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        ws = dataclasses.replace(w, seqlens=[n + 1 for n in path.lens],
+                                 seed=w.seed + 1000 * (s + 1))
+        acc_s = workloads.make_acc_zipf(ws, acc_device)
+        path.step(0, kn.to(DEV), vn.to(DEV), acc_s.to(DEV))
+        dec_o = gen.step(kn.numpy(), vn.numpy(), acc_s.cpu().numpy(), w.alpha_h, w.alpha_l,
+                         w.window)
+        dec_g = parity.np_(path.decided)
+        if not np.array_equal(dec_g, dec_o):
+            bad = np.argwhere(dec_g != dec_o)
+            raise AssertionError(f"step {s}: {len(bad)} decisions differ, first {bad[:4].tolist()}")
+        seen += np.bincount(dec_o.ravel(), minlength=256)
+        if (s + 1) % check_every == 0:
+            assert path.pool.status() == 0, f"step {s}: status {path.pool.status()}"
+            parity.compare_pool(path.pool, gen.pool)
+            _compare_heads(w, path, gen, sample_heads)
+            assert np.array_equal(parity.np_(path.packed_state()),
+                                  np.concatenate(gen.tiers)), f"step {s}: tier state"
+    torch.cuda.synchronize()
+    assert path.pool.status() == 0
+    parity.compare_pool(path.pool, gen.pool)
+    _compare_heads(w, path, gen, sample_heads)
+    q = workloads.make_queries(w, "cpu", 5)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    path.decode(0, q.to(DEV), out)
+    torch.cuda.synchronize()
+    G = w.group
+    heads = sample_heads or [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    for (b, h) in heads:
+        kd, vd = gen.head_dequantized(b, h)
+        want = oatt.decode_group(q.numpy()[b, h * G:(h + 1) * G], kd, vd, path.scale)
+        parity.assert_close_attention(parity.np_(out[b, h * G:(h + 1) * G]), want)
+    counts = {name: int(seen[t]) for name, t in
+              (("high", kvc.HIGH), ("low", kvc.LOW), ("pruned", kvc.PRUNE),
+               ("none", kvc.NO_TOKEN))}
+    print(f"[step] ok: {counts}, ring head {gen.pool.head}", flush=True)
+    return counts
+
+
+def test_ragged_short_and_empty_prompts():
+    # a request with no prompt and one shorter than the window: no token leaves the window
+    # for their first steps; HIGH pages fill and LOW pages open during the run
+    w = workloads.Workload("step-ragged", 1, 4, 16, 4, [300, 0, 9, 517], 1.0, 0.2, 16, 2048,
+                           "zipf", seed=51)
+    c = run_steps(w, steps=80)
+    assert min(c["high"], c["low"], c["pruned"], c["none"]) > 0, c
+
+
+@pytest.mark.parametrize("window,hq,hkv,alpha_l", [(1, 8, 8, 0.5), (64, 16, 2, 0.5),
+                                                   (112, 32, 4, 0.3)])
+def test_windows_and_group_sizes(window, hq, hkv, alpha_l):
+    # window 1 (the previous token is scored), the 64-token window, the largest window (the
+    # rewritten HIGH tail spans 8 pages); group sizes 1, 8 and 8
+    w = workloads.Workload(f"step-w{window}", 1, 3, hq, hkv, [200, 129, 64], 1.0, alpha_l,
+                           window, 4096, "zipf", seed=52 + window)
+    c = run_steps(w, steps=70, check_every=7)
+    assert c["low"] > 0 and c["pruned"] > 0, c
+
+
+def test_exhausted_pool_changes_nothing():
+    # a pool with no free page: the first step that needs one sets KVC_DEV_POOL_EXHAUSTED and
+    # leaves pages, table, counts and ring as they were.  Zero thresholds keep every token
+    # HIGH, so request 0's 64 tokens fill four HIGH pages per head and its new token needs a
+    # fifth.
+    from mixed_precision_paged_score_amd import pipeline, kvc
+    w = workloads.Workload("step-full", 1, 2, 16, 4, [64, 47], 0.0, 0.0, 16, 4096, "zipf",
+                           seed=53)
+    k, v = workloads.make_kv(w)
+    acc = workloads.make_acc(w, k)
+    tier0, count0, _ = parity.oracle_score(w, acc)
+    need = int(sum(-(-int(c[0]) // 16) + -(-int(c[1]) // 32) for c in count0.reshape(-1, 2)))
+    wf = dataclasses.replace(w, num_pages=need)
+    path = pipeline.GenerationPath(wf, max(w.seqlens) + 4, DEV, num_pages=need)
+    path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert path.pool.status() == 0
+    before = [parity.np_(t).copy() for t in (path.pool.pages, path.pool.page_table,
+                                             path.pool.count, path.pool.free_ring,
+                                             path.pool.ring_ctr)]
+    g = torch.Generator().manual_seed(5)
+    kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+    ws = dataclasses.replace(w, seqlens=[n + 1 for n in w.seqlens], seed=w.seed + 1)
+    path.step(0, kn.to(DEV), kn.to(DEV), workloads.make_acc_zipf(ws).to(DEV))
+    torch.cuda.synchronize()
+    assert path.pool.status() & kvc.DEV_POOL_EXHAUSTED
+    after = [parity.np_(t) for t in (path.pool.pages, path.pool.page_table, path.pool.count,
+                                     path.pool.free_ring, path.pool.ring_ctr)]
+    for x, y in zip(before, after):
+        assert np.array_equal(x, y)
+
+
+def test_workload4_shape_sampled():
+    # 16 requests x 4096-token prompts, 64 query / 8 KV heads, the 64-token window: 512 steps
+    # of the per-step policy; decisions of all 128 heads every step, allocator state every 64
+    # steps, codes and attention on 6 sampled heads
+    w = workloads.workload(4)
+    run_steps(w, steps=512, sample_heads=6, check_every=64, acc_device=DEV)
