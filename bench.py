@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-acc", action="store_true",
                     help="skip the extra timing of decode attention with score accumulation")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--gen-steps", type=int, default=64,
+                    help="steps of the per-step generation policy timed after the main steps "
+                         "(0: skip)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every library call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,6 +103,82 @@ def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (a.steps * nsteps_dec)
+
+
+def time_generation_step(a, w, k, v, acc, ev, stream, nsteps):
+    """The per-step generation policy (kvc_generation_step) over `nsteps` steps after the
+    workload's prompt: each step appends one token per (request, KV head) and scores the token
+    leaving the window.  Every request has the same length here, so the accumulator row
+    cu[b] + t_c of request b at step s is (b+1)(N+s+1) - 1 - W: one buffer holds every step's
+    rows without overlap (N > 16 nsteps), filled with Zipf(1.1) means times the W later
+    tokens.  The steps are captured into one graph; before each replay the pool is restored
+    from a snapshot taken after the prompt (outside the timed region).  Returns microseconds
+    per step and the decisions of the last replay."""
+    from mixed_precision_paged_score_amd import kvc, pipeline
+    B, Hkv, Hq, W = w.batch, w.num_kv_heads, w.num_q_heads, w.window
+    N = w.seqlens[0]
+    assert len(set(w.seqlens)) == 1 and N > 16 * nsteps and N > W
+    dev = k.device
+    gp = pipeline.GenerationPath(w, N + nsteps, dev)
+    gp.prompt(0, acc, k, v)
+    rng = np.random.default_rng(w.seed + 4242)
+    rows = np.array([(b + 1) * (N + s + 1) - 1 - W for s in range(nsteps) for b in range(B)])
+    harm = np.sum(np.arange(1, N + 1, dtype=np.float64) ** -1.1)
+    mean = (rng.integers(0, N, size=(len(rows), Hq)) + 1.0) ** -1.1 / harm
+    accg = torch.zeros((int(rows.max()) + 1, Hq), dtype=torch.float32, device=dev)
+    accg[torch.tensor(rows, device=dev)] = torch.tensor(mean * W, dtype=torch.float32,
+                                                        device=dev)
+    pos = [torch.full((B,), N + s, dtype=torch.int32, device=dev) for s in range(nsteps)]
+    cus = [torch.arange(B + 1, dtype=torch.int32, device=dev) * (N + s + 1)
+           for s in range(nsteps)]
+    gen = torch.Generator(device=dev).manual_seed(w.seed + 4243)
+    kn = [torch.randn((B, Hkv, 128), generator=gen, device=dev).to(torch.float16)
+          for _ in range(nsteps)]
+    vn = [torch.randn((B, Hkv, 128), generator=gen, device=dev).to(torch.float16)
+          for _ in range(nsteps)]
+    gp.ws_gen = kvc.workspace(gp.geom, kvc.OP_GENERATE, device=dev)
+    decided = torch.empty((nsteps, B, Hkv), dtype=torch.uint8, device=dev)
+    pool = gp.pool
+    state = [pool.pages, pool.page_table, pool.count, pool.owner, pool.free_ring,
+             pool.ring_ctr, pool.dev_status]
+    snap = [t.clone() for t in state]
+
+    def restore():
+        for t, s0 in zip(state, snap):
+            t.copy_(s0)
+
+    def run_steps():
+        for s in range(nsteps):
+            kvc.generation_step(gp.geom, 0, pool, kn[s], vn[s], pos[s], accg, cus[s],
+                                w.alpha_h, w.alpha_l, W, decided[s], gp.ws_gen)
+
+    run_steps()                     # eager once: checks the sequence before capture
+    torch.cuda.synchronize()
+    status = pool.status()
+    restore()
+    if a.eager:
+        run = run_steps
+    else:
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_steps()
+        run = g.replay
+    times = []
+    for _ in range(max(a.steps, 1)):
+        restore()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / nsteps)
+    status |= pool.status()
+    d = decided.cpu().numpy()
+    counts = {"kept_high": int((d == kvc.HIGH).sum()), "demoted_low": int((d == kvc.LOW).sum()),
+              "pruned": int((d == kvc.PRUNE).sum())}
+    del gp, snap, accg
+    return float(np.mean(times)), counts, status
 
 
 def traffic_record(workload):
@@ -249,6 +328,16 @@ def main():
     acc_us = None
     if not a.no_acc and nsteps_dec > 0:
         acc_us = time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream)
+    gen = None
+    if a.gen_steps > 0:
+        gen_us, gen_counts, gen_status = time_generation_step(a, w, k, v, acc, ev, stream,
+                                                              a.gen_steps)
+        gen = {"us_per_step": gen_us, "steps": a.gen_steps, "heads": w.batch * w.num_kv_heads,
+               "decisions": gen_counts, "status": gen_status}
+        if acc_us is not None:
+            # one generation step of one layer: accumulate this query's weights, then the
+            # policy step
+            gen["with_decode_acc_us"] = gen_us + acc_us
     comp_ms = [e0.elapsed_time(e1) for (e0, e1, e2) in recs]
     dec_ms = [e1.elapsed_time(e2) / max(nsteps_dec, 1) for (e0, e1, e2) in recs]
     count = path.new_count.cpu().numpy()
@@ -296,6 +385,7 @@ def main():
             "GBps": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9,
             "frac_hbm": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes": dbytes + acc_bytes},
+        "generation_step": gen,
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},

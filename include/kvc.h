@@ -115,7 +115,7 @@ const char *kvc_version(void);
 const char *kvc_last_error(void);
 
 /* Bytes of workspace `op` needs for this geometry.  max_seqlen is the longest request
- * (KVC_OP_QUANTIZE), unused otherwise.  Returns 0 for an unknown op. */
+ * (KVC_OP_QUANTIZE, KVC_OP_DECODE_ACC), unused otherwise.  Returns 0 for an unknown op. */
 size_t kvc_workspace_bytes(const kvc_geom *geom, int32_t op, int32_t max_seqlen);
 
 /* Empty pool: free_ring = 0..P-1, head = 0, tail = P, page table and owner = -1,
@@ -227,17 +227,23 @@ int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_po
  *   acc_sum     float32 [T][Hq], the layout kvc_score_tokens reads, 16-byte aligned;
  *               updated in place
  *   cu_seqlens  int32 [B+1] of the same requests (N_b = cu_seqlens[b+1] - cu_seqlens[b]); a
- *               live token with position >= N_b is skipped and sets KVC_DEV_SEQLEN
- *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE_ACC, 0) bytes, 256-B aligned (split
- *        partials, softmax max/sum per query head, logits of every live token).
- * Every (token, query head) is written by one thread: no atomics, deterministic.
+ *               live token with position >= N_b, or out of ascending order within its head
+ *               and tier, is skipped and sets KVC_DEV_SEQLEN
+ *   max_seqlen  bounds every N_b (a longer request gets no update and sets KVC_DEV_SEQLEN)
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE_ACC, max_seqlen) bytes, 256-B aligned
+ *        (split partials, softmax max/sum per query head, logits of every live token, the
+ *        first slot of every 64-position chunk per head and tier).
+ * The accumulator rows are updated 64 positions at a time, each row read and written whole
+ * once; every (token, query head) is added by one thread: no atomics, deterministic.
  * Errors: as kvc_paged_decode_attention; KVC_E_NULL if acc_sum or cu_seqlens is NULL,
- * KVC_E_ALIGN if acc_sum is not 16-byte aligned. */
+ * KVC_E_ALIGN if acc_sum is not 16-byte aligned, KVC_E_SHAPE if max_seqlen < 0 or
+ * Hq > 512. */
 int kvc_paged_decode_attention_acc(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                                    const uint16_t *q, float softmax_scale, void *out,
                                    int32_t out_is_fp32, float *acc_sum,
-                                   const int32_t *cu_seqlens, void *workspace,
-                                   size_t workspace_bytes, kvc_stream_t stream);
+                                   const int32_t *cu_seqlens, int32_t max_seqlen,
+                                   void *workspace, size_t workspace_bytes,
+                                   kvc_stream_t stream);
 
 /* One decode step under the per-step tier policy (DiffKV review page: Algorithm 1 as the
  * referee report describes it, major comment 2 and minor comment 4; free-parameter ledger

@@ -95,10 +95,12 @@ template <bool HIGH> struct Vals;
 template <> struct Vals<true> {
     uint4 va, vb;               // value unit 16j + (lane & 15): tokens 4j..4j+3, 8 channels
     uint4 p0, p1;               // parameters of tokens 4j..4j+3 of the lane's tile
+    uint32_t ps;                // (score accumulation) position of token 4j + (lane & 3)
 };
 template <> struct Vals<false> {
     uint2 va, vb;               // the tiles' halves of value unit 16j + (lane & 15)
     uint4 p0, p1;
+    uint32_t ps;
 };
 
 // Page reads are buffer loads: one descriptor per page (wave-uniform, scalar registers:
@@ -118,6 +120,9 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u2v x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 template <bool HIGH>
@@ -139,12 +144,14 @@ __device__ __forceinline__ Keys<HIGH> load_keys(__amdgpu_buffer_rsrc_t ra,
     return d;
 }
 
-template <bool HIGH>
+// LG: also the position of token 4j + (lane & 3) of the lane's own tile
+template <bool HIGH, bool LG>
 __device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
                                                 __amdgpu_buffer_rsrc_t rb, int fa, int fb,
                                                 int lane, bool own_b) {
     const uint32_t j = lane >> 4;
     Vals<HIGH> d;
+    d.ps = 0;
     if constexpr (HIGH) {
         d.va = ld16(ra, V_OFF + 16 * uint32_t(lane));
         d.vb = ld16(rb, V_OFF + 16 * uint32_t(lane));
@@ -153,9 +160,11 @@ __device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
         if (own_b) {
             d.p0 = ld16(rb, o);
             d.p1 = ld16(rb, o + 16);
+            if constexpr (LG) d.ps = ld4(rb, POS_OFF + 4 * (4 * j + (lane & 3)));
         } else {
             d.p0 = ld16(ra, o);
             d.p1 = ld16(ra, o + 16);
+            if constexpr (LG) d.ps = ld4(ra, POS_OFF + 4 * (4 * j + (lane & 3)));
         }
     } else {
         // the two LOW tiles of a pair are the halves of one page (ra and rb are the same)
@@ -164,6 +173,8 @@ __device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
         const uint32_t o = PARAM_OFF + 8 * (16 * uint32_t(own_b ? fb : fa) + 4 * j);
         d.p0 = ld16(ra, o);
         d.p1 = ld16(ra, o + 16);
+        if constexpr (LG)
+            d.ps = ld4(ra, POS_OFF + 4 * (16 * uint32_t(own_b ? fb : fa) + 4 * j + (lane & 3)));
     }
     return d;
 }
@@ -276,12 +287,13 @@ __device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_q
 }
 
 // LG: the lane also stores its four logits (log2 units, -inf for empty slots) at lg,
-// lg + lg_gt, ..., when lg is not null (the score-accumulating variant)
+// lg + lg_gt, ... when lg_on, and lanes with ps_on the position of token 4j + (lane & 3) of
+// its tile at lg - ps_off, when lg is not null (the score-accumulating variant)
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> &d, int live_own,
                                                 float sumq, float scale_log2, int lane,
                                                 const Magic &mg, WaveState &st, float *lg,
-                                                int lg_gt) {
+                                                int lg_gt, bool lg_on, bool ps_on, int ps_off) {
     const int j = lane >> 4, c = lane & 15;
     const bool own_b = c >= 8;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
@@ -299,8 +311,11 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
     }
     if constexpr (LG) {
         if (lg) {          // tokens 4j..4j+3 of the lane's tile, GT words apart
+            if (lg_on) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) lg[r * lg_gt] = L[r];
+                for (int r = 0; r < 4; ++r) lg[r * lg_gt] = L[r];
+            }
+            if (ps_on) reinterpret_cast<uint32_t *>(lg)[-ps_off] = d.ps;
         }
     }
     tmax = max_over_column(tmax);
@@ -381,15 +396,16 @@ __device__ __forceinline__ int first_chunk_pids(int t0, int t1, const int32_t *r
     return lane < np ? (HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)]) : 0;
 }
 
-// lgh (LG only): the head's logits [tile][16 tokens][GT] offset to this tier's first tile,
-// the lane's first token (4j) and its query head (null for lanes without a query head)
+// lgh (LG only): the head's tile records [tile][16 positions, then 16 tokens x GT logits]
+// offset to this tier's first tile, the lane's first token (4j) and its query head
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
                                              int C, const uint8_t *pages,
                                              const uint4 (*s_qa)[64], const uint4 (*s_qb)[64],
                                              float sumq, float scale_log2, int lane,
                                              const Magic &mg, WaveState &st, float *lgh,
-                                             int lg_tile_stride, int pid_first) {
+                                             int lg_tile_stride, int lg_gt, bool lg_on,
+                                             bool ps_on, int ps_off, int pid_first) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
     const bool own_b = (lane & 15) >= 8;
     const float acc0 = -(HIGH ? KOFF_HIGH : COFF) * sumq;   // the key codes' offset
@@ -419,8 +435,8 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         auto vals_at = [&](int t) {
             t = min(t, tlast);
             const int tb = tb_of(t);
-            return load_vals<HIGH>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1, tb & 1,
-                                   lane, own_b);
+            return load_vals<HIGH, LG>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1,
+                                       tb & 1, lane, own_b);
         };
         // the lane's logit slot for the pair starting at tile t (its own tile of the pair)
         auto lg_at = [&](int t) -> float * {
@@ -438,14 +454,16 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
             f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg, acc0);
             vb = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t), lg_tile_stride / 16);
+                                      scale_log2, lane, mg, st, lg_at(t), lg_gt, lg_on, ps_on,
+                                      ps_off);
             t += 2;
             if (t >= c1) break;
             ka = keys_at(t + 2);
             acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg, acc0);
             va = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t), lg_tile_stride / 16);
+                                      scale_log2, lane, mg, st, lg_at(t), lg_gt, lg_on, ps_on,
+                                      ps_off);
             t += 2;
             if (t >= c1) break;
         }
@@ -454,8 +472,9 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
 
 // grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
 // take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
-// LG: also store every live token's logit per query head into lg [head][tile][16][GT]
-// (tiles in the head's order: HIGH tiles, then LOW tiles), for the score accumulation
+// LG: also store, per tile of the head (HIGH tiles, then LOW tiles), its 16 slots' positions
+// and every token's logit per query head: lg [head][tile][16 + 16 * GT], for the score
+// accumulation
 template <bool LG>
 __global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(KVC_DEC_OCC)))
 void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
@@ -539,16 +558,20 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
-    float *lgh = nullptr;       // the lane's query head and first token in tile 0 of the head
-    if constexpr (LG) {
-        if (gq < G) lgh = lg + (int64_t(i) * tiles_cap * 16 + 4 * j) * GT + g0 + gq;
-    }
-    const int lg_stride = GT * 16;
+    // LG: tile records of 16 (GT + 1) words; the lane's logit word of token 4j, query head
+    // g0 + gq in tile 0 of the head (stored when gq < G); lanes gq < 4 of the first group
+    // also store the position of token 4j + gq, ps_off words before that logit word
+    const int lg_stride = 16 * (GT + 1);
+    float *lgh = nullptr;
+    if constexpr (LG) lgh = lg + int64_t(i) * tiles_cap * lg_stride + 16 + 4 * j * GT + g0 + gq;
+    const bool lg_on = gq < G, ps_on = g0 == 0 && gq < 4;
+    const int ps_off = 16 + 4 * j * (GT - 1);
     attend_range<true, LG>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2,
-                           lane, mg, st, lgh, lg_stride, pid_h);
+                           lane, mg, st, lgh, lg_stride, GT, lg_on, ps_on, ps_off, pid_h);
     attend_range<false, LG>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
                             scale_log2, lane, mg, st,
-                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride, pid_l);
+                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride, GT, lg_on,
+                            ps_on, ps_off, pid_l);
     // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
     for (int o = 8; o <= 32; o <<= 1) {
@@ -656,55 +679,176 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
 }
 
-// grid (B*Hkv, ACC_BLOCKS), 4 waves; wave w of block y takes tiles 4y + w, 4y + w +
-// 4*ACC_BLOCKS, ... of its head: acc_sum[cu[b] + pos][hq] += exp2(logit - M) / L for the
-// tile's live tokens and the head's GT query heads (lane k: token k / GT, query head k % GT,
-// so one token's query heads are neighbouring floats of one accumulator row), where M and L
-// are the query head's softmax max and sum over all splits.  Each (token, query head) is
-// written by one lane: no atomics, deterministic.
-constexpr int ACC_BLOCKS = 64;
-__global__ __launch_bounds__(256) void decode_acc_kernel(
-    const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
-    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int GT, int C,
-    const float *__restrict__ lg, int64_t tiles_cap, const float *__restrict__ mls,
-    float *__restrict__ acc, int32_t *status) {
-    const int lane = threadIdx.x & 63;
+// ---- score accumulation: acc_sum[cu[b] + pos][hq] += exp2(logit - M) / L -------------------
+// The decode kernel leaves, per tile of each head (HIGH tiles, then LOW tiles of 16 slots),
+// the tile's 16 positions and its logits; one accumulator row holds all query heads of one
+// position.  The update therefore runs over
+// chunks of ACC_R positions of one request: a workgroup loads the chunk's rows (ACC_R x Hq
+// floats, contiguous) into LDS, adds the weights of every head's live tokens whose positions
+// fall in the chunk, and writes the rows back whole.  Within a head and tier the slots are in
+// ascending position order, so the tokens of a chunk are one slot range per head and tier;
+// acc_index finds these ranges: start[c] = number of slots with position < c * ACC_R.
+
+// grid (B*Hkv, 2 * ACC_IDX_BLOCKS): y even = HIGH, odd = LOW.  Thread for slot s (position
+// p, previous slot's position prev, both from the tile records the decode kernel wrote)
+// writes start[c] = s for every c with prev < c*R <= p; the last slot also writes
+// start[c] = n for c*R > p up to c = ceil(N/R).
+constexpr int ACC_IDX_BLOCKS = 16;
+__global__ __launch_bounds__(256) void acc_index_kernel(
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int G,
+    int max_seqlen, int nch_cap, const float *__restrict__ lg, int64_t tiles_cap,
+    int32_t *__restrict__ idx, int32_t *status) {
     const int i = blockIdx.x;
-    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
-    const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
-    const int ntiles = int(min(int64_t(qH + tL), tiles_cap));
-    const int b = i / Hkv, h = i - b * Hkv;
-    const int Hq = Hkv * GT;
-    const int lo = cu[b], N = cu[b + 1] - lo;
-    const float *mlh = mls + 2 * (int64_t(b) * Hq + int64_t(h) * GT);
-    for (int tile = blockIdx.y * 4 + (threadIdx.x >> 6); tile < ntiles; tile += ACC_BLOCKS * 4) {
-        int page, slot0, live;
-        if (tile < qH) {
-            page = rows_l[int64_t(i) * C + tile];
-            slot0 = 0;
-            live = min(HS, nh - HS * tile);
-        } else {
-            const int t = tile - qH;
-            page = rows_l[int64_t(i) * C + C - 1 - (t >> 1)];
-            slot0 = 16 * (t & 1);
-            live = min(16, nl - 16 * t);
+    const bool high = (blockIdx.y & 1) == 0;
+    const int part = blockIdx.y >> 1;
+    const int b = i / Hkv;
+    const int N = cu[b + 1] - cu[b];
+    if (N < 0 || N > max_seqlen) {
+        if (blockIdx.y == 0 && threadIdx.x == 0) atomicOr(status, KVC_DEV_SEQLEN);
+        return;
+    }
+    const int nh = count_l[2 * i];
+    const int n = high ? nh : count_l[2 * i + 1];
+    const int nch = ceil_div(N, ACC_R);
+    int32_t *st = idx + (int64_t(i) * 2 + (high ? 0 : 1)) * nch_cap;
+    if (n == 0) {
+        for (int c = part * 256 + threadIdx.x; c <= nch; c += ACC_IDX_BLOCKS * 256) st[c] = 0;
+        return;
+    }
+    const int64_t ts = 16 * (G + 1);
+    const int32_t *rec = reinterpret_cast<const int32_t *>(lg) +
+                         (int64_t(i) * tiles_cap + (high ? 0 : ceil_div(nh, HS))) * ts;
+    auto pos_of = [&](int sl) { return rec[int64_t(sl >> 4) * ts + (sl & 15)]; };
+    const int ntl = ceil_div(n, 16);
+    for (int sl = part * 256 + threadIdx.x; sl < n; sl += ACC_IDX_BLOCKS * 256) {
+        if ((high ? 0 : ceil_div(nh, HS)) + ntl > tiles_cap) break;
+        const int p = pos_of(sl);
+        const int prev = sl > 0 ? pos_of(sl - 1) : -1;
+        if (p <= prev || p >= N) {
+            atomicOr(status, KVC_DEV_SEQLEN);
+            continue;
         }
-        const int32_t *pos =
-            reinterpret_cast<const int32_t *>(pages + int64_t(page) * PAGE + POS_OFF) + slot0;
-        const float *lt = lg + (int64_t(i) * tiles_cap + tile) * 16 * GT;
-        for (int k = lane; k < live * GT; k += 64) {
-            const int tok = k / GT, g = k - tok * GT;
-            const int p = pos[tok];
-            if (p < 0 || p >= N) {
+        const int c_hi = p / ACC_R;
+        for (int c = prev < 0 ? 0 : prev / ACC_R + 1; c <= c_hi; ++c) st[c] = sl;
+        if (sl == n - 1)
+            for (int c = c_hi + 1; c <= nch; ++c) st[c] = n;
+    }
+}
+
+// the GT query heads' logits of one slot
+template <int GT>
+__device__ __forceinline__ void load_logits(const float *src, float (&l)[GT]) {
+    if constexpr (GT >= 4) {
+#pragma unroll
+        for (int u = 0; u < GT / 4; ++u) {
+            const float4 x = reinterpret_cast<const float4 *>(src)[u];
+            l[4 * u] = x.x; l[4 * u + 1] = x.y; l[4 * u + 2] = x.z; l[4 * u + 3] = x.w;
+        }
+    } else if constexpr (GT == 2) {
+        const float2 x = *reinterpret_cast<const float2 *>(src);
+        l[0] = x.x; l[1] = x.y;
+    } else {
+        l[0] = src[0];
+    }
+}
+
+// grid (ceil(max_seqlen / R), B), 4 waves, dynamic LDS ACC_R * Hq + 2 * Hq floats.  The
+// (head, tier) ranges are the jobs: wave w takes jobs w, w + 4, ...; a range holds at most
+// ACC_R = 64 slots (the chunk's positions), so lane k takes slot s0 + k and all G query heads
+// of its head.  Each (position, query head) has one live slot at most, so every LDS word is
+// added to by one lane: no atomics, deterministic.
+template <int GT>
+__global__ __launch_bounds__(256) void acc_update_kernel(
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int G_rt,
+    int max_seqlen, int nch_cap, const int32_t *__restrict__ idx,
+    const float *__restrict__ lg, int64_t tiles_cap,
+    const float *__restrict__ mls, float *__restrict__ acc, int32_t *status) {
+    extern __shared__ float s_acc[];                 // [ACC_R][Hq + 4], then [Hq][2] (M, L)
+    const int G = GT > 0 ? GT : G_rt;
+    const int b = blockIdx.y, c = blockIdx.x;
+    const int lo = cu[b], N = cu[b + 1] - lo;
+    if (N <= 0 || N > max_seqlen) return;
+    const int t0 = c * ACC_R;
+    if (t0 >= N) return;
+    const int nr = min(ACC_R, N - t0);
+    const int Hq = Hkv * G;
+    const int ldr = Hq + 4;     // LDS row stride: rows 4 banks apart (lanes hold nearby rows)
+    float *s_ml = s_acc + ACC_R * ldr;
+    float *arow = acc + (int64_t(lo) + t0) * Hq;
+    const int nw = nr * Hq;
+    if ((Hq & 3) == 0) {
+        const int q4 = Hq >> 2;
+        for (int k = threadIdx.x; k < nw / 4; k += 256) {
+            const int r = k / q4, c4 = k - r * q4;
+            reinterpret_cast<float4 *>(s_acc + r * ldr)[c4] =
+                reinterpret_cast<const float4 *>(arow)[k];
+        }
+    } else {
+        for (int k = threadIdx.x; k < nw; k += 256) s_acc[(k / Hq) * ldr + k % Hq] = arow[k];
+    }
+    for (int k = threadIdx.x; k < 2 * Hq; k += 256) s_ml[k] = mls[int64_t(b) * 2 * Hq + k];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // per job: its slot, position and logits, loaded before the barrier so that the loads
+    // of all of a wave's jobs are in flight together
+    constexpr int JMAX = 4;                          // jobs per wave per pass (Hkv <= 8)
+    for (int j0 = 0; j0 < 2 * Hkv; j0 += 4 * JMAX) {
+        int pj[JMAX], hj[JMAX];
+        int64_t lj[JMAX];                            // the slot's logits: lg + lj
+        float l[JMAX][GT > 0 ? GT : 1];
+#pragma unroll
+        for (int u = 0; u < JMAX; ++u) {
+            const int seg = j0 + wave + 4 * u;
+            pj[u] = -1;
+            hj[u] = seg >> 1;
+            if (seg >= 2 * Hkv) continue;
+            const bool high = (seg & 1) == 0;
+            const int i = b * Hkv + hj[u];
+            const int nh = count_l[2 * i], n = high ? nh : count_l[2 * i + 1];
+            const int32_t *st = idx + (int64_t(i) * 2 + (high ? 0 : 1)) * nch_cap;
+            const int s0 = min(max(st[c], 0), n), s1 = min(max(st[c + 1], s0), n);
+            const int sl = s0 + lane;
+            if (sl >= s1) continue;
+            const int tile = (high ? 0 : ceil_div(nh, HS)) + (sl >> 4);
+            if (tile >= tiles_cap) continue;
+            const int64_t rb = (int64_t(i) * tiles_cap + tile) * (16 * (G + 1));
+            pj[u] = reinterpret_cast<const int32_t *>(lg)[rb + (sl & 15)];
+            lj[u] = rb + 16 + (sl & 15) * G;
+            if constexpr (GT > 0) load_logits<GT>(lg + lj[u], l[u]);
+        }
+        if (j0 == 0) __syncthreads();                // the rows and (M, L) are in LDS
+#pragma unroll
+        for (int u = 0; u < JMAX; ++u) {
+            const int p = pj[u];
+            if (p < 0) continue;                      // no slot for this lane
+            if (p < t0 || p >= t0 + nr) {
                 atomicOr(status, KVC_DEV_SEQLEN);
                 continue;
             }
-            const float2 ml = *reinterpret_cast<const float2 *>(mlh + 2 * g);
-            if (!(ml.y > 0.0f)) continue;
-            const float w = __builtin_amdgcn_exp2f(lt[k] - ml.x) / ml.y;
-            float *a = acc + (int64_t(lo) + p) * Hq + int64_t(h) * GT + g;
-            *a = *a + w;
+            float *dst = s_acc + (p - t0) * ldr + hj[u] * G;
+            const float *ml = s_ml + 2 * hj[u] * G;
+            if constexpr (GT > 0) {
+#pragma unroll
+                for (int g = 0; g < GT; ++g)
+                    if (ml[2 * g + 1] > 0.0f)
+                        dst[g] += __builtin_amdgcn_exp2f(l[u][g] - ml[2 * g]) / ml[2 * g + 1];
+            } else {
+                for (int g = 0; g < G; ++g)
+                    if (ml[2 * g + 1] > 0.0f)
+                        dst[g] += __builtin_amdgcn_exp2f(lg[lj[u] + g] - ml[2 * g]) /
+                                  ml[2 * g + 1];
+            }
         }
+    }
+    __syncthreads();
+    if ((Hq & 3) == 0) {
+        const int q4 = Hq >> 2;
+        for (int k = threadIdx.x; k < nw / 4; k += 256) {
+            const int r = k / q4, c4 = k - r * q4;
+            reinterpret_cast<float4 *>(arow)[k] =
+                reinterpret_cast<const float4 *>(s_acc + r * ldr)[c4];
+        }
+    } else {
+        for (int k = threadIdx.x; k < nw; k += 256) arow[k] = s_acc[(k / Hq) * ldr + k % Hq];
     }
 }
 
@@ -716,7 +860,8 @@ namespace {
 
 int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint16_t *q,
                 float softmax_scale, void *out, int32_t out_is_fp32, float *acc_sum,
-                const int32_t *cu, void *ws, size_t ws_bytes, kvc_stream_t stream) {
+                const int32_t *cu, int32_t max_seqlen, void *ws, size_t ws_bytes,
+                kvc_stream_t stream) {
     int rc = check_geom(g);
     if (rc) return rc;
     rc = check_pool(p);
@@ -729,7 +874,8 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
     if (layer < 0 || layer >= g->num_layers) return KVC_E_SHAPE;
     const int G = g->num_q_heads / g->num_kv_heads;
     if (G > 16) return KVC_E_SHAPE;
-    DecodeWs L(g, accum);
+    if (accum && (max_seqlen < 0 || g->num_q_heads > ACC_MAX_HQ)) return KVC_E_SHAPE;
+    DecodeWs L(g, accum, max_seqlen);
     if (!ws || ws_bytes < L.bytes) return KVC_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
     char *w = static_cast<char *>(ws);
@@ -758,9 +904,21 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
                        g->num_q_heads, G, L.splits, nqh, out, out_is_fp32, mls);
     rc = launch_check("kvc_paged_decode_attention/combine");
     if (rc || !accum) return rc;
-    const dim3 agrid(nheads, ACC_BLOCKS);
-    hipLaunchKernelGGL(decode_acc_kernel, agrid, dim3(256), 0, s, p->pages, rows_l, count_l, cu,
-                       Hkv, G, C, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
+    if (max_seqlen == 0) return KVC_OK;
+    int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);
+    hipLaunchKernelGGL(acc_index_kernel, dim3(nheads, 2 * ACC_IDX_BLOCKS), dim3(256), 0, s,
+                       count_l, cu, Hkv, G, max_seqlen, L.nch_cap, lg, L.tiles_cap, idx,
+                       p->dev_status);
+    rc = launch_check("kvc_paged_decode_attention_acc/index");
+    if (rc) return rc;
+    const size_t lds = sizeof(float) * (size_t(ACC_R) * (g->num_q_heads + 4) +
+                                        2 * size_t(g->num_q_heads));
+    auto upd = G == 8 ? acc_update_kernel<8> : G == 4 ? acc_update_kernel<4>
+             : G == 16 ? acc_update_kernel<16> : G == 2 ? acc_update_kernel<2>
+             : G == 1 ? acc_update_kernel<1> : acc_update_kernel<0>;
+    hipLaunchKernelGGL(upd, dim3(L.nch_cap - 1, B), dim3(256), lds, s, count_l, cu, Hkv, G,
+                       max_seqlen, L.nch_cap, idx, lg,
+                       L.tiles_cap, mls, acc_sum, p->dev_status);
     return launch_check("kvc_paged_decode_attention_acc/accumulate");
 }
 
@@ -770,7 +928,7 @@ extern "C" int kvc_paged_decode_attention(const kvc_geom *g, int32_t layer, cons
                                           const uint16_t *q, float softmax_scale, void *out,
                                           int32_t out_is_fp32, void *ws, size_t ws_bytes,
                                           kvc_stream_t stream) {
-    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, nullptr, nullptr, ws,
+    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, nullptr, nullptr, 0, ws,
                        ws_bytes, stream);
 }
 
@@ -778,8 +936,9 @@ extern "C" int kvc_paged_decode_attention_acc(const kvc_geom *g, int32_t layer,
                                               const kvc_pool *p, const uint16_t *q,
                                               float softmax_scale, void *out, int32_t out_is_fp32,
                                               float *acc_sum, const int32_t *cu_seqlens,
-                                              void *ws, size_t ws_bytes, kvc_stream_t stream) {
+                                              int32_t max_seqlen, void *ws, size_t ws_bytes,
+                                              kvc_stream_t stream) {
     if (!acc_sum || !cu_seqlens) return KVC_E_NULL;
-    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, acc_sum, cu_seqlens, ws,
-                       ws_bytes, stream);
+    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, acc_sum, cu_seqlens,
+                       max_seqlen, ws, ws_bytes, stream);
 }

@@ -100,23 +100,33 @@ inline int decode_splits(const kvc_geom *g) {
     return s;
 }
 
+constexpr int ACC_R = 64;          // positions per score-accumulation chunk
+constexpr int ACC_MAX_HQ = 512;    // query heads the accumulation's LDS rows hold
+
 struct DecodeWs {
     int splits;
     int64_t tiles_cap;     // tiles per head the logit buffer holds (HIGH pages + 2 x LOW pages)
-    size_t part, mls, lg, bytes;
-    // acc: also the buffers of the score-accumulating variant
-    DecodeWs(const kvc_geom *g, bool acc) {
+    int nch_cap;           // chunk-start entries per head and tier: ceil(max_seqlen / R) + 1
+    size_t part, mls, lg, idx, bytes;
+    // acc: also the buffers of the score-accumulating variant (requests up to max_seqlen)
+    DecodeWs(const kvc_geom *g, bool acc, int max_seqlen = 0) {
         splits = decode_splits(g);
         tiles_cap = 2 * int64_t(g->row_capacity);
         part = 0;          // float [B][Hkv][S][G][PART_STRIDE]
         bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
                          splits);
         mls = bytes;       // float [B][Hq][2]: the softmax's max and sum per query head
-        lg = mls;          // float [B*Hkv][tiles_cap][16][G]: logits in the heads' tile order
+        lg = mls;          // per head and tile (the head's tile order): 16 int32 positions,
+                           // then float logits [16][G]
+        idx = mls;         // int32 [B*Hkv][2][nch_cap]: first slot of each position chunk
+        nch_cap = (max_seqlen + ACC_R - 1) / ACC_R + 1;
         if (acc) {
             lg = mls + align256(sizeof(float) * 2 * size_t(g->batch) * g->num_q_heads);
-            bytes = lg + align256(sizeof(float) * size_t(g->batch) * g->num_q_heads *
-                                  size_t(tiles_cap) * 16);
+            const size_t G = size_t(g->num_q_heads / g->num_kv_heads);
+            idx = lg + align256(sizeof(float) * size_t(g->batch) * g->num_kv_heads *
+                                size_t(tiles_cap) * 16 * (G + 1));
+            bytes = idx + align256(sizeof(int32_t) * 2 * size_t(g->batch) * g->num_kv_heads *
+                                   size_t(nch_cap));
         }
     }
 };

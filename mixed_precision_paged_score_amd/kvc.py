@@ -59,7 +59,7 @@ _lib.kvc_quantize_and_place.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _i64, _i32,
                                         _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention_acc.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _vp,
-                                                _vp, _sz, _vp]
+                                                _i32, _vp, _sz, _vp]
 _lib.kvc_append_tokens.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_generation_step.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i32,
                                      _vp, _vp, _sz, _vp]
@@ -171,13 +171,13 @@ def paged_decode_attention(geom, layer, pool, q, softmax_scale, out, ws, stream=
                                            _stream(stream)), "kvc_paged_decode_attention")
 
 
-def paged_decode_attention_acc(geom, layer, pool, q, softmax_scale, out, acc_sum, cu_seqlens, ws,
-                               stream=None):
+def paged_decode_attention_acc(geom, layer, pool, q, softmax_scale, out, acc_sum, cu_seqlens,
+                               max_seqlen, ws, stream=None):
     _check(_lib.kvc_paged_decode_attention_acc(ctypes.byref(geom), int(layer),
                                                ctypes.byref(pool.c), _ptr(q), float(softmax_scale),
                                                _ptr(out), int(out.dtype == torch.float32),
-                                               _ptr(acc_sum), _ptr(cu_seqlens), _ptr(ws),
-                                               ws.numel(), _stream(stream)),
+                                               _ptr(acc_sum), _ptr(cu_seqlens), int(max_seqlen),
+                                               _ptr(ws), ws.numel(), _stream(stream)),
            "kvc_paged_decode_attention_acc")
 
 

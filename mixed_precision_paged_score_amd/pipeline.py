@@ -29,6 +29,7 @@ class PromptPath:
         self.ws_quant = kvc.workspace(self.geom, kvc.OP_QUANTIZE, self.max_seqlen, device=device)
         self.ws_decode = kvc.workspace(self.geom, kvc.OP_DECODE, device=device)
         self.ws_decode_acc = None           # made on first use (it holds every live logit)
+        self.seqlen_cap = self.max_seqlen   # longest request the workspaces are sized for
         self.scale = 1.0 / math.sqrt(kvc.HEAD_DIM)
 
     # -- steps ----------------------------------------------------------------------------
@@ -63,9 +64,10 @@ class PromptPath:
         """Decode attention that also adds every cached token's attention weight into
         `acc` ([T][Hq] float32, this path's current requests)."""
         if self.ws_decode_acc is None:
-            self.ws_decode_acc = kvc.workspace(self.geom, kvc.OP_DECODE_ACC, device=self.device)
+            self.ws_decode_acc = kvc.workspace(self.geom, kvc.OP_DECODE_ACC, self.seqlen_cap,
+                                               device=self.device)
         kvc.paged_decode_attention_acc(self.geom, layer, self.pool, q, self.scale, out, acc,
-                                       self.cu, self.ws_decode_acc)
+                                       self.cu, self.max_seqlen, self.ws_decode_acc)
 
     # -- HIP graphs -------------------------------------------------------------------------
     # Every library call is asynchronous on the current stream, reads its sizes from device

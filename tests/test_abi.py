@@ -32,8 +32,10 @@ def test_version_and_workspace_sizes():
     assert kvc.workspace_bytes(g, kvc.OP_QUANTIZE, 32768) >= 16 * 8 * 32768 * 4
     assert kvc.workspace_bytes(g, kvc.OP_DECODE) > 0
     # the accumulating decode also holds one logit per live token and query head
-    assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC) >= \
-        kvc.workspace_bytes(g, kvc.OP_DECODE) + 16 * 64 * 2 * 2049 * 16 * 4
+    assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC, 32768) >= \
+        kvc.workspace_bytes(g, kvc.OP_DECODE) + 16 * 64 * 2 * 2049 * 16 * 4 + \
+        16 * 8 * 2 * (32768 // 64 + 1) * 4
+    assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC, -1) == 0
     assert kvc.workspace_bytes(g, kvc.OP_GENERATE) > kvc.workspace_bytes(g, kvc.OP_COMPACT)
     assert kvc.workspace_bytes(g, 99) == 0
     bad = kvc.make_geom(1, 16, 60, 8, 2049, 1 << 18)        # Hq % Hkv != 0
@@ -74,9 +76,11 @@ def test_synchronous_errors_enqueue_nothing():
                                           256, 1 << 20, None) == kvc.E_ALIGN
     # accumulating decode: accumulators without sequence offsets, then a small workspace
     assert lib.kvc_paged_decode_attention_acc(ctypes.byref(g), 0, ctypes.byref(p), 16, 1.0, 16,
-                                              1, 256, None, 256, 1 << 30, None) == kvc.E_NULL
+                                              1, 256, None, 10, 256, 1 << 30, None) == kvc.E_NULL
     assert lib.kvc_paged_decode_attention_acc(ctypes.byref(g), 0, ctypes.byref(p), 16, 1.0, 16,
-                                              1, 256, 256, 256, 64, None) == kvc.E_WORKSPACE
+                                              1, 256, 256, 10, 256, 64, None) == kvc.E_WORKSPACE
+    assert lib.kvc_paged_decode_attention_acc(ctypes.byref(g), 0, ctypes.byref(p), 16, 1.0, 16,
+                                              1, 256, 256, -1, 256, 1 << 30, None) == kvc.E_SHAPE
     # generation step: no accumulators; window outside 1..KVC_GEN_MAX_WINDOW; small workspace
     f1, f0 = ctypes.c_float(1.0), ctypes.c_float(0.2)
     assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 16, 16, None, 16,

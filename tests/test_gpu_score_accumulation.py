@@ -112,7 +112,7 @@ def test_workload1_full():
     run_case(workloads.workload(1))
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 4), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (6, 2), (16, 4), (32, 4), (32, 2)])
 def test_ragged_group_sizes_and_two_steps(hq, hkv):
     w = workloads.Workload(f"acc-{hq}-{hkv}", 1, 5, hq, hkv, [1, 0, 37, 300, 777], 1.0, 0.2,
                            16, 4096, "causal", seed=41)
