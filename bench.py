@@ -15,7 +15,10 @@ part of the step; `decode_GBps` = algorithmic bytes of paged decode attention pe
 `roofline` is for the dominant work, the decode-attention call (main + combine kernel),
 timed with HIP events around the replayed decode steps on the stream they run on, divided
 by the number of calls; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+workload.  Beside the step: `decode_with_score_accumulation` (the same decode calls adding
+every cached token's weight into the accumulators) and `generation_loop` (64 generation steps
+of the layer after the prompt: decode with score accumulation into one padded accumulator
+buffer, then kvc_generation_step, captured as one graph).
 """
 import argparse
 import dataclasses
@@ -46,8 +49,8 @@ def parse():
                     help="skip the extra timing of decode attention with score accumulation")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
     ap.add_argument("--gen-steps", type=int, default=64,
-                    help="steps of the per-step generation policy timed after the main steps "
-                         "(0: skip)")
+                    help="steps of the generation loop (decode with score accumulation, then "
+                         "the per-step policy) timed after the main steps (0: skip)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every library call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -105,80 +108,88 @@ def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
     return e0.elapsed_time(e1) * 1e3 / (a.steps * nsteps_dec)
 
 
-def time_generation_step(a, w, k, v, acc, ev, stream, nsteps):
-    """The per-step generation policy (kvc_generation_step) over `nsteps` steps after the
-    workload's prompt: each step appends one token per (request, KV head) and scores the token
-    leaving the window.  Every request has the same length here, so the accumulator row
-    cu[b] + t_c of request b at step s is (b+1)(N+s+1) - 1 - W: one buffer holds every step's
-    rows without overlap (N > 16 nsteps), filled with Zipf(1.1) means times the W later
-    tokens.  The steps are captured into one graph; before each replay the pool is restored
-    from a snapshot taken after the prompt (outside the timed region).  Returns microseconds
-    per step and the decisions of the last replay."""
-    from mixed_precision_paged_score_amd import kvc, pipeline
+def time_generation_loop(a, w, k, v, acc, ev, stream, nsteps):
+    """The generation phase of one layer, `nsteps` steps after the workload's prompt, as a
+    caller runs it: each step is a decode with score accumulation (a fresh query per request
+    and query head) into one padded accumulator buffer [B][N + nsteps][Hq], then
+    kvc_generation_step on the same buffer (append the new tokens, score the token leaving
+    the window).  The steps are captured into one graph (positions advance on the device);
+    before each replay the pool, the accumulators and the positions are restored from a
+    snapshot taken after the prompt (outside the timed region).  Returns microseconds per step,
+    the policy step alone per step, and the decisions of the last replay."""
+    from mixed_precision_paged_score_amd import kvc, pipeline, workloads
     B, Hkv, Hq, W = w.batch, w.num_kv_heads, w.num_q_heads, w.window
-    N = w.seqlens[0]
-    assert len(set(w.seqlens)) == 1 and N > 16 * nsteps and N > W
+    N = max(w.seqlens)
     dev = k.device
     gp = pipeline.GenerationPath(w, N + nsteps, dev)
     gp.prompt(0, acc, k, v)
-    rng = np.random.default_rng(w.seed + 4242)
-    rows = np.array([(b + 1) * (N + s + 1) - 1 - W for s in range(nsteps) for b in range(B)])
-    harm = np.sum(np.arange(1, N + 1, dtype=np.float64) ** -1.1)
-    mean = (rng.integers(0, N, size=(len(rows), Hq)) + 1.0) ** -1.1 / harm
-    accg = torch.zeros((int(rows.max()) + 1, Hq), dtype=torch.float32, device=dev)
-    accg[torch.tensor(rows, device=dev)] = torch.tensor(mean * W, dtype=torch.float32,
-                                                        device=dev)
-    pos = [torch.full((B,), N + s, dtype=torch.int32, device=dev) for s in range(nsteps)]
-    cus = [torch.arange(B + 1, dtype=torch.int32, device=dev) * (N + s + 1)
-           for s in range(nsteps)]
+    cap = gp.seqlen_cap
+    cu_pad = gp.padded_cu()
+    acc_pad = torch.zeros((B * cap, Hq), dtype=torch.float32, device=dev)
+    cu = w.cu_seqlens()
+    for b, n in enumerate(w.seqlens):
+        acc_pad[b * cap:b * cap + n] = acc[int(cu[b]):int(cu[b + 1])]
+    pos = torch.tensor(w.seqlens, dtype=torch.int32, device=dev)
+    qs = [workloads.make_queries(w, dev, 1000 + s) for s in range(nsteps)]
     gen = torch.Generator(device=dev).manual_seed(w.seed + 4243)
     kn = [torch.randn((B, Hkv, 128), generator=gen, device=dev).to(torch.float16)
           for _ in range(nsteps)]
     vn = [torch.randn((B, Hkv, 128), generator=gen, device=dev).to(torch.float16)
           for _ in range(nsteps)]
-    gp.ws_gen = kvc.workspace(gp.geom, kvc.OP_GENERATE, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws_acc = kvc.workspace(gp.geom, kvc.OP_DECODE_ACC, cap, device=dev)
+    ws_gen = kvc.workspace(gp.geom, kvc.OP_GENERATE, device=dev)
     decided = torch.empty((nsteps, B, Hkv), dtype=torch.uint8, device=dev)
     pool = gp.pool
     state = [pool.pages, pool.page_table, pool.count, pool.owner, pool.free_ring,
-             pool.ring_ctr, pool.dev_status]
+             pool.ring_ctr, pool.dev_status, acc_pad, pos]
     snap = [t.clone() for t in state]
 
     def restore():
         for t, s0 in zip(state, snap):
             t.copy_(s0)
 
-    def run_steps():
+    def run_steps(with_decode=True):
         for s in range(nsteps):
-            kvc.generation_step(gp.geom, 0, pool, kn[s], vn[s], pos[s], accg, cus[s],
-                                w.alpha_h, w.alpha_l, W, decided[s], gp.ws_gen)
+            if with_decode:
+                kvc.paged_decode_attention_acc(gp.geom, 0, pool, qs[s], gp.scale, out, acc_pad,
+                                               cu_pad, cap, ws_acc)
+            kvc.generation_step(gp.geom, 0, pool, kn[s], vn[s], pos, acc_pad, cu_pad,
+                                w.alpha_h, w.alpha_l, W, decided[s], ws_gen)
+            pos.add_(1)
 
-    run_steps()                     # eager once: checks the sequence before capture
-    torch.cuda.synchronize()
-    status = pool.status()
-    restore()
-    if a.eager:
-        run = run_steps
-    else:
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run_steps()
-        run = g.replay
-    times = []
-    for _ in range(max(a.steps, 1)):
+    def timed(with_decode):
         restore()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        run()
-        e1.record(stream)
+        run_steps(with_decode)             # eager once: checks the sequence before capture
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3 / nsteps)
-    status |= pool.status()
+        status = pool.status()
+        restore()
+        if a.eager:
+            run = lambda: run_steps(with_decode)  # noqa: E731
+        else:
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_steps(with_decode)
+            run = g.replay
+        times = []
+        for _ in range(max(a.steps, 1)):
+            restore()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / nsteps)
+        return float(np.mean(times)), status | pool.status()
+
+    policy_us, st0 = timed(False)      # the policy step alone (prompt accumulators only)
+    step_us, st1 = timed(True)
     d = decided.cpu().numpy()
     counts = {"kept_high": int((d == kvc.HIGH).sum()), "demoted_low": int((d == kvc.LOW).sum()),
               "pruned": int((d == kvc.PRUNE).sum())}
-    del gp, snap, accg
-    return float(np.mean(times)), counts, status
+    del gp, snap, acc_pad
+    return step_us, policy_us, counts, st0 | st1
 
 
 def traffic_record(workload):
@@ -187,13 +198,14 @@ def traffic_record(workload):
     it was measured on are unchanged."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    none = {"decode": None, "compaction": None, "decode_acc": None}
     if not os.path.exists(path):
-        return None, None
+        return none
     text = open(path).read()
     try:
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (IndexError, ValueError):
-        return None, None
+        return none
     csrc = os.path.join(ROOT, "mixed_precision_paged_score_amd", "csrc")
 
     def same(names):
@@ -204,12 +216,15 @@ def traffic_record(workload):
             if hashlib.sha256(open(f, "rb").read()).hexdigest() != rec["kernel_sources_sha256"][n]:
                 return False
         return True
-    dec = rec["decode_call_bytes"]["total"] if same(["attention.hip", "workspace.h",
-                                                      "kvc_internal.h"]) else None
-    comp = rec["compaction_round_bytes"]["total"] if same(
-        ["score.hip", "compact.hip", "quantize.hip", "quant_row.h", "workspace.h",
-         "kvc_internal.h"]) else None
-    return dec, comp
+    dec_src = same(["attention.hip", "workspace.h", "kvc_internal.h"])
+    out = dict(none)
+    if dec_src:
+        out["decode"] = rec["decode_call_bytes"]["total"]
+        out["decode_acc"] = rec.get("decode_acc_call_bytes", {}).get("total")
+    if same(["score.hip", "compact.hip", "quantize.hip", "quant_row.h", "page_io.h",
+             "workspace.h", "kvc_internal.h"]):
+        out["compaction"] = rec["compaction_round_bytes"]["total"]
+    return out
 
 
 def decode_algorithmic_bytes(count, B, Hq):
@@ -330,14 +345,11 @@ def main():
         acc_us = time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream)
     gen = None
     if a.gen_steps > 0:
-        gen_us, gen_counts, gen_status = time_generation_step(a, w, k, v, acc, ev, stream,
-                                                              a.gen_steps)
-        gen = {"us_per_step": gen_us, "steps": a.gen_steps, "heads": w.batch * w.num_kv_heads,
-               "decisions": gen_counts, "status": gen_status}
-        if acc_us is not None:
-            # one generation step of one layer: accumulate this query's weights, then the
-            # policy step
-            gen["with_decode_acc_us"] = gen_us + acc_us
+        step_us, policy_us, gen_counts, gen_status = time_generation_loop(
+            a, w, k, v, acc, ev, stream, a.gen_steps)
+        gen = {"us_per_step": step_us, "policy_us_per_step": policy_us, "steps": a.gen_steps,
+               "heads": w.batch * w.num_kv_heads, "decisions": gen_counts,
+               "status": gen_status}
     comp_ms = [e0.elapsed_time(e1) for (e0, e1, e2) in recs]
     dec_ms = [e1.elapsed_time(e2) / max(nsteps_dec, 1) for (e0, e1, e2) in recs]
     count = path.new_count.cpu().numpy()
@@ -354,7 +366,8 @@ def main():
     comp_gbps = cbytes / comp_s / 1e9
     ms_per_step = wall / a.steps * 1e3
     nh, nl = int(count[..., 0].sum()), int(count[..., 1].sum())
-    dec_traffic, comp_traffic = traffic_record(w.name)
+    traffic = traffic_record(w.name)
+    dec_traffic, comp_traffic = traffic["decode"], traffic["compaction"]
     res = {
         "metric": "KV tokens compacted/s + paged decode attn GB/s (fraction of HBM peak)",
         "value": token_heads / comp_s,
@@ -384,8 +397,8 @@ def main():
             "us_per_call": acc_us,
             "GBps": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9,
             "frac_hbm": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9 / HBM_PEAK_GBPS,
-            "algorithmic_bytes": dbytes + acc_bytes},
-        "generation_step": gen,
+            "algorithmic_bytes": dbytes + acc_bytes, "traffic": traffic["decode_acc"]},
+        "generation_loop": gen,
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},

@@ -226,9 +226,11 @@ int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_po
  * uses: exp(s*q.k_hat - max) / sum over the head's live tokens.  Pruned tokens get nothing.
  *   acc_sum     float32 [T][Hq], the layout kvc_score_tokens reads, 16-byte aligned;
  *               updated in place
- *   cu_seqlens  int32 [B+1] of the same requests (N_b = cu_seqlens[b+1] - cu_seqlens[b]); a
- *               live token with position >= N_b, or out of ascending order within its head
- *               and tier, is skipped and sets KVC_DEV_SEQLEN
+ *   cu_seqlens  int32 [B+1]: request b owns rows cu[b] .. cu[b+1]-1 (N_b rows: its length, or
+ *               any larger capacity, so that a generation loop can keep one padded buffer;
+ *               every row of the range is read and written back); a live token with
+ *               position >= N_b, or out of ascending order within its head and tier, is
+ *               skipped and sets KVC_DEV_SEQLEN
  *   max_seqlen  bounds every N_b (a longer request gets no update and sets KVC_DEV_SEQLEN)
  *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE_ACC, max_seqlen) bytes, 256-B aligned
  *        (split partials, softmax max/sum per query head, logits of every live token, the
@@ -259,9 +261,10 @@ int kvc_paged_decode_attention_acc(const kvc_geom *geom, int32_t layer, const kv
  * from one allocation round of the kvc_compact_pages kind (no head is rebuilt; a HIGH count
  * never shrinks in a step).
  *   k_new, v_new  fp16 [B][Hkv][128], 16-byte aligned;  positions int32 [B]
- *   acc_sum       float32 [T][Hq] over the lengths after the new token (T = cu_seqlens[B]),
- *                 e.g. filled by kvc_paged_decode_attention_acc; read only
- *   cu_seqlens    int32 [B+1]; cu[b+1] - cu[b] must be N (else KVC_DEV_SEQLEN)
+ *   acc_sum       float32 [T][Hq], e.g. filled by kvc_paged_decode_attention_acc; read only
+ *   cu_seqlens    int32 [B+1]: request b's accumulator rows are cu[b] .. cu[b+1]-1, at least
+ *                 N of them (its length after the new token, or a larger capacity: the same
+ *                 padded layout as the accumulating decode's); fewer set KVC_DEV_SEQLEN
  *   window        1 .. KVC_GEN_MAX_WINDOW; the head's last `window` HIGH slots must hold
  *                 positions t_c .. N-2 (else KVC_DEV_COUNT_MISMATCH)
  *   tier_out      uint8 [B][Hkv]: the tier given to t_c, 255 where no token left the window

@@ -52,7 +52,7 @@ __global__ void gen_decide_kernel(const int32_t *__restrict__ count_l,
     int d = GEN_NONE;
     if (t_c >= 0) {
         const int lo = cu[b];
-        if (cu[b + 1] - lo != N) {
+        if (cu[b + 1] - lo < N) {
             atomicOr(status, KVC_DEV_SEQLEN);     // the accumulators do not cover this request
         } else if (nh < window ||
                    reinterpret_cast<const int32_t *>(

@@ -60,14 +60,17 @@ class PromptPath:
         kvc.paged_decode_attention(self.geom, layer, self.pool, q, self.scale, out,
                                    self.ws_decode)
 
-    def decode_acc(self, layer, q, out, acc):
+    def decode_acc(self, layer, q, out, acc, cu=None):
         """Decode attention that also adds every cached token's attention weight into
-        `acc` ([T][Hq] float32, this path's current requests)."""
+        `acc` ([T][Hq] float32 over this path's current requests, or rows laid out by `cu`,
+        e.g. a padded [B][seqlen_cap][Hq] buffer with cu = b * seqlen_cap)."""
         if self.ws_decode_acc is None:
             self.ws_decode_acc = kvc.workspace(self.geom, kvc.OP_DECODE_ACC, self.seqlen_cap,
                                                device=self.device)
         kvc.paged_decode_attention_acc(self.geom, layer, self.pool, q, self.scale, out, acc,
-                                       self.cu, self.max_seqlen, self.ws_decode_acc)
+                                       self.cu if cu is None else cu,
+                                       self.max_seqlen if cu is None else self.seqlen_cap,
+                                       self.ws_decode_acc)
 
     # -- HIP graphs -------------------------------------------------------------------------
     # Every library call is asynchronous on the current stream, reads its sizes from device
@@ -150,16 +153,23 @@ class GenerationPath(PromptPath):
         self.T += self.w.batch
         self.max_seqlen += 1
 
-    def step(self, layer, k_new, v_new, acc):
+    def padded_cu(self):
+        """Row offsets of a padded accumulator buffer [B][seqlen_cap][Hq]: the layout both
+        accumulating calls accept for every step of a generation run."""
+        return torch.arange(self.w.batch + 1, dtype=torch.int32,
+                            device=self.device) * self.seqlen_cap
+
+    def step(self, layer, k_new, v_new, acc, cu=None):
         """One decode step under the per-step policy: append the new tokens and give the
         token leaving the window its tier.  acc float32 [T + B][Hq] over the lengths after
-        the new tokens (the layout of cu_next)."""
+        the new tokens (the layout of cu_next), or rows laid out by `cu` (padded_cu())."""
         w = self.w
         if self.ws_gen is None:
             self.ws_gen = kvc.workspace(self.geom, kvc.OP_GENERATE, device=self.device)
         cu_next = self.cu + self._cu_step
         kvc.generation_step(self.geom, layer, self.pool, k_new, v_new, self.lens_dev, acc,
-                            cu_next, w.alpha_h, w.alpha_l, w.window, self.decided, self.ws_gen)
+                            cu_next if cu is None else cu, w.alpha_h, w.alpha_l, w.window,
+                            self.decided, self.ws_gen)
         # bookkeeping: the new positions are HIGH, the leaving token takes its tier
         pos = self.lens_dev.long()
         self.state[self._bidx, pos] = kvc.HIGH

@@ -140,3 +140,90 @@ def test_workload4_shape_sampled():
     # steps, codes and attention on 6 sampled heads
     w = workloads.workload(4)
     run_steps(w, steps=512, sample_heads=6, check_every=64, acc_device=DEV)
+
+
+def test_decode_acc_padded_layout_matches_packed():
+    # the accumulating decode over a padded [B][cap][Hq] buffer (cu = b * cap) adds the same
+    # values, bit for bit, as over the packed [T][Hq] layout, and leaves the padding rows as
+    # they were
+    from mixed_precision_paged_score_amd import pipeline
+    w = workloads.Workload("acc-pad", 1, 3, 16, 4, [300, 1, 517], 1.0, 0.2, 16, 2048, "zipf",
+                           seed=54)
+    k, v = workloads.make_kv(w)
+    acc = workloads.make_acc(w, k)
+    path = pipeline.GenerationPath(w, max(w.seqlens) + 40, DEV)
+    path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
+    cap = path.seqlen_cap
+    packed = torch.zeros((path.T, w.num_q_heads), dtype=torch.float32, device=DEV)
+    padded = torch.zeros((w.batch * cap, w.num_q_heads), dtype=torch.float32, device=DEV)
+    for b, n in enumerate(w.seqlens):
+        padded[b * cap + n:(b + 1) * cap] = 0.25         # padding rows: must stay as they are
+    out_a = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    out_b = torch.empty_like(out_a)
+    for s in range(2):
+        q = workloads.make_queries(w, DEV, s)
+        path.decode_acc(0, q, out_a, packed)
+        path.decode_acc(0, q, out_b, padded, cu=path.padded_cu())
+    torch.cuda.synchronize()
+    assert path.pool.status() == 0
+    assert torch.equal(out_a, out_b)
+    cu = w.cu_seqlens()
+    for b, n in enumerate(w.seqlens):
+        assert torch.equal(padded[b * cap:b * cap + n], packed[int(cu[b]):int(cu[b + 1])]), b
+        assert torch.all(padded[b * cap + n:(b + 1) * cap] == 0.25)
+
+
+def test_full_loop_on_padded_accumulators():
+    # the per-step loop of one layer as a caller runs it: decode attention with score
+    # accumulation into one padded buffer, then the policy step reading the same buffer.  The
+    # oracle's step gets the same accumulator values (read back), so decisions, allocator state
+    # and pages must agree bit for bit; the decode output agrees with the oracle's attention
+    # over its state before each step.
+    from mixed_precision_paged_score_amd import pipeline
+    w = workloads.Workload("loop-pad", 1, 3, 16, 4, [300, 5, 200], 1.0, 0.2, 16, 2048, "zipf",
+                           seed=55)
+    steps = 60
+    k, v = workloads.make_kv(w)
+    acc = workloads.make_acc(w, k)
+    path = pipeline.GenerationPath(w, max(w.seqlens) + steps, DEV)
+    path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
+    cap = path.seqlen_cap
+    cu_pad = path.padded_cu()
+    acc_pad = torch.zeros((w.batch * cap, w.num_q_heads), dtype=torch.float32, device=DEV)
+    cu = w.cu_seqlens()
+    for b, n in enumerate(w.seqlens):
+        acc_pad[b * cap:b * cap + n] = acc[int(cu[b]):int(cu[b + 1])].to(DEV)
+    tier0, _, _ = parity.oracle_score(w, acc)
+    gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages)
+    gen.prompt(k.numpy(), v.numpy(), tier0, cu)
+    g = torch.Generator().manual_seed(56)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    G = w.group
+    seen = np.zeros(256, np.int64)
+    for s in range(steps):
+        q = workloads.make_queries(w, "cpu", 100 + s)
+        kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
+        path.decode_acc(0, q.to(DEV), out, acc_pad, cu=cu_pad)
+        if s % 10 == 0:
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                for h in range(w.num_kv_heads):
+                    kd, vd = gen.head_dequantized(b, h)
+                    want = oatt.decode_group(q.numpy()[b, h * G:(h + 1) * G], kd, vd, path.scale)
+                    parity.assert_close_attention(parity.np_(out[b, h * G:(h + 1) * G]), want)
+        lens = list(path.lens)
+        path.step(0, kn.to(DEV), vn.to(DEV), acc_pad, cu=cu_pad)
+        a_np = parity.np_(acc_pad)
+        packed = np.concatenate([a_np[b * cap:b * cap + n + 1] for b, n in enumerate(lens)])
+        dec_o = gen.step(kn.numpy(), vn.numpy(), packed, w.alpha_h, w.alpha_l, w.window)
+        assert np.array_equal(parity.np_(path.decided), dec_o), f"step {s}"
+        seen += np.bincount(dec_o.ravel(), minlength=256)
+        if (s + 1) % 10 == 0:
+            assert path.pool.status() == 0
+            parity.compare_pool(path.pool, gen.pool)
+            _compare_heads(w, path, gen)
+    assert path.pool.status() == 0
+    print(f"[loop] decisions high {seen[2]} low {seen[1]} pruned {seen[0]} none {seen[255]}",
+          flush=True)
+    assert seen[2] > 0 and seen[1] > 0
