@@ -106,7 +106,7 @@ typedef struct {
 
 /* Operation ids for kvc_workspace_bytes */
 enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4,
-       KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6 };
+       KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6, KVC_OP_PREFILL = 7 };
 
 /* Version string of the library. */
 const char *kvc_version(void);
@@ -115,7 +115,8 @@ const char *kvc_version(void);
 const char *kvc_last_error(void);
 
 /* Bytes of workspace `op` needs for this geometry.  max_seqlen is the longest request
- * (KVC_OP_QUANTIZE, KVC_OP_DECODE_ACC), unused otherwise.  Returns 0 for an unknown op. */
+ * (KVC_OP_QUANTIZE, KVC_OP_DECODE_ACC, KVC_OP_PREFILL), unused otherwise.  Returns 0 for an
+ * unknown op. */
 size_t kvc_workspace_bytes(const kvc_geom *geom, int32_t op, int32_t max_seqlen);
 
 /* Empty pool: free_ring = 0..P-1, head = 0, tail = P, page table and owner = -1,
@@ -143,6 +144,30 @@ int kvc_score_tokens(const kvc_geom *geom, const float *acc_sum, const int32_t *
                      int32_t window, const uint8_t *prev_tier, uint8_t *tier,
                      int32_t *new_count, uint8_t *changed, int32_t *dev_status,
                      kvc_stream_t stream);
+
+/* Causal prefill attention of a batch of prompts, and the prompt's significance
+ * accumulators (DiffKV review page: "Assumptions", standard causal multi-head attention;
+ * "What carries the argument", a token's score is the mean of the attention it receives from
+ * subsequent tokens, so the sums over strictly later queries are what kvc_score_tokens reads).
+ * For request b (rows cu[b] .. cu[b+1]-1) and query head hq (KV head hq / G), query row i
+ * attends to keys j <= i of its request: p_ij = softmax_j(softmax_scale * q_i . k_j);
+ *   out[i][hq]    = sum_j p_ij v_j   (fp16 or float32 [T][Hq][128]);
+ *   acc_sum[t][hq] = sum over i > t of p_it   (float32 [T][Hq], overwritten; NULL: skipped).
+ * Scores and sums in float32 from fp16 inputs (matrix cores); the probabilities that weight V
+ * are rounded to fp16.  Each accumulator is summed by one workgroup in a fixed order:
+ * deterministic.
+ *   q fp16 [T][Hq][128]; k, v fp16 [T][Hkv][128]; all 16-byte aligned, as is out
+ *   max_seqlen  bounds every request length (a longer request is skipped and sets
+ *               KVC_DEV_SEQLEN in *dev_status; dev_status may be NULL)
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_PREFILL, max_seqlen) bytes, 256-B aligned
+ *               (each row's softmax max and sum); geom's batch, num_q_heads and num_kv_heads
+ *               are used
+ * Errors: KVC_E_NULL, KVC_E_ALIGN, KVC_E_SHAPE (Hq % Hkv, max_seqlen < 0), KVC_E_WORKSPACE. */
+int kvc_prefill_attention(const kvc_geom *geom, const uint16_t *q, const uint16_t *k,
+                          const uint16_t *v, const int32_t *cu_seqlens, int32_t max_seqlen,
+                          float softmax_scale, void *out, int32_t out_is_fp32, float *acc_sum,
+                          int32_t *dev_status, void *workspace, size_t workspace_bytes,
+                          kvc_stream_t stream);
 
 /* One allocation round for one layer: prefix sums over the B*Hkv heads (request-major) of
  * their page demand give each head a contiguous segment of the circular free list

@@ -1,0 +1,418 @@
+// kvc_prefill_attention: causal prefill attention of the prompt, and the prompt's significance
+// accumulators (the step before scoring).
+//
+// DiffKV review page: "Assumptions" (standard causal multi-head attention, the page's Eq. 1);
+// "What carries the argument" (a token's significance is the mean of the attention it
+// receives from subsequent tokens; referee major comment 2 counts the N - i later queries).
+// acc_sum[t][hq] is therefore the sum, over the strictly later queries i > t of the same
+// request, of query i's softmax weight on key t.
+//
+// Two launches:
+//   prefill_fwd     flash-attention forward (one workgroup per 128 queries of one request and
+//                   query head; 64-key blocks double-buffered in LDS): the output rows and
+//                   each row's softmax max and sum (log2 units) into the workspace.
+//   prefill_colsum  one workgroup per 64 keys of one request and query head: the scores
+//                   against every later query tile are recomputed, normalized with the rows'
+//                   max and sum, and summed per key; each accumulator is written once.
+// Matrix products are v_mfma_f32_16x16x32_f16 on S^T = K Q^T (a lane owns one query column,
+// so row statistics and rescales stay in the lane) and O^T = V^T P^T (P^T is already in the
+// operand layout: its k index is the key order of two S^T tiles).
+#include "kvc_internal.h"
+#include "workspace.h"
+
+#pragma clang fp contract(off)
+
+namespace kvc {
+namespace pf {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128;          // queries per forward workgroup (32 per wave)
+constexpr int BN = 64;           // keys per block
+constexpr int KS = D + 8;        // LDS key row stride (halves): rows 4 banks apart
+constexpr int VS = BN + 8;       // LDS transposed value row stride (halves)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float MARGIN = 8.0f;   // the running max moves only when exceeded by this (log2)
+constexpr float M_INIT = -1.0e30f;
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups of one query column)
+__device__ __forceinline__ float max_col(float x) {
+    uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    u = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ---- staging of one key block (64 keys of one request and KV head) ----------------------
+// K: thread t loads row (t / 16) + 16i, 16 bytes at column 8 (t % 16); stored row-major.
+// V: thread t loads rows 2m, 2m + 1 (m = t % 32) at column 8d (d = t / 32 + 8i) and stores
+// them transposed, a word holding both rows' halves of one column.
+struct KBlock {
+    uint4 k[4];
+};
+struct VBlock {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ uint4 ld_row(const uint16_t *base, int64_t row, bool ok, int col8) {
+    return ok ? *reinterpret_cast<const uint4 *>(base + row * D + 8 * col8)
+              : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void load_k(KBlock &kb, const uint16_t *K, int64_t lo, int N, int kb0,
+                                       int Hkv, int h, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = (tid >> 4) + 16 * i;
+        kb.k[i] = ld_row(K, (lo + kb0 + key) * Hkv + h, kb0 + key < N, tid & 15);
+    }
+}
+__device__ __forceinline__ void load_v(VBlock &vb, const uint16_t *V, int64_t lo, int N, int kb0,
+                                       int Hkv, int h, int tid) {
+    const int m = tid & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int d8 = (tid >> 5) + 8 * i;
+        vb.v[2 * i] = ld_row(V, (lo + kb0 + 2 * m) * Hkv + h, kb0 + 2 * m < N, d8);
+        vb.v[2 * i + 1] = ld_row(V, (lo + kb0 + 2 * m + 1) * Hkv + h, kb0 + 2 * m + 1 < N, d8);
+    }
+}
+__device__ __forceinline__ void store_k(const KBlock &kb, _Float16 *s_k, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4 *>(s_k + ((tid >> 4) + 16 * i) * KS + 8 * (tid & 15)) = kb.k[i];
+}
+__device__ __forceinline__ void store_v(const VBlock &vb, _Float16 *s_vt, int tid) {
+    const int m = tid & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int d8 = (tid >> 5) + 8 * i;
+        const uint32_t a[4] = {vb.v[2 * i].x, vb.v[2 * i].y, vb.v[2 * i].z, vb.v[2 * i].w};
+        const uint32_t b[4] = {vb.v[2 * i + 1].x, vb.v[2 * i + 1].y, vb.v[2 * i + 1].z,
+                               vb.v[2 * i + 1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t lo16 = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t hi16 = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            *reinterpret_cast<uint32_t *>(s_vt + (8 * d8 + e) * VS + 2 * m) = lo16 | (hi16 << 16);
+        }
+    }
+}
+
+// query operands of 32 queries (two column tiles) starting at q0: lane (c, g) holds query
+// q0 + 16 qt + c, dims 32 ks + 8 g .. + 7
+__device__ __forceinline__ void load_q(h8 (&qop)[2][4], const uint16_t *Q, int64_t lo, int N,
+                                       int q0, int Hq, int hq, int lane) {
+    const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qi = q0 + 16 * qt + c;
+        const bool ok = qi < N;
+        const uint16_t *row = Q + ((lo + qi) * Hq + hq) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4 u = ok ? *reinterpret_cast<const uint4 *>(row + 32 * ks)
+                               : make_uint4(0, 0, 0, 0);
+            qop[qt][ks] = __builtin_bit_cast(h8, u);
+        }
+    }
+}
+
+// S^T tiles of 64 keys x 32 queries: s[kt][qt], lane (c, g) holds query 16 qt + c, keys
+// 16 kt + 4 g + r.  Key operands from LDS rows (16 kt + c), dims 32 ks + 8 g.
+__device__ __forceinline__ void scores(f4 (&s)[4][2], const _Float16 *s_k,
+                                       const h8 (&qop)[2][4], int lane) {
+    const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const h8 a = *reinterpret_cast<const h8 *>(s_k + (16 * kt + c) * KS + 32 * ks + 8 * g);
+            s[kt][0] = mfma(a, qop[0][ks], s[kt][0]);
+            s[kt][1] = mfma(a, qop[1][ks], s[kt][1]);
+        }
+}
+
+// grid (ceil(max_seqlen / BM), Hq, B), 256 threads.  Query blocks run last-first (the
+// longest key ranges start first).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ cu, int Hq, int Hkv,
+    int max_seqlen, float scale_log2, void *__restrict__ out, int out_fp32,
+    float *__restrict__ ml, int32_t *status) {
+    __shared__ __attribute__((aligned(16))) _Float16 s_k[2][BN * KS];
+    __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
+    const int b = blockIdx.z, hq = blockIdx.y;
+    const int64_t lo = cu[b];
+    const int N = cu[b + 1] - cu[b];
+    if (N > max_seqlen) {
+        if (status && blockIdx.x == 0 && hq == 0 && threadIdx.x == 0)
+            atomicOr(status, KVC_DEV_SEQLEN);
+        return;
+    }
+    const int q0 = (gridDim.x - 1 - blockIdx.x) * BM;
+    if (q0 >= N) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int h = hq / (Hq / Hkv);
+    const int qw = q0 + 32 * wave;                   // the wave's first query
+    const int nblk = (min(q0 + BM, N) - 1) / BN + 1; // key blocks 0 .. nblk-1
+
+    h8 qop[2][4];
+    load_q(qop, Q, lo, N, qw, Hq, hq, lane);
+    KBlock kb;
+    VBlock vb;
+    load_k(kb, K, lo, N, 0, Hkv, h, tid);
+    load_v(vb, V, lo, N, 0, Hkv, h, tid);
+    store_k(kb, s_k[0], tid);
+    store_v(vb, s_vt[0], tid);
+    __syncthreads();
+
+    f4 o[8][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt][0] = o[dt][1] = f4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {M_INIT, M_INIT}, l[2] = {0.f, 0.f};
+
+    for (int j = 0; j < nblk; ++j) {
+        const int cur = j & 1;
+        const int kb0 = j * BN;
+        const bool more = j + 1 < nblk;
+        bool issued = false;
+        if (kb0 <= qw + 31) {                        // else every key is after the wave's queries
+            f4 s[4][2];
+            scores(s, s_k[cur], qop, lane);
+            const bool diag = kb0 + BN - 1 > qw;
+            h8 pb[2][2];                             // P^T operands [qt][u]
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const int qi = qw + 16 * qt + c;
+                float x[16];
+                float mx = M_INIT;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float v = s[kt][qt][r] * scale_log2;
+                        if (diag && kb0 + 16 * kt + 4 * g + r > qi) v = -__builtin_inff();
+                        x[4 * kt + r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                mx = max_col(mx);
+                if (__ballot(mx > m[qt] + MARGIN) != 0ull) {
+                    const float mn = fmaxf(m[qt], mx);
+                    const float corr = __builtin_amdgcn_exp2f(m[qt] - mn);
+                    m[qt] = mn;
+                    l[qt] *= corr;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= corr;
+                }
+                float ls = 0.f;
+                _Float16 p[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(x[e] - m[qt]);
+                    ls += pe;
+                    p[e] = _Float16(pe);
+                }
+                l[qt] += ls;
+                // P^T operand u: keys 32u + 4g + e (e < 4) from tile 2u, 32u + 16 + 4g + e - 4
+                // from tile 2u + 1
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    pb[qt][u] = h8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
+                                   p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]};
+            }
+            // the next block's rows are requested now (the score registers are free) and land
+            // while the PV products run
+            if (more) {
+                load_k(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
+                load_v(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+                issued = true;
+            }
+            // O^T += V^T P^T; V^T operand: dim row 16 dt + c, keys in the same order as P^T's k
+            const _Float16 *vt = s_vt[cur];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const _Float16 *vrow = vt + (16 * dt + c) * VS + 4 * g;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const h4 a0 = *reinterpret_cast<const h4 *>(vrow + 32 * u);
+                    const h4 a1 = *reinterpret_cast<const h4 *>(vrow + 32 * u + 16);
+                    const h8 a = h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    o[dt][0] = mfma(a, pb[0][u], o[dt][0]);
+                    o[dt][1] = mfma(a, pb[1][u], o[dt][1]);
+                }
+            }
+        }
+        if (more) {
+            if (!issued) {
+                load_k(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
+                load_v(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+            }
+            store_k(kb, s_k[cur ^ 1], tid);
+            store_v(vb, s_vt[cur ^ 1], tid);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        float lt = l[qt];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int qi = qw + 16 * qt + c;
+        if (qi >= N) continue;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        const int64_t row = (lo + qi) * Hq + hq;
+        if (g == 0) *reinterpret_cast<float2 *>(ml + 2 * row) = make_float2(m[qt], lt);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const int d0 = 16 * dt + 4 * g;
+            const f4 v = o[dt][qt] * inv;
+            if (out_fp32) {
+                *reinterpret_cast<float4 *>(static_cast<float *>(out) + row * D + d0) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                const uint32_t w0 = uint32_t(f2h_rn(v[0])) | (uint32_t(f2h_rn(v[1])) << 16);
+                const uint32_t w1 = uint32_t(f2h_rn(v[2])) | (uint32_t(f2h_rn(v[3])) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + row * D + d0) =
+                    make_uint2(w0, w1);
+            }
+        }
+    }
+}
+
+// grid (ceil(max_seqlen / BN), Hq, B), 256 threads.  The 64 keys' operands stay in registers;
+// wave w takes query tiles of 32 from the block's start: kb0/32 + w, + 4, ...
+__global__ __launch_bounds__(256) void prefill_colsum_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const int32_t *__restrict__ cu,
+    int Hq, int Hkv, int max_seqlen, float scale_log2, const float *__restrict__ ml,
+    float *__restrict__ acc) {
+    __shared__ __attribute__((aligned(16))) _Float16 s_k[BN * KS];
+    __shared__ float s_cs[4][BN];
+    const int b = blockIdx.z, hq = blockIdx.y;
+    const int64_t lo = cu[b];
+    const int N = cu[b + 1] - cu[b];
+    if (N > max_seqlen) return;
+    const int kb0 = blockIdx.x * BN;
+    if (kb0 >= N) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int h = hq / (Hq / Hkv);
+    {
+        KBlock kb;
+        load_k(kb, K, lo, N, kb0, Hkv, h, tid);
+        store_k(kb, s_k, tid);
+    }
+    __syncthreads();
+    h8 ka[4][4];                                     // [kt][ks]
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            ka[kt][ks] = *reinterpret_cast<const h8 *>(s_k + (16 * kt + c) * KS + 32 * ks + 8 * g);
+    float cs[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cs[kt][r] = 0.f;
+    for (int q0 = kb0 + 32 * wave; q0 < N; q0 += 128) {
+        h8 qop[2][4];
+        load_q(qop, Q, lo, N, q0, Hq, hq, lane);
+        float mq[2], il[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int qi = q0 + 16 * qt + c;
+            const float2 x = qi < N ? *reinterpret_cast<const float2 *>(ml + 2 * ((lo + qi) * Hq + hq))
+                                    : make_float2(0.f, 0.f);
+            mq[qt] = x.x;
+            il[qt] = x.y > 0.f ? 1.0f / x.y : 0.f;
+        }
+        f4 s[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) s[kt][0] = s[kt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                s[kt][0] = mfma(ka[kt][ks], qop[0][ks], s[kt][0]);
+                s[kt][1] = mfma(ka[kt][ks], qop[1][ks], s[kt][1]);
+            }
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int qi = q0 + 16 * qt + c;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ki = kb0 + 16 * kt + 4 * g + r;
+                    const float p = __builtin_amdgcn_exp2f(s[kt][qt][r] * scale_log2 - mq[qt]) *
+                                    il[qt];
+                    cs[kt][r] += (qi > ki && qi < N) ? p : 0.f;
+                }
+        }
+    }
+    // sum over the 16 query columns of each lane group, then over the four waves
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x = cs[kt][r];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+            if (c == 0) s_cs[wave][16 * kt + 4 * g + r] = x;
+        }
+    __syncthreads();
+    if (tid < BN && kb0 + tid < N)
+        acc[(lo + kb0 + tid) * Hq + hq] = (s_cs[0][tid] + s_cs[1][tid]) + (s_cs[2][tid] + s_cs[3][tid]);
+}
+
+}  // namespace pf
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvc_prefill_attention(const kvc_geom *g, const uint16_t *q, const uint16_t *k,
+                                     const uint16_t *v, const int32_t *cu_seqlens,
+                                     int32_t max_seqlen, float softmax_scale, void *out,
+                                     int32_t out_is_fp32, float *acc_sum, int32_t *dev_status,
+                                     void *ws, size_t ws_bytes, kvc_stream_t stream) {
+    if (!g) return KVC_E_NULL;
+    if (g->batch <= 0 || g->num_q_heads <= 0 || g->num_kv_heads <= 0 ||
+        g->num_q_heads % g->num_kv_heads)
+        return KVC_E_SHAPE;
+    if (!q || !k || !v || !cu_seqlens || !out) return KVC_E_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KVC_E_ALIGN;
+    if (max_seqlen < 0) return KVC_E_SHAPE;
+    PrefillWs L(g, max_seqlen);
+    if (!ws || ws_bytes < L.bytes) return KVC_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
+    if (max_seqlen == 0) return KVC_OK;
+    float *ml = reinterpret_cast<float *>(static_cast<char *>(ws) + L.ml);
+    hipStream_t s = (hipStream_t)stream;
+    const int Hq = g->num_q_heads, Hkv = g->num_kv_heads, B = g->batch;
+    const float sl2 = softmax_scale * pf::LOG2E;
+    hipLaunchKernelGGL(pf::prefill_fwd_kernel, dim3((max_seqlen + pf::BM - 1) / pf::BM, Hq, B),
+                       dim3(256), 0, s, q, k, v, cu_seqlens, Hq, Hkv, max_seqlen, sl2, out,
+                       out_is_fp32, ml, dev_status);
+    int rc = launch_check("kvc_prefill_attention/forward");
+    if (rc || !acc_sum) return rc;
+    hipLaunchKernelGGL(pf::prefill_colsum_kernel,
+                       dim3((max_seqlen + pf::BN - 1) / pf::BN, Hq, B), dim3(256), 0, s, q, k,
+                       cu_seqlens, Hq, Hkv, max_seqlen, sl2, ml, acc_sum);
+    return launch_check("kvc_prefill_attention/column sums");
+}

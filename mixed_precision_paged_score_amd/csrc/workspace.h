@@ -62,6 +62,16 @@ struct GenWs {
     }
 };
 
+// ---- prefill_attention -------------------------------------------------------------------
+struct PrefillWs {
+    size_t ml, bytes;
+    PrefillWs(const kvc_geom *g, int max_seqlen) {
+        ml = 0;            // float [T][Hq][2]: each query row's softmax max (log2) and sum
+        bytes = align256(sizeof(float) * 2 * size_t(g->batch) * size_t(max_seqlen > 0 ? max_seqlen : 1) *
+                         size_t(g->num_q_heads));
+    }
+};
+
 // ---- quantize_and_place ----------------------------------------------------------------
 constexpr int QTILE = 256;        // tokens per rank tile
 

@@ -16,6 +16,7 @@ DEV_POOL_EXHAUSTED, DEV_ROW_OVERFLOW, DEV_SHRINK, DEV_COUNT_MISMATCH, DEV_SEQLEN
 DEV_INTERNAL, DEV_BAD_TIER = 32, 64
 PRUNE, LOW, HIGH, FRESH = 0, 1, 2, 3
 OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC, OP_GENERATE = 1, 2, 3, 4, 5, 6
+OP_PREFILL = 7
 HEAD_DIM, HIGH_SLOTS, LOW_SLOTS, PAGE_BYTES = 128, 16, 32, 3456
 GEN_MAX_WINDOW = 112
 NO_TOKEN = 255      # generation step: no token left the window
@@ -23,7 +24,7 @@ NO_TOKEN = 255      # generation step: no token left the window
 EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_init",
            "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
-           "kvc_generation_step"]
+           "kvc_generation_step", "kvc_prefill_attention"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -63,9 +64,11 @@ _lib.kvc_paged_decode_attention_acc.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i
 _lib.kvc_append_tokens.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_generation_step.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i32,
                                      _vp, _vp, _sz, _vp]
+_lib.kvc_prefill_attention.argtypes = [_G, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp,
+                                       _vp, _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
-           "kvc_generation_step"):
+           "kvc_generation_step", "kvc_prefill_attention"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -194,3 +197,14 @@ def generation_step(geom, layer, pool, k_new, v_new, positions, acc_sum, cu_seql
                                     _ptr(cu_seqlens), float(alpha_h), float(alpha_l),
                                     int(window), _ptr(tier_out), _ptr(ws), ws.numel(),
                                     _stream(stream)), "kvc_generation_step")
+
+
+def prefill_attention(geom, q, k, v, cu_seqlens, max_seqlen, softmax_scale, out, acc_sum, ws,
+                      dev_status=None, stream=None):
+    _check(_lib.kvc_prefill_attention(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(cu_seqlens), int(max_seqlen), float(softmax_scale),
+                                      _ptr(out), int(out.dtype == torch.float32),
+                                      None if acc_sum is None else _ptr(acc_sum),
+                                      None if dev_status is None else _ptr(dev_status),
+                                      _ptr(ws), ws.numel(), _stream(stream)),
+           "kvc_prefill_attention")

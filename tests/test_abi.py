@@ -37,6 +37,7 @@ def test_version_and_workspace_sizes():
         16 * 8 * 2 * (32768 // 64 + 1) * 4
     assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC, -1) == 0
     assert kvc.workspace_bytes(g, kvc.OP_GENERATE) > kvc.workspace_bytes(g, kvc.OP_COMPACT)
+    assert kvc.workspace_bytes(g, kvc.OP_PREFILL, 32768) >= 16 * 32768 * 64 * 8
     assert kvc.workspace_bytes(g, 99) == 0
     bad = kvc.make_geom(1, 16, 60, 8, 2049, 1 << 18)        # Hq % Hkv != 0
     assert kvc.workspace_bytes(bad, kvc.OP_COMPACT) == 0
@@ -92,6 +93,15 @@ def test_synchronous_errors_enqueue_nothing():
                                    f1, f0, 8, 16, 256, 64, None) == kvc.E_WORKSPACE
     assert lib.kvc_generation_step(ctypes.byref(g), 0, ctypes.byref(p), 16, 18, 16, 16, 16,
                                    f1, f0, 8, 16, 256, 1 << 20, None) == kvc.E_ALIGN
+    # prefill: missing cu_seqlens, misaligned keys, negative max_seqlen, small workspace
+    assert lib.kvc_prefill_attention(ctypes.byref(g), 16, 16, 16, None, 8, f1, 16, 1, 16, None,
+                                     256, 1 << 20, None) == kvc.E_NULL
+    assert lib.kvc_prefill_attention(ctypes.byref(g), 16, 18, 16, 16, 8, f1, 16, 1, 16, None,
+                                     256, 1 << 20, None) == kvc.E_ALIGN
+    assert lib.kvc_prefill_attention(ctypes.byref(g), 16, 16, 16, 16, -1, f1, 16, 1, 16, None,
+                                     256, 1 << 20, None) == kvc.E_SHAPE
+    assert lib.kvc_prefill_attention(ctypes.byref(g), 16, 16, 16, 16, 8, f1, 16, 1, 16, None,
+                                     256, 8, None) == kvc.E_WORKSPACE
     # score: negative window
     assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
                                 ctypes.c_float(0.1), -1, None, 16, 16, None, None,
