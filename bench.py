@@ -18,7 +18,9 @@ by the number of calls; `cpu_baseline` times the CPU oracle on a bounded sample 
 workload.  Beside the step: `decode_with_score_accumulation` (the same decode calls adding
 every cached token's weight into the accumulators) and `generation_loop` (64 generation steps
 of the layer after the prompt: decode with score accumulation into one padded accumulator
-buffer, then kvc_generation_step, captured as one graph).
+buffer, then kvc_generation_step, captured as one graph) and `prefill` (the causal prefill
+attention of the workload's prompts with the accumulators, kvc_prefill_attention, against the
+fp16 matrix-core peak).
 """
 import argparse
 import dataclasses
@@ -35,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
 
 
 def parse():
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--gen-steps", type=int, default=64,
                     help="steps of the generation loop (decode with score accumulation, then "
                          "the per-step policy) timed after the main steps (0: skip)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the causal prefill (prompt accumulator producer) timing")
     ap.add_argument("--eager", action="store_true",
                     help="launch every library call from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -190,6 +195,45 @@ def time_generation_loop(a, w, k, v, acc, ev, stream, nsteps):
               "pruned": int((d == kvc.PRUNE).sum())}
     del gp, snap, acc_pad
     return step_us, policy_us, counts, st0 | st1
+
+
+def prefill_flops(seqlens, Hq):
+    """Matrix flops of the causal prefill with column sums: the forward pass multiplies
+    q.k and p.v over the N(N+1)/2 causal pairs (4 d flops per pair); the column-sum pass
+    recomputes q.k over the N(N-1)/2 strictly-later pairs (2 d flops each)."""
+    fwd = sum(n * (n + 1) / 2 for n in seqlens) * Hq * 4 * 128
+    cs = sum(n * (n - 1) / 2 for n in seqlens) * Hq * 2 * 128
+    return fwd, cs
+
+
+def time_prefill(a, w, k, v, ev, stream):
+    """kvc_prefill_attention on the workload's prompts (fresh fp16 queries, fp16 output, the
+    accumulators): milliseconds per call over a few calls after one warmup."""
+    from mixed_precision_paged_score_amd import kvc
+    dev = k.device
+    T, Hq = w.total_tokens, w.num_q_heads
+    g = torch.Generator(device=dev).manual_seed(w.seed + 5151)
+    q = torch.randn((T, Hq, 128), generator=g, device=dev).to(torch.float16)
+    out = torch.empty((T, Hq, 128), dtype=torch.float16, device=dev)
+    acc = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    cu = torch.tensor(w.cu_seqlens(), device=dev)
+    ms = max(w.seqlens)
+    geom = kvc.make_geom(1, w.batch, Hq, w.num_kv_heads, 1, 1)
+    ws = kvc.workspace(geom, kvc.OP_PREFILL, ms, device=dev)
+    scale = 1.0 / math.sqrt(128)
+    kvc.prefill_attention(geom, q, k, v, cu, ms, scale, out, acc, ws)
+    torch.cuda.synchronize()
+    reps = max(1, min(a.steps, 3))
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(reps):
+        kvc.prefill_attention(geom, q, k, v, cu, ms, scale, out, acc, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    del q, out, acc, ws
+    torch.cuda.empty_cache()
+    return t
 
 
 def traffic_record(workload):
@@ -350,6 +394,14 @@ def main():
         gen = {"us_per_step": step_us, "policy_us_per_step": policy_us, "steps": a.gen_steps,
                "heads": w.batch * w.num_kv_heads, "decisions": gen_counts,
                "status": gen_status}
+    pre = None
+    if not a.no_prefill:
+        pre_ms = time_prefill(a, w, k, v, ev, stream)
+        fl_fwd, fl_cs = prefill_flops(w.seqlens, w.num_q_heads)
+        pre = {"ms_per_call": pre_ms, "TFLOPs": (fl_fwd + fl_cs) / pre_ms / 1e9,
+               "frac_mfma_fp16": (fl_fwd + fl_cs) / pre_ms / 1e9 / MFMA_FP16_PEAK_TFLOPS,
+               "flops": fl_fwd + fl_cs, "flops_forward": fl_fwd, "flops_column_sums": fl_cs,
+               "peak_TFLOPs": MFMA_FP16_PEAK_TFLOPS}
     comp_ms = [e0.elapsed_time(e1) for (e0, e1, e2) in recs]
     dec_ms = [e1.elapsed_time(e2) / max(nsteps_dec, 1) for (e0, e1, e2) in recs]
     count = path.new_count.cpu().numpy()
@@ -399,6 +451,7 @@ def main():
             "frac_hbm": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes": dbytes + acc_bytes, "traffic": traffic["decode_acc"]},
         "generation_loop": gen,
+        "prefill": pre,
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},

@@ -11,9 +11,10 @@
 //   prefill_fwd     flash-attention forward (one workgroup per 128 queries of one request and
 //                   query head; 64-key blocks double-buffered in LDS): the output rows and
 //                   each row's softmax max and sum (log2 units) into the workspace.
-//   prefill_colsum  one workgroup per 64 keys of one request and query head: the scores
-//                   against every later query tile are recomputed, normalized with the rows'
-//                   max and sum, and summed per key; each accumulator is written once.
+//   prefill_colsum  one workgroup per 256 keys of one request and query head (64 per wave):
+//                   the scores against every later 32-query tile (staged once in LDS for the
+//                   four waves) are recomputed, normalized with the rows' max and sum, and
+//                   summed per key; each accumulator is written once.
 // Matrix products are v_mfma_f32_16x16x32_f16 on S^T = K Q^T (a lane owns one query column,
 // so row statistics and rescales stay in the lane) and O^T = V^T P^T (P^T is already in the
 // operand layout: its k index is the key order of two S^T tiles).
@@ -29,7 +30,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;          // queries per forward workgroup (32 per wave)
+#ifndef KVC_PF_WAVES
+#define KVC_PF_WAVES 8           // forward waves per workgroup (32 queries each)
+#endif
 constexpr int BN = 64;           // keys per block
 constexpr int KS = D + 8;        // LDS key row stride (halves): rows 4 banks apart
 constexpr int VS = BN + 8;       // LDS transposed value row stride (halves)
@@ -67,34 +70,41 @@ __device__ __forceinline__ uint4 ld_row(const uint16_t *base, int64_t row, bool 
               : make_uint4(0, 0, 0, 0);
 }
 
+// NT threads stage a block: K rows (tid / 16) + (NT / 16) i, V row pairs (tid % 32) at
+// columns 8 ((tid / 32) + (NT / 32) i)
+template <int NT>
 __device__ __forceinline__ void load_k(KBlock &kb, const uint16_t *K, int64_t lo, int N, int kb0,
                                        int Hkv, int h, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = (tid >> 4) + 16 * i;
+    for (int i = 0; i < 1024 / NT; ++i) {
+        const int key = (tid >> 4) + (NT / 16) * i;
         kb.k[i] = ld_row(K, (lo + kb0 + key) * Hkv + h, kb0 + key < N, tid & 15);
     }
 }
+template <int NT>
 __device__ __forceinline__ void load_v(VBlock &vb, const uint16_t *V, int64_t lo, int N, int kb0,
                                        int Hkv, int h, int tid) {
     const int m = tid & 31;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int d8 = (tid >> 5) + 8 * i;
+    for (int i = 0; i < 512 / NT; ++i) {
+        const int d8 = (tid >> 5) + (NT / 32) * i;
         vb.v[2 * i] = ld_row(V, (lo + kb0 + 2 * m) * Hkv + h, kb0 + 2 * m < N, d8);
         vb.v[2 * i + 1] = ld_row(V, (lo + kb0 + 2 * m + 1) * Hkv + h, kb0 + 2 * m + 1 < N, d8);
     }
 }
+template <int NT>
 __device__ __forceinline__ void store_k(const KBlock &kb, _Float16 *s_k, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4 *>(s_k + ((tid >> 4) + 16 * i) * KS + 8 * (tid & 15)) = kb.k[i];
+    for (int i = 0; i < 1024 / NT; ++i)
+        *reinterpret_cast<uint4 *>(s_k + ((tid >> 4) + (NT / 16) * i) * KS + 8 * (tid & 15)) =
+            kb.k[i];
 }
+template <int NT>
 __device__ __forceinline__ void store_v(const VBlock &vb, _Float16 *s_vt, int tid) {
     const int m = tid & 31;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int d8 = (tid >> 5) + 8 * i;
+    for (int i = 0; i < 512 / NT; ++i) {
+        const int d8 = (tid >> 5) + (NT / 32) * i;
         const uint32_t a[4] = {vb.v[2 * i].x, vb.v[2 * i].y, vb.v[2 * i].z, vb.v[2 * i].w};
         const uint32_t b[4] = {vb.v[2 * i + 1].x, vb.v[2 * i + 1].y, vb.v[2 * i + 1].z,
                                vb.v[2 * i + 1].w};
@@ -145,9 +155,11 @@ __device__ __forceinline__ void scores(f4 (&s)[4][2], const _Float16 *s_k,
         }
 }
 
-// grid (ceil(max_seqlen / BM), Hq, B), 256 threads.  Query blocks run last-first (the
-// longest key ranges start first).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(
+// grid (ceil(max_seqlen / (32 NW)), Hq, B), 64 NW threads: wave w takes queries q0 + 32 w ..
+// + 31 of the workgroup's block.  Query blocks run last-first (the longest key ranges start
+// first).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ cu, int Hq, int Hkv,
     int max_seqlen, float scale_log2, void *__restrict__ out, int out_fp32,
@@ -162,23 +174,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             atomicOr(status, KVC_DEV_SEQLEN);
         return;
     }
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * BM;
+    constexpr int NT = 64 * NW, BQ = 32 * NW;
+    const int q0 = (gridDim.x - 1 - blockIdx.x) * BQ;
     if (q0 >= N) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const int h = hq / (Hq / Hkv);
     const int qw = q0 + 32 * wave;                   // the wave's first query
-    const int nblk = (min(q0 + BM, N) - 1) / BN + 1; // key blocks 0 .. nblk-1
+    const int nblk = (min(q0 + BQ, N) - 1) / BN + 1; // key blocks 0 .. nblk-1
 
     h8 qop[2][4];
     load_q(qop, Q, lo, N, qw, Hq, hq, lane);
     KBlock kb;
     VBlock vb;
-    load_k(kb, K, lo, N, 0, Hkv, h, tid);
-    load_v(vb, V, lo, N, 0, Hkv, h, tid);
-    store_k(kb, s_k[0], tid);
-    store_v(vb, s_vt[0], tid);
+    load_k<NT>(kb, K, lo, N, 0, Hkv, h, tid);
+    load_v<NT>(vb, V, lo, N, 0, Hkv, h, tid);
+    store_k<NT>(kb, s_k[0], tid);
+    store_v<NT>(vb, s_vt[0], tid);
     __syncthreads();
 
     f4 o[8][2];
@@ -199,18 +212,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 const int qi = qw + 16 * qt + c;
+                // raw scores; keys after the query (diagonal blocks only) become -inf.  The max
+                // is taken before scaling (scale_log2 > 0 and rounding are monotone)
                 float x[16];
-                float mx = M_INIT;
+                float mx = -__builtin_inff();
+                if (diag) {
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = s[kt][qt][r] * scale_log2;
-                        if (diag && kb0 + 16 * kt + 4 * g + r > qi) v = -__builtin_inff();
-                        x[4 * kt + r] = v;
-                        mx = fmaxf(mx, v);
-                    }
-                mx = max_col(mx);
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = kb0 + 16 * kt + 4 * g + r > qi ? -__builtin_inff()
+                                                                         : s[kt][qt][r];
+                            x[4 * kt + r] = v;
+                            mx = fmaxf(mx, v);
+                        }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            x[4 * kt + r] = s[kt][qt][r];
+                            mx = fmaxf(mx, s[kt][qt][r]);
+                        }
+                }
+                mx = fmaxf(max_col(mx) * scale_log2, M_INIT);
                 if (__ballot(mx > m[qt] + MARGIN) != 0ull) {
                     const float mn = fmaxf(m[qt], mx);
                     const float corr = __builtin_amdgcn_exp2f(m[qt] - mn);
@@ -223,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 _Float16 p[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(x[e] - m[qt]);
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m[qt]));
                     ls += pe;
                     p[e] = _Float16(pe);
                 }
@@ -238,8 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             // the next block's rows are requested now (the score registers are free) and land
             // while the PV products run
             if (more) {
-                load_k(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
-                load_v(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+                load_k<NT>(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
+                load_v<NT>(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
                 issued = true;
             }
             // O^T += V^T P^T; V^T operand: dim row 16 dt + c, keys in the same order as P^T's k
@@ -259,11 +284,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
         if (more) {
             if (!issued) {
-                load_k(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
-                load_v(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+                load_k<NT>(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
+                load_v<NT>(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
             }
-            store_k(kb, s_k[cur ^ 1], tid);
-            store_v(vb, s_vt[cur ^ 1], tid);
+            store_k<NT>(kb, s_k[cur ^ 1], tid);
+            store_v<NT>(vb, s_vt[cur ^ 1], tid);
         }
         __syncthreads();
     }
@@ -295,78 +320,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 }
 
-// grid (ceil(max_seqlen / BN), Hq, B), 256 threads.  The 64 keys' operands stay in registers;
-// wave w takes query tiles of 32 from the block's start: kb0/32 + w, + 4, ...
+// grid (ceil(max_seqlen / CK), Hq, B), 256 threads.  Wave w owns keys kb0 + 64 w .. + 63,
+// their operands in registers; all four waves walk the same 32-query tiles from kb0 on, each
+// tile's rows and statistics staged once in LDS (double-buffered) for the four waves.
+constexpr int CK = 4 * BN;       // keys per column-sum workgroup
+constexpr int QT = 32;           // queries per staged tile
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const int32_t *__restrict__ cu,
     int Hq, int Hkv, int max_seqlen, float scale_log2, const float *__restrict__ ml,
     float *__restrict__ acc) {
-    __shared__ __attribute__((aligned(16))) _Float16 s_k[BN * KS];
-    __shared__ float s_cs[4][BN];
+    __shared__ __attribute__((aligned(16))) _Float16 s_q[2][QT * KS];
+    __shared__ float s_m[2][QT];
     const int b = blockIdx.z, hq = blockIdx.y;
     const int64_t lo = cu[b];
     const int N = cu[b + 1] - cu[b];
     if (N > max_seqlen) return;
-    const int kb0 = blockIdx.x * BN;
+    const int kb0 = blockIdx.x * CK;
     if (kb0 >= N) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const int h = hq / (Hq / Hkv);
-    {
-        KBlock kb;
-        load_k(kb, K, lo, N, kb0, Hkv, h, tid);
-        store_k(kb, s_k, tid);
-    }
-    __syncthreads();
-    h8 ka[4][4];                                     // [kt][ks]
+    const int kw = kb0 + BN * wave;                  // the wave's first key
+    // key operands [kt][ks]: row 16 kt + c of the wave's keys, dims 32 ks + 8 g
+    h8 ka[4][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+        const int ki = kw + 16 * kt + c;
+        const uint16_t *row = K + ((lo + ki) * Hkv + h) * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            ka[kt][ks] = *reinterpret_cast<const h8 *>(s_k + (16 * kt + c) * KS + 32 * ks + 8 * g);
+            ka[kt][ks] = __builtin_bit_cast(
+                h8, ki < N ? *reinterpret_cast<const uint4 *>(row + 32 * ks) : make_uint4(0, 0, 0, 0));
+    }
     float cs[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) cs[kt][r] = 0.f;
-    for (int q0 = kb0 + 32 * wave; q0 < N; q0 += 128) {
-        h8 qop[2][4];
-        load_q(qop, Q, lo, N, q0, Hq, hq, lane);
-        float mq[2], il[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int qi = q0 + 16 * qt + c;
-            const float2 x = qi < N ? *reinterpret_cast<const float2 *>(ml + 2 * ((lo + qi) * Hq + hq))
-                                    : make_float2(0.f, 0.f);
-            mq[qt] = x.x;
-            il[qt] = x.y > 0.f ? 1.0f / x.y : 0.f;
+    // staging: thread t loads query row t / 8 of the tile, 32 bytes at column 16 (t % 8); lanes
+    // 0..31 of wave 0 also load the rows' (max, sum), stored as m + log2(sum) (+inf past the end)
+    auto load_tile = [&](uint4 (&u)[2], float &mq, int q0) {
+        const int qi = q0 + (tid >> 3);
+        const uint16_t *row = Q + ((lo + qi) * Hq + hq) * D + 16 * (tid & 7);
+        u[0] = qi < N ? *reinterpret_cast<const uint4 *>(row) : make_uint4(0, 0, 0, 0);
+        u[1] = qi < N ? *reinterpret_cast<const uint4 *>(row + 8) : make_uint4(0, 0, 0, 0);
+        mq = __builtin_inff();
+        if (tid < QT && q0 + tid < N) {
+            const float2 x = *reinterpret_cast<const float2 *>(ml + 2 * ((lo + q0 + tid) * Hq + hq));
+            mq = x.y > 0.f ? x.x + __builtin_amdgcn_logf(x.y) : __builtin_inff();
         }
-        f4 s[4][2];
+    };
+    auto store_tile = [&](const uint4 (&u)[2], float mq, int buf) {
+        _Float16 *dst = s_q[buf] + (tid >> 3) * KS + 16 * (tid & 7);
+        reinterpret_cast<uint4 *>(dst)[0] = u[0];
+        reinterpret_cast<uint4 *>(dst)[1] = u[1];
+        if (tid < QT) s_m[buf][tid] = mq;
+    };
+    uint4 u[2];
+    float mq;
+    load_tile(u, mq, kb0);
+    store_tile(u, mq, 0);
+    __syncthreads();
+    const int ntile = (N - kb0 + QT - 1) / QT;
+    for (int it = 0; it < ntile; ++it) {
+        const int buf = it & 1;
+        const int q0 = kb0 + QT * it;
+        const bool more = it + 1 < ntile;
+        if (more) load_tile(u, mq, q0 + QT);
+        // queries q0 .. q0 + 31 against the wave's keys: nothing if every query precedes or
+        // is the first key; masks only where the ranges overlap
+        if (q0 + QT - 1 > kw) {
+            const _Float16 *sq = s_q[buf];
+            f4 sc[4][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) s[kt][0] = s[kt][1] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; ++kt) sc[kt][0] = sc[kt][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < 4; ++ks) {
+                const h8 b0 = *reinterpret_cast<const h8 *>(sq + c * KS + 32 * ks + 8 * g);
+                const h8 b1 = *reinterpret_cast<const h8 *>(sq + (16 + c) * KS + 32 * ks + 8 * g);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                s[kt][0] = mfma(ka[kt][ks], qop[0][ks], s[kt][0]);
-                s[kt][1] = mfma(ka[kt][ks], qop[1][ks], s[kt][1]);
-            }
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int qi = q0 + 16 * qt + c;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ki = kb0 + 16 * kt + 4 * g + r;
-                    const float p = __builtin_amdgcn_exp2f(s[kt][qt][r] * scale_log2 - mq[qt]) *
-                                    il[qt];
-                    cs[kt][r] += (qi > ki && qi < N) ? p : 0.f;
+                for (int kt = 0; kt < 4; ++kt) {
+                    sc[kt][0] = mfma(ka[kt][ks], b0, sc[kt][0]);
+                    sc[kt][1] = mfma(ka[kt][ks], b1, sc[kt][1]);
                 }
+            }
+            const bool diag = q0 <= kw + BN - 1;
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const int qi = q0 + 16 * qt + c;
+                const float m = s_m[buf][16 * qt + c];
+                if (diag) {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float p = __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(sc[kt][qt][r], scale_log2, -m));
+                            cs[kt][r] += qi > kw + 16 * kt + 4 * g + r ? p : 0.f;
+                        }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            cs[kt][r] += __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(sc[kt][qt][r], scale_log2, -m));
+                }
+            }
         }
+        if (more) store_tile(u, mq, buf ^ 1);
+        __syncthreads();
     }
-    // sum over the 16 query columns of each lane group, then over the four waves
+    // sum over the 16 query columns of each lane group; lane c == 0 of group g holds keys
+    // 16 kt + 4 g + r of the wave
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -374,11 +441,9 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
             float x = cs[kt][r];
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-            if (c == 0) s_cs[wave][16 * kt + 4 * g + r] = x;
+            const int ki = kw + 16 * kt + 4 * g + r;
+            if (c == 0 && ki < N) acc[(lo + ki) * Hq + hq] = x;
         }
-    __syncthreads();
-    if (tid < BN && kb0 + tid < N)
-        acc[(lo + kb0 + tid) * Hq + hq] = (s_cs[0][tid] + s_cs[1][tid]) + (s_cs[2][tid] + s_cs[3][tid]);
 }
 
 }  // namespace pf
@@ -406,13 +471,15 @@ extern "C" int kvc_prefill_attention(const kvc_geom *g, const uint16_t *q, const
     hipStream_t s = (hipStream_t)stream;
     const int Hq = g->num_q_heads, Hkv = g->num_kv_heads, B = g->batch;
     const float sl2 = softmax_scale * pf::LOG2E;
-    hipLaunchKernelGGL(pf::prefill_fwd_kernel, dim3((max_seqlen + pf::BM - 1) / pf::BM, Hq, B),
-                       dim3(256), 0, s, q, k, v, cu_seqlens, Hq, Hkv, max_seqlen, sl2, out,
-                       out_is_fp32, ml, dev_status);
+    constexpr int NW = KVC_PF_WAVES;
+    hipLaunchKernelGGL(pf::prefill_fwd_kernel<NW>,
+                       dim3((max_seqlen + 32 * NW - 1) / (32 * NW), Hq, B), dim3(64 * NW), 0, s,
+                       q, k, v, cu_seqlens, Hq, Hkv, max_seqlen, sl2, out, out_is_fp32, ml,
+                       dev_status);
     int rc = launch_check("kvc_prefill_attention/forward");
     if (rc || !acc_sum) return rc;
     hipLaunchKernelGGL(pf::prefill_colsum_kernel,
-                       dim3((max_seqlen + pf::BN - 1) / pf::BN, Hq, B), dim3(256), 0, s, q, k,
+                       dim3((max_seqlen + pf::CK - 1) / pf::CK, Hq, B), dim3(256), 0, s, q, k,
                        cu_seqlens, Hq, Hkv, max_seqlen, sl2, ml, acc_sum);
     return launch_check("kvc_prefill_attention/column sums");
 }
