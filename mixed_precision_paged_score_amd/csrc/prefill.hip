@@ -54,6 +54,22 @@ __device__ __forceinline__ float max_col(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by flat index, and each XCD has its own
+// L2.  Both kernels therefore decode their flat index L as (XCD x = L % 8, slot j = L / 8) and
+// give XCD x the groups x, x + 8, ... whole, W workgroups each: workgroups that stream the same
+// keys and values (forward) or the same queries (column sums) share one L2.  Returns the
+// group (or -1 past the last one) and the workgroup's index r within it.
+constexpr int XCDS = 8;
+__device__ __forceinline__ int xcd_group(int L, int W, int ngroups, int &r) {
+    const int x = L % XCDS, j = L / XCDS;
+    const int grp = x + XCDS * (j / W);
+    r = j % W;
+    return grp < ngroups ? grp : -1;
+}
+__host__ __device__ inline int xcd_grid(int ngroups, int W) {
+    return XCDS * ((ngroups + XCDS - 1) / XCDS) * W;
+}
+
 // ---- staging of one key block (64 keys of one request and KV head) ----------------------
 // K: thread t loads row (t / 16) + 16i, 16 bytes at column 8 (t % 16); stored row-major.
 // V: thread t loads rows 2m, 2m + 1 (m = t % 32) at column 8d (d = t / 32 + 8i) and stores
@@ -155,32 +171,37 @@ __device__ __forceinline__ void scores(f4 (&s)[4][2], const _Float16 *s_k,
         }
 }
 
-// grid (ceil(max_seqlen / (32 NW)), Hq, B), 64 NW threads: wave w takes queries q0 + 32 w ..
-// + 31 of the workgroup's block.  Query blocks run last-first (the longest key ranges start
-// first).
+// flat grid xcd_grid(B * Hkv, nqb * G), 64 NW threads; group = (request, KV head), its
+// workgroups (query block, query head of the group) in the order: query blocks last-first
+// (the longest key ranges start first), the G query heads of a block together.  Wave w takes
+// queries q0 + 32 w .. + 31 of the workgroup's block.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ cu, int Hq, int Hkv,
-    int max_seqlen, float scale_log2, void *__restrict__ out, int out_fp32,
+    int max_seqlen, int B, float scale_log2, void *__restrict__ out, int out_fp32,
     float *__restrict__ ml, int32_t *status) {
     __shared__ __attribute__((aligned(16))) _Float16 s_k[2][BN * KS];
     __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
-    const int b = blockIdx.z, hq = blockIdx.y;
+    constexpr int NT = 64 * NW, BQ = 32 * NW;
+    const int G = Hq / Hkv;
+    const int nqb = (max_seqlen + BQ - 1) / BQ;
+    int r;
+    const int grp = xcd_group(blockIdx.x, nqb * G, B * Hkv, r);
+    if (grp < 0) return;
+    const int b = grp / Hkv, h = grp - b * Hkv;
+    const int hq = h * G + r % G;
     const int64_t lo = cu[b];
     const int N = cu[b + 1] - cu[b];
     if (N > max_seqlen) {
-        if (status && blockIdx.x == 0 && hq == 0 && threadIdx.x == 0)
-            atomicOr(status, KVC_DEV_SEQLEN);
+        if (status && r == 0 && threadIdx.x == 0) atomicOr(status, KVC_DEV_SEQLEN);
         return;
     }
-    constexpr int NT = 64 * NW, BQ = 32 * NW;
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * BQ;
+    const int q0 = (nqb - 1 - r / G) * BQ;
     if (q0 >= N) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int h = hq / (Hq / Hkv);
     const int qw = q0 + 32 * wave;                   // the wave's first query
     const int nblk = (min(q0 + BQ, N) - 1) / BN + 1; // key blocks 0 .. nblk-1
 
@@ -320,22 +341,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
-// grid (ceil(max_seqlen / CK), Hq, B), 256 threads.  Wave w owns keys kb0 + 64 w .. + 63,
-// their operands in registers; all four waves walk the same 32-query tiles from kb0 on, each
-// tile's rows and statistics staged once in LDS (double-buffered) for the four waves.
+// flat grid xcd_grid(B * Hq, nkb), 256 threads; group = (request, query head), its workgroups
+// the key blocks.  Wave w owns keys kb0 + 64 w .. + 63, their operands in registers; all four
+// waves walk the same 32-query tiles, each tile's rows and statistics staged once in LDS
+// (double-buffered) for the four waves.  The walk runs from the request's last tile back to
+// kb0, so the group's workgroups on one XCD read the same query tiles at about the same time.
 constexpr int CK = 4 * BN;       // keys per column-sum workgroup
 constexpr int QT = 32;           // queries per staged tile
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const int32_t *__restrict__ cu,
-    int Hq, int Hkv, int max_seqlen, float scale_log2, const float *__restrict__ ml,
+    int Hq, int Hkv, int max_seqlen, int B, float scale_log2, const float *__restrict__ ml,
     float *__restrict__ acc) {
     __shared__ __attribute__((aligned(16))) _Float16 s_q[2][QT * KS];
     __shared__ float s_m[2][QT];
-    const int b = blockIdx.z, hq = blockIdx.y;
+    const int nkb = (max_seqlen + CK - 1) / CK;
+    int r;
+    const int grp = xcd_group(blockIdx.x, nkb, B * Hq, r);
+    if (grp < 0) return;
+    const int b = grp / Hq, hq = grp - b * Hq;
     const int64_t lo = cu[b];
     const int N = cu[b + 1] - cu[b];
     if (N > max_seqlen) return;
-    const int kb0 = blockIdx.x * CK;
+    const int kb0 = r * CK;
     if (kb0 >= N) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -379,15 +406,15 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     };
     uint4 u[2];
     float mq;
-    load_tile(u, mq, kb0);
+    const int ntile = (N - kb0 + QT - 1) / QT;
+    load_tile(u, mq, kb0 + QT * (ntile - 1));
     store_tile(u, mq, 0);
     __syncthreads();
-    const int ntile = (N - kb0 + QT - 1) / QT;
     for (int it = 0; it < ntile; ++it) {
         const int buf = it & 1;
-        const int q0 = kb0 + QT * it;
+        const int q0 = kb0 + QT * (ntile - 1 - it);  // last tile first
         const bool more = it + 1 < ntile;
-        if (more) load_tile(u, mq, q0 + QT);
+        if (more) load_tile(u, mq, q0 - QT);
         // queries q0 .. q0 + 31 against the wave's keys: nothing if every query precedes or
         // is the first key; masks only where the ranges overlap
         if (q0 + QT - 1 > kw) {
@@ -472,14 +499,14 @@ extern "C" int kvc_prefill_attention(const kvc_geom *g, const uint16_t *q, const
     const int Hq = g->num_q_heads, Hkv = g->num_kv_heads, B = g->batch;
     const float sl2 = softmax_scale * pf::LOG2E;
     constexpr int NW = KVC_PF_WAVES;
-    hipLaunchKernelGGL(pf::prefill_fwd_kernel<NW>,
-                       dim3((max_seqlen + 32 * NW - 1) / (32 * NW), Hq, B), dim3(64 * NW), 0, s,
-                       q, k, v, cu_seqlens, Hq, Hkv, max_seqlen, sl2, out, out_is_fp32, ml,
-                       dev_status);
+    const int nqb = (max_seqlen + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL(pf::prefill_fwd_kernel<NW>, dim3(pf::xcd_grid(B * Hkv, nqb * (Hq / Hkv))),
+                       dim3(64 * NW), 0, s, q, k, v, cu_seqlens, Hq, Hkv, max_seqlen, B, sl2, out,
+                       out_is_fp32, ml, dev_status);
     int rc = launch_check("kvc_prefill_attention/forward");
     if (rc || !acc_sum) return rc;
-    hipLaunchKernelGGL(pf::prefill_colsum_kernel,
-                       dim3((max_seqlen + pf::CK - 1) / pf::CK, Hq, B), dim3(256), 0, s, q, k,
-                       cu_seqlens, Hq, Hkv, max_seqlen, sl2, ml, acc_sum);
+    const int nkb = (max_seqlen + pf::CK - 1) / pf::CK;
+    hipLaunchKernelGGL(pf::prefill_colsum_kernel, dim3(pf::xcd_grid(B * Hq, nkb)), dim3(256), 0,
+                       s, q, k, cu_seqlens, Hq, Hkv, max_seqlen, B, sl2, ml, acc_sum);
     return launch_check("kvc_prefill_attention/column sums");
 }
