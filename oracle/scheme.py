@@ -1,0 +1,139 @@
+"""Oracle: precision-scheme variants of the two tiers and their page images (test
+infrastructure only; nothing in the library imports it).
+
+Source: DiffKV review page.  The free-parameter ledger says the K8V4-K4V2 scheme was chosen by
+comparing K8V4, K4V8, K8V2, K4V2, K2V4 and K4V1; the reading notes report that mirror
+configurations giving values more bits than keys collapse in accuracy; the referee report
+(minor comment 5) lists the configurations K8V4-K4V2, K8V4-K4V2-Pr and K8V4-Prune.
+
+Readings taken: a scheme gives each tier its own key and value bit widths (1, 2, 4 or 8),
+quantized with the same per-token min/max quantizer as K8V4/K4V2 (``quant.py``) at 2^b - 1
+levels.  Pages keep their geometry (3456 bytes; 16 HIGH or 32 LOW slots, so allocation is
+unchanged); a tier's format must fit its slots into the first 3072 bytes:
+slots * 16 * (kb + vb) <= 3072.  The page layout of these variants is the plain slot-major one:
+slot s occupies bytes [s * 16 (kb + vb), (s + 1) * 16 (kb + vb)), first its 128 key codes,
+then its 128 value codes, code i at bits [i b, (i + 1) b) counted little-endian from the
+field's first byte; the bytes after the last slot up to 3072 are zero; parameters (k scale,
+k zero, v scale, v zero as fp16) at 3072 + 8 s and positions (int32, -1 when empty) at
+3328 + 4 s for all 32 slot indices, as in the K8V4/K4V2 layout.
+"""
+import numpy as np
+
+from . import quant
+
+D = 128
+PAGE_BYTES = 3456
+CODE_BYTES = 3072
+PARAM_OFF, POS_OFF = 3072, 3328
+HIGH, LOW = 2, 1
+SLOTS = {HIGH: 16, LOW: 32}
+BITS = (1, 2, 4, 8)
+
+# the single-tier formats the pages compare, as (key bits, value bits)
+FORMATS = {"K8V4": (8, 4), "K4V8": (4, 8), "K8V2": (8, 2), "K4V2": (4, 2), "K2V4": (2, 4),
+           "K4V1": (4, 1)}
+
+
+def fits(tier, kb, vb):
+    """Whether a (key bits, value bits) format fits a tier's slots in one page."""
+    return kb in BITS and vb in BITS and SLOTS[tier] * 16 * (kb + vb) <= CODE_BYTES
+
+
+class Scheme:
+    """Bit widths of the two tiers: HIGH (kh, vh), LOW (kl, vl)."""
+
+    def __init__(self, kh, vh, kl, vl):
+        if not (fits(HIGH, kh, vh) and fits(LOW, kl, vl)):
+            raise ValueError("format does not fit the tier's page")
+        self.bits = {HIGH: (kh, vh), LOW: (kl, vl)}
+
+    @classmethod
+    def named(cls, high, low):
+        return cls(*FORMATS[high], *FORMATS[low])
+
+    def slot_bytes(self, tier):
+        kb, vb = self.bits[tier]
+        return 16 * (kb + vb)
+
+
+def pack_codes(codes, b):
+    """codes uint8 [..., 128] of b bits -> bytes [..., 16 b], code i at bits i b .. i b + b - 1."""
+    codes = np.asarray(codes, np.int64)
+    n = codes.shape[-1]
+    bits = ((codes[..., :, None] >> np.arange(b)) & 1).reshape(codes.shape[:-1] + (n * b,))
+    weights = 1 << np.arange(8)
+    return (bits.reshape(codes.shape[:-1] + (n * b // 8, 8)) * weights).sum(-1).astype(np.uint8)
+
+
+def unpack_codes(data, b, n=D):
+    """Inverse of pack_codes."""
+    data = np.asarray(data, np.int64)
+    bits = ((data[..., :, None] >> np.arange(8)) & 1).reshape(data.shape[:-1] + (data.shape[-1] * 8,))
+    bits = bits[..., :n * b].reshape(data.shape[:-1] + (n, b))
+    return (bits * (1 << np.arange(b))).sum(-1).astype(np.uint8)
+
+
+def build_page(scheme, tier, k_codes, v_codes, k_scale, k_zero, v_scale, v_zero, pos):
+    """Page image (uint8 [3456]) of m live tokens in slots 0..m-1 of a scheme's tier."""
+    kb, vb = scheme.bits[tier]
+    m = len(pos)
+    assert m <= SLOTS[tier]
+    page = np.zeros(PAGE_BYTES, np.uint8)
+    sb = scheme.slot_bytes(tier)
+    for s in range(m):
+        page[s * sb:s * sb + 16 * kb] = pack_codes(k_codes[s], kb)
+        page[s * sb + 16 * kb:(s + 1) * sb] = pack_codes(v_codes[s], vb)
+    params = np.zeros((32, 4), np.float16)
+    params[:m, 0] = k_scale
+    params[:m, 1] = k_zero
+    params[:m, 2] = v_scale
+    params[:m, 3] = v_zero
+    page[PARAM_OFF:POS_OFF] = params.view(np.uint8).ravel()
+    posv = np.full(32, -1, np.int32)
+    posv[:m] = pos
+    page[POS_OFF:PAGE_BYTES] = posv.view(np.uint8)
+    return page
+
+
+def read_page(page, scheme, tier, m):
+    """Codes, parameters and positions of the first m slots of a page image."""
+    kb, vb = scheme.bits[tier]
+    sb = scheme.slot_bytes(tier)
+    page = np.asarray(page, np.uint8)
+    k = np.stack([unpack_codes(page[s * sb:s * sb + 16 * kb], kb) for s in range(m)]) if m else \
+        np.zeros((0, D), np.uint8)
+    v = np.stack([unpack_codes(page[s * sb + 16 * kb:(s + 1) * sb], vb) for s in range(m)]) if m \
+        else np.zeros((0, D), np.uint8)
+    params = page[PARAM_OFF:POS_OFF].copy().view(np.float16).reshape(32, 4)[:m]
+    pos = page[POS_OFF:PAGE_BYTES].copy().view(np.int32)[:m]
+    return k, v, params[:, 0], params[:, 1], params[:, 2], params[:, 3], pos
+
+
+def head_pages(k_rows, v_rows, tier_col, scheme):
+    """Prompt placement of one head under a scheme: {HIGH: [images], LOW: [images]}, tokens in
+    ascending position order within each tier (as for K8V4/K4V2)."""
+    out = {}
+    for tier in (HIGH, LOW):
+        kb, vb = scheme.bits[tier]
+        pos = np.nonzero(np.asarray(tier_col) == tier)[0]
+        kc, ks, kz = quant.quantize_rows(k_rows[pos], kb)
+        vc, vs, vz = quant.quantize_rows(v_rows[pos], vb)
+        per = SLOTS[tier]
+        out[tier] = [build_page(scheme, tier, kc[p0:p0 + per], vc[p0:p0 + per], ks[p0:p0 + per],
+                                kz[p0:p0 + per], vs[p0:p0 + per], vz[p0:p0 + per],
+                                pos[p0:p0 + per]) for p0 in range(0, len(pos), per)]
+    return out
+
+
+def head_dequantized(k_rows, v_rows, tier_col, scheme):
+    """float32 keys and values of one head's live tokens under a scheme, HIGH tokens first then
+    LOW tokens, each in ascending position order."""
+    ks, vs = [], []
+    for tier in (HIGH, LOW):
+        kb, vb = scheme.bits[tier]
+        pos = np.nonzero(np.asarray(tier_col) == tier)[0]
+        kc, s, z = quant.quantize_rows(k_rows[pos], kb)
+        ks.append(quant.dequantize_rows(kc, s, z))
+        vc, s, z = quant.quantize_rows(v_rows[pos], vb)
+        vs.append(quant.dequantize_rows(vc, s, z))
+    return np.concatenate(ks), np.concatenate(vs)

@@ -1,0 +1,87 @@
+"""Pins of the precision-scheme oracle: hand-derived packed bytes, round trips, exact bit
+coverage of a page's code region, the capacity rule, the quantizer at 1 and 2 bits, and the
+K8V4-K4V2 scheme's reconstructions equal to the ones of the default layout's oracle."""
+import numpy as np
+import pytest
+
+from oracle import place, quant, scheme as osch
+
+
+def test_hand_packed_bytes():
+    c = np.zeros(128, np.uint8)
+    c[:4] = [1, 2, 3, 0]
+    # 2 bits: byte 0 = 1 | 2 << 2 | 3 << 4 | 0 << 6
+    assert osch.pack_codes(c, 2)[0] == 0b00111001
+    # 4 bits: low nibble first
+    assert osch.pack_codes(c, 4)[0] == 0x21 and osch.pack_codes(c, 4)[1] == 0x03
+    # 1 bit: code i at bit i
+    b = np.zeros(128, np.uint8)
+    b[[0, 3, 8, 127]] = 1
+    p = osch.pack_codes(b, 1)
+    assert p[0] == 0b1001 and p[1] == 1 and p[15] == 0x80 and p.sum() == 0b1001 + 1 + 0x80
+    # 8 bits: bytes as they are
+    e = np.arange(128, dtype=np.uint8)
+    assert np.array_equal(osch.pack_codes(e, 8), e)
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+def test_round_trip(b):
+    rng = np.random.default_rng(b)
+    c = rng.integers(0, 2 ** b, size=(5, 128)).astype(np.uint8)
+    assert np.array_equal(osch.unpack_codes(osch.pack_codes(c, b), b), c)
+
+
+@pytest.mark.parametrize("high,low", [("K8V4", "K4V2"), ("K4V8", "K2V4"), ("K8V2", "K4V1"),
+                                      ("K4V2", "K4V2"), ("K2V4", "K4V1")])
+def test_page_bit_coverage(high, low):
+    # all-ones codes light exactly slots * 16 (kb + vb) bytes; nothing else in the code region
+    sc = osch.Scheme.named(high, low)
+    for tier in (osch.HIGH, osch.LOW):
+        kb, vb = sc.bits[tier]
+        S = osch.SLOTS[tier]
+        ones_k = np.full((S, 128), 2 ** kb - 1, np.uint8)
+        ones_v = np.full((S, 128), 2 ** vb - 1, np.uint8)
+        z = np.zeros(S, np.float16)
+        page = osch.build_page(sc, tier, ones_k, ones_v, z, z, z, z, np.arange(S))
+        n = S * 16 * (kb + vb)
+        assert np.all(page[:n] == 0xFF) and np.all(page[n:osch.CODE_BYTES] == 0)
+        k, v, *_, pos = osch.read_page(page, sc, tier, S)
+        assert np.array_equal(k, ones_k) and np.array_equal(v, ones_v)
+        assert np.array_equal(pos, np.arange(S))
+
+
+def test_capacity_rule():
+    assert osch.fits(osch.HIGH, 8, 4) and osch.fits(osch.HIGH, 4, 8)
+    assert not osch.fits(osch.HIGH, 8, 8)          # 16 * 16 * 16 = 4096 > 3072
+    assert osch.fits(osch.LOW, 4, 2) and osch.fits(osch.LOW, 2, 4) and osch.fits(osch.LOW, 4, 1)
+    assert not osch.fits(osch.LOW, 4, 4) and not osch.fits(osch.LOW, 8, 2)
+    assert not osch.fits(osch.HIGH, 3, 4)
+    with pytest.raises(ValueError):
+        osch.Scheme(8, 8, 4, 2)
+
+
+@pytest.mark.parametrize("b", [1, 2])
+def test_low_bit_quantizer(b):
+    # codes stay in 0 .. 2^b - 1, the row's min and max map to 0 and 2^b - 1, and the
+    # reconstruction is within half a step (plus rounding) of the input
+    rng = np.random.default_rng(10 + b)
+    x = rng.standard_normal((6, 128)).astype(np.float16)
+    c, s, z = quant.quantize_rows(x, b)
+    assert c.max() <= 2 ** b - 1
+    for r in range(6):
+        assert c[r, np.argmin(x[r])] == 0 and c[r, np.argmax(x[r])] == 2 ** b - 1
+    xh = quant.dequantize_rows(c, s, z)
+    step = s.astype(np.float64)[:, None]
+    assert np.all(np.abs(xh - x.astype(np.float64)) <= step * (0.5 + 2 ** -12) + 1e-3)
+
+
+def test_default_scheme_matches_default_layout_reconstruction():
+    # under K8V4-K4V2 the reconstructions are the default path's (only the byte layout differs)
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((90, 128)).astype(np.float16)
+    v = rng.standard_normal((90, 128)).astype(np.float16)
+    tier = rng.choice([0, 1, 2], size=90).astype(np.uint8)
+    sc = osch.Scheme.named("K8V4", "K4V2")
+    a = osch.head_dequantized(k, v, tier, sc)
+    b = place.head_dequantized(k, v, tier)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
