@@ -104,6 +104,13 @@ typedef struct {
     int32_t *dev_status; /* [1]: sticky KVC_DEV_* bits                                     */
 } kvc_pool;
 
+/* Precision scheme of the two tiers (key and value bits: 1, 2, 4 or 8).  A tier's format must
+ * fit its page: 16 slots * 16 (k + v) bytes <= 3072 for HIGH, 32 slots * 16 (k + v) <= 3072
+ * for LOW; e.g. K8V4, K4V8, K8V2 for HIGH and K4V2, K2V4, K4V1 for LOW. */
+typedef struct {
+    int32_t k_bits_high, v_bits_high, k_bits_low, v_bits_low;
+} kvc_scheme;
+
 /* Operation ids for kvc_workspace_bytes */
 enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4,
        KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6, KVC_OP_PREFILL = 7 };
@@ -215,6 +222,36 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
                            const uint8_t *prev_tier, const uint8_t *changed,
                            const int32_t *old_rows, const int32_t *old_count,
                            void *workspace, size_t workspace_bytes, kvc_stream_t stream);
+
+/* Prompt placement under a precision scheme (DiffKV review page: the free-parameter ledger's
+ * comparison of K8V4, K4V8, K8V2, K4V2, K2V4 and K4V1; referee minor comment 5 for the
+ * K8V4-K4V2 / K8V4-Prune configurations).  Same contract as kvc_quantize_and_place in prompt
+ * mode (same ranks, pages and slots; the K8V4-Prune and no-prune configurations are threshold
+ * settings of kvc_score_tokens), but each tier is quantized at the scheme's bit widths with the
+ * same per-token min/max quantizer (2^b - 1 levels) and written in the slot-major page layout:
+ * slot s at bytes [s * 16 (k + v), (s + 1) * 16 (k + v)), first its 128 key codes, then its 128
+ * value codes, code i at bits [i b, (i + 1) b) little-endian from the field's first byte; the
+ * bytes after the last slot up to 3072 are zero; parameters and positions as in the default
+ * layout.  Pages written this way are read by kvc_paged_decode_attention_scheme only.
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_QUANTIZE, max_seqlen)
+ * Errors: as kvc_quantize_and_place, and KVC_E_SHAPE for a scheme that does not fit. */
+int kvc_quantize_and_place_scheme(const kvc_geom *geom, const kvc_scheme *scheme, int32_t layer,
+                                  const kvc_pool *pool, const uint16_t *k, const uint16_t *v,
+                                  const int32_t *cu_seqlens, int64_t total_tokens,
+                                  int32_t max_seqlen, const uint8_t *tier, void *workspace,
+                                  size_t workspace_bytes, kvc_stream_t stream);
+
+/* Decode attention over pages written by kvc_quantize_and_place_scheme with the same scheme:
+ * the contract of kvc_paged_decode_attention (codes reconstructed as code * scale + zero, all
+ * live tokens, a head with none yields zeros), G <= 16.
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_DECODE, 0)
+ * Errors: as kvc_paged_decode_attention, and KVC_E_SHAPE for a scheme that does not fit or
+ * G > 16. */
+int kvc_paged_decode_attention_scheme(const kvc_geom *geom, const kvc_scheme *scheme,
+                                      int32_t layer, const kvc_pool *pool, const uint16_t *q,
+                                      float softmax_scale, void *out, int32_t out_is_fp32,
+                                      void *workspace, size_t workspace_bytes,
+                                      kvc_stream_t stream);
 
 /* Append one freshly generated token per (request, KV head) to layer `layer` during
  * decoding: the token enters its head's HIGH tier (DiffKV review page, free-parameter ledger:

@@ -852,6 +852,15 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
     }
 }
 
+// the combine launch of a split-K decode (shared with the precision-scheme decode)
+int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,
+                          int out_fp32, float *mls, hipStream_t s) {
+    const int nqh = B * Hq;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((nqh + 3) / 4), dim3(256), 0, s, part, Hq, G,
+                       S, nqh, out, out_fp32, mls);
+    return launch_check("decode/combine");
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -899,10 +908,7 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
                            part, nullptr, int64_t(0));
     rc = launch_check("kvc_paged_decode_attention/main");
     if (rc) return rc;
-    const int nqh = B * g->num_q_heads;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((nqh + 3) / 4), dim3(256), 0, s, part,
-                       g->num_q_heads, G, L.splits, nqh, out, out_is_fp32, mls);
-    rc = launch_check("kvc_paged_decode_attention/combine");
+    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls, s);
     if (rc || !accum) return rc;
     if (max_seqlen == 0) return KVC_OK;
     int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);

@@ -28,6 +28,10 @@ int launch_compact(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                    const int32_t *new_count, const uint8_t *changed, int32_t *old_rows_out,
                    int32_t *old_count_out, void *ws, hipStream_t s);
 
+// the combine launch of a split-K decode (attention.hip); partials [B*Hkv][S][G][132]
+int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,
+                          int out_fp32, float *mls, hipStream_t s);
+
 inline int launch_check(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -48,6 +52,17 @@ inline int check_geom(const kvc_geom *g) {
     if (g->num_pages >= (int64_t(1) << 31)) return KVC_E_SHAPE;
     int64_t rows = int64_t(g->num_layers) * g->batch * g->num_kv_heads * g->row_capacity;
     if (rows >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+    return KVC_OK;
+}
+
+inline bool scheme_bits_ok(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+inline int check_scheme(const kvc_scheme *sc) {
+    if (!sc) return KVC_E_NULL;
+    if (!scheme_bits_ok(sc->k_bits_high) || !scheme_bits_ok(sc->v_bits_high) ||
+        !scheme_bits_ok(sc->k_bits_low) || !scheme_bits_ok(sc->v_bits_low))
+        return KVC_E_SHAPE;
+    if (HS * 16 * (sc->k_bits_high + sc->v_bits_high) > PARAM_OFF) return KVC_E_SHAPE;
+    if (LS * 16 * (sc->k_bits_low + sc->v_bits_low) > PARAM_OFF) return KVC_E_SHAPE;
     return KVC_OK;
 }
 

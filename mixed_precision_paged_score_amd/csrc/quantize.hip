@@ -361,6 +361,94 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     }
 }
 
+// ---- precision schemes: slot-major pages --------------------------------------------------
+// the lane's 8 codes (b bits each, channels 8c .. 8c + 7) as b bytes at dst (b = 1, 2, 4, 8:
+// naturally aligned stores)
+__device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t w, int b) {
+    if (b == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(uint32_t(w), uint32_t(w >> 32));
+    else if (b == 4) *reinterpret_cast<uint32_t *>(dst) = uint32_t(w);
+    else if (b == 2) *reinterpret_cast<uint16_t *>(dst) = uint16_t(w);
+    else *dst = uint8_t(w);
+}
+
+// grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole:
+// 16 lanes per row (channels 8c .. 8c + 7), four slots per pass; the code bytes past the last
+// slot are zero, parameters and positions of all 32 slot indices as in the default layout.
+__global__ __launch_bounds__(256) void scheme_pages_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
+    const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ ok, const int32_t *__restrict__ poslist, int kh, int vh, int kl,
+    int vl, uint8_t *__restrict__ pages) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.y;
+    const int nheads = gridDim.y;
+    if (ok[nheads] != 0 || !ok[i]) return;
+    const int b = i / Hkv, h = i - b * Hkv;
+    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int qH = ceil_div(nh, HS), qL = ceil_div(nl, LS);
+    const int pi = blockIdx.x * QP_WAVES + wave;
+    bool high;
+    int first, m, page;
+    if (pi < qH) {
+        high = true;
+        first = pi * HS;
+        m = min(HS, nh - first);
+        page = rows_l[int64_t(i) * C + pi];
+    } else if (pi - qH < qL) {
+        high = false;
+        first = (pi - qH) * LS;
+        m = min(LS, nl - first);
+        page = rows_l[int64_t(i) * C + C - 1 - (pi - qH)];
+    } else {
+        return;
+    }
+    const int kb = high ? kh : kl, vb = high ? vh : vl;
+    const int S = high ? HS : LS;
+    const int sb = 16 * (kb + vb);
+    uint8_t *pg = pages + int64_t(page) * PAGE;
+    const int32_t *pl = poslist + int64_t(i) * max_seqlen;
+    const int lo = cu[b];
+    const int rg = lane >> 4, c = lane & 15;
+    const float lk = float((1 << kb) - 1), lv = float((1 << vb) - 1);
+    for (int pass = 0; pass < S / 4; ++pass) {
+        const int sl = 4 * pass + rg;
+        const bool live = sl < m;
+        int pos = 0;
+        if (live) pos = high ? pl[first + sl] : pl[max_seqlen - 1 - (first + sl)];
+        const int64_t roff = ((int64_t(lo) + pos) * Hkv + h) * D + 8 * c;
+        float xk[8], xv[8];
+        load_row8(K + roff, live, xk);
+        load_row8(V + roff, live, xv);
+        const RowQ qk = row_params(xk, lk);
+        const RowQ qv = row_params(xv, lv);
+        uint64_t wk = 0, wv = 0;
+        if (live) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wk |= uint64_t(code_of(xk[e], qk)) << (kb * e);
+                wv |= uint64_t(code_of(xv[e], qv)) << (vb * e);
+            }
+        }
+        uint8_t *slot = pg + sl * sb;
+        store_codes(slot + c * kb, wk, kb);
+        store_codes(slot + 16 * kb + c * vb, wv, vb);
+        if (c == 0) {
+            const uint32_t a = live ? uint32_t(qk.s16) | (uint32_t(qk.z16) << 16) : 0u;
+            const uint32_t bb = live ? uint32_t(qv.s16) | (uint32_t(qv.z16) << 16) : 0u;
+            *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * sl) = make_uint2(a, bb);
+            reinterpret_cast<int32_t *>(pg + POS_OFF)[sl] = live ? pos : -1;
+        }
+    }
+    // code bytes past the last slot (S * sb is a multiple of 16), and slots S..31's fields
+    for (int k = S * sb / 16 + lane; k < PARAM_OFF / 16; k += 64)
+        reinterpret_cast<uint4 *>(pg)[k] = make_uint4(0, 0, 0, 0);
+    if (lane >= S && lane < LS) {
+        *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * lane) = make_uint2(0u, 0u);
+        reinterpret_cast<int32_t *>(pg + POS_OFF)[lane] = -1;
+    }
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -425,4 +513,55 @@ extern "C" int kvc_quantize_and_place(const kvc_geom *g, int32_t layer, const kv
                            Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, nullptr, nullptr,
                            nullptr, p->pages, p->dev_status);
     return launch_check("kvc_quantize_and_place/pages");
+}
+
+extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme *sc,
+                                             int32_t layer, const kvc_pool *p, const uint16_t *k,
+                                             const uint16_t *v, const int32_t *cu,
+                                             int64_t total_tokens, int32_t max_seqlen,
+                                             const uint8_t *tier, void *ws, size_t ws_bytes,
+                                             kvc_stream_t stream) {
+    int rc = check_geom(g);
+    if (rc) return rc;
+    rc = check_pool(p);
+    if (rc) return rc;
+    rc = check_scheme(sc);
+    if (rc) return rc;
+    if (!cu) return KVC_E_NULL;
+    if (total_tokens > 0 && (!tier || !k || !v)) return KVC_E_NULL;
+    if (layer < 0 || layer >= g->num_layers || max_seqlen < 0 || total_tokens < 0)
+        return KVC_E_SHAPE;
+    if (g->num_kv_heads > 256) return KVC_E_SHAPE;
+    if ((k && !aligned16(k)) || (v && !aligned16(v))) return KVC_E_ALIGN;
+    QuantWs L(g, max_seqlen);
+    if (!ws || ws_bytes < L.bytes) return KVC_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
+    char *w = static_cast<char *>(ws);
+    int32_t *tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
+    int32_t *tile_base = reinterpret_cast<int32_t *>(w + L.tile_base);
+    int32_t *ok = reinterpret_cast<int32_t *>(w + L.ok);
+    int32_t *poslist = reinterpret_cast<int32_t *>(w + L.poslist);
+    const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
+    const int nheads = B * Hkv;
+    const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
+    const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(quant_count_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, nullptr, cu,
+                       Hkv, L.ntq, max_seqlen, p->dev_status, tile_cnt, nullptr, ok, nheads);
+    rc = launch_check("kvc_quantize_and_place_scheme/count");
+    if (rc) return rc;
+    hipLaunchKernelGGL(quant_scan_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, nullptr, cu,
+                       Hkv, L.ntq, max_seqlen, count_l, nullptr, nullptr, tile_base, nullptr, ok,
+                       p->dev_status);
+    rc = launch_check("kvc_quantize_and_place_scheme/scan");
+    if (rc) return rc;
+    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, nullptr, cu,
+                       Hkv, L.ntq, max_seqlen, tile_base, nullptr, ok, poslist, nullptr);
+    rc = launch_check("kvc_quantize_and_place_scheme/select");
+    if (rc) return rc;
+    hipLaunchKernelGGL(scheme_pages_kernel, dim3((C + QP_WAVES - 1) / QP_WAVES, nheads),
+                       dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv, C, max_seqlen, rows_l, count_l,
+                       ok, poslist, sc->k_bits_high, sc->v_bits_high, sc->k_bits_low,
+                       sc->v_bits_low, p->pages);
+    return launch_check("kvc_quantize_and_place_scheme/pages");
 }

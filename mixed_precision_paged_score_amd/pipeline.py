@@ -56,6 +56,18 @@ class PromptPath:
         self.compact(layer)
         self.place(layer, k, v)
 
+    def prompt_scheme(self, layer, acc, k, v, scheme):
+        """A prompt round whose pages use a precision scheme (kvc.make_scheme): score,
+        compact, then the scheme's page writer."""
+        self.score(acc)
+        self.compact(layer)
+        kvc.quantize_and_place_scheme(self.geom, scheme, layer, self.pool, k, v, self.cu, self.T,
+                                      self.max_seqlen, self.tier, self.ws_quant)
+
+    def decode_scheme(self, layer, q, out, scheme):
+        kvc.paged_decode_attention_scheme(self.geom, scheme, layer, self.pool, q, self.scale, out,
+                                          self.ws_decode)
+
     def decode(self, layer, q, out):
         kvc.paged_decode_attention(self.geom, layer, self.pool, q, self.scale, out,
                                    self.ws_decode)

@@ -102,6 +102,23 @@ def test_synchronous_errors_enqueue_nothing():
                                      256, 1 << 20, None) == kvc.E_SHAPE
     assert lib.kvc_prefill_attention(ctypes.byref(g), 16, 16, 16, 16, 8, f1, 16, 1, 16, None,
                                      256, 8, None) == kvc.E_WORKSPACE
+    # schemes: no scheme, bit widths that do not fit, small workspace
+    sc_bad = kvc.Scheme(8, 8, 4, 2)
+    sc_ok = kvc.make_scheme("K8V2", "K4V1")
+    assert lib.kvc_paged_decode_attention_scheme(ctypes.byref(g), None, 0, ctypes.byref(p), 16,
+                                                 1.0, 16, 1, 256, 1 << 20, None) == kvc.E_NULL
+    assert lib.kvc_paged_decode_attention_scheme(ctypes.byref(g), ctypes.byref(sc_bad), 0,
+                                                 ctypes.byref(p), 16, 1.0, 16, 1, 256, 1 << 20,
+                                                 None) == kvc.E_SHAPE
+    assert lib.kvc_paged_decode_attention_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0,
+                                                 ctypes.byref(p), 16, 1.0, 16, 1, 256, 8,
+                                                 None) == kvc.E_WORKSPACE
+    assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(kvc.Scheme(8, 4, 4, 4)),
+                                             0, ctypes.byref(p), 16, 16, 16, 10, 5, 16, 256,
+                                             1 << 20, None) == kvc.E_SHAPE
+    assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0,
+                                             ctypes.byref(p), 16, 18, 16, 10, 5, 16, 256,
+                                             1 << 20, None) == kvc.E_ALIGN
     # score: negative window
     assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
                                 ctypes.c_float(0.1), -1, None, 16, 16, None, None,
