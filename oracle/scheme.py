@@ -10,12 +10,14 @@ Readings taken: a scheme gives each tier its own key and value bit widths (1, 2,
 quantized with the same per-token min/max quantizer as K8V4/K4V2 (``quant.py``) at 2^b - 1
 levels.  Pages keep their geometry (3456 bytes; 16 HIGH or 32 LOW slots, so allocation is
 unchanged); a tier's format must fit its slots into the first 3072 bytes:
-slots * 16 * (kb + vb) <= 3072.  The page layout of these variants is the plain slot-major one:
-slot s occupies bytes [s * 16 (kb + vb), (s + 1) * 16 (kb + vb)), first its 128 key codes,
-then its 128 value codes, code i at bits [i b, (i + 1) b) counted little-endian from the
-field's first byte; the bytes after the last slot up to 3072 are zero; parameters (k scale,
-k zero, v scale, v zero as fp16) at 3072 + 8 s and positions (int32, -1 when empty) at
-3328 + 4 s for all 32 slot indices, as in the K8V4/K4V2 layout.
+slots * 16 * (kb + vb) <= 3072.  The page layout of these variants (this project's own):
+keys slot-major, slot s's 128 codes at bytes [16 kb s, 16 kb (s + 1)), code i at bits
+[i kb, (i + 1) kb); then values channel-major from byte 16 kb S (S = 16 or 32 slots): channel
+d's S codes at bytes [16 kb S + d S vb / 8, ...), slot s's code at bits [s vb, (s + 1) vb) of
+that run; bits are counted little-endian from a field's first byte; the bytes after the values
+up to 3072 are zero; parameters (k scale, k zero, v scale, v zero as fp16) at 3072 + 8 s and
+positions (int32, -1 when empty) at 3328 + 4 s for all 32 slot indices, as in the K8V4/K4V2
+layout.
 """
 import numpy as np
 
@@ -77,12 +79,17 @@ def build_page(scheme, tier, k_codes, v_codes, k_scale, k_zero, v_scale, v_zero,
     """Page image (uint8 [3456]) of m live tokens in slots 0..m-1 of a scheme's tier."""
     kb, vb = scheme.bits[tier]
     m = len(pos)
-    assert m <= SLOTS[tier]
+    S = SLOTS[tier]
+    assert m <= S
     page = np.zeros(PAGE_BYTES, np.uint8)
-    sb = scheme.slot_bytes(tier)
     for s in range(m):
-        page[s * sb:s * sb + 16 * kb] = pack_codes(k_codes[s], kb)
-        page[s * sb + 16 * kb:(s + 1) * sb] = pack_codes(v_codes[s], vb)
+        page[16 * kb * s:16 * kb * (s + 1)] = pack_codes(k_codes[s], kb)
+    vs_all = np.zeros((S, D), np.uint8)
+    vs_all[:m] = np.asarray(v_codes, np.uint8)[:m]
+    v0 = 16 * kb * S
+    run = S * vb // 8
+    for d in range(D):
+        page[v0 + d * run:v0 + (d + 1) * run] = pack_codes(vs_all[:, d], vb)
     params = np.zeros((32, 4), np.float16)
     params[:m, 0] = k_scale
     params[:m, 1] = k_zero
@@ -98,12 +105,14 @@ def build_page(scheme, tier, k_codes, v_codes, k_scale, k_zero, v_scale, v_zero,
 def read_page(page, scheme, tier, m):
     """Codes, parameters and positions of the first m slots of a page image."""
     kb, vb = scheme.bits[tier]
-    sb = scheme.slot_bytes(tier)
+    S = SLOTS[tier]
     page = np.asarray(page, np.uint8)
-    k = np.stack([unpack_codes(page[s * sb:s * sb + 16 * kb], kb) for s in range(m)]) if m else \
-        np.zeros((0, D), np.uint8)
-    v = np.stack([unpack_codes(page[s * sb + 16 * kb:(s + 1) * sb], vb) for s in range(m)]) if m \
-        else np.zeros((0, D), np.uint8)
+    k = np.stack([unpack_codes(page[16 * kb * s:16 * kb * (s + 1)], kb) for s in range(m)]) \
+        if m else np.zeros((0, D), np.uint8)
+    v0 = 16 * kb * S
+    run = S * vb // 8
+    cols = np.stack([unpack_codes(page[v0 + d * run:v0 + (d + 1) * run], vb, S) for d in range(D)])
+    v = cols.T[:m].astype(np.uint8)
     params = page[PARAM_OFF:POS_OFF].copy().view(np.float16).reshape(32, 4)[:m]
     pos = page[POS_OFF:PAGE_BYTES].copy().view(np.int32)[:m]
     return k, v, params[:, 0], params[:, 1], params[:, 2], params[:, 3], pos

@@ -50,6 +50,28 @@ def test_page_bit_coverage(high, low):
         assert np.array_equal(pos, np.arange(S))
 
 
+def test_hand_placed_fields():
+    # K4V2 in a LOW page (32 slots): slot 1's key code 3 sits at byte 64 (16 * 4 * 1), low
+    # nibble; its value code for channel 5 sits in channel 5's run (32 slots * 2 bits = 8
+    # bytes, from byte 16 * 4 * 32 = 2048 + 40) at bits 2..3
+    sc = osch.Scheme.named("K8V4", "K4V2")
+    k = np.zeros((2, 128), np.uint8)
+    v = np.zeros((2, 128), np.uint8)
+    k[1, 0] = 3
+    v[1, 5] = 2
+    z = np.zeros(2, np.float16)
+    page = osch.build_page(sc, osch.LOW, k, v, z, z, z, z, [7, 9])
+    assert page[64] == 3 and page[2048 + 40] == 2 << 2
+    assert np.count_nonzero(page[:osch.CODE_BYTES]) == 2
+    # K8V4 in a HIGH page: channel 0's run of 16 slots x 4 bits is bytes 2048 .. 2055
+    k2 = np.zeros((16, 128), np.uint8)
+    v2 = np.zeros((16, 128), np.uint8)
+    v2[15, 0] = 0xF
+    z2 = np.zeros(16, np.float16)
+    page = osch.build_page(sc, osch.HIGH, k2, v2, z2, z2, z2, z2, np.arange(16))
+    assert page[2048 + 7] == 0xF0 and np.count_nonzero(page[:osch.CODE_BYTES]) == 1
+
+
 def test_capacity_rule():
     assert osch.fits(osch.HIGH, 8, 4) and osch.fits(osch.HIGH, 4, 8)
     assert not osch.fits(osch.HIGH, 8, 8)          # 16 * 16 * 16 = 4096 > 3072
