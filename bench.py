@@ -20,7 +20,8 @@ every cached token's weight into the accumulators) and `generation_loop` (64 gen
 of the layer after the prompt: decode with score accumulation into one padded accumulator
 buffer, then kvc_generation_step, captured as one graph) and `prefill` (the causal prefill
 attention of the workload's prompts with the accumulators, kvc_prefill_attention, against the
-fp16 matrix-core peak).
+fp16 matrix-core peak) and `precision_schemes` (decode over pages placed in other precision
+schemes, kvc_quantize_and_place_scheme + kvc_paged_decode_attention_scheme).
 """
 import argparse
 import dataclasses
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--gen-steps", type=int, default=64,
                     help="steps of the generation loop (decode with score accumulation, then "
                          "the per-step policy) timed after the main steps (0: skip)")
+    ap.add_argument("--no-schemes", action="store_true",
+                    help="skip the precision-scheme decode timings")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill (prompt accumulator producer) timing")
     ap.add_argument("--eager", action="store_true",
@@ -236,6 +239,47 @@ def time_prefill(a, w, k, v, ev, stream):
     return t
 
 
+SCHEME_PAIRS = [("K8V4", "K4V2"), ("K4V8", "K2V4"), ("K8V2", "K4V1"), ("K4V2", "K4V1")]
+
+
+def time_schemes(a, w, k, v, acc, qs, ev, stream):
+    """Decode attention over pages in each precision scheme's slot-major layout (the prompt
+    placed with kvc_quantize_and_place_scheme, then the workload's decode steps with
+    kvc_paged_decode_attention_scheme): microseconds per call and algorithmic bytes, a live
+    token costing 16 (k + v) code bytes, 8 parameter bytes and 4 position bytes."""
+    from mixed_precision_paged_score_amd import kvc, pipeline
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=k.device)
+    res = {}
+    path = pipeline.PromptPath(w, k.device)
+    for high, low in SCHEME_PAIRS:
+        sc = kvc.make_scheme(high, low)
+        path.prompt_scheme(0, acc, k, v, sc)
+        for q in qs[:2]:
+            path.decode_scheme(0, q, out, sc)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for q in qs:
+            path.decode_scheme(0, q, out, sc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / len(qs)
+        count = path.new_count.cpu().numpy()
+        nh, nl = int(count[..., 0].sum()), int(count[..., 1].sum())
+        pages = int(np.ceil(count[..., 0] / 16).sum() + np.ceil(count[..., 1] / 32).sum())
+        kh, vh = kvc.FORMATS[high]
+        kl, vl = kvc.FORMATS[low]
+        byts = (nh * (16 * (kh + vh) + 12) + nl * (16 * (kl + vl) + 12) + 4 * pages +
+                w.batch * w.num_q_heads * 128 * 6)
+        res[f"{high}-{low}"] = {"us_per_call": us, "algorithmic_bytes": byts,
+                                "GBps": byts / (us * 1e-6) / 1e9,
+                                "frac_hbm": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                "status": path.pool.status()}
+    del path
+    torch.cuda.empty_cache()
+    return res
+
+
 def traffic_record(workload):
     """HBM bytes per decode call and per compaction round from the committed rocprofv3
     counter summary (profiles/traffic_<workload>.md), each kept only while the kernel sources
@@ -394,6 +438,9 @@ def main():
         gen = {"us_per_step": step_us, "policy_us_per_step": policy_us, "steps": a.gen_steps,
                "heads": w.batch * w.num_kv_heads, "decisions": gen_counts,
                "status": gen_status}
+    schemes = None
+    if not a.no_schemes and nsteps_dec > 0:
+        schemes = time_schemes(a, w, k, v, acc, qs, ev, stream)
     pre = None
     if not a.no_prefill:
         pre_ms = time_prefill(a, w, k, v, ev, stream)
@@ -452,6 +499,7 @@ def main():
             "algorithmic_bytes": dbytes + acc_bytes, "traffic": traffic["decode_acc"]},
         "generation_loop": gen,
         "prefill": pre,
+        "precision_schemes": schemes,
         "roofline": {"bound": "hbm", "kernel": "paged_decode_attention (main + combine)",
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},

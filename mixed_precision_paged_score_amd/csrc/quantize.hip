@@ -371,15 +371,18 @@ __device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t w, int b) {
     else *dst = uint8_t(w);
 }
 
-// grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole:
-// 16 lanes per row (channels 8c .. 8c + 7), four slots per pass; the code bytes past the last
-// slot are zero, parameters and positions of all 32 slot indices as in the default layout.
+// grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
+// Keys slot-major (16 lanes per row, channels 8c .. 8c + 7, four slots per pass, stored from
+// registers); values channel-major: the slots' codes are staged in LDS (one byte per code),
+// then lane d (and d + 64) packs channel d's run of S codes; the code bytes past the values are
+// zero, parameters and positions of all 32 slot indices as in the default layout.
 __global__ __launch_bounds__(256) void scheme_pages_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
     const int32_t *__restrict__ ok, const int32_t *__restrict__ poslist, int kh, int vh, int kl,
     int vl, uint8_t *__restrict__ pages) {
+    __shared__ uint8_t s_vc[QP_WAVES][LS][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = blockIdx.y;
     const int nheads = gridDim.y;
@@ -405,12 +408,12 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
     }
     const int kb = high ? kh : kl, vb = high ? vh : vl;
     const int S = high ? HS : LS;
-    const int sb = 16 * (kb + vb);
     uint8_t *pg = pages + int64_t(page) * PAGE;
     const int32_t *pl = poslist + int64_t(i) * max_seqlen;
     const int lo = cu[b];
     const int rg = lane >> 4, c = lane & 15;
     const float lk = float((1 << kb) - 1), lv = float((1 << vb) - 1);
+    uint8_t (*vc)[D] = s_vc[wave];
     for (int pass = 0; pass < S / 4; ++pass) {
         const int sl = 4 * pass + rg;
         const bool live = sl < m;
@@ -422,17 +425,19 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
         load_row8(V + roff, live, xv);
         const RowQ qk = row_params(xk, lk);
         const RowQ qv = row_params(xv, lv);
-        uint64_t wk = 0, wv = 0;
+        uint64_t wk = 0;
+        uint32_t v0 = 0, v1 = 0;
         if (live) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                wk |= uint64_t(code_of(xk[e], qk)) << (kb * e);
-                wv |= uint64_t(code_of(xv[e], qv)) << (vb * e);
+            for (int e = 0; e < 8; ++e) wk |= uint64_t(code_of(xk[e], qk)) << (kb * e);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v0 |= code_of(xv[e], qv) << (8 * e);
+                v1 |= code_of(xv[4 + e], qv) << (8 * e);
             }
         }
-        uint8_t *slot = pg + sl * sb;
-        store_codes(slot + c * kb, wk, kb);
-        store_codes(slot + 16 * kb + c * vb, wv, vb);
+        store_codes(pg + 16 * kb * sl + c * kb, wk, kb);
+        *reinterpret_cast<uint2 *>(&vc[sl][8 * c]) = make_uint2(v0, v1);
         if (c == 0) {
             const uint32_t a = live ? uint32_t(qk.s16) | (uint32_t(qk.z16) << 16) : 0u;
             const uint32_t bb = live ? uint32_t(qv.s16) | (uint32_t(qv.z16) << 16) : 0u;
@@ -440,8 +445,28 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
             reinterpret_cast<int32_t *>(pg + POS_OFF)[sl] = live ? pos : -1;
         }
     }
-    // code bytes past the last slot (S * sb is a multiple of 16), and slots S..31's fields
-    for (int k = S * sb / 16 + lane; k < PARAM_OFF / 16; k += 64)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // channel runs: S codes of vb bits, S vb / 8 bytes (2 .. 16), naturally aligned
+    const int run = S * vb / 8;
+    uint8_t *vbase = pg + 16 * kb * S;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int d = lane + 64 * half;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int sl = 0; sl < S; ++sl) {
+            const int bit = sl * vb;
+            w[bit >> 5] |= uint32_t(vc[sl][d]) << (bit & 31);
+        }
+        uint8_t *dst = vbase + d * run;
+        if (run == 16) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        else if (run == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+        else if (run == 4) *reinterpret_cast<uint32_t *>(dst) = w[0];
+        else *reinterpret_cast<uint16_t *>(dst) = uint16_t(w[0]);
+    }
+    // code bytes past the values (16 S (kb + vb) is a multiple of 16), slots S..31's fields
+    for (int k = S * (kb + vb) + lane; k < PARAM_OFF / 16; k += 64)
         reinterpret_cast<uint4 *>(pg)[k] = make_uint4(0, 0, 0, 0);
     if (lane >= S && lane < LS) {
         *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * lane) = make_uint2(0u, 0u);
