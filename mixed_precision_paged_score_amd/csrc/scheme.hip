@@ -2,21 +2,26 @@
 // scheme's layout (kvc_quantize_and_place_scheme: keys slot-major, values channel-major).
 //
 // DiffKV review page: the free-parameter ledger's comparison of precision schemes (K8V4, K4V8,
-// K8V2, K4V2, K2V4, K4V1); "Assumptions" for the attention itself.  The arithmetic is the
-// default decode's: codes enter the matrix products as the fp16 numbers 1024 + code (exact),
-// the offset and the per-token scales and zeros are applied around them:
-// q.k_hat = s_k (q.(1024 + code) - 1024 sum(q)) + z_k sum(q), and
-// sum_t p_t v_hat_t = sum_t (p_t s_v)(1024 + code_t) - 1024 sum_t p_t s_v + sum_t p_t z_v,
-// with p s_v split into fp16 hi + lo.
+// K8V2, K4V2, K2V4, K4V1); "Assumptions" for the attention itself.  Codes enter the matrix
+// products as exact fp16 numbers and the per-token scales and zeros are applied around them.
+// Keys: 1024 + code, q.k_hat = s_k (q.(1024 + code) - 1024 sum(q)) + z_k sum(q).  Values:
+// sum_t p_t v_hat_t = sum_t (p_t s_v) code_t + sum_t p_t z_v, with p s_v split into fp16 hi +
+// lo; 2- and 4-bit codes enter as 1024 + 2^(10-b) code against p s_v 2^-(10-b) (an offset of
+// 2^b code steps that the fp32 sums remove at the end), other widths as the code itself.
 //
 // Grid: S workgroups per (request, KV head) (the default decode's split count), 4 waves each;
 // the head's 16-slot tiles (HIGH pages, then LOW half-pages) are cut into 4 S contiguous
-// ranges, one per wave.  Per tile, with v_mfma_f32_16x16x16_f16 and operands straight from the
-// page: S^T = codes . q^T (lane (c, g): token c's 32 channels 32 g .. 32 g + 31 as the A
-// operand, query head c's same channels as B; D: query head c, tokens 4 g + r), an online
-// softmax per query-head column, and O^T += V^T . P^T (A: channel 16 dt + c's codes of tokens
-// 4 g .. 4 g + 3, one 32-bit word of the channel's run; B: the lane's own P^T entries).  The
-// four waves merge in LDS into the default decode's partials; its combine kernel finishes.
+// ranges, one per wave; each wave runs its HIGH tiles, then its LOW tiles, in two loops
+// compiled for the tiers' widths.  Per tile, with v_mfma_f32_16x16x32_f16 and operands read
+// straight from the page (buffer loads; the next tile's are requested before this tile's
+// products): S^T = codes . q^T (lane (c, g): 32 channels of the token in score row c as the
+// A operand, query head c's same channels as B; D: query head c, score rows 4 g + r), an
+// online softmax per query-head column, and O^T += V^T . P^T with k = the lane's four tokens
+// against the high parts of p s_v, then the same tokens against the low parts (A: channel
+// 16 dt + c's codes of those tokens, from one 32-bit word of the channel's run).  The four
+// waves merge in LDS into the default decode's partials; its combine kernel finishes.
+#include <type_traits>
+
 #include "kvc_internal.h"
 #include "workspace.h"
 
@@ -34,8 +39,35 @@ constexpr float MARGIN = 8.0f;
 constexpr float M_INIT = -1.0e30f;
 constexpr float CODE_OFF = 1024.0f;
 
-__device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h8 cat(h4 a, h4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Page reads are buffer loads: one descriptor per page (wave-uniform: the page's address,
+// its size as the range) and a 32-bit per-lane offset
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(page), 0, PAGE, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u4v x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u2v x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 __device__ __forceinline__ float max_col(float x) {
@@ -47,19 +79,28 @@ __device__ __forceinline__ float max_col(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// 32 codes of b bits (4 b bytes at p, naturally aligned) into w[0 .. b-1]
-__device__ __forceinline__ void load_codes32(const uint8_t *p, int b, uint32_t (&w)[8]) {
-    if (b == 8) {
-        const uint4 x = reinterpret_cast<const uint4 *>(p)[0], y = reinterpret_cast<const uint4 *>(p)[1];
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w; w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
-    } else if (b == 4) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
+// 32 codes of b bits (4 b bytes at offset o of a page, naturally aligned) into w[0 .. b-1]
+template <int KB>
+__device__ __forceinline__ void load_codes32(__amdgpu_buffer_rsrc_t rs, uint32_t o, int b,
+                                             uint32_t (&w)[KB ? KB : 8]) {
+    if (KB == 8 || (KB == 0 && b == 8)) {
+        const uint4 x = ld16(rs, o), y = ld16(rs, o + 16);
         w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-    } else if (b == 2) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        w[0] = x.x; w[1] = x.y;
+        if constexpr (KB == 8 || KB == 0) {
+            w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+        }
+    } else if (KB == 4 || (KB == 0 && b == 4)) {
+        const uint4 x = ld16(rs, o);
+        w[0] = x.x;
+        if constexpr (KB >= 4 || KB == 0) {
+            w[1] = x.y; w[2] = x.z; w[3] = x.w;
+        }
+    } else if (KB == 2 || (KB == 0 && b == 2)) {
+        const uint2 x = ld8(rs, o);
+        w[0] = x.x;
+        if constexpr (KB >= 2 || KB == 0) w[1] = x.y;
     } else {
-        w[0] = *reinterpret_cast<const uint32_t *>(p);
+        w[0] = ld4(rs, o);
     }
 }
 
@@ -71,10 +112,132 @@ __device__ __forceinline__ uint2 codes4(uint32_t w, int b) {
                       (c2 | 0x6400u) | ((c3 | 0x6400u) << 16));
 }
 
+template <int N> using ic = std::integral_constant<int, N>;
+
+// For widths known at compile time, codes are converted two at a time: one shift and one
+// and-or turn two codes 16 bits apart into the fp16 pair (1024 + a, 1024 + b) (byte permutes
+// for 8 bits).  The k order of the matrix products follows the codes:
+// * key k-step ks takes channels key_chan(ks, 0..3) of the lane's 32, and the query operand is
+//   permuted the same way (once per tier);
+// * score row 4 g + r of a tile loads slot row_slot(g, r), so that each lane's four tokens
+//   pair up 16 bits apart in a 2- or 4-bit value channel's run; the other widths keep the
+//   natural order (slot 4 g + r), 8-bit codes going through byte permutes.
+// Width 0 (run-time widths) keeps the natural orders and converts code by code.
+template <int KB>
+__device__ __forceinline__ constexpr int key_chan(int ks, int e) {
+    if constexpr (KB == 0 || KB == 8) {
+        return 4 * ks + e;
+    } else {
+        constexpr int n = 32 / KB, ppw = 16 / KB, hpw = 8 / KB;
+        const int base = (ks / hpw) * n + 2 * (ks % hpw);
+        return e == 0 ? base : e == 1 ? base + ppw : e == 2 ? base + 1 : base + 1 + ppw;
+    }
+}
+// 2- and 4-bit values: lane g's rows r = 0..3 are slots base + {0, P, 1, P + 1}, P = 16 / VB
+// (codes 16 bits apart in the run) with base = 2 g (VB 2) or 8 (g / 2) + 2 (g % 2) (VB 4:
+// the four slots share one 32-bit word)
+template <int VB>
+__device__ __forceinline__ constexpr bool paired() { return VB == 2 || VB == 4; }
+template <int VB>
+__device__ __forceinline__ int row_base(int g) {
+    if constexpr (VB == 4) return 8 * (g >> 1) + 2 * (g & 1);
+    else if constexpr (VB == 2) return 2 * g;
+    else return 4 * g;
+}
+template <int VB>
+__device__ __forceinline__ int row_slot(int g, int r) {
+    if constexpr (paired<VB>()) {
+        constexpr int P = 16 / VB;
+        return row_base<VB>(g) + (r == 1 ? P : r == 2 ? 1 : r == 3 ? P + 1 : 0);
+    } else {
+        return 4 * g + r;
+    }
+}
+constexpr uint32_t MAGIC = 0x64006400u;   // fp16 1024 in both halves
+// bytes 0, 1 and 2, 3 of x as fp16 pairs (1024 + byte)
+__device__ __forceinline__ h4 bytes4(uint32_t x) {
+    return __builtin_bit_cast(h4, make_uint2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
+                                             __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)));
+}
+template <int KB>
+__device__ __forceinline__ h4 key_op(const uint32_t (&w)[KB ? KB : 8], int ks, int kb_rt) {
+    if constexpr (KB == 8) {
+        return bytes4(w[ks]);
+    } else if constexpr (KB > 0) {
+        constexpr int hpw = 8 / KB;
+        constexpr uint32_t M = ((1u << KB) - 1u) * 0x00010001u;
+        const uint32_t x = w[ks / hpw];
+        const int u = ks % hpw;
+        return __builtin_bit_cast(h4, make_uint2(((x >> (2 * KB * u)) & M) | MAGIC,
+                                                 ((x >> (KB * (2 * u + 1))) & M) | MAGIC));
+    } else {
+        const uint32_t word = kb_rt == 8 ? w[ks] : kb_rt == 4 ? w[ks >> 1]
+                            : kb_rt == 2 ? w[ks >> 2] : w[0];
+        return __builtin_bit_cast(h4, codes4(word >> ((4 * ks * kb_rt) & 31), kb_rt));
+    }
+}
+// Value operands.  For 2- and 4-bit codes a rotation puts the lane's codes in the top bits of
+// the fp16 mantissa, 1024 + 2^(10-b) code, and the tier's value scales are multiplied by
+// 2^-(10-b) (exact), so a product term is p s_v (2^b + code): the offset that the fp32 sums
+// cancel at the end (1024 per unit of the scaled p s_v) is 2^b code steps, not 1024.  Other
+// widths convert to 1024 + code and subtract 1024 in fp16 (exact): no offset at all.
+template <int VB>
+__device__ __forceinline__ constexpr bool val_offset() { return VB == 2 || VB == 4; }
+template <int VB>
+__device__ __forceinline__ constexpr float val_scale() {
+    return VB == 4 ? 1.0f / 64.0f : VB == 2 ? 1.0f / 256.0f : 1.0f;
+}
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t minus1024(uint32_t x) {
+    const h2 r = __builtin_bit_cast(h2, x) - h2{(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n) {
+    return __builtin_amdgcn_alignbit(x, x, n);
+}
+// the lane's four tokens (row_slot order) of one value channel, from the word of its run that
+// holds them: 2- and 4-bit codes rotated by rl / rh (the codes of rows 0, 1 / 2, 3 to the
+// mantissa's top bits), other widths shifted right by sh first
+template <int VB>
+__device__ __forceinline__ h4 val_op(uint32_t w, uint32_t rl, uint32_t rh, int sh, int vb_rt) {
+    if constexpr (VB == 4) {
+        return __builtin_bit_cast(h4, make_uint2((rotr(w, rl) & 0x03C003C0u) | MAGIC,
+                                                 (rotr(w, rh) & 0x03C003C0u) | MAGIC));
+    } else if constexpr (VB == 2) {
+        return __builtin_bit_cast(h4, make_uint2((rotr(w, rl) & 0x03000300u) | MAGIC,
+                                                 (rotr(w, rh) & 0x03000300u) | MAGIC));
+    } else {
+        uint2 u;
+        if constexpr (VB == 8) {
+            u = make_uint2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
+        } else if constexpr (VB == 1) {
+            // bits 0..3 = rows 0..3; x | x << 15 moves bit 1 to bit 16
+            const uint32_t x = w >> sh, lo = x & 3u, hi = (x >> 2) & 3u;
+            u = make_uint2(((lo | (lo << 15)) & 0x00010001u) | MAGIC,
+                           ((hi | (hi << 15)) & 0x00010001u) | MAGIC);
+        } else {
+            u = codes4(w >> sh, vb_rt);
+        }
+        return __builtin_bit_cast(h4, make_uint2(minus1024(u.x), minus1024(u.y)));
+    }
+}
+
+// one tile's raw operands: the key codes of row c's slot (the lane's 32 channels), the
+// parameters of the lane's four tokens (two slot pairs), and per channel 16 dt + c the word of
+// its run that holds those tokens' value codes
+template <int KB>
+struct Tile {
+    uint32_t wk[KB ? KB : 8];
+    uint4 pa, pb;
+    uint32_t wv[8];
+    int live;
+};
+
 // grid (S * B * Hkv), 256 threads; workgroup x: head x / S, split x % S.  KH, VH, KL, VL: the
 // scheme's bit widths when compiled for it (0: taken from the arguments at run time).
 template <int KH, int VH, int KL, int VL>
-__global__ __launch_bounds__(256) void scheme_decode_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_decode_kernel(
     const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
     int C, int S, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
@@ -95,8 +258,9 @@ __global__ __launch_bounds__(256) void scheme_decode_kernel(
     const int t0 = int(int64_t(T) * cc / NC), t1 = int(int64_t(T) * (cc + 1) / NC);
     const int32_t *row = rows_l + int64_t(i) * C;
 
-    // query operands: column c = query head (zero beyond G), channels 32 g + 4 ks + e
-    h4 qop[8];
+    // query: the lane's channels 32 g .. 32 g + 31 of query head c (zero beyond G), natural
+    // order; each tier's loop permutes them into its key order
+    h4 qn[8];
     float sumq = 0.f;
     {
         uint4 u[4] = {};
@@ -105,12 +269,12 @@ __global__ __launch_bounds__(256) void scheme_decode_kernel(
             u[0] = qp[0]; u[1] = qp[1]; u[2] = qp[2]; u[3] = qp[3];
         }
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const uint4 &x = u[ks >> 1];
-            qop[ks] = __builtin_bit_cast(h4, (ks & 1) ? make_uint2(x.z, x.w) : make_uint2(x.x, x.y));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sumq += float(qop[ks][e]);
+        for (int j = 0; j < 4; ++j) {
+            qn[2 * j] = __builtin_bit_cast(h4, make_uint2(u[j].x, u[j].y));
+            qn[2 * j + 1] = __builtin_bit_cast(h4, make_uint2(u[j].z, u[j].w));
         }
+#pragma unroll
+        for (int p = 0; p < 32; ++p) sumq += float(qn[p >> 2][p & 3]);
         sumq += __shfl_xor(sumq, 16, 64);
         sumq += __shfl_xor(sumq, 32, 64);
     }
@@ -120,106 +284,151 @@ __global__ __launch_bounds__(256) void scheme_decode_kernel(
     for (int dt = 0; dt < 8; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
     float m = M_INIT, l = 0.f, lz = 0.f, lp = 0.f;
 
-    // one tile's raw operands: key codes of token c (channels 32 g ..), parameters of tokens
-    // 4 g .. 4 g + 3, and the value-code words of channels 16 dt + c
-    struct Raw {
-        uint32_t wk[8];
-        uint4 pa, pb;
-        uint32_t wv[8];
-        int live, kb, vb, vsh;
+    // tiles [ta, tb) of one tier (HIGH: tile t = page row[t]; LOW: tile t = half t % 2 of page
+    // row[C - 1 - t / 2]), two register sets: the next tile's operands are requested before
+    // this tile's products
+    auto run_tier = [&](int ta, int tb, auto highc, auto kbc, auto vbc) {
+        constexpr bool HIGH = decltype(highc)::value;
+        constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
+        if (ta >= tb) return;
+        const int kb = KB ? KB : (HIGH ? kh : kl), vb = VB ? VB : (HIGH ? vh : vl);
+        constexpr int Sp = HIGH ? HS : LS;
+        const int run = Sp * vb / 8;
+        // 16x16x32 product m2: k-steps 2 m2 and 2 m2 + 1 of the key order
+        h8 qop[4];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ch = key_chan<KB>(ks, e);
+                qop[ks >> 1][4 * (ks & 1) + e] = qn[ch >> 2][ch & 3];
+            }
+        // value words: byte offset in the run (beyond the half-page's); rotations of 2- and
+        // 4-bit codes (rows 0, 1 and rows 2, 3 to the mantissa's top bits)
+        uint32_t voff = 0, rl = 0, rh = 0;
+        if constexpr (VB == 4) {
+            const uint32_t sh = 8 * (g & 1);   // slot 2 (g % 2) of the word at bit 8 (g % 2)
+            voff = 4 * (g >> 1);
+            rl = (sh - 6) & 31;
+            rh = (sh - 2) & 31;
+        } else if constexpr (VB == 2) {
+            const uint32_t sh = 4 * g;         // slot 2 g at bit 4 g
+            rl = (sh - 8) & 31;
+            rh = (sh - 6) & 31;
+        } else if constexpr (VB == 8) {
+            voff = 4 * g;
+        }
+        const int krow = row_slot<VB>(c >> 2, c & 3);
+        auto load = [&](Tile<KB> &r, int t) {
+            const int page = HIGH ? row[t] : row[C - 1 - (t >> 1)];
+            const uint32_t slot0 = HIGH ? 0u : 16u * uint32_t(t & 1);
+            r.live = min(16, (HIGH ? nh : nl) - 16 * t);
+            const __amdgpu_buffer_rsrc_t rs = page_rsrc(pages + int64_t(page) * PAGE);
+            load_codes32<KB>(rs, 16 * kb * (slot0 + krow) + 4 * g * kb, kb, r.wk);
+            // parameter pairs: slots (sa, sa + 1) and (sb, sb + 1)
+            const uint32_t sa = slot0 + row_base<VB>(g);
+            const uint32_t sb = sa + (paired<VB>() ? 16 / (VB ? VB : 1) : 2);
+            r.pa = ld16(rs, PARAM_OFF + 8 * sa);
+            r.pb = ld16(rs, PARAM_OFF + 8 * sb);
+            // offset of the tile's codes in a run: slot0 vb / 8 bytes (whole words for the
+            // compiled widths; 1-bit and run-time widths read the word holding bit slot0 vb)
+            uint32_t off = 16 * kb * Sp + c * run + voff;
+            if constexpr (VB == 4 || VB == 2 || VB == 8) off += slot0 * VB / 8;
+            else off += 4 * (((slot0 + 4 * g) * vb) >> 5);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t o = off + 16 * dt * run;
+                if constexpr (VB == 1 || VB == 0) {
+                    // a 2-byte run (16 one-bit codes) is read as such
+                    r.wv[dt] = run == 2 ? ld2(rs, o) : ld4(rs, o);
+                } else {
+                    r.wv[dt] = ld4(rs, o);
+                }
+            }
+        };
+        auto compute = [&](const Tile<KB> &r, int t) {
+            f4 acc = f4{acc0, acc0, acc0, acc0};
+#pragma unroll
+            for (int m2 = 0; m2 < 4; ++m2)
+                acc = mfma(cat(key_op<KB>(r.wk, 2 * m2, kb), key_op<KB>(r.wk, 2 * m2 + 1, kb)),
+                           qop[m2], acc);
+            // rows' parameters: paired orders are {sa, sb, sa + 1, sb + 1}, the natural order
+            // {sa, sa + 1, sb, sb + 1}
+            uint2 par[4];
+            if constexpr (paired<VB>()) {
+                par[0] = make_uint2(r.pa.x, r.pa.y); par[1] = make_uint2(r.pb.x, r.pb.y);
+                par[2] = make_uint2(r.pa.z, r.pa.w); par[3] = make_uint2(r.pb.z, r.pb.w);
+            } else {
+                par[0] = make_uint2(r.pa.x, r.pa.y); par[1] = make_uint2(r.pa.z, r.pa.w);
+                par[2] = make_uint2(r.pb.x, r.pb.y); par[3] = make_uint2(r.pb.z, r.pb.w);
+            }
+            float x[4], vs[4], vz[4];
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu));
+                const float kz = h2f(uint16_t(par[q4].x >> 16));
+                vs[q4] = h2f(uint16_t(par[q4].y & 0xffffu)) * val_scale<VB>();
+                vz[q4] = h2f(uint16_t(par[q4].y >> 16));
+                const float xv = (ksc * acc[q4] + kz * sumq) * scale_log2;
+                x[q4] = row_slot<VB>(g, q4) < r.live ? xv : -__builtin_inff();
+                mx = fmaxf(mx, x[q4]);
+            }
+            mx = fmaxf(max_col(mx), M_INIT);
+            // the branch is uniform; written as a per-lane condition (an opaque lane value that
+            // is always 1) the compiler predicates it instead of splitting the accumulators'
+            // live ranges, which would copy all 32 of them on the common path
+            int one = 1;
+            asm volatile("" : "+v"(one));
+            if (one && __ballot(mx > m + MARGIN) != 0ull) {
+                const float mn = fmaxf(m, mx);
+                const float corr = __builtin_amdgcn_exp2f(m - mn);
+                m = mn;
+                l *= corr;
+                lz *= corr;
+                lp *= corr;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt] *= corr;
+            }
+            _Float16 hi[4], lo[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float p = __builtin_amdgcn_exp2f(x[q4] - m);
+                const float pv = p * vs[q4];
+                hi[q4] = _Float16(pv);
+                lo[q4] = _Float16(pv - float(hi[q4]));
+                l += p;
+                lz += p * vz[q4];
+                if constexpr (val_offset<VB>()) lp += pv;
+            }
+            // k = 8 g + e: the lane's four tokens with P' = p s_v's fp16 high parts (e < 4),
+            // then the same tokens with its low parts (e >= 4)
+            const h8 bp = h8{hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]};
+            // 1-bit and run-time widths: the tokens' first bit within the word
+            const int sh = (VB == 4 || VB == 2 || VB == 8)
+                               ? 0 : ((((HIGH ? 0 : 16 * (t & 1)) + 4 * g) * vb) & 31);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const h4 a = val_op<VB>(r.wv[dt], rl, rh, sh, vb);
+                o[dt] = mfma(cat(a, a), bp, o[dt]);
+            }
+        };
+        // past the tier's last tile the loads repeat it (cache hits), which keeps the loop
+        // free of branches around loads and of register copies
+        const int tl = tb - 1;
+        Tile<KB> ra, rb;
+        load(ra, ta);
+        for (int t = ta;;) {
+            load(rb, min(t + 1, tl));
+            compute(ra, t);
+            if (++t >= tb) break;
+            load(ra, min(t + 1, tl));
+            compute(rb, t);
+            if (++t >= tb) break;
+        }
     };
-    auto load_tile = [&](Raw &r, int t) {
-        const bool high = t < qH;
-        const int page = high ? row[t] : row[C - 1 - ((t - qH) >> 1)];
-        const int slot0 = high ? 0 : 16 * ((t - qH) & 1);
-        r.live = high ? min(16, nh - 16 * t) : min(16, nl - 16 * (t - qH));
-        r.kb = high ? kh : kl;
-        r.vb = high ? vh : vl;
-        const int Sp = high ? HS : LS;
-        const uint8_t *pg = pages + int64_t(page) * PAGE;
-        load_codes32(pg + 16 * r.kb * (slot0 + c) + 4 * g * r.kb, r.kb, r.wk);
-        r.pa = *reinterpret_cast<const uint4 *>(pg + PARAM_OFF + 8 * (slot0 + 4 * g));
-        r.pb = *reinterpret_cast<const uint4 *>(pg + PARAM_OFF + 8 * (slot0 + 4 * g) + 16);
-        // 4 vb bits of one naturally aligned word of channel 16 dt + c's run (a 2-byte run,
-        // 16 slots of 1 bit, is read as such)
-        const int run = Sp * r.vb / 8;
-        const uint8_t *vbase = pg + 16 * r.kb * Sp;
-        const int vbit = (slot0 + 4 * g) * r.vb;
-        r.vsh = vbit & 31;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const uint8_t *vr = vbase + (16 * dt + c) * run;
-            r.wv[dt] = run == 2 ? uint32_t(*reinterpret_cast<const uint16_t *>(vr))
-                                : *reinterpret_cast<const uint32_t *>(vr + 4 * (vbit >> 5));
-        }
-    };
-    auto compute = [&](const Raw &r) {
-        f4 acc = f4{acc0, acc0, acc0, acc0};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            // channels 4 ks .. 4 ks + 3 of the lane's 32: bits 4 ks kb .. of the run; the word
-            // index is chosen from the four widths so that every register index is static
-            const uint32_t word = r.kb == 8 ? r.wk[ks] : r.kb == 4 ? r.wk[ks >> 1]
-                                : r.kb == 2 ? r.wk[ks >> 2] : r.wk[0];
-            const h4 a = __builtin_bit_cast(h4, codes4(word >> ((4 * ks * r.kb) & 31), r.kb));
-            acc = mfma(a, qop[ks], acc);
-        }
-        const uint32_t pw[8] = {r.pa.x, r.pa.y, r.pa.z, r.pa.w, r.pb.x, r.pb.y, r.pb.z, r.pb.w};
-        float x[4], vs[4], vz[4];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float ksc = h2f(uint16_t(pw[2 * q4] & 0xffffu));
-            const float kz = h2f(uint16_t(pw[2 * q4] >> 16));
-            vs[q4] = h2f(uint16_t(pw[2 * q4 + 1] & 0xffffu));
-            vz[q4] = h2f(uint16_t(pw[2 * q4 + 1] >> 16));
-            x[q4] = 4 * g + q4 < r.live ? (ksc * acc[q4] + kz * sumq) * scale_log2
-                                        : -__builtin_inff();
-            mx = fmaxf(mx, x[q4]);
-        }
-        mx = fmaxf(max_col(mx), M_INIT);
-        if (__ballot(mx > m + MARGIN) != 0ull) {
-            const float mn = fmaxf(m, mx);
-            const float corr = __builtin_amdgcn_exp2f(m - mn);
-            m = mn;
-            l *= corr;
-            lz *= corr;
-            lp *= corr;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[dt] *= corr;
-        }
-        _Float16 hi[4], lo[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float p = __builtin_amdgcn_exp2f(x[q4] - m);
-            const float pv = p * vs[q4];
-            hi[q4] = _Float16(pv);
-            lo[q4] = _Float16(pv - float(hi[q4]));
-            l += p;
-            lz += p * vz[q4];
-            lp += pv;
-        }
-        const h4 bh = h4{hi[0], hi[1], hi[2], hi[3]}, bl = h4{lo[0], lo[1], lo[2], lo[3]};
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const h4 a = __builtin_bit_cast(h4, codes4(r.wv[dt] >> r.vsh, r.vb));
-            o[dt] = mfma(a, bh, o[dt]);
-            o[dt] = mfma(a, bl, o[dt]);
-        }
-    };
-    // two register sets: the next tile's operands are requested before this tile's products
-    if (t0 < t1) {
-        Raw ra, rb;
-        load_tile(ra, t0);
-        for (int t = t0;;) {
-            if (t + 1 < t1) load_tile(rb, t + 1);
-            compute(ra);
-            if (++t >= t1) break;
-            if (t + 1 < t1) load_tile(ra, t + 1);
-            compute(rb);
-            if (++t >= t1) break;
-        }
-    }
+    run_tier(t0, min(t1, qH), ic<1>{}, ic<KH>{}, ic<VH>{});
+    run_tier(max(t0, qH) - qH, t1 - qH, ic<0>{}, ic<KL>{}, ic<VL>{});
     // column sums over the four lane groups, then the four waves' merge
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
