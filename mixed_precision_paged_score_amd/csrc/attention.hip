@@ -144,11 +144,13 @@ __device__ __forceinline__ Keys<HIGH> load_keys(__amdgpu_buffer_rsrc_t ra,
     return d;
 }
 
-// LG: also the position of token 4j + (lane & 3) of the lane's own tile
+// LG: also the position of token 4j + (lane & 3) of the lane's own tile.  own: the page of
+// the lane's own tile (HIGH: page A or B by lane; read by per-lane addresses, since a buffer
+// descriptor chosen per lane would make the compiler serialize the load over the two pages)
 template <bool HIGH, bool LG>
 __device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
                                                 __amdgpu_buffer_rsrc_t rb, int fa, int fb,
-                                                int lane, bool own_b) {
+                                                int lane, bool own_b, const uint8_t *own) {
     const uint32_t j = lane >> 4;
     Vals<HIGH> d;
     d.ps = 0;
@@ -156,16 +158,11 @@ __device__ __forceinline__ Vals<HIGH> load_vals(__amdgpu_buffer_rsrc_t ra,
         d.va = ld16(ra, V_OFF + 16 * uint32_t(lane));
         d.vb = ld16(rb, V_OFF + 16 * uint32_t(lane));
         // parameters of the lane's own tile: each half-wave reads its tile's page
-        const uint32_t o = PARAM_OFF + 32 * j;
-        if (own_b) {
-            d.p0 = ld16(rb, o);
-            d.p1 = ld16(rb, o + 16);
-            if constexpr (LG) d.ps = ld4(rb, POS_OFF + 4 * (4 * j + (lane & 3)));
-        } else {
-            d.p0 = ld16(ra, o);
-            d.p1 = ld16(ra, o + 16);
-            if constexpr (LG) d.ps = ld4(ra, POS_OFF + 4 * (4 * j + (lane & 3)));
-        }
+        const uint4 *op = reinterpret_cast<const uint4 *>(own + PARAM_OFF + 32 * j);
+        d.p0 = op[0];
+        d.p1 = op[1];
+        if constexpr (LG)
+            d.ps = *reinterpret_cast<const uint32_t *>(own + POS_OFF + 4 * (4 * j + (lane & 3)));
     } else {
         // the two LOW tiles of a pair are the halves of one page (ra and rb are the same)
         d.va = ld8(ra, V_OFF + 16 * uint32_t(lane) + 8 * uint32_t(fa));
@@ -435,8 +432,9 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
         auto vals_at = [&](int t) {
             t = min(t, tlast);
             const int tb = tb_of(t);
-            return load_vals<HIGH, LG>(page_rsrc(page_of(t)), page_rsrc(page_of(tb)), t & 1,
-                                       tb & 1, lane, own_b);
+            const uint8_t *pa = page_of(t), *pb = page_of(tb);
+            return load_vals<HIGH, LG>(page_rsrc(pa), page_rsrc(pb), t & 1, tb & 1, lane, own_b,
+                                       own_b ? pb : pa);
         };
         // the lane's logit slot for the pair starting at tile t (its own tile of the pair)
         auto lg_at = [&](int t) -> float * {

@@ -91,7 +91,12 @@ __device__ __forceinline__ int find_request(const int32_t *cu, int B, int64_t r)
 __device__ __forceinline__ float h2f(uint16_t b) {
     return __half2float(__ushort_as_half(b));
 }
+// fp16 rounding (nearest, ties to even) of the float32 value f.  The empty asm makes f a
+// finished float32 value: without it the compiler may fuse the multiply-add that produced f
+// into an fp16-result v_fma_mix, one rounding of the exact result instead of the float32
+// rounding followed by the fp16 one (they differ where the float32 value is an fp16 tie)
 __device__ __forceinline__ uint16_t f2h_rn(float f) {
+    asm("" : "+v"(f));
     return __half_as_ushort(__float2half_rn(f));
 }
 

@@ -254,22 +254,23 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     // quantize the lane's 8 channels of slot s from float rows (or store a zero slot), write
     // the key codes to the page and stage value codes and parameters in LDS
     auto emit_fresh = [&](int s, bool live, const float (&xk)[8], const float (&xv)[8]) {
-        uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
+        uint32_t kw0 = 0, kw1 = 0;
         const RowQ qk = row_params(xk, high ? 255.0f : 15.0f);
+        uint32_t kb[8], vb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kb[e] = code_bits(xk[e], qk);
         if (high) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kw0 |= code_of(xk[e], qk) << (8 * e);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kw1 |= code_of(xk[4 + e], qk) << (8 * e);
+            kw0 = gather4(kb[0], kb[1], kb[2], kb[3]);
+            kw1 = gather4(kb[4], kb[5], kb[6], kb[7]);
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kw0 |= code_of(xk[e], qk) << (4 * k_nib(e));
+            // nibble k_nib(e) holds channel e: bytes (c0 c1) (c4 c5) (c2 c3) (c6 c7), low first
+            kw0 = gather4(kb[0], kb[4], kb[2], kb[6]) | (gather4(kb[1], kb[5], kb[3], kb[7]) << 4);
         }
         const RowQ qv = row_params(xv, high ? 15.0f : 3.0f);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vw0 |= code_of(xv[e], qv) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vw1 |= code_of(xv[4 + e], qv) << (8 * e);
+        for (int e = 0; e < 8; ++e) vb[e] = code_bits(xv[e], qv);
+        const uint32_t vw0 = gather4(vb[0], vb[1], vb[2], vb[3]);
+        const uint32_t vw1 = gather4(vb[4], vb[5], vb[6], vb[7]);
         store_slot(pg, sv, s_par[wave], high, s, c, live, kw0, kw1, vw0, vw1, qk.s16, qk.z16,
                    qv.s16, qv.z16);
     };

@@ -127,3 +127,17 @@ def test_fp16_rounding_is_nearest_even():
     # a tie rounds to the even neighbour
     one = np.float32(1.0) + np.float32(2.0 ** -11)      # halfway between 1 and 1+2^-10
     assert np.float16(one) == np.float16(1.0)
+
+
+def test_scale_on_an_fp16_tie_rounds_to_even():
+    # row min -1.7587890625, max 34.4375 at 4 bits: the range 36.1962890625 is exact in float32
+    # and range / 15 = 2.4130859375 exactly, the midpoint of the fp16 neighbours 2.412109375
+    # (mantissa 211) and 2.4140625 (mantissa 212): the float32 quotient is the tie itself and
+    # the fp16 rounding takes the even mantissa
+    x = np.zeros((1, 128), np.float16)
+    x[0, 0], x[0, 1] = -1.7587890625, 34.4375
+    assert Fraction(float(x[0, 1])) - Fraction(float(x[0, 0])) == Fraction(36.1962890625)
+    assert Fraction(36.1962890625) / 15 == (Fraction(2.412109375) + Fraction(2.4140625)) / 2
+    codes, s, z = quant.quantize_rows(x, 4)
+    assert float(s[0]) == 2.4140625 and float(z[0]) == -1.7587890625
+    assert codes[0, 0] == 0 and codes[0, 1] == 15
