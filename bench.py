@@ -88,6 +88,37 @@ def copy_calibration():
           flush=True)
 
 
+def measure_ceilings():
+    """Streaming rates of plain device kernels on the same GPU, for context beside the path's
+    GB/s: a 1 GiB device copy (read + write), an elementwise add over 1 GiB of fp16 (read +
+    write) and a 1 GiB fill (write); the median of 10 launches each, outside the timed steps."""
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.float16, device="cuda:0")
+    b = torch.empty_like(a)
+
+    def rate(fn, nbytes):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(x.elapsed_time(y) for x, y in evs)[5]
+        return nbytes / (ms / 1e3) / 1e9
+
+    res = {"copy_GBps": rate(lambda: b.copy_(a), 2 * n),
+           "stream_add_GBps": rate(lambda: torch.add(a, 1.0, out=b), 2 * n),
+           "fill_GBps": rate(lambda: b.fill_(2.0), n)}
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
     """Decode attention with score accumulation (every cached token's weight added into fp32
     accumulators), the same decode steps, replayed as one graph outside the timed steps;
@@ -504,6 +535,7 @@ def main():
                      "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": dec_traffic},
         "pool_status": status,
+        "ceilings": measure_ceilings(),
     }
     if not a.no_cpu_baseline:
         from threadpoolctl import threadpool_limits

@@ -372,11 +372,42 @@ __device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t w, int b) {
     else *dst = uint8_t(w);
 }
 
+// one lane's share of a value block (16 slots) in the decode's operand order: lane L = 16 g + c
+// packs the codes of channels 16 n + c (n < 8) for slots 16 f + 4 g + r (r < 4), code (n, r)
+// at bit 32 (n / p) + 16 (r % 2) + VB (2 (n % p) + r / 2) with p = 8 / VB, and stores its
+// 4 VB bytes at dst (naturally aligned)
+template <int VB>
+__device__ __forceinline__ void pack_value_block(uint8_t *dst, const uint8_t (*vc)[D], int f,
+                                                 int g, int c) {
+    constexpr int P = 8 / VB;
+    uint32_t w[VB];
+#pragma unroll
+    for (int j = 0; j < VB; ++j) w[j] = 0u;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t code = vc[16 * f + 4 * g + r][16 * n + c];
+            w[n / P] |= code << (16 * (r & 1) + VB * (2 * (n % P) + (r >> 1)));
+        }
+    if constexpr (VB == 8) {
+        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else if constexpr (VB == 4) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (VB == 2) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+    } else {
+        *reinterpret_cast<uint32_t *>(dst) = w[0];
+    }
+}
+
 // grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
 // Keys slot-major (16 lanes per row, channels 8c .. 8c + 7, four slots per pass, stored from
-// registers); values channel-major: the slots' codes are staged in LDS (one byte per code),
-// then lane d (and d + 64) packs channel d's run of S codes; the code bytes past the values are
-// zero, parameters and positions of all 32 slot indices as in the default layout.
+// registers); values in blocks of 16 slots in the decode's operand order: the slots' codes
+// are staged in LDS (one byte per code), then every lane packs its share of each block
+// (pack_value_block); the code bytes past the values are zero, parameters and positions of
+// all 32 slot indices as in the default layout.
 __global__ __launch_bounds__(256) void scheme_pages_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
@@ -449,22 +480,14 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // channel runs: S codes of vb bits, S vb / 8 bytes (2 .. 16), naturally aligned
-    const int run = S * vb / 8;
+    // value blocks of 16 slots, 256 vb bytes each
     uint8_t *vbase = pg + 16 * kb * S;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int d = lane + 64 * half;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (int sl = 0; sl < S; ++sl) {
-            const int bit = sl * vb;
-            w[bit >> 5] |= uint32_t(vc[sl][d]) << (bit & 31);
-        }
-        uint8_t *dst = vbase + d * run;
-        if (run == 16) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-        else if (run == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-        else if (run == 4) *reinterpret_cast<uint32_t *>(dst) = w[0];
-        else *reinterpret_cast<uint16_t *>(dst) = uint16_t(w[0]);
+    for (int f = 0; f < S / 16; ++f) {
+        uint8_t *dst = vbase + 256 * vb * f + 4 * vb * lane;
+        if (vb == 8) pack_value_block<8>(dst, vc, f, rg, c);
+        else if (vb == 4) pack_value_block<4>(dst, vc, f, rg, c);
+        else if (vb == 2) pack_value_block<2>(dst, vc, f, rg, c);
+        else pack_value_block<1>(dst, vc, f, rg, c);
     }
     // code bytes past the values (16 S (kb + vb) is a multiple of 16), slots S..31's fields
     for (int k = S * (kb + vb) + lane; k < PARAM_OFF / 16; k += 64)

@@ -114,15 +114,13 @@ __device__ __forceinline__ uint2 codes4(uint32_t w, int b) {
 
 template <int N> using ic = std::integral_constant<int, N>;
 
-// For widths known at compile time, codes are converted two at a time: one shift and one
-// and-or turn two codes 16 bits apart into the fp16 pair (1024 + a, 1024 + b) (byte permutes
-// for 8 bits).  The k order of the matrix products follows the codes:
-// * key k-step ks takes channels key_chan(ks, 0..3) of the lane's 32, and the query operand is
-//   permuted the same way (once per tier);
-// * score row 4 g + r of a tile loads slot row_slot(g, r), so that each lane's four tokens
-//   pair up 16 bits apart in a 2- or 4-bit value channel's run; the other widths keep the
-//   natural order (slot 4 g + r), 8-bit codes going through byte permutes.
-// Width 0 (run-time widths) keeps the natural orders and converts code by code.
+// For widths known at compile time, codes are converted two at a time: one shift (or
+// rotation) and one and-or turn two codes 16 bits apart into an fp16 pair (byte permutes for
+// 8-bit codes).  Keys: k-step ks of the score product takes channels key_chan(ks, 0..3) of the
+// lane's 32, and the query operand is permuted the same way (once per tier).  Values: the page
+// stores each lane's codes in the operand order (channels 16 n + c, slots 4 g + r of a
+// 16-slot block, code (n, r) at bit 32 (n / p) + 16 (r % 2) + vb (2 (n % p) + r / 2), p = 8 / vb),
+// so one load per tile brings all of them.  Width 0 (run-time widths) converts code by code.
 template <int KB>
 __device__ __forceinline__ constexpr int key_chan(int ks, int e) {
     if constexpr (KB == 0 || KB == 8) {
@@ -131,26 +129,6 @@ __device__ __forceinline__ constexpr int key_chan(int ks, int e) {
         constexpr int n = 32 / KB, ppw = 16 / KB, hpw = 8 / KB;
         const int base = (ks / hpw) * n + 2 * (ks % hpw);
         return e == 0 ? base : e == 1 ? base + ppw : e == 2 ? base + 1 : base + 1 + ppw;
-    }
-}
-// 2- and 4-bit values: lane g's rows r = 0..3 are slots base + {0, P, 1, P + 1}, P = 16 / VB
-// (codes 16 bits apart in the run) with base = 2 g (VB 2) or 8 (g / 2) + 2 (g % 2) (VB 4:
-// the four slots share one 32-bit word)
-template <int VB>
-__device__ __forceinline__ constexpr bool paired() { return VB == 2 || VB == 4; }
-template <int VB>
-__device__ __forceinline__ int row_base(int g) {
-    if constexpr (VB == 4) return 8 * (g >> 1) + 2 * (g & 1);
-    else if constexpr (VB == 2) return 2 * g;
-    else return 4 * g;
-}
-template <int VB>
-__device__ __forceinline__ int row_slot(int g, int r) {
-    if constexpr (paired<VB>()) {
-        constexpr int P = 16 / VB;
-        return row_base<VB>(g) + (r == 1 ? P : r == 2 ? 1 : r == 3 ? P + 1 : 0);
-    } else {
-        return 4 * g + r;
     }
 }
 constexpr uint32_t MAGIC = 0x64006400u;   // fp16 1024 in both halves
@@ -176,16 +154,16 @@ __device__ __forceinline__ h4 key_op(const uint32_t (&w)[KB ? KB : 8], int ks, i
         return __builtin_bit_cast(h4, codes4(word >> ((4 * ks * kb_rt) & 31), kb_rt));
     }
 }
-// Value operands.  For 2- and 4-bit codes a rotation puts the lane's codes in the top bits of
-// the fp16 mantissa, 1024 + 2^(10-b) code, and the tier's value scales are multiplied by
+// Value operands.  For 1-, 2- and 4-bit codes a rotation puts a pair of codes in the top bits
+// of the fp16 mantissas, 1024 + 2^(10-b) code, and the tier's value scales are multiplied by
 // 2^-(10-b) (exact), so a product term is p s_v (2^b + code): the offset that the fp32 sums
-// cancel at the end (1024 per unit of the scaled p s_v) is 2^b code steps, not 1024.  Other
-// widths convert to 1024 + code and subtract 1024 in fp16 (exact): no offset at all.
+// cancel at the end (1024 per unit of the scaled p s_v) is 2^b code steps, not 1024.  8-bit
+// and run-time widths convert to 1024 + code and subtract 1024 in fp16 (exact): no offset.
 template <int VB>
-__device__ __forceinline__ constexpr bool val_offset() { return VB == 2 || VB == 4; }
+__device__ __forceinline__ constexpr bool val_offset() { return VB == 1 || VB == 2 || VB == 4; }
 template <int VB>
 __device__ __forceinline__ constexpr float val_scale() {
-    return VB == 4 ? 1.0f / 64.0f : VB == 2 ? 1.0f / 256.0f : 1.0f;
+    return VB == 4 ? 1.0f / 64.0f : VB == 2 ? 1.0f / 256.0f : VB == 1 ? 1.0f / 512.0f : 1.0f;
 }
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t minus1024(uint32_t x) {
@@ -195,44 +173,76 @@ __device__ __forceinline__ uint32_t minus1024(uint32_t x) {
 __device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n) {
     return __builtin_amdgcn_alignbit(x, x, n);
 }
-// the lane's four tokens (row_slot order) of one value channel, from the word of its run that
-// holds them: 2- and 4-bit codes rotated by rl / rh (the codes of rows 0, 1 / 2, 3 to the
-// mantissa's top bits), other widths shifted right by sh first
+// the lane's value words of one 16-slot block: VB of them (run-time widths: vb)
 template <int VB>
-__device__ __forceinline__ h4 val_op(uint32_t w, uint32_t rl, uint32_t rh, int sh, int vb_rt) {
-    if constexpr (VB == 4) {
-        return __builtin_bit_cast(h4, make_uint2((rotr(w, rl) & 0x03C003C0u) | MAGIC,
-                                                 (rotr(w, rh) & 0x03C003C0u) | MAGIC));
-    } else if constexpr (VB == 2) {
-        return __builtin_bit_cast(h4, make_uint2((rotr(w, rl) & 0x03000300u) | MAGIC,
-                                                 (rotr(w, rh) & 0x03000300u) | MAGIC));
+__device__ __forceinline__ void load_val_words(__amdgpu_buffer_rsrc_t rs, uint32_t o, int vb,
+                                               uint32_t (&w)[VB ? VB : 8]) {
+    load_codes32<VB>(rs, o, vb, w);   // 4 vb bytes, naturally aligned: the same shapes as keys
+}
+// rows r = 0..3 (slots 4 g + r) of channel 16 n + c as an h4 operand
+template <int VB>
+__device__ __forceinline__ h4 val_op(const uint32_t (&w)[VB ? VB : 8], int n, int vb_rt) {
+    if constexpr (VB == 1 || VB == 2 || VB == 4) {
+        constexpr int P = 8 / VB, T = 10 - VB;
+        constexpr uint32_t M = (((1u << VB) - 1u) << T) * 0x00010001u;
+        const uint32_t x = w[n / P];
+        const int s0 = VB * 2 * (n % P);
+        return __builtin_bit_cast(h4, make_uint2((rotr(x, uint32_t(s0 - T) & 31u) & M) | MAGIC,
+                                                 (rotr(x, uint32_t(s0 + VB - T) & 31u) & M) | MAGIC));
+    } else if constexpr (VB == 8) {
+        // bytes (r0, r2, r1, r3)
+        const uint32_t x = w[n];
+        return __builtin_bit_cast(h4, make_uint2(
+            minus1024(__builtin_amdgcn_perm(0x64646464u, x, 0x04020400u)),
+            minus1024(__builtin_amdgcn_perm(0x64646464u, x, 0x04030401u))));
     } else {
-        uint2 u;
-        if constexpr (VB == 8) {
-            u = make_uint2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u),
-                           __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
-        } else if constexpr (VB == 1) {
-            // bits 0..3 = rows 0..3; x | x << 15 moves bit 1 to bit 16
-            const uint32_t x = w >> sh, lo = x & 3u, hi = (x >> 2) & 3u;
-            u = make_uint2(((lo | (lo << 15)) & 0x00010001u) | MAGIC,
-                           ((hi | (hi << 15)) & 0x00010001u) | MAGIC);
-        } else {
-            u = codes4(w >> sh, vb_rt);
-        }
-        return __builtin_bit_cast(h4, make_uint2(minus1024(u.x), minus1024(u.y)));
+        const int vb = vb_rt, p = 8 / vb;
+        const uint32_t x = vb == 8 ? w[n] : vb == 4 ? w[n >> 1] : vb == 2 ? w[n >> 2] : w[0];
+        const int s0 = vb * 2 * (n % p);
+        const uint32_t m = (1u << vb) - 1u;
+        const uint32_t c0 = (x >> s0) & m, c2 = (x >> (s0 + vb)) & m;
+        const uint32_t c1 = (x >> (s0 + 16)) & m, c3 = (x >> (s0 + vb + 16)) & m;
+        return __builtin_bit_cast(h4, make_uint2(minus1024((c0 | 0x6400u) | ((c1 | 0x6400u) << 16)),
+                                                 minus1024((c2 | 0x6400u) | ((c3 | 0x6400u) << 16))));
     }
 }
 
 // one tile's raw operands: the key codes of row c's slot (the lane's 32 channels), the
-// parameters of the lane's four tokens (two slot pairs), and per channel 16 dt + c the word of
-// its run that holds those tokens' value codes
-template <int KB>
+// parameters of the lane's four tokens (slots 4 g .. 4 g + 3), and its value words
+template <int KB, int VB>
 struct Tile {
     uint32_t wk[KB ? KB : 8];
     uint4 pa, pb;
-    uint32_t wv[8];
+    uint32_t wv[VB ? VB : 8];
     int live;
 };
+
+// the four waves' partial results of one workgroup (split sp of head i) merged into the
+// default decode's partials: per query head the max m, the sum l and 128 output sums
+__device__ __forceinline__ void merge_waves(const float (*s_o)[16][D], const float (*s_m)[16],
+                                            const float (*s_l)[16], float *part, int i, int sp,
+                                            int S, int G) {
+    float *hp = part + int64_t(i) * S * G * PART_STRIDE;
+    for (int e = threadIdx.x; e < G * D; e += 64 * WAVES) {
+        const int gg = e / D, d = e - gg * D;
+        float M = M_INIT;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][gg]);
+        float Ls = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_m[w][gg] - M);
+            O += s_o[w][gg][d] * f;
+            Ls += s_l[w][gg] * f;
+        }
+        float *pp = hp + (int64_t(sp) * G + gg) * PART_STRIDE;
+        if (d == 0) {
+            pp[0] = M;
+            pp[1] = Ls;
+        }
+        pp[4 + d] = O;
+    }
+}
 
 // grid (S * B * Hkv), 256 threads; workgroup x: head x / S, split x % S.  KH, VH, KL, VL: the
 // scheme's bit widths when compiled for it (0: taken from the arguments at run time).
@@ -293,7 +303,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         if (ta >= tb) return;
         const int kb = KB ? KB : (HIGH ? kh : kl), vb = VB ? VB : (HIGH ? vh : vl);
         constexpr int Sp = HIGH ? HS : LS;
-        const int run = Sp * vb / 8;
         // 16x16x32 product m2: k-steps 2 m2 and 2 m2 + 1 of the key order
         h8 qop[4];
 #pragma unroll
@@ -303,65 +312,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
                 const int ch = key_chan<KB>(ks, e);
                 qop[ks >> 1][4 * (ks & 1) + e] = qn[ch >> 2][ch & 3];
             }
-        // value words: byte offset in the run (beyond the half-page's); rotations of 2- and
-        // 4-bit codes (rows 0, 1 and rows 2, 3 to the mantissa's top bits)
-        uint32_t voff = 0, rl = 0, rh = 0;
-        if constexpr (VB == 4) {
-            const uint32_t sh = 8 * (g & 1);   // slot 2 (g % 2) of the word at bit 8 (g % 2)
-            voff = 4 * (g >> 1);
-            rl = (sh - 6) & 31;
-            rh = (sh - 2) & 31;
-        } else if constexpr (VB == 2) {
-            const uint32_t sh = 4 * g;         // slot 2 g at bit 4 g
-            rl = (sh - 8) & 31;
-            rh = (sh - 6) & 31;
-        } else if constexpr (VB == 8) {
-            voff = 4 * g;
-        }
-        const int krow = row_slot<VB>(c >> 2, c & 3);
-        auto load = [&](Tile<KB> &r, int t) {
+        auto load = [&](Tile<KB, VB> &r, int t) {
             const int page = HIGH ? row[t] : row[C - 1 - (t >> 1)];
-            const uint32_t slot0 = HIGH ? 0u : 16u * uint32_t(t & 1);
+            const uint32_t f = HIGH ? 0u : uint32_t(t & 1);     // 16-slot block of the page
             r.live = min(16, (HIGH ? nh : nl) - 16 * t);
             const __amdgpu_buffer_rsrc_t rs = page_rsrc(pages + int64_t(page) * PAGE);
-            load_codes32<KB>(rs, 16 * kb * (slot0 + krow) + 4 * g * kb, kb, r.wk);
-            // parameter pairs: slots (sa, sa + 1) and (sb, sb + 1)
-            const uint32_t sa = slot0 + row_base<VB>(g);
-            const uint32_t sb = sa + (paired<VB>() ? 16 / (VB ? VB : 1) : 2);
-            r.pa = ld16(rs, PARAM_OFF + 8 * sa);
-            r.pb = ld16(rs, PARAM_OFF + 8 * sb);
-            // offset of the tile's codes in a run: slot0 vb / 8 bytes (whole words for the
-            // compiled widths; 1-bit and run-time widths read the word holding bit slot0 vb)
-            uint32_t off = 16 * kb * Sp + c * run + voff;
-            if constexpr (VB == 4 || VB == 2 || VB == 8) off += slot0 * VB / 8;
-            else off += 4 * (((slot0 + 4 * g) * vb) >> 5);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const uint32_t o = off + 16 * dt * run;
-                if constexpr (VB == 1 || VB == 0) {
-                    // a 2-byte run (16 one-bit codes) is read as such
-                    r.wv[dt] = run == 2 ? ld2(rs, o) : ld4(rs, o);
-                } else {
-                    r.wv[dt] = ld4(rs, o);
-                }
-            }
+            load_codes32<KB>(rs, 16 * kb * (16 * f + c) + 4 * g * kb, kb, r.wk);
+            r.pa = ld16(rs, PARAM_OFF + 8 * (16 * f + 4 * g));
+            r.pb = ld16(rs, PARAM_OFF + 8 * (16 * f + 4 * g + 2));
+            load_val_words<VB>(rs, 16 * kb * Sp + 256 * vb * f + 4 * vb * lane, vb, r.wv);
         };
-        auto compute = [&](const Tile<KB> &r, int t) {
+        auto compute = [&](const Tile<KB, VB> &r, int t) {
             f4 acc = f4{acc0, acc0, acc0, acc0};
 #pragma unroll
             for (int m2 = 0; m2 < 4; ++m2)
                 acc = mfma(cat(key_op<KB>(r.wk, 2 * m2, kb), key_op<KB>(r.wk, 2 * m2 + 1, kb)),
                            qop[m2], acc);
-            // rows' parameters: paired orders are {sa, sb, sa + 1, sb + 1}, the natural order
-            // {sa, sa + 1, sb, sb + 1}
-            uint2 par[4];
-            if constexpr (paired<VB>()) {
-                par[0] = make_uint2(r.pa.x, r.pa.y); par[1] = make_uint2(r.pb.x, r.pb.y);
-                par[2] = make_uint2(r.pa.z, r.pa.w); par[3] = make_uint2(r.pb.z, r.pb.w);
-            } else {
-                par[0] = make_uint2(r.pa.x, r.pa.y); par[1] = make_uint2(r.pa.z, r.pa.w);
-                par[2] = make_uint2(r.pb.x, r.pb.y); par[3] = make_uint2(r.pb.z, r.pb.w);
-            }
+            const uint2 par[4] = {make_uint2(r.pa.x, r.pa.y), make_uint2(r.pa.z, r.pa.w),
+                                  make_uint2(r.pb.x, r.pb.y), make_uint2(r.pb.z, r.pb.w)};
             float x[4], vs[4], vz[4];
             float mx = -__builtin_inff();
 #pragma unroll
@@ -371,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
                 vs[q4] = h2f(uint16_t(par[q4].y & 0xffffu)) * val_scale<VB>();
                 vz[q4] = h2f(uint16_t(par[q4].y >> 16));
                 const float xv = (ksc * acc[q4] + kz * sumq) * scale_log2;
-                x[q4] = row_slot<VB>(g, q4) < r.live ? xv : -__builtin_inff();
+                x[q4] = 4 * g + q4 < r.live ? xv : -__builtin_inff();
                 mx = fmaxf(mx, x[q4]);
             }
             mx = fmaxf(max_col(mx), M_INIT);
@@ -404,19 +372,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             // k = 8 g + e: the lane's four tokens with P' = p s_v's fp16 high parts (e < 4),
             // then the same tokens with its low parts (e >= 4)
             const h8 bp = h8{hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]};
-            // 1-bit and run-time widths: the tokens' first bit within the word
-            const int sh = (VB == 4 || VB == 2 || VB == 8)
-                               ? 0 : ((((HIGH ? 0 : 16 * (t & 1)) + 4 * g) * vb) & 31);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                const h4 a = val_op<VB>(r.wv[dt], rl, rh, sh, vb);
+                const h4 a = val_op<VB>(r.wv, dt, vb);
                 o[dt] = mfma(cat(a, a), bp, o[dt]);
             }
         };
         // past the tier's last tile the loads repeat it (cache hits), which keeps the loop
         // free of branches around loads and of register copies
         const int tl = tb - 1;
-        Tile<KB> ra, rb;
+        Tile<KB, VB> ra, rb;
         load(ra, ta);
         for (int t = ta;;) {
             load(rb, min(t + 1, tl));
@@ -446,26 +411,250 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         s_l[wave][c] = l;
     }
     __syncthreads();
-    float *hp = part + int64_t(i) * S * G * PART_STRIDE;
-    for (int e = threadIdx.x; e < G * D; e += 64 * WAVES) {
-        const int gg = e / D, d = e - gg * D;
-        float M = M_INIT;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][gg]);
-        float Ls = 0.f, O = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float f = __builtin_amdgcn_exp2f(s_m[w][gg] - M);
-            O += s_o[w][gg][d] * f;
-            Ls += s_l[w][gg] * f;
+    merge_waves(s_o, s_m, s_l, part, i, sp, S, G);
+}
+
+
+// Two tiles per pass (query groups of at most 8 heads).  Tile A's scores fill columns 0..7 of
+// the score product and tile B's columns 8..15 (query operands qa, qb: the lane's head in
+// its half, zero in the other), so every lane's softmax work is useful: lane (c, g) scores
+// tokens 4 g + r of tile (c < 8 ? A : B) for query head c % 8, and columns c and c ^ 8 share
+// one running max.  O = P . V: A = P with rows c < 8 tile A's heads and c >= 8 tile B's
+// (k = 8 g + e: tile A's tokens 4 g + e, then tile B's, the other tile's half zero), B = the
+// value codes of channel 16 n + c (tile A's four tokens, then tile B's); rows h and h + 8 of
+// O add up at the end.
+template <int KB, int VB>
+struct PairTiles {
+    uint32_t wka[KB ? KB : 8], wkb[KB ? KB : 8];
+    uint32_t wva[VB ? VB : 8], wvb[VB ? VB : 8];
+    uint4 pa, pb;        // the lane's own tile's parameters (slots 4 g .. 4 g + 3)
+    int live;            // the lane's own tile's live tokens
+};
+
+template <int KH, int VH, int KL, int VL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_pair_kernel(
+    const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
+    const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
+    int C, int S, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
+    const int kh = KH ? KH : kh_rt, vh = VH ? VH : vh_rt, kl = KL ? KL : kl_rt,
+              vl = VL ? VL : vl_rt;
+    __shared__ float s_o[WAVES][16][D];
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+    __shared__ uint4 s_q[2][2][4][64];     // [tier: HIGH, LOW][tile A, B][product][lane]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, g = lane >> 4, hc = c & 7;
+    const bool own_b = c >= 8;
+    const int i = blockIdx.x / S, sp = blockIdx.x - i * S;
+    const int b = i / Hkv, h = i - b * Hkv;
+    const int Hq = Hkv * G;
+    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
+    const int T = qH + tL;
+    const int cc = sp * WAVES + wave, NC = S * WAVES;
+    const int t0 = int(int64_t(T) * cc / NC), t1 = int(int64_t(T) * (cc + 1) / NC);
+    const int32_t *row = rows_l + int64_t(i) * C;
+
+    // query head hc's channels 32 g .. 32 g + 31 (zero beyond G); wave 0 stores both tiers'
+    // operands in their key orders
+    float sumq = 0.f;
+    {
+        uint4 u[4] = {};
+        if (hc < G) {
+            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (int64_t(b) * Hq + h * G + hc) * D + 32 * g);
+            u[0] = qp[0]; u[1] = qp[1]; u[2] = qp[2]; u[3] = qp[3];
         }
-        float *pp = hp + (int64_t(sp) * G + gg) * PART_STRIDE;
-        if (d == 0) {
-            pp[0] = M;
-            pp[1] = Ls;
+        h4 qn[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qn[2 * j] = __builtin_bit_cast(h4, make_uint2(u[j].x, u[j].y));
+            qn[2 * j + 1] = __builtin_bit_cast(h4, make_uint2(u[j].z, u[j].w));
         }
-        pp[4 + d] = O;
+#pragma unroll
+        for (int p = 0; p < 32; ++p) sumq += float(qn[p >> 2][p & 3]);
+        sumq += __shfl_xor(sumq, 16, 64);
+        sumq += __shfl_xor(sumq, 32, 64);
+        if (wave == 0) {
+            auto store = [&](int tier, auto kbc) {
+                constexpr int KB = decltype(kbc)::value;
+#pragma unroll
+                for (int m2 = 0; m2 < 4; ++m2) {
+                    h8 v;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int ch = key_chan<KB>(2 * m2 + (e >> 2), e & 3);
+                        v[e] = qn[ch >> 2][ch & 3];
+                    }
+                    const uint4 w = __builtin_bit_cast(uint4, v);
+                    s_q[tier][0][m2][lane] = own_b ? make_uint4(0, 0, 0, 0) : w;
+                    s_q[tier][1][m2][lane] = own_b ? w : make_uint4(0, 0, 0, 0);
+                }
+            };
+            store(0, ic<KH>{});
+            store(1, ic<KL>{});
+        }
     }
+    __syncthreads();
+    const float acc0 = -CODE_OFF * sumq;
+    f4 o[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = M_INIT, l = 0.f, lz = 0.f, lp = 0.f;
+
+    // tile pairs (t, t + 1) of tiles [ta, tb) of one tier; a missing tile B repeats tile A's
+    // loads with no live token
+    auto run_tier = [&](int ta, int tb, auto highc, auto kbc, auto vbc) {
+        constexpr bool HIGH = decltype(highc)::value;
+        constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
+        constexpr int TIER = HIGH ? 0 : 1;
+        if (ta >= tb) return;
+        const int kb = KB ? KB : (HIGH ? kh : kl), vb = VB ? VB : (HIGH ? vh : vl);
+        constexpr int Sp = HIGH ? HS : LS;
+        const int nt = HIGH ? nh : nl;
+        auto page_of = [&](int t) -> const uint8_t * {
+            return pages + int64_t(HIGH ? row[t] : row[C - 1 - (t >> 1)]) * PAGE;
+        };
+        auto block_of = [&](int t) -> uint32_t { return HIGH ? 0u : uint32_t(t & 1); };
+        auto load = [&](PairTiles<KB, VB> &r, int t) {
+            const int tbb = t + 1 < tb ? t + 1 : t;
+            const uint8_t *pga = page_of(t), *pgb = page_of(tbb);
+            const uint32_t fa = block_of(t), fb = block_of(tbb);
+            const __amdgpu_buffer_rsrc_t ra = page_rsrc(pga), rb = page_rsrc(pgb);
+            load_codes32<KB>(ra, 16 * kb * (16 * fa + c) + 4 * g * kb, kb, r.wka);
+            load_codes32<KB>(rb, 16 * kb * (16 * fb + c) + 4 * g * kb, kb, r.wkb);
+            const uint32_t vo = 16 * kb * Sp + 4 * vb * lane;
+            load_val_words<VB>(ra, vo + 256 * vb * fa, vb, r.wva);
+            load_val_words<VB>(rb, vo + 256 * vb * fb, vb, r.wvb);
+            // the lane's own tile's parameters, read by per-lane address (a buffer descriptor
+            // chosen per lane would make the compiler serialize the load over both pages)
+            const uint8_t *own = own_b ? pgb : pga;
+            const uint4 *op = reinterpret_cast<const uint4 *>(
+                own + PARAM_OFF + 8 * (16 * (own_b ? fb : fa) + 4 * g));
+            r.pa = op[0];
+            r.pb = op[1];
+            const int tl = own_b ? (t + 1 < tb ? t + 1 : -1) : t;
+            r.live = tl < 0 ? 0 : min(16, nt - 16 * tl);
+        };
+        auto compute = [&](const PairTiles<KB, VB> &r) {
+            // an opaque lane index keeps the compiler from hoisting the query reads out of the
+            // loop (which would pin 32 registers)
+            int li = lane;
+            asm volatile("" : "+v"(li));
+            f4 acc = f4{acc0, acc0, acc0, acc0};
+#pragma unroll
+            for (int m2 = 0; m2 < 4; ++m2) {
+                const h8 qa = __builtin_bit_cast(h8, s_q[TIER][0][m2][li]);
+                const h8 qb = __builtin_bit_cast(h8, s_q[TIER][1][m2][li]);
+                acc = mfma(cat(key_op<KB>(r.wka, 2 * m2, kb), key_op<KB>(r.wka, 2 * m2 + 1, kb)), qa, acc);
+                acc = mfma(cat(key_op<KB>(r.wkb, 2 * m2, kb), key_op<KB>(r.wkb, 2 * m2 + 1, kb)), qb, acc);
+            }
+            const uint2 par[4] = {make_uint2(r.pa.x, r.pa.y), make_uint2(r.pa.z, r.pa.w),
+                                  make_uint2(r.pb.x, r.pb.y), make_uint2(r.pb.z, r.pb.w)};
+            float x[4], vs[4], vz[4];
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu));
+                const float kz = h2f(uint16_t(par[q4].x >> 16));
+                vs[q4] = h2f(uint16_t(par[q4].y & 0xffffu)) * val_scale<VB>();
+                vz[q4] = h2f(uint16_t(par[q4].y >> 16));
+                const float xv = (ksc * acc[q4] + kz * sumq) * scale_log2;
+                x[q4] = 4 * g + q4 < r.live ? xv : -__builtin_inff();
+                mx = fmaxf(mx, x[q4]);
+            }
+            mx = max_col(mx);
+            mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xf,
+                                                                   0xf, false)));   // row_ror:8
+            mx = fmaxf(mx, M_INIT);
+            int one = 1;
+            asm volatile("" : "+v"(one));
+            if (one && __ballot(mx > m + MARGIN) != 0ull) {
+                const float mn = fmaxf(m, mx);
+                const float corr = __builtin_amdgcn_exp2f(m - mn);
+                m = mn;
+                l *= corr;
+                lz *= corr;
+                lp *= corr;
+                // O's row 4 g + r holds query head (4 g + r) % 8: its factor from that column
+                float cr[4];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) cr[r4] = __shfl(corr, (4 * g + r4) & 7, 64);
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) o[n][r4] *= cr[r4];
+            }
+            _Float16 hi[4], lo[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float p = __builtin_amdgcn_exp2f(x[q4] - m);
+                const float pv = p * vs[q4];
+                hi[q4] = _Float16(pv);
+                lo[q4] = _Float16(pv - float(hi[q4]));
+                l += p;
+                lz += p * vz[q4];
+                if constexpr (val_offset<VB>()) lp += pv;
+            }
+            const h4 z4 = h4{0, 0, 0, 0};
+            const h4 ph = h4{hi[0], hi[1], hi[2], hi[3]}, pl = h4{lo[0], lo[1], lo[2], lo[3]};
+            const h8 ah = own_b ? cat(z4, ph) : cat(ph, z4);
+            const h8 al = own_b ? cat(z4, pl) : cat(pl, z4);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const h8 bv = cat(val_op<VB>(r.wva, n, vb), val_op<VB>(r.wvb, n, vb));
+                o[n] = mfma(ah, bv, o[n]);
+                o[n] = mfma(al, bv, o[n]);
+            }
+        };
+        // past the last pair the loads repeat it (cache hits): no branch around a load
+        const int tlast = ta + ((tb - 1 - ta) & ~1);
+        PairTiles<KB, VB> ra, rb;
+        load(ra, ta);
+        for (int t = ta;;) {
+            load(rb, min(t + 2, tlast));
+            compute(ra);
+            t += 2;
+            if (t >= tb) break;
+            load(ra, min(t + 2, tlast));
+            compute(rb);
+            t += 2;
+            if (t >= tb) break;
+        }
+    };
+    run_tier(t0, min(t1, qH), ic<1>{}, ic<KH>{}, ic<VH>{});
+    run_tier(max(t0, qH) - qH, t1 - qH, ic<0>{}, ic<KL>{}, ic<VL>{});
+
+    // per query head: sums over the lane groups and the two column halves; O rows h and h + 8
+    // (tile A's and tile B's parts of head h) added across the wave's halves
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    l += __shfl_xor(l, 8, 64);
+    lz += __shfl_xor(lz, 16, 64);
+    lz += __shfl_xor(lz, 32, 64);
+    lz += __shfl_xor(lz, 8, 64);
+    lp += __shfl_xor(lp, 16, 64);
+    lp += __shfl_xor(lp, 32, 64);
+    lp += __shfl_xor(lp, 8, 64);
+    // per row head (4 g + r) % 8: its sums from that column
+    float lzr[4], lpr[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        lzr[r4] = __shfl(lz, (4 * g + r4) & 7, 64);
+        lpr[r4] = __shfl(lp, (4 * g + r4) & 7, 64);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float other = __shfl_xor(o[n][r4], 32, 64);   // rows 4 g + r + 8
+            if (g < 2) s_o[wave][4 * g + r4][16 * n + c] = o[n][r4] + other - CODE_OFF * lpr[r4] + lzr[r4];
+        }
+    if (g == 0 && c < 8) {
+        s_m[wave][c] = m;
+        s_l[wave][c] = l;
+    }
+    __syncthreads();
+    merge_waves(s_o, s_m, s_l, part, i, sp, S, G);
 }
 
 }  // namespace sch
@@ -500,18 +689,24 @@ extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_sc
     hipStream_t s = (hipStream_t)stream;
     // the schemes the pages compare are compiled with their widths; others run the generic
     // instance
-    auto kern = sch::scheme_decode_kernel<0, 0, 0, 0>;
     const int key = sc->k_bits_high * 1000 + sc->v_bits_high * 100 + sc->k_bits_low * 10 +
                     sc->v_bits_low;
+    // query groups of up to 8 heads take two tiles per pass
+    auto kern = G <= 8 ? sch::scheme_pair_kernel<0, 0, 0, 0> : sch::scheme_decode_kernel<0, 0, 0, 0>;
+#define KVC_SCHEME_CASE(k, a, b, c2, d)                                                      \
+    case k:                                                                                  \
+        kern = G <= 8 ? sch::scheme_pair_kernel<a, b, c2, d> : sch::scheme_decode_kernel<a, b, c2, d>; \
+        break;
     switch (key) {
-        case 8442: kern = sch::scheme_decode_kernel<8, 4, 4, 2>; break;
-        case 4824: kern = sch::scheme_decode_kernel<4, 8, 2, 4>; break;
-        case 8241: kern = sch::scheme_decode_kernel<8, 2, 4, 1>; break;
-        case 4241: kern = sch::scheme_decode_kernel<4, 2, 4, 1>; break;
-        case 8441: kern = sch::scheme_decode_kernel<8, 4, 4, 1>; break;
-        case 8424: kern = sch::scheme_decode_kernel<8, 4, 2, 4>; break;
+        KVC_SCHEME_CASE(8442, 8, 4, 4, 2)
+        KVC_SCHEME_CASE(4824, 4, 8, 2, 4)
+        KVC_SCHEME_CASE(8241, 8, 2, 4, 1)
+        KVC_SCHEME_CASE(4241, 4, 2, 4, 1)
+        KVC_SCHEME_CASE(8441, 8, 4, 4, 1)
+        KVC_SCHEME_CASE(8424, 8, 4, 2, 4)
         default: break;
     }
+#undef KVC_SCHEME_CASE
     hipLaunchKernelGGL(kern, dim3(L.splits * nheads), dim3(256), 0, s, q,
                        softmax_scale * sch::LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
                        sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, part);

@@ -10,14 +10,19 @@ Readings taken: a scheme gives each tier its own key and value bit widths (1, 2,
 quantized with the same per-token min/max quantizer as K8V4/K4V2 (``quant.py``) at 2^b - 1
 levels.  Pages keep their geometry (3456 bytes; 16 HIGH or 32 LOW slots, so allocation is
 unchanged); a tier's format must fit its slots into the first 3072 bytes:
-slots * 16 * (kb + vb) <= 3072.  The page layout of these variants (this project's own):
-keys slot-major, slot s's 128 codes at bytes [16 kb s, 16 kb (s + 1)), code i at bits
-[i kb, (i + 1) kb); then values channel-major from byte 16 kb S (S = 16 or 32 slots): channel
-d's S codes at bytes [16 kb S + d S vb / 8, ...), slot s's code at bits [s vb, (s + 1) vb) of
-that run; bits are counted little-endian from a field's first byte; the bytes after the values
-up to 3072 are zero; parameters (k scale, k zero, v scale, v zero as fp16) at 3072 + 8 s and
-positions (int32, -1 when empty) at 3328 + 4 s for all 32 slot indices, as in the K8V4/K4V2
-layout.
+slots * 16 * (kb + vb) <= 3072.  The page layout of these variants (this project's own, with
+bits counted little-endian from a field's first byte):
+* keys slot-major: slot s's 128 codes at bytes [16 kb s, 16 kb (s + 1)), code i at bits
+  [i kb, (i + 1) kb);
+* values from byte 16 kb S (S = 16 or 32 slots) in blocks of 16 slots (a HIGH page has one,
+  a LOW page two), 256 vb bytes each, in the decode's operand order: block f's bytes
+  [4 vb L, 4 vb (L + 1)) (L = 16 g + c, g < 4, c < 16) hold the codes of channels 16 n + c
+  (n < 8) for slots 16 f + 4 g + r (r < 4); with p = 8 / vb channels-groups per 32-bit word,
+  code (n, r) sits at bit 32 (n // p) + 16 (r % 2) + vb (2 (n % p) + r // 2) of that range
+  (each pair of codes that the decode converts together lies 16 bits apart in one word);
+* the bytes after the values up to 3072 are zero; parameters (k scale, k zero, v scale,
+  v zero as fp16) at 3072 + 8 s and positions (int32, -1 when empty) at 3328 + 4 s for all 32
+  slot indices, as in the K8V4/K4V2 layout.
 """
 import numpy as np
 
@@ -75,6 +80,39 @@ def unpack_codes(data, b, n=D):
     return (bits * (1 << np.arange(b))).sum(-1).astype(np.uint8)
 
 
+def value_bit(vb, s, d):
+    """Bit index, from the start of the value region, of slot s's code for channel d."""
+    f, g, r = s // 16, (s % 16) // 4, s % 4
+    n, c = d // 16, d % 16
+    p = 8 // vb
+    lane = 16 * g + c
+    return 8 * (256 * vb * f + 4 * vb * lane) + 32 * (n // p) + 16 * (r % 2) + vb * (2 * (n % p) + r // 2)
+
+
+def pack_values(v_codes, vb):
+    """v_codes uint8 [S][128] (S = 16 or 32) -> the value region's bytes [16 vb S]."""
+    S = v_codes.shape[0]
+    bits = np.zeros(16 * vb * S * 8, np.uint8)
+    for s in range(S):
+        for d in range(D):
+            b0 = value_bit(vb, s, d)
+            code = int(v_codes[s, d])
+            for k in range(vb):
+                bits[b0 + k] = (code >> k) & 1
+    return (bits.reshape(-1, 8).astype(np.int64) << np.arange(8)).sum(1).astype(np.uint8)
+
+
+def unpack_values(data, vb, S):
+    """Inverse of pack_values: bytes [16 vb S] -> uint8 [S][128]."""
+    bits = ((np.asarray(data, np.int64)[:, None] >> np.arange(8)) & 1).reshape(-1)
+    out = np.zeros((S, D), np.uint8)
+    for s in range(S):
+        for d in range(D):
+            b0 = value_bit(vb, s, d)
+            out[s, d] = int((bits[b0:b0 + vb] << np.arange(vb)).sum())
+    return out
+
+
 def build_page(scheme, tier, k_codes, v_codes, k_scale, k_zero, v_scale, v_zero, pos):
     """Page image (uint8 [3456]) of m live tokens in slots 0..m-1 of a scheme's tier."""
     kb, vb = scheme.bits[tier]
@@ -87,9 +125,7 @@ def build_page(scheme, tier, k_codes, v_codes, k_scale, k_zero, v_scale, v_zero,
     vs_all = np.zeros((S, D), np.uint8)
     vs_all[:m] = np.asarray(v_codes, np.uint8)[:m]
     v0 = 16 * kb * S
-    run = S * vb // 8
-    for d in range(D):
-        page[v0 + d * run:v0 + (d + 1) * run] = pack_codes(vs_all[:, d], vb)
+    page[v0:v0 + 16 * vb * S] = pack_values(vs_all, vb)
     params = np.zeros((32, 4), np.float16)
     params[:m, 0] = k_scale
     params[:m, 1] = k_zero
@@ -110,9 +146,7 @@ def read_page(page, scheme, tier, m):
     k = np.stack([unpack_codes(page[16 * kb * s:16 * kb * (s + 1)], kb) for s in range(m)]) \
         if m else np.zeros((0, D), np.uint8)
     v0 = 16 * kb * S
-    run = S * vb // 8
-    cols = np.stack([unpack_codes(page[v0 + d * run:v0 + (d + 1) * run], vb, S) for d in range(D)])
-    v = cols.T[:m].astype(np.uint8)
+    v = unpack_values(page[v0:v0 + 16 * vb * S], vb, S)[:m]
     params = page[PARAM_OFF:POS_OFF].copy().view(np.float16).reshape(32, 4)[:m]
     pos = page[POS_OFF:PAGE_BYTES].copy().view(np.int32)[:m]
     return k, v, params[:, 0], params[:, 1], params[:, 2], params[:, 3], pos

@@ -52,8 +52,8 @@ def test_page_bit_coverage(high, low):
 
 def test_hand_placed_fields():
     # K4V2 in a LOW page (32 slots): slot 1's key code 3 sits at byte 64 (16 * 4 * 1), low
-    # nibble; its value code for channel 5 sits in channel 5's run (32 slots * 2 bits = 8
-    # bytes, from byte 16 * 4 * 32 = 2048 + 40) at bits 2..3
+    # nibble.  Its value code for channel 5 (block 0, g = 0, r = 1, n = 0, c = 5: lane 5's
+    # 8 bytes from 2048 + 40, bit 16 (r odd) + 0) is at byte 2048 + 42, bits 0..1
     sc = osch.Scheme.named("K8V4", "K4V2")
     k = np.zeros((2, 128), np.uint8)
     v = np.zeros((2, 128), np.uint8)
@@ -61,15 +61,33 @@ def test_hand_placed_fields():
     v[1, 5] = 2
     z = np.zeros(2, np.float16)
     page = osch.build_page(sc, osch.LOW, k, v, z, z, z, z, [7, 9])
-    assert page[64] == 3 and page[2048 + 40] == 2 << 2
+    assert page[64] == 3 and page[2048 + 42] == 2
     assert np.count_nonzero(page[:osch.CODE_BYTES]) == 2
-    # K8V4 in a HIGH page: channel 0's run of 16 slots x 4 bits is bytes 2048 .. 2055
+    # K8V4 in a HIGH page: slot 15 = g 3, r 3; channel 0 = n 0, c 0: lane 48's 16 bytes from
+    # 2048 + 768; r = 3 puts the code at bit 16 + 4 = 20: byte 770, high nibble
     k2 = np.zeros((16, 128), np.uint8)
     v2 = np.zeros((16, 128), np.uint8)
     v2[15, 0] = 0xF
     z2 = np.zeros(16, np.float16)
     page = osch.build_page(sc, osch.HIGH, k2, v2, z2, z2, z2, z2, np.arange(16))
-    assert page[2048 + 7] == 0xF0 and np.count_nonzero(page[:osch.CODE_BYTES]) == 1
+    assert page[2048 + 770] == 0xF0 and np.count_nonzero(page[:osch.CODE_BYTES]) == 1
+    # K4V8 in a HIGH page: an 8-bit code sits in one byte; slot 6 = g 1, r 2 of channel 37
+    # (n 2, c 5): lane 21's 32 bytes from 16 * 4 * 16 + 32 * 21 = 1696, word 2, bit 8: byte 1705
+    sc8 = osch.Scheme.named("K4V8", "K2V4")
+    v3 = np.zeros((16, 128), np.uint8)
+    v3[6, 37] = 0xA5
+    page = osch.build_page(sc8, osch.HIGH, k2, v3, z2, z2, z2, z2, np.arange(16))
+    assert page[1705] == 0xA5 and np.count_nonzero(page[:osch.CODE_BYTES]) == 1
+
+
+def test_value_bits_are_a_bijection():
+    # every (slot, channel) code of every width lands on its own vb bits inside the region
+    for vb in (1, 2, 4, 8):
+        for S in (16, 32):
+            if 16 * vb * S > osch.CODE_BYTES:
+                continue
+            starts = sorted(osch.value_bit(vb, s, d) for s in range(S) for d in range(128))
+            assert starts == list(range(0, 16 * vb * S * 8, vb))
 
 
 def test_capacity_rule():
