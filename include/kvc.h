@@ -228,11 +228,17 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
  * K8V4-K4V2 / K8V4-Prune configurations).  Same contract as kvc_quantize_and_place in prompt
  * mode (same ranks, pages and slots; the K8V4-Prune and no-prune configurations are threshold
  * settings of kvc_score_tokens), but each tier is quantized at the scheme's bit widths with the
- * same per-token min/max quantizer (2^b - 1 levels) and written in the slot-major page layout:
- * slot s at bytes [s * 16 (k + v), (s + 1) * 16 (k + v)), first its 128 key codes, then its 128
- * value codes, code i at bits [i b, (i + 1) b) little-endian from the field's first byte; the
- * bytes after the last slot up to 3072 are zero; parameters and positions as in the default
- * layout.  Pages written this way are read by kvc_paged_decode_attention_scheme only.
+ * same per-token min/max quantizer (2^b - 1 levels) and written in this layout (bits counted
+ * little-endian from a field's first byte; S = 16 slots for HIGH, 32 for LOW):
+ *   keys, slot-major: slot s's 128 codes at bytes [16 kb s, 16 kb (s + 1)), code i at bits
+ *     [i kb, (i + 1) kb);
+ *   values from byte 16 kb S in blocks of 16 slots (S / 16 of them), 256 vb bytes each, in the
+ *     decode's operand order: bytes [4 vb L, 4 vb (L + 1)) of block f, L = 16 g + c (g < 4,
+ *     c < 16), hold the codes of channels 16 n + c (n < 8) for slots 16 f + 4 g + r (r < 4),
+ *     code (n, r) at bit 32 (n / p) + 16 (r % 2) + vb (2 (n % p) + r / 2), p = 8 / vb;
+ *   the bytes after the values up to 3072 are zero; parameters and positions as in the
+ *   default layout.
+ * Pages written this way are read by kvc_paged_decode_attention_scheme only.
  *   workspace >= kvc_workspace_bytes(geom, KVC_OP_QUANTIZE, max_seqlen)
  * Errors: as kvc_quantize_and_place, and KVC_E_SHAPE for a scheme that does not fit. */
 int kvc_quantize_and_place_scheme(const kvc_geom *geom, const kvc_scheme *scheme, int32_t layer,
