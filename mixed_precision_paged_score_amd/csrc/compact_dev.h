@@ -1,0 +1,124 @@
+// Per-head pieces of the page allocation round (kvc_compact_pages), shared by the allocation
+// kernels and the generation step's fused kernels.
+#pragma once
+
+#include "kvc_internal.h"
+#include "workspace.h"
+
+namespace kvc {
+
+struct HeadDemand {
+    int pH, pL, qH, qL, alloc, free, rebuilt, err;
+};
+
+__device__ __forceinline__ HeadDemand head_demand(const int32_t *count_l,
+                                                  const int32_t *new_count,
+                                                  const uint8_t *changed, int i, int C) {
+    HeadDemand d;
+    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int mh = new_count[2 * i], ml = new_count[2 * i + 1];
+    d.pH = ceil_div(nh, HS);
+    d.pL = ceil_div(nl, LS);
+    d.qH = ceil_div(mh, HS);
+    d.qL = ceil_div(ml, LS);
+    d.rebuilt = changed == nullptr || changed[i] != 0;
+    d.err = 0;
+    if (d.rebuilt) {
+        d.alloc = d.qH + d.qL;
+        d.free = d.pH + d.pL;
+    } else {
+        if (d.qH < d.pH || d.qL < d.pL) d.err |= KVC_DEV_SHRINK;
+        d.alloc = max(d.qH - d.pH, 0) + max(d.qL - d.pL, 0);
+        d.free = 0;
+    }
+    if (d.qH + d.qL > C || mh < 0 || ml < 0) d.err |= KVC_DEV_ROW_OVERFLOW;
+    if (d.err) d.alloc = d.free = 0;   // keep sums in range; the call fails anyway
+    return d;
+}
+
+// inclusive block scan of two ints over 256 threads (4 wave64s): wave scans by shuffles,
+// then a scan of the 4 wave totals in LDS
+__device__ __forceinline__ void block_scan2(int &a, int &f, int *s_wa, int *s_wf) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int ua = __shfl_up(a, o, 64), uf = __shfl_up(f, o, 64);
+        if (lane >= o) {
+            a += ua;
+            f += uf;
+        }
+    }
+    if (lane == 63) {
+        s_wa[wave] = a;
+        s_wf[wave] = f;
+    }
+    __syncthreads();
+    int pa = 0, pf = 0;
+    for (int w = 0; w < wave; ++w) {
+        pa += s_wa[w];
+        pf += s_wf[w];
+    }
+    a += pa;
+    f += pf;
+}
+
+// Head i's commit by one workgroup (all its threads call it): snapshot the old row and counts
+// when asked, then, if the round commits (pool status clear at entry, no head overflowed or
+// shrank, the total demand fits the free pages), return the rebuilt head's old pages to the
+// ring's tail, take its new pages from the ring's head (off[i] / foff[i] into the round's
+// regions), rewrite its row, the reverse map and its counts; head 0 moves the ring counters.
+// Returns whether the round committed (the same answer in every workgroup).
+__device__ __forceinline__ bool commit_head(
+    int i, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C, int64_t P,
+    int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
+    int32_t *__restrict__ owner, const CompactHdr *hdr, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ foff, int32_t *__restrict__ old_rows,
+    int32_t *__restrict__ old_count) {
+    if (hdr->entry_status != 0) return false;          // sticky failure: no-op
+    int32_t *row = rows_l + int64_t(i) * C;
+    if (old_rows)
+        for (int p = threadIdx.x; p < C; p += blockDim.x) old_rows[int64_t(i) * C + p] = row[p];
+    if (old_count && threadIdx.x < 2) old_count[2 * i + threadIdx.x] = count_l[2 * i + threadIdx.x];
+    const uint64_t head0 = hdr->head0, tail0 = hdr->tail0;
+    uint32_t err = hdr->err;
+    if (uint64_t(hdr->total_alloc) > tail0 - head0) err |= KVC_DEV_POOL_EXHAUSTED;
+    if (err) {
+        if (i == 0 && threadIdx.x == 0) atomicOr(status, int(err));
+        return false;
+    }
+    const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
+    __syncthreads();   // every thread has read the old counts and row before they change
+    const int gid = layer_gid0 + i;
+    if (d.rebuilt) {
+        // return the old pages to the ring's tail: HIGH in row order, then LOW from the end
+        const int64_t base = int64_t(tail0 % uint64_t(P)) + foff[i];
+        for (int k = threadIdx.x; k < d.free; k += blockDim.x) {
+            const int p = k < d.pH ? k : C - 1 - (k - d.pH);
+            const int page = row[p];
+            ring[(base + k) % P] = page;
+            owner[page] = -1;
+        }
+        __syncthreads();
+        for (int p = threadIdx.x; p < C; p += blockDim.x) row[p] = -1;
+        __syncthreads();
+    }
+    const int h0 = d.rebuilt ? 0 : d.pH;       // first new HIGH row position
+    const int l0 = d.rebuilt ? 0 : d.pL;       // first new LOW page index (from the right)
+    const int nH = d.qH - h0;
+    const int64_t abase = int64_t(head0 % uint64_t(P)) + off[i];
+    for (int k = threadIdx.x; k < d.alloc; k += blockDim.x) {
+        const int page = ring[(abase + k) % P];
+        const int p = k < nH ? h0 + k : C - 1 - (l0 + (k - nH));
+        row[p] = page;
+        owner[page] = gid * C + p;
+    }
+    if (threadIdx.x < 2) count_l[2 * i + threadIdx.x] = new_count[2 * i + threadIdx.x];
+    if (i == 0 && threadIdx.x == 0) {
+        ctr[0] = head0 + uint64_t(hdr->total_alloc);
+        ctr[1] = tail0 + uint64_t(hdr->total_free);
+    }
+    return true;
+}
+
+}  // namespace kvc

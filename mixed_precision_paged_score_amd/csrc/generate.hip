@@ -16,7 +16,10 @@
 // Launches: gen_decide (per head: the leaving token's tier and the new counts), the three
 // allocation kernels, gen_place (one workgroup per head: the head's HIGH tail pages, from
 // t_c's page on, are gathered into LDS as per-slot codes, shifted over t_c, extended by the
-// new token and written back whole; the demoted token goes into the next LOW slot).
+// new token and written back whole; the demoted token goes into the next LOW slot).  Up to
+// 256 heads take two launches instead: gen_plan (decisions and the allocation scan in one
+// workgroup) and gen_place<FUSED> (each workgroup commits its head's allocation, then places).
+#include "compact_dev.h"
 #include "kvc_internal.h"
 #include "page_io.h"
 #include "quant_row.h"
@@ -29,18 +32,19 @@ namespace kvc {
 constexpr int GEN_NONE = 255;               // no token left the window
 constexpr int GEN_TAIL = GEN_MAX_WINDOW + 16; // HIGH slots a step may rewrite
 
-__global__ void gen_decide_kernel(const int32_t *__restrict__ count_l,
-                                  const int32_t *__restrict__ rows_l, int C,
-                                  const uint8_t *__restrict__ pages,
-                                  const int32_t *__restrict__ positions,
-                                  const float *__restrict__ acc, const int32_t *__restrict__ cu,
-                                  int Hkv, int G, float alpha_h, float alpha_l, int window,
-                                  int nheads, int32_t *__restrict__ new_count,
-                                  int32_t *__restrict__ old_count, uint8_t *__restrict__ changed,
-                                  uint8_t *__restrict__ decided, uint8_t *__restrict__ tier_out,
-                                  int32_t *status) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nheads) return;
+// head i's decision: the leaving token's tier (GEN_NONE if none left), the new counts
+__device__ __forceinline__ void decide_head(int i, const int32_t *__restrict__ count_l,
+                                            const int32_t *__restrict__ rows_l, int C,
+                                            const uint8_t *__restrict__ pages,
+                                            const int32_t *__restrict__ positions,
+                                            const float *__restrict__ acc,
+                                            const int32_t *__restrict__ cu, int Hkv, int G,
+                                            float alpha_h, float alpha_l, int window,
+                                            int32_t *__restrict__ new_count,
+                                            int32_t *__restrict__ old_count,
+                                            uint8_t *__restrict__ changed,
+                                            uint8_t *__restrict__ decided,
+                                            uint8_t *__restrict__ tier_out, int32_t *status) {
     const int b = i / Hkv, h = i - b * Hkv;
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
     old_count[2 * i] = nh;
@@ -76,14 +80,75 @@ __global__ void gen_decide_kernel(const int32_t *__restrict__ count_l,
     new_count[2 * i + 1] = nl + (d == LOW ? 1 : 0);
 }
 
-// one workgroup (4 waves) per head
+__global__ void gen_decide_kernel(const int32_t *__restrict__ count_l,
+                                  const int32_t *__restrict__ rows_l, int C,
+                                  const uint8_t *__restrict__ pages,
+                                  const int32_t *__restrict__ positions,
+                                  const float *__restrict__ acc, const int32_t *__restrict__ cu,
+                                  int Hkv, int G, float alpha_h, float alpha_l, int window,
+                                  int nheads, int32_t *__restrict__ new_count,
+                                  int32_t *__restrict__ old_count, uint8_t *__restrict__ changed,
+                                  uint8_t *__restrict__ decided, uint8_t *__restrict__ tier_out,
+                                  int32_t *status) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nheads) return;
+    decide_head(i, count_l, rows_l, C, pages, positions, acc, cu, Hkv, G, alpha_h, alpha_l,
+                window, new_count, old_count, changed, decided, tier_out, status);
+}
+
+// up to 256 heads in one workgroup: every head's decision, then the allocation round's scan
+// (the heads' page demands, their exclusive prefix sums and the round's totals) without the
+// multi-tile look-back of compact_scan
+__global__ __launch_bounds__(256) void gen_plan_kernel(
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ rows_l, int C,
+    const uint8_t *__restrict__ pages, const int32_t *__restrict__ positions,
+    const float *__restrict__ acc, const int32_t *__restrict__ cu, int Hkv, int G, float alpha_h,
+    float alpha_l, int window, int nheads, int32_t *__restrict__ new_count,
+    int32_t *__restrict__ old_count, uint8_t *__restrict__ changed,
+    uint8_t *__restrict__ decided, uint8_t *__restrict__ tier_out, int32_t *status,
+    const uint64_t *ctr, CompactHdr *hdr, int32_t *__restrict__ off, int32_t *__restrict__ foff) {
+    __shared__ int s_wa[4], s_wf[4];
+    __shared__ uint32_t s_err;
+    if (threadIdx.x == 0) s_err = 0u;
+    __syncthreads();
+    const int i = threadIdx.x;
+    HeadDemand d{};
+    if (i < nheads) {
+        decide_head(i, count_l, rows_l, C, pages, positions, acc, cu, Hkv, G, alpha_h, alpha_l,
+                    window, new_count, old_count, changed, decided, tier_out, status);
+        d = head_demand(count_l, new_count, changed, i, C);
+        if (d.err) atomicOr(&s_err, uint32_t(d.err));
+    }
+    int a = d.alloc, f = d.free;
+    block_scan2(a, f, s_wa, s_wf);       // inclusive; the last thread holds the totals
+    if (i < nheads) {
+        off[i] = a - d.alloc;
+        foff[i] = f - d.free;
+    }
+    __syncthreads();
+    if (threadIdx.x == blockDim.x - 1) {
+        hdr->err = s_err;
+        hdr->total_alloc = a;
+        hdr->total_free = f;
+        hdr->head0 = ctr[0];
+        hdr->tail0 = ctr[1];
+        // the decisions' status bits included (set by this workgroup's atomics)
+        hdr->entry_status = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// one workgroup (4 waves) per head.  FUSED: the workgroup first commits its head's part of
+// the allocation round (gen_plan_kernel did the scan), then places
+template <bool FUSED>
 __global__ __launch_bounds__(256) void gen_place_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ positions, int Hkv, int C, int nheads, int window,
-    const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
+    int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
     const int32_t *__restrict__ new_count, const int32_t *__restrict__ old_count,
-    const uint8_t *__restrict__ decided, uint8_t *__restrict__ pages,
-    const int32_t *__restrict__ status) {
+    const uint8_t *__restrict__ decided, uint8_t *__restrict__ pages, int32_t *status,
+    const uint8_t *__restrict__ changed, int64_t P, int layer_gid0, uint64_t *ctr,
+    int32_t *__restrict__ ring, int32_t *__restrict__ owner, const CompactHdr *hdr,
+    const int32_t *__restrict__ off, const int32_t *__restrict__ foff) {
     __shared__ uint8_t s_k[GEN_TAIL][D];            // key codes per slot (one per byte)
     __shared__ uint8_t s_v[GEN_TAIL][D];            // value codes per slot
     __shared__ uint32_t s_par[GEN_TAIL][2];         // (key scale|zero, value scale|zero)
@@ -92,10 +157,20 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     __shared__ uint32_t s_lpar[2];
     const int i = blockIdx.x;
     if (i >= nheads) return;
-    // any status bit (set before this call, by the decision or by the allocation round)
-    // means the round committed nothing: the step leaves every page as it was
-    if (*status != 0) return;
-    if (count_l[2 * i] != new_count[2 * i] || count_l[2 * i + 1] != new_count[2 * i + 1]) return;
+    if constexpr (FUSED) {
+        // a round that does not commit (status bits at its start, the decisions' included,
+        // or a failed allocation) leaves every page as it was
+        if (!commit_head(i, rows_l, count_l, new_count, changed, C, P, layer_gid0, status, ctr,
+                         ring, owner, hdr, off, foff, nullptr, nullptr))
+            return;
+        __syncthreads();                             // the head's new row and counts
+    } else {
+        // any status bit (set before this call, by the decision or by the allocation round)
+        // means the round committed nothing: the step leaves every page as it was
+        if (*status != 0) return;
+        if (count_l[2 * i] != new_count[2 * i] || count_l[2 * i + 1] != new_count[2 * i + 1])
+            return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = lane >> 4, c = lane & 15;
     const int b = i / Hkv;
@@ -285,6 +360,28 @@ extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_p
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
+    int32_t *rows_w = p->page_table + int64_t(layer) * nheads * C;
+    int32_t *count_w = p->count + int64_t(layer) * nheads * 2;
+    if (nheads <= 256) {
+        // two launches: decisions + scan in one workgroup, then commit + placement per head
+        const CompactWs Lc(g);
+        char *wc = w + L.compact;
+        CompactHdr *hdr = reinterpret_cast<CompactHdr *>(wc + Lc.hdr);
+        int32_t *off = reinterpret_cast<int32_t *>(wc + Lc.off);
+        int32_t *foff = reinterpret_cast<int32_t *>(wc + Lc.foff);
+        hipLaunchKernelGGL(gen_plan_kernel, dim3(1), dim3(256), 0, s, count_l, rows_l, C,
+                           p->pages, positions, acc_sum, cu_seqlens, g->num_kv_heads, G, alpha_h,
+                           alpha_l, window, nheads, new_count, old_count, changed, decided,
+                           tier_out, p->dev_status, p->ring_ctr, hdr, off, foff);
+        rc = launch_check("kvc_generation_step/plan");
+        if (rc) return rc;
+        hipLaunchKernelGGL(gen_place_kernel<true>, dim3(nheads), dim3(256), 0, s, k_new, v_new,
+                           positions, g->num_kv_heads, C, nheads, window, rows_w, count_w,
+                           new_count, old_count, decided, p->pages, p->dev_status, changed,
+                           g->num_pages, layer * nheads, p->ring_ctr, p->free_ring, p->owner, hdr,
+                           off, foff);
+        return launch_check("kvc_generation_step/place");
+    }
     hipLaunchKernelGGL(gen_decide_kernel, dim3((nheads + 255) / 256), dim3(256), 0, s, count_l,
                        rows_l, C, p->pages, positions, acc_sum, cu_seqlens, g->num_kv_heads, G, alpha_h, alpha_l,
                        window, nheads, new_count, old_count, changed, decided, tier_out,
@@ -293,8 +390,9 @@ extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_p
     if (rc) return rc;
     rc = launch_compact(g, layer, p, new_count, changed, nullptr, nullptr, w + L.compact, s);
     if (rc) return rc;
-    hipLaunchKernelGGL(gen_place_kernel, dim3(nheads), dim3(256), 0, s, k_new, v_new, positions,
-                       g->num_kv_heads, C, nheads, window, rows_l, count_l, new_count, old_count,
-                       decided, p->pages, p->dev_status);
+    hipLaunchKernelGGL(gen_place_kernel<false>, dim3(nheads), dim3(256), 0, s, k_new, v_new,
+                       positions, g->num_kv_heads, C, nheads, window, rows_w, count_w, new_count,
+                       old_count, decided, p->pages, p->dev_status, nullptr, int64_t(0), 0,
+                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     return launch_check("kvc_generation_step/place");
 }

@@ -134,6 +134,17 @@ def test_exhausted_pool_changes_nothing():
         assert np.array_equal(x, y)
 
 
+def test_more_heads_than_one_scan_tile():
+    # 40 requests x 8 KV heads = 320 heads: more than one workgroup's worth, so the step takes
+    # the general path (separate decision launch and the three allocation launches) rather
+    # than the fused one used up to 256 heads
+    rng = np.random.default_rng(58)
+    lens = [int(x) for x in rng.integers(20, 160, 40)]
+    w = workloads.Workload("step-wide", 1, 40, 16, 8, lens, 1.0, 0.3, 16, 8192, "zipf", seed=58)
+    c = run_steps(w, steps=40, sample_heads=8, check_every=10)
+    assert c["low"] > 0 and c["pruned"] > 0, c
+
+
 def test_workload4_shape_sampled():
     # 16 requests x 4096-token prompts, 64 query / 8 KV heads, the 64-token window: 512 steps
     # of the per-step policy; decisions of all 128 heads every step, allocator state every 64
