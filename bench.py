@@ -340,8 +340,8 @@ def traffic_record(workload):
     if dec_src:
         out["decode"] = rec["decode_call_bytes"]["total"]
         out["decode_acc"] = rec.get("decode_acc_call_bytes", {}).get("total")
-    if same(["score.hip", "compact.hip", "quantize.hip", "quant_row.h", "page_io.h",
-             "workspace.h", "kvc_internal.h"]):
+    if same(["score.hip", "compact.hip", "compact_dev.h", "quantize.hip", "quant_row.h",
+             "page_io.h", "workspace.h", "kvc_internal.h"]):
         out["compaction"] = rec["compaction_round_bytes"]["total"]
     return out
 
