@@ -6,7 +6,8 @@
 // happen on the GPU in one coordinated step.  "Core claim": circular free list and
 // bidirectional page table (page table rows + the owner reverse map).
 //
-// Three launches on the caller's stream:
+// Three launches on the caller's stream (up to 256 heads, one scan tile: compact_scan1, one
+// workgroup doing the whole scan with nothing to clear, then the commit):
 //   1. compact_zero   clears the scan header and tile descriptors (a fill kernel, so the
 //                     sequence stays valid inside a captured graph)
 //   2. compact_scan   single-pass scan over heads: LDS block scan of (alloc, free) per
@@ -113,6 +114,38 @@ __global__ __launch_bounds__(SCAN_TILE) void compact_scan_kernel(
     }
 }
 
+// up to SCAN_TILE heads: the whole scan in one workgroup (no look-back state to clear)
+__global__ __launch_bounds__(SCAN_TILE) void compact_scan1_kernel(
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ new_count,
+    const uint8_t *__restrict__ changed, int nheads, int C, const int32_t *status,
+    const uint64_t *ctr, CompactHdr *hdr, int32_t *off, int32_t *foff) {
+    __shared__ int s_wa[4], s_wf[4];
+    __shared__ uint32_t s_err;
+    if (threadIdx.x == 0) s_err = 0u;
+    __syncthreads();
+    const int i = threadIdx.x;
+    HeadDemand d{};
+    if (i < nheads) {
+        d = head_demand(count_l, new_count, changed, i, C);
+        if (d.err) atomicOr(&s_err, uint32_t(d.err));
+    }
+    int a = d.alloc, f = d.free;
+    block_scan2(a, f, s_wa, s_wf);       // inclusive; the last thread holds the totals
+    if (i < nheads) {
+        off[i] = a - d.alloc;
+        foff[i] = f - d.free;
+    }
+    __syncthreads();
+    if (threadIdx.x == SCAN_TILE - 1) {
+        hdr->err = s_err;
+        hdr->total_alloc = a;
+        hdr->total_free = f;
+        hdr->head0 = ctr[0];
+        hdr->tail0 = ctr[1];
+        hdr->entry_status = *status;
+    }
+}
+
 // one workgroup per head: snapshot the old row, then (if the call commits) rewrite it
 __global__ __launch_bounds__(256) void compact_commit_kernel(
     int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
@@ -144,14 +177,22 @@ int launch_compact(const kvc_geom *g, int32_t layer, const kvc_pool *p,
     const int C = g->row_capacity;
     int32_t *rows_l = p->page_table + int64_t(layer) * L.nheads * C;
     int32_t *count_l = p->count + int64_t(layer) * L.nheads * 2;
-    hipLaunchKernelGGL(compact_zero_kernel, dim3((L.ntiles + 255) / 256), dim3(256), 0, s, hdr,
-                       st, L.ntiles);
-    int rc = launch_check("compact/zero");
-    if (rc) return rc;
-    hipLaunchKernelGGL(compact_scan_kernel, dim3(L.ntiles), dim3(SCAN_TILE), 0, s, count_l,
-                       new_count, changed, L.nheads, C, p->dev_status, p->ring_ctr, hdr, st,
-                       off, foff);
-    rc = launch_check("compact/scan");
+    int rc;
+    if (L.ntiles == 1) {
+        hipLaunchKernelGGL(compact_scan1_kernel, dim3(1), dim3(SCAN_TILE), 0, s, count_l,
+                           new_count, changed, L.nheads, C, p->dev_status, p->ring_ctr, hdr, off,
+                           foff);
+        rc = launch_check("compact/scan1");
+    } else {
+        hipLaunchKernelGGL(compact_zero_kernel, dim3((L.ntiles + 255) / 256), dim3(256), 0, s,
+                           hdr, st, L.ntiles);
+        rc = launch_check("compact/zero");
+        if (rc) return rc;
+        hipLaunchKernelGGL(compact_scan_kernel, dim3(L.ntiles), dim3(SCAN_TILE), 0, s, count_l,
+                           new_count, changed, L.nheads, C, p->dev_status, p->ring_ctr, hdr, st,
+                           off, foff);
+        rc = launch_check("compact/scan");
+    }
     if (rc) return rc;
     hipLaunchKernelGGL(compact_commit_kernel, dim3(L.nheads), dim3(256), 0, s, rows_l, count_l,
                        new_count, changed, C, g->num_pages, layer * L.nheads, p->dev_status,
