@@ -335,7 +335,7 @@ def traffic_record(workload):
             if hashlib.sha256(open(f, "rb").read()).hexdigest() != rec["kernel_sources_sha256"][n]:
                 return False
         return True
-    dec_src = same(["attention.hip", "workspace.h", "kvc_internal.h"])
+    dec_src = same(["attention.hip", "page_load.h", "workspace.h", "kvc_internal.h"])
     out = dict(none)
     if dec_src:
         out["decode"] = rec["decode_call_bytes"]["total"]

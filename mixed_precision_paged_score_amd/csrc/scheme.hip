@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "kvc_internal.h"
+#include "page_load.h"
 #include "workspace.h"
 
 #pragma clang fp contract(off)
@@ -48,27 +49,6 @@ __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Page reads are buffer loads: one descriptor per page (wave-uniform: the page's address,
-// its size as the range) and a 32-bit per-lane offset
-typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *page) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(page), 0, PAGE, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u4v x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u2v x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_uint2(x[0], x[1]);
-}
-__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
 
 __device__ __forceinline__ float max_col(float x) {
     uint32_t u = __float_as_uint(x);
