@@ -42,13 +42,6 @@ constexpr float M_INIT = -1.0e30f;          // finite "minus infinity" for the r
 #define KVC_DEC_OCC 3
 #endif
 constexpr int DEC_WAVES = KVC_DEC_WAVES;    // waves per workgroup (slices of one head)
-#ifndef KVC_DEC_UH
-#define KVC_DEC_UH 3
-#endif
-#ifndef KVC_DEC_UL
-#define KVC_DEC_UL 2
-#endif
-constexpr int DEC_UH = KVC_DEC_UH, DEC_UL = KVC_DEC_UL;   // slice weights of HIGH / LOW tiles
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -457,7 +450,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(
 void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
                         const uint8_t *__restrict__ pages, const int32_t *__restrict__ rows_l,
                         const int32_t *__restrict__ count_l, int Hkv, int GT, int C, int S,
-                        float *__restrict__ part, float *__restrict__ lg, int64_t tiles_cap) {
+                        int wt, float *__restrict__ part, float *__restrict__ lg,
+                        int64_t tiles_cap) {
     __shared__ float s_o[DEC_WAVES][8][D];      // [wave][query head][channel]
     __shared__ float s_m[DEC_WAVES][16], s_l[DEC_WAVES][16], s_lz[DEC_WAVES][16],
         s_lp[DEC_WAVES][16];
@@ -468,7 +462,6 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, j = lane >> 4, gq = c & 7;
     const int NGP = (GT + 7) >> 3;             // groups of 8 query heads per KV head
-    const int s = blockIdx.x % S;
     const int gp = (blockIdx.x / S) % NGP;
     const int i = blockIdx.x / (S * NGP);      // head index b*Hkv + h
     const int b = i / Hkv, h = i - b * Hkv;
@@ -482,13 +475,16 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
         qv[0] = qp[0]; qv[1] = qp[1]; qv[2] = qp[2]; qv[3] = qp[3];
     }
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int SH = active_splits(nh, nl, S, wt);   // the head's workgroups; the rest exit
+    const int s = split_of_slot(blockIdx.x % S, i, SH, S);
+    if (s >= SH) return;
     const int qH = ceil_div(nh, HS);
     const int tL = ceil_div(nl, 16);
     // work units: a HIGH tile (one page) weighs DEC_UH, a LOW tile (half a page) DEC_UL;
     // slices start on even LOW tiles (pairs stay in a page)
     const int64_t WH = int64_t(DEC_UH) * qH;
     const int64_t W = WH + int64_t(DEC_UL) * tL;
-    const int NC = S * DEC_WAVES;
+    const int NC = SH * DEC_WAVES;
     const int cc = s * DEC_WAVES + wave;
     auto tile_of = [&](int64_t x) -> int {
         int t = x <= WH ? int((x + DEC_UH - 1) / DEC_UH)
@@ -608,7 +604,9 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
                                                              int Hq, int G, int S, int nqh,
                                                              void *out, int out_fp32,
-                                                             float *__restrict__ mls) {
+                                                             float *__restrict__ mls,
+                                                             const int32_t *__restrict__ count_l,
+                                                             int wt) {
     const int lane = threadIdx.x & 63;
     const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);    // b*Hq + hq
     if (qh >= nqh) return;
@@ -617,30 +615,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     const int Hkv = Hq / G;
     const int64_t sstride = int64_t(G) * PART_STRIDE;
     const float *hp = part + ((int64_t(b) * Hkv + h) * S * G + gg) * PART_STRIDE;
+    // the head's splits that wrote partials
+    const int64_t hi = int64_t(b) * Hkv + h;
+    const int SH = active_splits(count_l[2 * hi], count_l[2 * hi + 1], S, wt);
     float ms = M_INIT, ls = 0.0f;
-    if (lane < S) {
+    if (lane < SH) {
         ms = hp[lane * sstride];
         ls = hp[lane * sstride + 1];
     }
     float M = ms;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float w = lane < S ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+    const float w = lane < SH ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
     float Ls = ls * w;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
     float r0 = 0.0f, r1 = 0.0f;
-    for (int k0 = 0; k0 < S; k0 += 8) {
+    for (int k0 = 0; k0 < SH; k0 += 8) {
         float2 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int k = min(k0 + u, S - 1);          // past the end: reload, weight 0
+            const int k = min(k0 + u, SH - 1);          // past the end: reload, weight 0
             v[u] = *reinterpret_cast<const float2 *>(hp + k * sstride + 4 + 2 * lane);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int wk = __builtin_amdgcn_readlane(__float_as_int(w), min(k0 + u, 63));
-            const float wf = k0 + u < S ? __int_as_float(wk) : 0.0f;
+            const float wf = k0 + u < SH ? __int_as_float(wk) : 0.0f;
             r0 += v[u].x * wf;
             r1 += v[u].y * wf;
         }
@@ -831,10 +832,11 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
 
 // the combine launch of a split-K decode (shared with the precision-scheme decode)
 int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,
-                          int out_fp32, float *mls, hipStream_t s) {
+                          int out_fp32, float *mls, const int32_t *count_l, int wt,
+                          hipStream_t s) {
     const int nqh = B * Hq;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((nqh + 3) / 4), dim3(256), 0, s, part, Hq, G,
-                       S, nqh, out, out_fp32, mls);
+                       S, nqh, out, out_fp32, mls, count_l, wt);
     return launch_check("decode/combine");
 }
 
@@ -878,14 +880,15 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
     if (accum)
         hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, block, 0, s, q,
                            softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
-                           part, lg, L.tiles_cap);
+                           L.wt, part, lg, L.tiles_cap);
     else
         hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, block, 0, s, q,
                            softmax_scale * LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
-                           part, nullptr, int64_t(0));
+                           L.wt, part, nullptr, int64_t(0));
     rc = launch_check("kvc_paged_decode_attention/main");
     if (rc) return rc;
-    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls, s);
+    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
+                               count_l, L.wt, s);
     if (rc || !accum) return rc;
     if (max_seqlen == 0) return KVC_OK;
     int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);

@@ -230,7 +230,7 @@ template <int KH, int VH, int KL, int VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_decode_kernel(
     const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
-    int C, int S, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
+    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
     const int kh = KH ? KH : kh_rt, vh = VH ? VH : vh_rt, kl = KL ? KL : kl_rt,
               vl = VL ? VL : vl_rt;
     __shared__ float s_o[WAVES][16][D];
@@ -238,13 +238,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int i = blockIdx.x / S, sp = blockIdx.x - i * S;
+    const int i = blockIdx.x / S;
     const int b = i / Hkv, h = i - b * Hkv;
     const int Hq = Hkv * G;
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int SH = active_splits(nh, nl, S, wt);   // the head's workgroups; the rest exit
+    const int sp = split_of_slot(blockIdx.x - i * S, i, SH, S);
+    if (sp >= SH) return;
     const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
     const int T = qH + tL;
-    const int cc = sp * WAVES + wave, NC = S * WAVES;
+    const int cc = sp * WAVES + wave, NC = SH * WAVES;
     const int t0 = int(int64_t(T) * cc / NC), t1 = int(int64_t(T) * (cc + 1) / NC);
     const int32_t *row = rows_l + int64_t(i) * C;
 
@@ -415,7 +418,7 @@ template <int KH, int VH, int KL, int VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_pair_kernel(
     const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
-    int C, int S, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
+    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
     const int kh = KH ? KH : kh_rt, vh = VH ? VH : vh_rt, kl = KL ? KL : kl_rt,
               vl = VL ? VL : vl_rt;
     __shared__ float s_o[WAVES][16][D];
@@ -425,13 +428,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4, hc = c & 7;
     const bool own_b = c >= 8;
-    const int i = blockIdx.x / S, sp = blockIdx.x - i * S;
+    const int i = blockIdx.x / S;
     const int b = i / Hkv, h = i - b * Hkv;
     const int Hq = Hkv * G;
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int SH = active_splits(nh, nl, S, wt);   // the head's workgroups; the rest exit
+    const int sp = split_of_slot(blockIdx.x - i * S, i, SH, S);
+    if (sp >= SH) return;
     const int qH = ceil_div(nh, HS), tL = ceil_div(nl, 16);
     const int T = qH + tL;
-    const int cc = sp * WAVES + wave, NC = S * WAVES;
+    const int cc = sp * WAVES + wave, NC = SH * WAVES;
     const int t0 = int(int64_t(T) * cc / NC), t1 = int(int64_t(T) * (cc + 1) / NC);
     const int32_t *row = rows_l + int64_t(i) * C;
 
@@ -689,9 +695,9 @@ extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_sc
 #undef KVC_SCHEME_CASE
     hipLaunchKernelGGL(kern, dim3(L.splits * nheads), dim3(256), 0, s, q,
                        softmax_scale * sch::LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
-                       sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, part);
+                       L.wt, sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, part);
     rc = launch_check("kvc_paged_decode_attention_scheme/main");
     if (rc) return rc;
     return launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, nullptr,
-                                 s);
+                                 count_l, L.wt, s);
 }

@@ -101,26 +101,72 @@ constexpr int PART_STRIDE = 132;  // floats per partial: m, l, pad, pad, o[128]
 #ifndef KVC_DEC_SPLIT_TARGET
 #define KVC_DEC_SPLIT_TARGET 2048      // workgroups per decode launch to aim for
 #endif
+#ifndef KVC_DEC_WT_MAX
+#define KVC_DEC_WT_MAX 256             // work units per workgroup at most (about 100 tiles)
+#endif
+#ifndef KVC_DEC_UH
+#define KVC_DEC_UH 3
+#endif
+#ifndef KVC_DEC_UL
+#define KVC_DEC_UL 2
+#endif
+constexpr int DEC_UH = KVC_DEC_UH, DEC_UL = KVC_DEC_UL;   // work units of a HIGH / LOW tile
 
-inline int decode_splits(const kvc_geom *g) {
-    int heads = g->batch * g->num_kv_heads;
-    int s = (KVC_DEC_SPLIT_TARGET + heads - 1) / heads;
-    if (s < 1) s = 1;
-    if (s > 64) s = 64;
-    return s;
+// Split-K plan of the decode.  The grid has `splits` workgroup slots per head; head h uses
+// active_splits() = min(splits, ceil(W_h / wt)) of them, W_h its work units (HIGH tiles weigh
+// DEC_UH, LOW half-page tiles DEC_UL), so that a long head gets more workgroups than a short
+// one and every workgroup about wt units; the other slots exit at once.  The slot count is
+// the batch's share of the workgroup target, at least 16 and at most 64 (16 and 32 are
+// multiples of the 8 XCDs, which the kernels' slot order relies on), and no more than the
+// largest possible head needs (its tiles are at most the row capacity C + 1); wt spreads that
+// largest head over the slots, but never hands one workgroup more than KVC_DEC_WT_MAX units.
+struct DecodePlan {
+    int splits, wt;
+};
+inline DecodePlan decode_plan(const kvc_geom *g) {
+    const int heads = g->batch * g->num_kv_heads;
+    int s0 = (KVC_DEC_SPLIT_TARGET + heads - 1) / heads;
+    if (s0 < 16) s0 = 16;
+    if (s0 > 64) s0 = 64;
+    const int64_t wmax = int64_t(DEC_UH) * (int64_t(g->row_capacity) + 1);
+    int64_t wt = (wmax + s0 - 1) / s0;
+    if (wt > KVC_DEC_WT_MAX) wt = KVC_DEC_WT_MAX;
+    if (wt < 1) wt = 1;
+    int64_t splits = (wmax + wt - 1) / wt;
+    if (splits > s0) splits = s0;
+    if (splits < 1) splits = 1;
+    return {int(splits), int(wt)};
+}
+// the workgroups head (nh HIGH, nl LOW tokens) uses of its `splits` (at least one)
+__host__ __device__ inline int active_splits(int nh, int nl, int splits, int wt) {
+    const int64_t w = int64_t(DEC_UH) * ((nh + HS - 1) / HS) + int64_t(DEC_UL) * ((nl + 15) / 16);
+    const int64_t a = (w + wt - 1) / wt;
+    return int(a < 1 ? 1 : (a > splits ? splits : a));
+}
+// The split that workgroup slot `slot` of head i serves (>= SH: none).  Workgroups go to the
+// XCDs round-robin, so with a slot count that is a multiple of 8 slot k of every head runs on
+// XCD k mod 8.  A head that uses all its slots keeps that order (the fastest measured for
+// batches of equal heads); a head that uses fewer turns its splits by its index, so that the
+// workgroups of short heads spread over all the XCDs instead of crowding the first ones.
+__device__ inline int split_of_slot(int slot, int i, int SH, int splits) {
+    if (SH == splits) return slot;
+    const int s = slot - i % splits;
+    return s < 0 ? s + splits : s;
 }
 
 constexpr int ACC_R = 64;          // positions per score-accumulation chunk
 constexpr int ACC_MAX_HQ = 512;    // query heads the accumulation's LDS rows hold
 
 struct DecodeWs {
-    int splits;
+    int splits, wt;
     int64_t tiles_cap;     // tiles per head the logit buffer holds (HIGH pages + 2 x LOW pages)
     int nch_cap;           // chunk-start entries per head and tier: ceil(max_seqlen / R) + 1
     size_t part, mls, lg, idx, bytes;
     // acc: also the buffers of the score-accumulating variant (requests up to max_seqlen)
     DecodeWs(const kvc_geom *g, bool acc, int max_seqlen = 0) {
-        splits = decode_splits(g);
+        const DecodePlan pl = decode_plan(g);
+        splits = pl.splits;
+        wt = pl.wt;
         tiles_cap = 2 * int64_t(g->row_capacity);
         part = 0;          // float [B][Hkv][S][G][PART_STRIDE]
         bytes = align256(sizeof(float) * PART_STRIDE * size_t(g->batch) * g->num_q_heads *
