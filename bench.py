@@ -8,7 +8,8 @@ steps of paged_decode_attention (fresh queries).  Default workload: one layer, 1
 32,768 tokens, 64 query / 8 KV heads, Zipf(1.1) accumulators, 64 decode steps; the pool has
 room for two layouts of the layer (2 x 2^18 pages).  The step's library calls are captured
 into two HIP graphs (prompt round, decode steps) and replayed; --eager launches them from
-Python instead.
+Python instead.  Each step starts with a ~200 us GPU spin outside the timed region, so that
+the host has queued the step before the GPU reaches it.
 
 Prints one JSON line.  `value` = KV token-heads compacted per second over the compaction
 part of the step; `decode_GBps` = algorithmic bytes of paged decode attention per second;
@@ -117,6 +118,23 @@ def measure_ceilings():
     del a, b
     torch.cuda.empty_cache()
     return res
+
+
+def spin_cycles(stream, target_us=200.0):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about target_us: queued
+    before a timed region, it lets the host submit the region's whole graph first, so that the
+    events time the GPU's work and not the host's submission of each node (which shows when a
+    long graph before has left the GPU idle)."""
+    probe = 1 << 20
+    torch.cuda._sleep(probe)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(probe)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    return int(probe * target_us / us)
 
 
 def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
@@ -431,8 +449,11 @@ def main():
         g_dec = path.capture_decode(0, qs, out)
         torch.cuda.synchronize()
 
+    spin = spin_cycles(stream)
+
     def step(record):
         e0, e1, e2 = ev(), ev(), ev()
+        torch.cuda._sleep(spin)            # the host queues the step while the GPU spins
         e0.record(stream)
         if a.eager:
             path.prompt(0, acc, k, v)
