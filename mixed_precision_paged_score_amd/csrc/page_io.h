@@ -8,6 +8,22 @@
 
 namespace kvc {
 
+typedef unsigned int pio_u2 __attribute__((ext_vector_type(2)));
+typedef unsigned int pio_u4 __attribute__((ext_vector_type(4)));
+// Page stores are non-temporal: a page image is written once and read back only by a later
+// launch, so streaming it out keeps a prompt round's hundreds of MB from filling the caches
+// with dirty lines that the next kernel would have to write back first.
+__device__ __forceinline__ void st_page4(uint8_t *p, uint32_t a) {
+    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t *>(p));
+}
+__device__ __forceinline__ void st_page8(uint8_t *p, uint32_t a, uint32_t b) {
+    __builtin_nontemporal_store(pio_u2{a, b}, reinterpret_cast<pio_u2 *>(p));
+}
+__device__ __forceinline__ void st_page16(uint8_t *p, uint32_t a, uint32_t b, uint32_t c,
+                                          uint32_t d) {
+    __builtin_nontemporal_store(pio_u4{a, b, c, d}, reinterpret_cast<pio_u4 *>(p));
+}
+
 __device__ __forceinline__ int k_nib(int e) { return (e & 1) + 2 * (e >> 2) + 4 * ((e >> 1) & 1); }
 
 // codes of the lane's 8 channels 8c..8c+7 of slot `so` in an old page of tier `t`
@@ -57,8 +73,8 @@ __device__ __forceinline__ void store_slot(uint8_t *pg, uint8_t *sv, uint16_t (*
                                            uint32_t vw0, uint32_t vw1, uint16_t ks, uint16_t kz,
                                            uint16_t vs, uint16_t vz) {
     if (!live) kw0 = kw1 = vw0 = vw1 = 0;
-    if (high) *reinterpret_cast<uint2 *>(pg + K_OFF + s * 128 + 8 * c) = make_uint2(kw0, kw1);
-    else *reinterpret_cast<uint32_t *>(pg + K_OFF + s * 64 + 4 * c) = kw0;
+    if (high) st_page8(pg + K_OFF + s * 128 + 8 * c, kw0, kw1);
+    else st_page4(pg + K_OFF + s * 64 + 4 * c, kw0);
     *reinterpret_cast<uint2 *>(sv + s * D + 8 * c) = make_uint2(vw0, vw1);
     if (c == 0) {
         par[s][0] = live ? ks : 0;
@@ -97,7 +113,7 @@ __device__ __forceinline__ void pack_values(uint8_t *pg, const uint8_t *sv, bool
                     w[q] |= code << (2 * (2 * nn + (r >> 1) + 8 * (r & 1)));
                 }
     }
-    *reinterpret_cast<uint4 *>(pg + V_OFF + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    st_page16(pg + V_OFF + 16 * lane, w[0], w[1], w[2], w[3]);
 }
 
 }  // namespace kvc

@@ -357,8 +357,8 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
             bb = uint32_t(s_par[wave][s][2]) | (uint32_t(s_par[wave][s][3]) << 16);
             pos = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
         }
-        *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * s) = make_uint2(a, bb);
-        *reinterpret_cast<int32_t *>(pg + POS_OFF + 4 * s) = pos;
+        st_page8(pg + PARAM_OFF + 8 * s, a, bb);
+        st_page4(pg + POS_OFF + 4 * s, uint32_t(pos));
     }
 }
 
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
 // the lane's 8 codes (b bits each, channels 8c .. 8c + 7) as b bytes at dst (b = 1, 2, 4, 8:
 // naturally aligned stores)
 __device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t w, int b) {
-    if (b == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(uint32_t(w), uint32_t(w >> 32));
-    else if (b == 4) *reinterpret_cast<uint32_t *>(dst) = uint32_t(w);
+    if (b == 8) st_page8(dst, uint32_t(w), uint32_t(w >> 32));
+    else if (b == 4) st_page4(dst, uint32_t(w));
     else if (b == 2) *reinterpret_cast<uint16_t *>(dst) = uint16_t(w);
     else *dst = uint8_t(w);
 }
@@ -391,14 +391,14 @@ __device__ __forceinline__ void pack_value_block(uint8_t *dst, const uint8_t (*v
             w[n / P] |= code << (16 * (r & 1) + VB * (2 * (n % P) + (r >> 1)));
         }
     if constexpr (VB == 8) {
-        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        st_page16(dst, w[0], w[1], w[2], w[3]);
+        st_page16(dst + 16, w[4], w[5], w[6], w[7]);
     } else if constexpr (VB == 4) {
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        st_page16(dst, w[0], w[1], w[2], w[3]);
     } else if constexpr (VB == 2) {
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+        st_page8(dst, w[0], w[1]);
     } else {
-        *reinterpret_cast<uint32_t *>(dst) = w[0];
+        st_page4(dst, w[0]);
     }
 }
 
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
         if (c == 0) {
             const uint32_t a = live ? uint32_t(qk.s16) | (uint32_t(qk.z16) << 16) : 0u;
             const uint32_t bb = live ? uint32_t(qv.s16) | (uint32_t(qv.z16) << 16) : 0u;
-            *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * sl) = make_uint2(a, bb);
-            reinterpret_cast<int32_t *>(pg + POS_OFF)[sl] = live ? pos : -1;
+            st_page8(pg + PARAM_OFF + 8 * sl, a, bb);
+            st_page4(pg + POS_OFF + 4 * sl, uint32_t(live ? pos : -1));
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -491,10 +491,10 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
     }
     // code bytes past the values (16 S (kb + vb) is a multiple of 16), slots S..31's fields
     for (int k = S * (kb + vb) + lane; k < PARAM_OFF / 16; k += 64)
-        reinterpret_cast<uint4 *>(pg)[k] = make_uint4(0, 0, 0, 0);
+        st_page16(pg + 16 * k, 0u, 0u, 0u, 0u);
     if (lane >= S && lane < LS) {
-        *reinterpret_cast<uint2 *>(pg + PARAM_OFF + 8 * lane) = make_uint2(0u, 0u);
-        reinterpret_cast<int32_t *>(pg + POS_OFF)[lane] = -1;
+        st_page8(pg + PARAM_OFF + 8 * lane, 0u, 0u);
+        st_page4(pg + POS_OFF + 4 * lane, uint32_t(-1));
     }
 }
 
