@@ -95,9 +95,15 @@ __device__ __forceinline__ uint32_t gather4(uint32_t a, uint32_t b, uint32_t c, 
     return (__builtin_amdgcn_perm(d, c, 0x0c0c0400u) << 16) | __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
 }
 
+// one fp16 row slice of 8 channels; a non-temporal load, since the prompt's K/V rows are
+// read once and streaming them keeps the caches for the page images and tables
+typedef unsigned int qr_u4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load_row8(const uint16_t *src, bool live, float (&x)[8]) {
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (live) u = *reinterpret_cast<const uint4 *>(src);
+    if (live) {
+        const qr_u4 x = __builtin_nontemporal_load(reinterpret_cast<const qr_u4 *>(src));
+        u = make_uint4(x[0], x[1], x[2], x[3]);
+    }
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
