@@ -189,6 +189,21 @@ def test_row_overflow_sets_status():
     assert int(path.pool.ring_ctr[0].item()) == 0
 
 
+# 16 requests x 8 KV heads give the decode 16 workgroup slots per head.  With every token
+# HIGH (alpha_h = 0) the heads of the two 16K-token requests fill all 16 slots and keep their
+# slot order, while the heads of the short and empty requests use one or two slots and turn
+# their splits by head index; with (1.0, 0.2) the long heads use fewer than 16.  Every head's
+# attention must still be the oracle's.
+SPLIT_LENS = [16384, 0, 1, 37, 300, 777, 2048, 16384, 5000, 100, 64, 65, 3000, 15, 900, 4000]
+
+
+@pytest.mark.parametrize("ah,al", [(0.0, 0.0), (1.0, 0.2)])
+def test_decode_split_plan_long_and_short_heads(ah, al):
+    w = workloads.Workload(f"split-plan-{ah}-{al}", 1, 16, 64, 8, SPLIT_LENS, ah, al, 64,
+                           1 << 16, "zipf", seed=29)
+    run_prompt_and_check(w, gen_device=DEV)
+
+
 def test_workload2_full():
     run_prompt_and_check(workloads.workload(2), gen_device=DEV)
 

@@ -110,6 +110,18 @@ def test_prune_and_no_prune_configurations():
     assert not np.any(t == 0) and np.any(t == 1)
 
 
+@pytest.mark.parametrize("hq", [64, 128])
+def test_split_plan_long_and_short_heads(hq):
+    """16 requests x 8 KV heads, every token HIGH: the two 8K-token requests' heads fill all
+    16 workgroup slots of the decode, the short and empty ones use one or two (8 and 16
+    query heads per KV head: both decode kernels)."""
+    lens = [8192, 0, 1, 37, 300, 777, 2048, 8192, 5000, 100, 64, 65, 3000, 15, 900, 4000]
+    w = workloads.Workload(f"scheme-split-plan-{hq}", 1, 16, hq, 8, lens, 0.0, 0.0, 64, 1 << 16,
+                           "zipf", seed=31)
+    heads = [(0, h) for h in range(8)] + [(b, (3 * b) % 8) for b in range(1, 16)]
+    run_scheme(w, "K8V4", "K4V2", heads=heads)
+
+
 def test_workload2_sampled():
     w = workloads.workload(2)
     rng = np.random.default_rng(5)
