@@ -19,9 +19,11 @@
 //     term is added back per query head from a running sum;
 //   * the running max is only moved when a tile exceeds it by more than 2^8 (in log2 units),
 //     so the accumulator rescale (a cross-lane shuffle) is rare;
-//   * four waves per workgroup take consecutive slices of one head's tiles (balanced by
-//     bytes: a HIGH tile counts twice a LOW tile) and merge in LDS; each wave keeps DEPTH
-//     tiles in flight in registers, with the page ids of up to 64 tiles preloaded in one
+//   * split-K with a per-head plan: a head's tiles are weighed in work units (HIGH 3, LOW 2,
+//     their measured relative cost) and the head takes one workgroup per ~wt units of its
+//     workgroup slots (long heads of a ragged batch get more); four waves per workgroup take
+//     consecutive slices of the workgroup's range and merge in LDS; each wave keeps a pair
+//     of tiles in flight in registers, with the page ids of up to 64 tiles preloaded in one
 //     lane-indexed register (no load waits on another load);
 //   * a second kernel merges each query head's S (max, sum, output) partials in float32 (a
 //     fused last-workgroup merge needs device-scope fences, which on a multi-XCD part write

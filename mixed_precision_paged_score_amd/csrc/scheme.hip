@@ -9,9 +9,9 @@
 // lo; 2- and 4-bit codes enter as 1024 + 2^(10-b) code against p s_v 2^-(10-b) (an offset of
 // 2^b code steps that the fp32 sums remove at the end), other widths as the code itself.
 //
-// Grid: S workgroups per (request, KV head) (the default decode's split count), 4 waves each;
-// the head's 16-slot tiles (HIGH pages, then LOW half-pages) are cut into 4 S contiguous
-// ranges, one per wave; each wave runs its HIGH tiles, then its LOW tiles, in two loops
+// Grid: S workgroup slots per (request, KV head), 4 waves each, with the default decode's
+// per-head plan: the head uses SH of them (more for a long head), and its 16-slot tiles (HIGH
+// pages, then LOW half-pages) are cut into 4 SH contiguous ranges, one per wave; each wave runs its HIGH tiles, then its LOW tiles, in two loops
 // compiled for the tiers' widths.  Per tile, with v_mfma_f32_16x16x32_f16 and operands read
 // straight from the page (buffer loads; the next tile's are requested before this tile's
 // products): S^T = codes . q^T (lane (c, g): 32 channels of the token in score row c as the
