@@ -617,7 +617,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     const int Hkv = Hq / G;
     const int64_t sstride = int64_t(G) * PART_STRIDE;
     const float *hp = part + ((int64_t(b) * Hkv + h) * S * G + gg) * PART_STRIDE;
-    // the head's splits that wrote partials
+    // The head's split count first; then its splits' (max, sum) and the first PRE splits'
+    // outputs are requested together, so the merge waits for two round trips (a slot past
+    // SH reloads split SH - 1, a cache hit, and gets weight 0)
     const int64_t hi = int64_t(b) * Hkv + h;
     const int SH = active_splits(count_l[2 * hi], count_l[2 * hi + 1], S, wt);
     float ms = M_INIT, ls = 0.0f;
@@ -625,6 +627,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
         ms = hp[lane * sstride];
         ls = hp[lane * sstride + 1];
     }
+    constexpr int PRE = 16;
+    float2 vp[PRE];
+#pragma unroll
+    for (int u = 0; u < PRE; ++u)
+        vp[u] = *reinterpret_cast<const float2 *>(hp + min(u, SH - 1) * sstride + 4 + 2 * lane);
     float M = ms;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -633,7 +640,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
     float r0 = 0.0f, r1 = 0.0f;
-    for (int k0 = 0; k0 < SH; k0 += 8) {
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+        if (u < SH) {
+            r0 += vp[u].x * wf;
+            r1 += vp[u].y * wf;
+        }
+    }
+    for (int k0 = PRE; k0 < SH; k0 += 8) {
         float2 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
