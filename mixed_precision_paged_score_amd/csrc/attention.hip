@@ -257,14 +257,14 @@ __device__ __forceinline__ f4 pair_scores(const Keys<HIGH> &d, const uint4 (*s_q
     return acc;
 }
 
-// LG: the lane also stores its four logits (log2 units, -inf for empty slots) at lg,
-// lg + lg_gt, ... when lg_on, and lanes with ps_on the position of token 4j + (lane & 3) of
-// its tile at lg - ps_off, when lg is not null (the score-accumulating variant)
+// LG: the lane also stores its four logits (log2 units, -inf for empty slots) as one 16-byte
+// store at lg when lg_on, and lanes with ps_on the position of token 4j + (lane & 3) of its
+// tile at lg - ps_off, when lg is not null (the score-accumulating variant)
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> &d, int live_own,
                                                 float sumq, float scale_log2, int lane,
                                                 const Magic &mg, WaveState &st, float *lg,
-                                                int lg_gt, bool lg_on, bool ps_on, int ps_off) {
+                                                bool lg_on, bool ps_on, int ps_off) {
     const int j = lane >> 4, c = lane & 15;
     const bool own_b = c >= 8;
     const uint32_t pw[8] = {d.p0.x, d.p0.y, d.p0.z, d.p0.w, d.p1.x, d.p1.y, d.p1.z, d.p1.w};
@@ -281,11 +281,8 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
         tmax = fmaxf(tmax, L[r]);
     }
     if constexpr (LG) {
-        if (lg) {          // tokens 4j..4j+3 of the lane's tile, GT words apart
-            if (lg_on) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lg[r * lg_gt] = L[r];
-            }
+        if (lg) {          // tokens 4j..4j+3 of the lane's tile and query head, contiguous
+            if (lg_on) *reinterpret_cast<float4 *>(lg) = make_float4(L[0], L[1], L[2], L[3]);
             if (ps_on) reinterpret_cast<uint32_t *>(lg)[-ps_off] = d.ps;
         }
     }
@@ -367,15 +364,15 @@ __device__ __forceinline__ int first_chunk_pids(int t0, int t1, const int32_t *r
     return lane < np ? (HIGH ? row[p0 + lane] : row[C - 1 - (p0 + lane)]) : 0;
 }
 
-// lgh (LG only): the head's tile records [tile][16 positions, then 16 tokens x GT logits]
-// offset to this tier's first tile, the lane's first token (4j) and its query head
+// lgh (LG only): the head's tile records [tile][16 positions, then GT query heads x 16
+// tokens of logits] offset to this tier's first tile, the lane's query head and first token
 template <bool HIGH, bool LG>
 __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const int32_t *row,
                                              int C, const uint8_t *pages,
                                              const uint4 (*s_qa)[64], const uint4 (*s_qb)[64],
                                              float sumq, float scale_log2, int lane,
                                              const Magic &mg, WaveState &st, float *lgh,
-                                             int lg_tile_stride, int lg_gt, bool lg_on,
+                                             int lg_tile_stride, bool lg_on,
                                              bool ps_on, int ps_off, int pid_first) {
     constexpr int TPP = HIGH ? 1 : 2;             // tiles per page
     const bool own_b = (lane & 15) >= 8;
@@ -426,16 +423,14 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
             f4 acc = pair_scores<HIGH>(ka, s_qa, s_qb, lane, mg, acc0);
             vb = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, va, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t), lg_gt, lg_on, ps_on,
-                                      ps_off);
+                                      scale_log2, lane, mg, st, lg_at(t), lg_on, ps_on, ps_off);
             t += 2;
             if (t >= c1) break;
             ka = keys_at(t + 2);
             acc = pair_scores<HIGH>(kb, s_qa, s_qb, lane, mg, acc0);
             va = vals_at(t + 2);
             pair_softmax_pv<HIGH, LG>(acc, vb, own_b ? live_of(t + 1) : live_of(t), sumq_s,
-                                      scale_log2, lane, mg, st, lg_at(t), lg_gt, lg_on, ps_on,
-                                      ps_off);
+                                      scale_log2, lane, mg, st, lg_at(t), lg_on, ps_on, ps_off);
             t += 2;
             if (t >= c1) break;
         }
@@ -445,8 +440,8 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
 // grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
 // take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
 // LG: also store, per tile of the head (HIGH tiles, then LOW tiles), its 16 slots' positions
-// and every token's logit per query head: lg [head][tile][16 + 16 * GT], for the score
-// accumulation
+// and every token's logit per query head: lg [head][tile][16 + GT * 16] (positions, then per
+// query head its 16 tokens), for the score accumulation
 template <bool LG>
 __global__ __launch_bounds__(64 * DEC_WAVES) __attribute__((amdgpu_waves_per_eu(KVC_DEC_OCC)))
 void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
@@ -533,19 +528,20 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 
     Magic mg{0x64646464u, 0x4C004C00u};
     asm volatile("" : "+v"(mg.k8), "+v"(mg.c16));   // keep the constants in VGPRs
-    // LG: tile records of 16 (GT + 1) words; the lane's logit word of token 4j, query head
-    // g0 + gq in tile 0 of the head (stored when gq < G); lanes gq < 4 of the first group
-    // also store the position of token 4j + gq, ps_off words before that logit word
+    // LG: tile records of 16 (GT + 1) words; the lane's logit words of tokens 4j..4j+3,
+    // query head g0 + gq in tile 0 of the head (stored when gq < G); lanes gq < 4 of the first
+    // group also store the position of token 4j + gq, ps_off words before those logits
     const int lg_stride = 16 * (GT + 1);
     float *lgh = nullptr;
-    if constexpr (LG) lgh = lg + int64_t(i) * tiles_cap * lg_stride + 16 + 4 * j * GT + g0 + gq;
+    if constexpr (LG)
+        lgh = lg + int64_t(i) * tiles_cap * lg_stride + 16 + 16 * (g0 + gq) + 4 * j;
     const bool lg_on = gq < G, ps_on = g0 == 0 && gq < 4;
-    const int ps_off = 16 + 4 * j * (GT - 1);
+    const int ps_off = 16 + 15 * gq;
     attend_range<true, LG>(u0, min(u1, qH), nh, row, C, pages, s_qa, s_qb, sumq, scale_log2,
-                           lane, mg, st, lgh, lg_stride, GT, lg_on, ps_on, ps_off, pid_h);
+                           lane, mg, st, lgh, lg_stride, lg_on, ps_on, ps_off, pid_h);
     attend_range<false, LG>(max(u0, qH) - qH, u1 - qH, nl, row, C, pages, s_qa, s_qb, sumq,
                             scale_log2, lane, mg, st,
-                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride, GT, lg_on,
+                            lgh ? lgh + int64_t(qH) * lg_stride : nullptr, lg_stride, lg_on,
                             ps_on, ps_off, pid_l);
     // per query head gq: sums over the lane's 4 groups and over the two column halves
 #pragma unroll
@@ -730,21 +726,11 @@ __global__ __launch_bounds__(256) void acc_index_kernel(
     }
 }
 
-// the GT query heads' logits of one slot
+// the GT query heads' logits of one slot (16 words apart in the tile record)
 template <int GT>
 __device__ __forceinline__ void load_logits(const float *src, float (&l)[GT]) {
-    if constexpr (GT >= 4) {
 #pragma unroll
-        for (int u = 0; u < GT / 4; ++u) {
-            const float4 x = reinterpret_cast<const float4 *>(src)[u];
-            l[4 * u] = x.x; l[4 * u + 1] = x.y; l[4 * u + 2] = x.z; l[4 * u + 3] = x.w;
-        }
-    } else if constexpr (GT == 2) {
-        const float2 x = *reinterpret_cast<const float2 *>(src);
-        l[0] = x.x; l[1] = x.y;
-    } else {
-        l[0] = src[0];
-    }
+    for (int g = 0; g < GT; ++g) l[g] = src[16 * g];
 }
 
 // grid (ceil(max_seqlen / R), B), 4 waves, dynamic LDS ACC_R * Hq + 2 * Hq floats.  The
@@ -807,7 +793,7 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
             if (tile >= tiles_cap) continue;
             const int64_t rb = (int64_t(i) * tiles_cap + tile) * (16 * (G + 1));
             pj[u] = reinterpret_cast<const int32_t *>(lg)[rb + (sl & 15)];
-            lj[u] = rb + 16 + (sl & 15) * G;
+            lj[u] = rb + 16 + (sl & 15);
             if constexpr (GT > 0) load_logits<GT>(lg + lj[u], l[u]);
         }
         if (j0 == 0) __syncthreads();                // the rows and (M, L) are in LDS
@@ -829,7 +815,7 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
             } else {
                 for (int g = 0; g < G; ++g)
                     if (ml[2 * g + 1] > 0.0f)
-                        dst[g] += __builtin_amdgcn_exp2f(lg[lj[u] + g] - ml[2 * g]) /
+                        dst[g] += __builtin_amdgcn_exp2f(lg[lj[u] + 16 * g] - ml[2 * g]) /
                                   ml[2 * g + 1];
             }
         }
