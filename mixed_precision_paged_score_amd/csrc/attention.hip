@@ -437,8 +437,9 @@ __device__ __forceinline__ void attend_range(int t0, int t1, int n_tier, const i
     }
 }
 
-// grid: S workgroups per (request, KV head, group of up to 8 query heads); 4 waves each
-// take consecutive slices of the head's tiles (a HIGH tile counts twice a LOW tile)
+// grid: S workgroup slots per (request, KV head, group of up to 8 query heads), of which the
+// head uses active_splits(); the 4 waves of a workgroup take consecutive slices of its share
+// of the head's tiles, weighed in work units (a HIGH tile DEC_UH, a LOW tile DEC_UL)
 // LG: also store, per tile of the head (HIGH tiles, then LOW tiles), its 16 slots' positions
 // and every token's logit per query head: lg [head][tile][16 + GT * 16] (positions, then per
 // query head its 16 tokens), for the score accumulation
