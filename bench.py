@@ -22,7 +22,9 @@ of the layer after the prompt: decode with score accumulation into one padded ac
 buffer, then kvc_generation_step, captured as one graph) and `prefill` (the causal prefill
 attention of the workload's prompts with the accumulators, kvc_prefill_attention, against the
 fp16 matrix-core peak) and `precision_schemes` (decode over pages placed in other precision
-schemes, kvc_quantize_and_place_scheme + kvc_paged_decode_attention_scheme).
+schemes, kvc_quantize_and_place_scheme + kvc_paged_decode_attention_scheme) and, for a
+workload with re-tier rounds, `retier_round` (one round after `round_every` appended tokens:
+re-score with the previous tiers as ceiling, compact the changed heads, rebuild their pages).
 """
 import argparse
 import dataclasses
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--gen-steps", type=int, default=64,
                     help="steps of the generation loop (decode with score accumulation, then "
                          "the per-step policy) timed after the main steps (0: skip)")
+    ap.add_argument("--no-retier", action="store_true",
+                    help="skip the timing of a re-tier round (workloads with one)")
     ap.add_argument("--no-schemes", action="store_true",
                     help="skip the precision-scheme decode timings")
     ap.add_argument("--no-prefill", action="store_true",
@@ -135,6 +139,53 @@ def spin_cycles(stream, target_us=200.0):
     torch.cuda.synchronize()
     us = max(e0.elapsed_time(e1) * 1e3, 1.0)
     return int(probe * target_us / us)
+
+
+def time_retier_round(w, k, v, acc, ev, stream, spin, reps=3):
+    """A re-tier round of a generation run (the chain-of-thought growth workload has one every
+    128 decode steps).  Setup,
+    outside the timed region and redone for every round timed: the prompt, then `round_every`
+    appended tokens per (request, KV head) and that round's Zipf accumulators over the live
+    positions.  Timed with HIP events on the stream: score_tokens with the previous tiers as
+    ceiling, compact_pages with the changed heads, quantize_and_place in re-tier mode (pages of
+    changed heads rebuilt from their old pages).  Returns (us per round, token-heads re-scored,
+    heads rebuilt)."""
+    from mixed_precision_paged_score_amd import kvc, pipeline, workloads
+    R = int(w.extra["round_every"])
+    times, heads = [], 0
+    for rep in range(reps + 1):                      # the first round is a warm-up
+        g = torch.Generator(device="cuda").manual_seed(w.seed + 99)
+        path = pipeline.GenerationPath(w, max(w.seqlens) + R, "cuda:0")
+        path.prompt(0, acc, k, v)
+        for _ in range(R):
+            kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g, device="cuda")
+            vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g, device="cuda")
+            path.append(0, kn.half(), vn.half())
+        wr = dataclasses.replace(w, seqlens=list(path.lens), seed=w.seed + 1000 * R)
+        acc_r = workloads.make_acc_zipf(wr, "cuda:0")
+        prev = path.packed_state()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        torch.cuda._sleep(spin)
+        e0.record(stream)
+        kvc.score_tokens(path.geom, acc_r, path.cu, path.T, path.max_seqlen, w.alpha_h,
+                         w.alpha_l, w.window, path.tier, path.new_count, prev_tier=prev,
+                         changed=path.changed, dev_status=path.score_status)
+        kvc.compact_pages(path.geom, 0, path.pool, path.new_count, path.ws_compact,
+                          changed=path.changed, old_rows=path.old_rows, old_count=path.old_count)
+        kvc.quantize_and_place(path.geom, 0, path.pool, None, None, path.cu, path.T,
+                               path.max_seqlen, path.tier, path.ws_quant, prev_tier=prev,
+                               changed=path.changed, old_rows=path.old_rows,
+                               old_count=path.old_count)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert path.pool.status() == 0, f"re-tier round status {path.pool.status()}"
+        if rep > 0:
+            times.append(e0.elapsed_time(e1) * 1e3)
+        heads = int(path.changed.sum().item())
+        token_heads = path.T * w.num_kv_heads
+        del path, acc_r, prev
+    return float(np.median(times)), token_heads, heads
 
 
 def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
@@ -480,6 +531,12 @@ def main():
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    retier = None
+    if "round_every" in w.extra and not a.no_retier:
+        r_us, r_th, r_heads = time_retier_round(w, k, v, acc, ev, stream, spin)
+        retier = {"us_per_round": r_us, "token_heads": r_th, "heads_rebuilt": r_heads,
+                  "heads": w.batch * w.num_kv_heads, "round_every": w.extra["round_every"],
+                  "token_heads_per_s": r_th / (r_us * 1e-6)}
     acc_us = None
     if not a.no_acc and nsteps_dec > 0:
         acc_us = time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream)
@@ -544,6 +601,7 @@ def main():
         "decode_GBps": dec_gbps,
         "decode": {"us_per_call": dec_s * 1e6, "GBps": dec_gbps,
                    "frac_hbm": dec_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes},
+        "retier_round": retier,
         "decode_with_score_accumulation": None if acc_us is None else {
             "us_per_call": acc_us,
             "GBps": (dbytes + acc_bytes) / (acc_us / 1e6) / 1e9,
