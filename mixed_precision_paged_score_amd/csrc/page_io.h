@@ -60,6 +60,40 @@ __device__ __forceinline__ void old_codes(const uint8_t *pg, int t, int so, int 
     vpar = par.y;
 }
 
+// old_codes with the value words taken from LDS: u holds the 16 value units (256 B) of the
+// slot's unit group, units 16 ((so & 15) >> 2) .. + 15 of its old page, which the slot's 16
+// lanes loaded together (one 16-byte unit each) in place of 8 scattered 4-byte loads per lane
+__device__ __forceinline__ void old_codes_staged(const uint8_t *pg, const uint4 *u, int t, int so,
+                                                 int c, uint32_t (&kc)[8], uint32_t (&vc)[8],
+                                                 uint32_t &kpar, uint32_t &vpar) {
+    if (t == HIGH) {
+        const uint2 kw = *reinterpret_cast<const uint2 *>(pg + K_OFF + so * 128 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kc[e] = (kw.x >> (8 * e)) & 255u;
+            kc[4 + e] = (kw.y >> (8 * e)) & 255u;
+        }
+    } else {
+        const uint32_t kw = *reinterpret_cast<const uint32_t *>(pg + K_OFF + so * 64 + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kc[e] = (kw >> (4 * k_nib(e))) & 15u;
+    }
+    const int n = c >> 1, r = so & 3;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t *uw = reinterpret_cast<const uint32_t *>(u + 8 * (c & 1) + e);
+        if (t == HIGH) {
+            vc[e] = (uw[n >> 1] >> (4 * (2 * (n & 1) + (r >> 1) + 4 * (r & 1)))) & 15u;
+        } else {
+            const int f = so >> 4;
+            vc[e] = (uw[2 * f + (n >> 2)] >> (2 * (2 * (n & 3) + (r >> 1) + 8 * (r & 1)))) & 3u;
+        }
+    }
+    const uint2 par = *reinterpret_cast<const uint2 *>(pg + PARAM_OFF + 8 * so);
+    kpar = par.x;
+    vpar = par.y;
+}
+
 // fp16 rounding of a code's reconstruction code*scale + zero (one float32 rounding, then RNE)
 __device__ __forceinline__ float recon16(uint32_t code, uint32_t par) {
     const float r = fmaf(float(code), h2f(uint16_t(par & 0xffffu)), h2f(uint16_t(par >> 16)));

@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     const int32_t *__restrict__ oldrank, uint8_t *__restrict__ pages, int32_t *status) {
     __shared__ uint8_t s_v[QP_WAVES][VST_BYTES];
     __shared__ uint16_t s_par[QP_WAVES][LS][4];
+    __shared__ uint4 s_ov[REBUILD ? QP_WAVES : 1][4][16];   // re-tier: old value unit groups
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = blockIdx.y;
     const int nheads = gridDim.y;
@@ -279,69 +280,110 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         if (high) fresh_slots<HS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, true, rg, c, emit_fresh);
         else fresh_slots<LS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, false, rg, c, emit_fresh);
     } else {
-    for (int pass = 0; pass < nslots / 4; ++pass) {
-        const int s = pass * 4 + rg;
-        const bool live = s < m;
-        int pos = 0;
-        if (live) pos = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
-        const int64_t grow = int64_t(lo) + pos;
-        const int src = live ? int(prev[grow * Hkv + h]) : int(FRESH);
-        bool valid = live;
-        if (live) {
-            // a tier never rises, and a fresh token needs its fp16 rows
-            valid = src == T || (src == HIGH && T == LOW) || (src == FRESH && K != nullptr);
-            if (!valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
-        }
-        if (!valid) {
-            store_slot(pg, sv, s_par[wave], high, s, c, false, 0, 0, 0, 0, 0, 0, 0, 0);
-        } else if (src == T) {
-            // unchanged tier: copy the token's codes and parameters from its old page
-            uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
-            const int so = oldrank[int64_t(i) * max_seqlen + pos];
-            const int opage = T == HIGH ? old_rows[int64_t(i) * C + (so >> 4)]
-                                        : old_rows[int64_t(i) * C + C - 1 - (so >> 5)];
-            const int sop = T == HIGH ? (so & 15) : (so & 31);
-            uint32_t kc[8], vc[8], kp, vp;
-            old_codes(pages + int64_t(opage) * PAGE, T, sop, c, kc, vc, kp, vp);
+    // re-tier placement.  Every slot's position, previous tier, old rank and old page id are
+    // looked up for all of the page's passes first (four dependent lookups, each issued for
+    // all passes at once); then each pass reads its old codes (or fp16 rows) and emits.
+    auto rebuild = [&](auto np_c) {
+        constexpr int NP = decltype(np_c)::value;
+        int pos[NP], src[NP], so[NP], opg[NP];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vw0 |= vc[e] << (8 * e);
-                vw1 |= vc[4 + e] << (8 * e);
+        for (int p = 0; p < NP; ++p) {
+            const int s = 4 * p + rg;
+            pos[p] = 0;
+            if (s < m) pos[p] = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            src[p] = int(FRESH);
+            so[p] = 0;
+            if (4 * p + rg < m) {
+                src[p] = int(prev[(int64_t(lo) + pos[p]) * Hkv + h]);
+                so[p] = oldrank[int64_t(i) * max_seqlen + pos[p]];
             }
-            if (high) {
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            opg[p] = 0;
+            if (4 * p + rg < m) {
+                if (src[p] == T && T == LOW)
+                    opg[p] = old_rows[int64_t(i) * C + C - 1 - (so[p] >> 5)];
+                else if (src[p] == HIGH)        // a kept or a demoted HIGH token
+                    opg[p] = old_rows[int64_t(i) * C + (so[p] >> 4)];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int s = 4 * p + rg;
+            const bool live = s < m;
+            bool valid = live;
+            if (live) {
+                // a tier never rises, and a fresh token needs its fp16 rows
+                valid = src[p] == T || (src[p] == HIGH && T == LOW) ||
+                        (src[p] == FRESH && K != nullptr);
+                if (!valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
+            }
+            // a slot read from an old page: its row's 16 lanes load the slot's 256-byte value
+            // unit group together into LDS (the row's slot is the same for all 16 lanes)
+            const int osl = src[p] == HIGH ? (so[p] & 15) : (so[p] & 31);   // old slot
+            uint4 ov = make_uint4(0u, 0u, 0u, 0u);
+            if (valid && src[p] != FRESH)
+                ov = *reinterpret_cast<const uint4 *>(pages + int64_t(opg[p]) * PAGE + V_OFF +
+                                                      16 * (16 * ((osl & 15) >> 2) + c));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            s_ov[wave][rg][c] = ov;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (!valid) {
+                store_slot(pg, sv, s_par[wave], high, s, c, false, 0, 0, 0, 0, 0, 0, 0, 0);
+            } else if (src[p] == T) {
+                // unchanged tier: copy the token's codes and parameters from its old page
+                uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
+                uint32_t kc[8], vc[8], kp, vp;
+                old_codes_staged(pages + int64_t(opg[p]) * PAGE, s_ov[wave][rg], T, osl, c, kc,
+                                 vc, kp, vp);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    kw0 |= kc[e] << (8 * e);
-                    kw1 |= kc[4 + e] << (8 * e);
+                    vw0 |= vc[e] << (8 * e);
+                    vw1 |= vc[4 + e] << (8 * e);
                 }
-            } else {
+                if (high) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kw0 |= kc[e] << (4 * k_nib(e));
-            }
-            store_slot(pg, sv, s_par[wave], high, s, c, true, kw0, kw1, vw0, vw1,
-                       uint16_t(kp & 0xffffu), uint16_t(kp >> 16), uint16_t(vp & 0xffffu),
-                       uint16_t(vp >> 16));
-        } else {
-            // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
-            float xk[8], xv[8];
-            if (src == FRESH) {
-                const int64_t roff = (grow * Hkv + h) * D + 8 * c;
-                load_row8(K + roff, true, xk);
-                load_row8(V + roff, true, xv);
-            } else {
-                const int so = oldrank[int64_t(i) * max_seqlen + pos];   // old HIGH rank
-                const int opage = old_rows[int64_t(i) * C + (so >> 4)];
-                uint32_t kc[8], vc[8], kp, vp;
-                old_codes(pages + int64_t(opage) * PAGE, HIGH, so & 15, c, kc, vc, kp, vp);
+                    for (int e = 0; e < 4; ++e) {
+                        kw0 |= kc[e] << (8 * e);
+                        kw1 |= kc[4 + e] << (8 * e);
+                    }
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xk[e] = recon16(kc[e], kp);
-                    xv[e] = recon16(vc[e], vp);
+                    for (int e = 0; e < 8; ++e) kw0 |= kc[e] << (4 * k_nib(e));
                 }
+                store_slot(pg, sv, s_par[wave], high, s, c, true, kw0, kw1, vw0, vw1,
+                           uint16_t(kp & 0xffffu), uint16_t(kp >> 16), uint16_t(vp & 0xffffu),
+                           uint16_t(vp >> 16));
+            } else {
+                // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
+                float xk[8], xv[8];
+                if (src[p] == FRESH) {
+                    const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
+                    load_row8(K + roff, true, xk);
+                    load_row8(V + roff, true, xv);
+                } else {
+                    uint32_t kc[8], vc[8], kp, vp;
+                    old_codes_staged(pages + int64_t(opg[p]) * PAGE, s_ov[wave][rg], HIGH, osl,
+                                     c, kc, vc, kp, vp);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        xk[e] = recon16(kc[e], kp);
+                        xv[e] = recon16(vc[e], vp);
+                    }
+                }
+                emit_fresh(s, true, xk, xv);
             }
-            emit_fresh(s, true, xk, xv);
         }
-    }
+    };
+    if (high) rebuild(std::integral_constant<int, HS / 4>{});
+    else rebuild(std::integral_constant<int, LS / 4>{});
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
