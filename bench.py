@@ -184,8 +184,18 @@ def time_retier_round(w, k, v, acc, ev, stream, spin, reps=3):
             times.append(e0.elapsed_time(e1) * 1e3)
         heads = int(path.changed.sum().item())
         token_heads = path.T * w.num_kv_heads
+        # algorithmic bytes: the accumulators, previous and new tiers, and for every rebuilt
+        # head its old pages read and its new pages written whole
+        chg = path.changed.cpu().numpy().astype(bool)
+        old_c = path.old_count.cpu().numpy()[chg]
+        new_c = path.new_count.cpu().numpy()[chg]
+
+        def pages(cnt):
+            return int((-(-cnt[:, 0] // 16)).sum() + (-(-cnt[:, 1] // 32)).sum())
+        nbytes = (path.T * w.num_q_heads * 4 + 2 * token_heads
+                  + (pages(old_c) + pages(new_c)) * kvc.PAGE_BYTES)
         del path, acc_r, prev
-    return float(np.median(times)), token_heads, heads
+    return float(np.median(times)), token_heads, heads, nbytes
 
 
 def time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream):
@@ -533,10 +543,12 @@ def main():
     wall = time.perf_counter() - t0
     retier = None
     if "round_every" in w.extra and not a.no_retier:
-        r_us, r_th, r_heads = time_retier_round(w, k, v, acc, ev, stream, spin)
+        r_us, r_th, r_heads, r_bytes = time_retier_round(w, k, v, acc, ev, stream, spin)
         retier = {"us_per_round": r_us, "token_heads": r_th, "heads_rebuilt": r_heads,
                   "heads": w.batch * w.num_kv_heads, "round_every": w.extra["round_every"],
-                  "token_heads_per_s": r_th / (r_us * 1e-6)}
+                  "token_heads_per_s": r_th / (r_us * 1e-6), "algorithmic_bytes": r_bytes,
+                  "GBps": r_bytes / r_us / 1e3,
+                  "frac_hbm": r_bytes / r_us / 1e3 / HBM_PEAK_GBPS}
     acc_us = None
     if not a.no_acc and nsteps_dec > 0:
         acc_us = time_decode_acc(a, path, qs, out, nsteps_dec, ev, stream)
