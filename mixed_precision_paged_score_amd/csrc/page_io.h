@@ -60,23 +60,21 @@ __device__ __forceinline__ void old_codes(const uint8_t *pg, int t, int so, int 
     vpar = par.y;
 }
 
-// old_codes with the value words taken from LDS: u holds the 16 value units (256 B) of the
-// slot's unit group, units 16 ((so & 15) >> 2) .. + 15 of its old page, which the slot's 16
-// lanes loaded together (one 16-byte unit each) in place of 8 scattered 4-byte loads per lane
-__device__ __forceinline__ void old_codes_staged(const uint8_t *pg, const uint4 *u, int t, int so,
-                                                 int c, uint32_t (&kc)[8], uint32_t (&vc)[8],
-                                                 uint32_t &kpar, uint32_t &vpar) {
+// The codes of slot `so` of an old page of tier t from words already loaded: kw its key
+// words (HIGH: 8 bytes, LOW: the first 4), u the 16 value units (256 B) of its unit group,
+// units 16 ((so & 15) >> 2) .. + 15 of the page, staged in LDS by the slot's 16 lanes (one
+// 16-byte unit each) in place of 8 scattered 4-byte loads per lane
+__device__ __forceinline__ void old_codes_staged(uint2 kw, const uint4 *u, int t, int so, int c,
+                                                 uint32_t (&kc)[8], uint32_t (&vc)[8]) {
     if (t == HIGH) {
-        const uint2 kw = *reinterpret_cast<const uint2 *>(pg + K_OFF + so * 128 + 8 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             kc[e] = (kw.x >> (8 * e)) & 255u;
             kc[4 + e] = (kw.y >> (8 * e)) & 255u;
         }
     } else {
-        const uint32_t kw = *reinterpret_cast<const uint32_t *>(pg + K_OFF + so * 64 + 4 * c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kc[e] = (kw >> (4 * k_nib(e))) & 15u;
+        for (int e = 0; e < 8; ++e) kc[e] = (kw.x >> (4 * k_nib(e))) & 15u;
     }
     const int n = c >> 1, r = so & 3;
 #pragma unroll
@@ -89,9 +87,6 @@ __device__ __forceinline__ void old_codes_staged(const uint8_t *pg, const uint4 
             vc[e] = (uw[2 * f + (n >> 2)] >> (2 * (2 * (n & 3) + (r >> 1) + 8 * (r & 1)))) & 3u;
         }
     }
-    const uint2 par = *reinterpret_cast<const uint2 *>(pg + PARAM_OFF + 8 * so);
-    kpar = par.x;
-    vpar = par.y;
 }
 
 // fp16 rounding of a code's reconstruction code*scale + zero (one float32 rounding, then RNE)

@@ -311,24 +311,38 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                     opg[p] = old_rows[int64_t(i) * C + (so[p] >> 4)];
             }
         }
+        // a pass's slot validity and, for a slot read from an old page, its old-page words:
+        // the 16-byte value unit this lane loads for the row (the row's 16 lanes share the
+        // slot and load its 256-byte unit group), key words and parameters
+        auto valid_of = [&](int p) {
+            if (4 * p + rg >= m) return false;
+            // a tier never rises, and a fresh token needs its fp16 rows
+            return src[p] == T || (src[p] == HIGH && T == LOW) || (src[p] == FRESH && K != nullptr);
+        };
+        auto old_words = [&](int p, uint4 &ov, uint2 &okw, uint2 &opar) {
+            ov = make_uint4(0u, 0u, 0u, 0u);
+            okw = opar = make_uint2(0u, 0u);
+            if (!valid_of(p) || src[p] == FRESH) return;
+            const uint8_t *op = pages + int64_t(opg[p]) * PAGE;
+            const int osl = src[p] == HIGH ? (so[p] & 15) : (so[p] & 31);
+            ov = *reinterpret_cast<const uint4 *>(op + V_OFF + 16 * (16 * ((osl & 15) >> 2) + c));
+            if (src[p] == HIGH)
+                okw = *reinterpret_cast<const uint2 *>(op + K_OFF + osl * 128 + 8 * c);
+            else
+                okw.x = *reinterpret_cast<const uint32_t *>(op + K_OFF + osl * 64 + 4 * c);
+            opar = *reinterpret_cast<const uint2 *>(op + PARAM_OFF + 8 * osl);
+        };
+        // pass p + 1's old words are requested before pass p waits on its LDS staging
+        uint4 ov, ovn = make_uint4(0u, 0u, 0u, 0u);
+        uint2 okw, opar, okwn = make_uint2(0u, 0u), oparn = make_uint2(0u, 0u);
+        old_words(0, ov, okw, opar);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int s = 4 * p + rg;
-            const bool live = s < m;
-            bool valid = live;
-            if (live) {
-                // a tier never rises, and a fresh token needs its fp16 rows
-                valid = src[p] == T || (src[p] == HIGH && T == LOW) ||
-                        (src[p] == FRESH && K != nullptr);
-                if (!valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
-            }
-            // a slot read from an old page: its row's 16 lanes load the slot's 256-byte value
-            // unit group together into LDS (the row's slot is the same for all 16 lanes)
+            const bool valid = valid_of(p);
+            if (4 * p + rg < m && !valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
+            if (p + 1 < NP) old_words(p + 1, ovn, okwn, oparn);
             const int osl = src[p] == HIGH ? (so[p] & 15) : (so[p] & 31);   // old slot
-            uint4 ov = make_uint4(0u, 0u, 0u, 0u);
-            if (valid && src[p] != FRESH)
-                ov = *reinterpret_cast<const uint4 *>(pages + int64_t(opg[p]) * PAGE + V_OFF +
-                                                      16 * (16 * ((osl & 15) >> 2) + c));
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             s_ov[wave][rg][c] = ov;
@@ -340,9 +354,9 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
             } else if (src[p] == T) {
                 // unchanged tier: copy the token's codes and parameters from its old page
                 uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
-                uint32_t kc[8], vc[8], kp, vp;
-                old_codes_staged(pages + int64_t(opg[p]) * PAGE, s_ov[wave][rg], T, osl, c, kc,
-                                 vc, kp, vp);
+                uint32_t kc[8], vc[8];
+                old_codes_staged(okw, s_ov[wave][rg], T, osl, c, kc, vc);
+                const uint32_t kp = opar.x, vp = opar.y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     vw0 |= vc[e] << (8 * e);
@@ -369,9 +383,9 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                     load_row8(K + roff, true, xk);
                     load_row8(V + roff, true, xv);
                 } else {
-                    uint32_t kc[8], vc[8], kp, vp;
-                    old_codes_staged(pages + int64_t(opg[p]) * PAGE, s_ov[wave][rg], HIGH, osl,
-                                     c, kc, vc, kp, vp);
+                    uint32_t kc[8], vc[8];
+                    old_codes_staged(okw, s_ov[wave][rg], HIGH, osl, c, kc, vc);
+                    const uint32_t kp = opar.x, vp = opar.y;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         xk[e] = recon16(kc[e], kp);
@@ -380,6 +394,9 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                 }
                 emit_fresh(s, true, xk, xv);
             }
+            ov = ovn;
+            okw = okwn;
+            opar = oparn;
         }
     };
     if (high) rebuild(std::integral_constant<int, HS / 4>{});
