@@ -101,6 +101,12 @@ constexpr int PART_STRIDE = 132;  // floats per partial: m, l, pad, pad, o[128]
 #ifndef KVC_DEC_SPLIT_TARGET
 #define KVC_DEC_SPLIT_TARGET 2048      // workgroups per decode launch to aim for
 #endif
+#ifndef KVC_DEC_SLOTS_MAX
+#define KVC_DEC_SLOTS_MAX 8192         // workgroup slots per decode launch at most
+#endif
+#ifndef KVC_DEC_WT_MIN
+#define KVC_DEC_WT_MIN 128             // work units per workgroup at least (about 50 tiles)
+#endif
 #ifndef KVC_DEC_WT_MAX
 #define KVC_DEC_WT_MAX 256             // work units per workgroup at most (about 100 tiles)
 #endif
@@ -118,8 +124,11 @@ constexpr int DEC_UH = KVC_DEC_UH, DEC_UL = KVC_DEC_UL;   // work units of a HIG
 // one and every workgroup about wt units; the other slots exit at once.  The slot count is
 // the batch's share of the workgroup target, at least 16 and at most 64 (16 and 32 are
 // multiples of the 8 XCDs, which the kernels' slot order relies on), and no more than the
-// largest possible head needs (its tiles are at most the row capacity C + 1); wt spreads that
-// largest head over the slots, but never hands one workgroup more than KVC_DEC_WT_MAX units.
+// largest possible head needs (its tiles are at most the row capacity C + 1), nor more than
+// KVC_DEC_SLOTS_MAX over all heads (a batch of more than 512 heads gets fewer than 16); wt
+// spreads that largest head over the slots, within [KVC_DEC_WT_MIN, KVC_DEC_WT_MAX] units per
+// workgroup: below the minimum a batch of many short heads would be cut into tens of
+// thousands of workgroups of a tile or two.
 struct DecodePlan {
     int splits, wt;
 };
@@ -131,9 +140,14 @@ inline DecodePlan decode_plan(const kvc_geom *g) {
     const int64_t wmax = int64_t(DEC_UH) * (int64_t(g->row_capacity) + 1);
     int64_t wt = (wmax + s0 - 1) / s0;
     if (wt > KVC_DEC_WT_MAX) wt = KVC_DEC_WT_MAX;
+    if (wt < KVC_DEC_WT_MIN) wt = KVC_DEC_WT_MIN;
     if (wt < 1) wt = 1;
     int64_t splits = (wmax + wt - 1) / wt;
     if (splits > s0) splits = s0;
+    // at most KVC_DEC_SLOTS_MAX slots per launch: a slot a head leaves unused still costs a
+    // workgroup launch, which a batch of thousands of heads would pay tens of thousands of times
+    const int64_t cap = KVC_DEC_SLOTS_MAX / heads;
+    if (splits > cap) splits = cap;
     if (splits < 1) splits = 1;
     return {int(splits), int(wt)};
 }

@@ -204,6 +204,18 @@ def test_decode_split_plan_long_and_short_heads(ah, al):
     run_prompt_and_check(w, gen_device=DEV)
 
 
+def test_decode_split_plan_many_heads():
+    """2,048 KV heads (256 requests x 8): the decode grid is capped at 4 slots per head, fewer
+    than the 8 XCDs; short heads turn their splits by head index and the longest ones fill
+    all 4 slots."""
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 160, size=256)]
+    lens[3], lens[100], lens[200] = 3000, 2500, 0
+    w = workloads.Workload("split-plan-2048-heads", 1, 256, 16, 8, lens, 1.0, 0.2, 16, 1 << 16,
+                           "zipf", seed=43)
+    run_prompt_and_check(w, gen_device=DEV, sample_heads=96)
+
+
 def test_workload2_full():
     run_prompt_and_check(workloads.workload(2), gen_device=DEV)
 
