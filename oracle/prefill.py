@@ -82,3 +82,26 @@ def prefill_colsums(q, k, cu, num_kv_heads, scale, b, hq, cols):
         sel = cols < i
         res[sel] += p[cols[sel]]
     return res
+
+
+def prefill_head(q, k, v, scale, block=1024):
+    """One request and query head, the same definition as prefill() taken a block of query rows
+    at a time so that no n x n matrix is held: q, k, v [n][d] -> (out float64 [n][d],
+    acc float64 [n]).  Row i's softmax runs over keys 0..i; acc[t] sums p_it over rows i > t."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[0]
+    out = np.zeros((n, q.shape[1]), np.float64)
+    acc = np.zeros(n, np.float64)
+    for i0 in range(0, n, block):
+        i1 = min(n, i0 + block)
+        s = (q[i0:i1] @ k[:i1].T) * float(scale)              # rows i0..i1-1, keys 0..i1-1
+        rows = np.arange(i0, i1)[:, None]
+        s[np.arange(i1)[None, :] > rows] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[i0:i1] = p @ v[:i1]
+        p[np.arange(i1 - i0), np.arange(i0, i1)] = 0.0         # a token's own query
+        acc[:i1] += p.sum(axis=0)
+    return out, acc

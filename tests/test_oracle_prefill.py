@@ -103,6 +103,23 @@ def test_sampled_helpers_match_full():
                        atol=1e-12)
 
 
+def test_blocked_head_matches_full_and_closed_form():
+    # the row-blocked form (for 32K-token checks) against the unblocked definition on a ragged
+    # size that leaves a partial last block, and against the harmonic closed form
+    rng = np.random.default_rng(5)
+    n = 300
+    q, k, v = _rand(rng, (n, 1, 32)), _rand(rng, (n, 1, 32)), _rand(rng, (n, 1, 32))
+    out, acc = op.prefill(q, k, v, [0, n], 1, 0.17)
+    for block in (1, 64, 77, 1024):
+        bo, ba = op.prefill_head(q[:, 0], k[:, 0], v[:, 0], 0.17, block=block)
+        assert np.allclose(bo, out[:, 0], atol=1e-12)
+        assert np.allclose(ba, acc[:, 0], atol=1e-12)
+    kk = np.tile(_rand(rng, (1, 32)), (n, 1))
+    _, ba = op.prefill_head(q[:, 0], kk, v[:, 0], 0.17, block=64)
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    assert np.allclose(ba, H[n] - H[1:], atol=1e-12)
+
+
 def test_planted_mistake_is_caught():
     # counting the diagonal (a token's own query) breaks the harmonic closed form
     n = 6

@@ -110,6 +110,39 @@ def test_requantize_demotion_is_quantize_of_fp16_reconstruction():
     assert np.all(z4 == z8)
 
 
+def test_demotion_hand_worked_vector():
+    # keys on a grid of 1/16 with a zero point of -3: x_i = -3 + c_i / 16, c_i in 0..255 with
+    # both ends present.  At 8 bits the range is 255/16, the scale exactly 1/16 and the codes
+    # the c_i themselves, so the reconstruction is x itself.  Demoted to 4 bits: range
+    # 15.9375, scale 15.9375 / 15 = 1.0625 (exact in fp16), zero -3, and code_i =
+    # rint((c_i / 16) / 1.0625) = rint(c_i / 17), never a tie (c_i / 17 is at least 1/34 from
+    # a half-integer)
+    c = np.array(list(range(0, 256, 2)), np.int64)
+    c[-1] = 255
+    x = (np.float64(-3.0) + c / 16.0).astype(np.float16)[None]
+    c8, s8, z8 = quant.quantize_rows(x, 8)
+    assert float(s8[0]) == 1.0 / 16 and float(z8[0]) == -3.0
+    assert np.array_equal(c8[0], c)
+    c4, s4, z4 = quant.requantize_from(c8, s8, z8, 4)
+    assert float(s4[0]) == 1.0625 and float(z4[0]) == -3.0
+    # a few by hand: 8/17 = 0.47 -> 0, 10/17 = 0.59 -> 1, 24/17 = 1.41 -> 1, 26/17 = 1.53 -> 2,
+    # 252/17 = 14.82 -> 15, 255/17 = 15 -> 15
+    hand = {0: 0, 8: 0, 10: 1, 24: 1, 26: 2, 128: 8, 252: 15, 255: 15}
+    for ci, want in hand.items():
+        assert c4[0, list(c).index(ci)] == want, ci
+    assert np.array_equal(c4[0], np.floor(c / 17.0 + 0.5).astype(np.int64))
+    # values on a grid of 1/4, codes 0..15 (V4), demoted to 2 bits: range 3.75, scale 1.25
+    # (exact), code = rint(c / 5): 0..2 -> 0, 3..7 -> 1, 8..12 -> 2, 13..15 -> 3
+    cv = np.tile(np.arange(16), 8)
+    xv = (cv / 4.0).astype(np.float16)[None]
+    v4, sv4, zv4 = quant.quantize_rows(xv, 4)
+    assert float(sv4[0]) == 0.25 and np.array_equal(v4[0], cv)
+    v2, sv2, zv2 = quant.requantize_from(v4, sv4, zv4, 2)
+    assert float(sv2[0]) == 1.25 and float(zv2[0]) == 0.0
+    want = np.array([0, 0, 0, 1, 1, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3])
+    assert np.array_equal(v2[0], np.tile(want, 8))
+
+
 def test_fp16_rounding_is_nearest_even():
     # numpy's float32 -> float16 conversion (used for scales) agrees with torch's on ties
     import torch
