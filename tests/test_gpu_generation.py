@@ -1,6 +1,7 @@
 """Generation phase on the GPU vs the oracle's record simulation (MI355X only): per-step
 appends (kvc_append_tokens) and re-tier rounds (score with previous tiers, compact with the
-rebuilt heads, quantize/place in re-tier mode), compared bit-exactly after every round."""
+rebuilt heads, quantize/place in re-tier mode), compared bit-exactly after every round; the
+chain-of-thought workload runs its full 16,384 generated tokens (128 rounds)."""
 import os
 import sys
 
@@ -37,7 +38,26 @@ def _compare_heads(w, path, gen, heads=None):
                                      f"first {bad[:6].tolist()}")
 
 
-def run_generation(w, steps, round_every, sample_heads=None, check_every_round=True):
+def _check_attention(w, path, gen, sample_heads, seed):
+    """Decode attention of the current state (fresh queries) on the tracked heads."""
+    q = workloads.make_queries(w, "cpu", seed)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    path.decode(0, q.to(DEV), out)
+    torch.cuda.synchronize()
+    G = w.group
+    heads = sample_heads or [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    worst = 0.0
+    for (b, h) in heads:
+        kd, vd = gen.head_dequantized(b, h)
+        want = oatt.decode_group(q.numpy()[b, h * G:(h + 1) * G], kd, vd, path.scale)
+        worst = max(worst, parity.assert_close_attention(parity.np_(out[b, h * G:(h + 1) * G]),
+                                                         want))
+    print(f"[generation] attention ok at lengths {path.lens[:3]}...: {len(heads)} heads, "
+          f"max err {worst:.2e}", flush=True)
+
+
+def run_generation(w, steps, round_every, sample_heads=None, check_every_round=True,
+                   attn_every=None, acc_device="cpu"):
     from mixed_precision_paged_score_amd import pipeline
     print(f"[generation] B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
           f"prompt={w.seqlens} steps={steps} round={round_every} P={w.num_pages}", flush=True)
@@ -64,9 +84,10 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
         if (s + 1) % round_every == 0:
             import dataclasses
             wr = dataclasses.replace(w, seqlens=list(path.lens), seed=w.seed + 1000 * (s + 1))
-            acc_r = workloads.make_acc_zipf(wr)
-            path.retier(0, acc_r.to(DEV))
-            tier_o, _, changed_o = gen.retier(acc_r.numpy(), w.alpha_h, w.alpha_l, w.window)
+            # drawn where it is cheapest; both sides receive the same float32 values
+            acc_r = workloads.make_acc_zipf(wr, acc_device).to(DEV)
+            path.retier(0, acc_r)
+            tier_o, _, changed_o = gen.retier(parity.np_(acc_r), w.alpha_h, w.alpha_l, w.window)
             rounds += 1
             if check_every_round:
                 torch.cuda.synchronize()
@@ -74,21 +95,17 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
                 assert np.array_equal(parity.np_(path.tier[:path.T]), tier_o)
                 parity.compare_pool(path.pool, gen.pool)
                 _compare_heads(w, path, gen, sample_heads)
+                print(f"[generation] step {s + 1}: round {rounds} ok, "
+                      f"{int(changed_o.sum())} heads rebuilt, ring head {gen.pool.head}",
+                      flush=True)
+        if attn_every and (s + 1) % attn_every == 0:
+            _check_attention(w, path, gen, sample_heads, seed=s + 1)
     torch.cuda.synchronize()
     assert path.pool.status() == 0
     parity.compare_pool(path.pool, gen.pool)
     _compare_heads(w, path, gen, sample_heads)
     # decode attention over the final state
-    q = workloads.make_queries(w, "cpu", 7)
-    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
-    path.decode(0, q.to(DEV), out)
-    torch.cuda.synchronize()
-    G = w.group
-    heads = sample_heads or [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
-    for (b, h) in heads:
-        kd, vd = gen.head_dequantized(b, h)
-        want = oatt.decode_group(q.numpy()[b, h * G:(h + 1) * G], kd, vd, path.scale)
-        parity.assert_close_attention(parity.np_(out[b, h * G:(h + 1) * G]), want)
+    _check_attention(w, path, gen, sample_heads, seed=7)
     n_demoted = sum(int((t == ogen.LOW).sum()) for t in gen.tiers)
     print(f"[generation] ok: {rounds} rounds, {n_demoted} LOW tokens, ring head {gen.pool.head}",
           flush=True)
@@ -107,9 +124,12 @@ def test_generation_group8_with_pruning_and_page_boundaries():
     run_generation(w, steps=70, round_every=20)
 
 
-def test_workload4_shape_sampled():
-    # 16 requests x (4096-token prompt + 512 generated tokens), 64 query / 8 KV heads, a
-    # re-tier round every 128 steps, 2^18 pages; codes and attention on 6 sampled heads,
-    # tiers and allocator state for all heads after every round
+def test_workload4_full_length():
+    # 16 requests x (4096-token prompt + 16,384 generated tokens), 64 query / 8 KV heads, a
+    # re-tier round every 128 steps (128 rounds), 2^18 pages, in lockstep with the oracle:
+    # after every round the rebuilt-head flags, the tiers of every position and the allocator
+    # state of all 128 heads bit-exact, and every page byte of 6 sampled heads; decode
+    # attention of those heads every 1,024 steps
     w = workloads.workload(4)
-    run_generation(w, steps=512, round_every=128, sample_heads=6)
+    run_generation(w, steps=16384, round_every=128, sample_heads=6, attn_every=1024,
+                   acc_device=DEV)

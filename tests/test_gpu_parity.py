@@ -220,5 +220,50 @@ def test_workload2_full():
     run_prompt_and_check(workloads.workload(2), gen_device=DEV)
 
 
-def test_workload3_sampled():
-    run_prompt_and_check(workloads.workload(3), gen_device=DEV, sample_heads=6)
+def test_workload3_full():
+    """16 requests x 32,768 tokens, 64 query / 8 KV heads, Zipf(1.1) accumulators: tiers,
+    counts and allocator state of every head, every byte of every page of all 128 heads, and
+    attention of every query head on 4 of the workload's 64 decode steps (first, last and two
+    between), each with its own fresh queries."""
+    from mixed_precision_paged_score_amd import pipeline
+    from oracle import attention as oatt, place
+    w = workloads.workload(3)
+    _log(f"[parity] {w.name} full: all heads' pages, attention on 4 decode steps")
+    k, v, acc, _ = _inputs(w, DEV)
+    path = pipeline.PromptPath(w, DEV)
+    path.prompt(0, acc, k, v)
+    steps = [0, 21, 42, 63]
+    outs = []
+    for s in steps:
+        q = workloads.make_queries(w, DEV, s)
+        out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
+        path.decode(0, q, out)
+        outs.append((parity.np_(q), out))
+    torch.cuda.synchronize()
+    assert path.pool.status() == 0
+    tier, count, _ = parity.oracle_score(w, acc)
+    assert np.array_equal(parity.np_(path.tier[:w.total_tokens]), tier)
+    assert np.array_equal(parity.np_(path.new_count), count)
+    opl = opool.Pool(1, w.batch, w.num_kv_heads, w.row_capacity, w.num_pages)
+    opl.compact(0, count)
+    parity.compare_pool(path.pool, opl)
+    kc, vc = parity.np_(k), parity.np_(v)
+    del k, v, acc
+    got = [parity.np_(o) for _, o in outs]
+    cu = w.cu_seqlens()
+    G = w.group
+    npages, worst = 0, 0.0
+    for b in range(w.batch):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for h in range(w.num_kv_heads):
+            npages += parity.compare_head_pages(w, path.pool, 0, b, h, kc, vc, tier)
+            kd, vd = place.head_dequantized(kc[lo:hi, h], vc[lo:hi, h], tier[lo:hi, h])
+            # the 4 steps' query groups in one call: rows are (step, query head)
+            qg = np.concatenate([qn[b, h * G:(h + 1) * G] for qn, _ in outs])
+            want = oatt.decode_group(qg, kd, vd, path.scale).reshape(len(steps), G, 128)
+            for n in range(len(steps)):
+                worst = max(worst, parity.assert_close_attention(
+                    got[n][b, h * G:(h + 1) * G], want[n]))
+        _log(f"[parity] w3 request {b}: pages and attention ok")
+    _log(f"[parity] w3 full ok: {npages} pages bit-exact, attention on steps {steps} "
+         f"max err {worst:.2e}")

@@ -156,3 +156,28 @@ def test_long_requests_sampled(n, hq, hkv):
                                     [0, N], 1, scale)
         parity.assert_close_attention(parity.np_(out[lo:hi, hh]), want_o[:, 0])
         _check_acc(parity.np_(acc[lo:hi, hh]).astype(np.float64), want_a[:, 0])
+
+
+def test_request_of_32768_tokens():
+    # the prompt length the bench times: one 32,768-token request (and a short one), G = 8;
+    # one query head checked in full (every output row and every accumulator) by the oracle's
+    # row-blocked form, two more on sampled rows and columns
+    n, hq, hkv = 32768, 8, 1
+    lens = [n, 777]
+    q, k, v, cu = _inputs(lens, hq, hkv, seed=3276)
+    out, acc, st, scale = _run(q, k, v, cu, hq, hkv)
+    assert st == 0
+    qn, kn, vn = q.numpy(), k.numpy(), v.numpy()
+    rng = np.random.default_rng(32768)
+    hh = int(rng.integers(0, hq))
+    want_o, want_a = op.prefill_head(qn[:n, hh], kn[:n, 0], vn[:n, 0], scale)
+    parity.assert_close_attention(parity.np_(out[:n, hh]), want_o)
+    _check_acc(parity.np_(acc[:n, hh]).astype(np.float64), want_a)
+    print(f"[prefill] 32,768 tokens: head {hh} in full ok", flush=True)
+    for h2 in rng.choice([x for x in range(hq) if x != hh], 2, replace=False):
+        rows = sorted(set([0, 1, 4095, 4096, 16383, n - 1] + list(rng.integers(0, n, 8))))
+        want = op.prefill_rows(qn, kn, vn, cu, hkv, scale, 0, int(h2), rows)
+        parity.assert_close_attention(parity.np_(out[np.array(rows), int(h2)]), want)
+        cols = sorted(set([n - 1, n - 2, n - 65, n - 300] + list(rng.integers(n - 600, n, 4))))
+        want_c = op.prefill_colsums(qn, kn, cu, hkv, scale, 0, int(h2), cols)
+        _check_acc(parity.np_(acc[np.array(cols), int(h2)]).astype(np.float64), want_c)
