@@ -5,7 +5,7 @@
 // page: the memory manager serves attention over the compressed paged cache; "Assumptions"
 // lists standard causal multi-head attention, the page's Eq. 1).
 //
-// Matrix-core design (gfx950, wave64, v_mfma_f32_16x16x16_f16):
+// Matrix-core design (gfx950, wave64, v_mfma_f32_16x16x32_f16):
 //   * a tile is 16 tokens: one HIGH page, or one half of a LOW page;
 //   * S^T = K_codes * Q^T on MFMA: rows are the tile's tokens, columns the G query heads of
 //     the KV head (padded to 16).  Codes become exact fp16 operands with one bit trick
@@ -17,8 +17,9 @@
 //     ~22 bits; O += P' * V_codes on MFMA, with the values' page layout already in the
 //     operand's token-major order (value codes enter as exact small integers); the zero_v
 //     term is added back per query head from a running sum;
-//   * the running max is only moved when a tile exceeds it by more than 2^8 (in log2 units),
-//     so the accumulator rescale (a cross-lane shuffle) is rare;
+//   * the running max is only moved when a tile exceeds it by more than 8 (in log2 units),
+//     so the accumulator rescale (a cross-lane shuffle) is rare; it is also forced for a pair
+//     holding a value scale above 65504 / 2^8, which keeps P' = p * scale_v within fp16;
 //   * split-K with a per-head plan: a head's tiles are weighed in work units (HIGH 3, LOW 2,
 //     their measured relative cost) and the head takes one workgroup per ~wt units of its
 //     workgroup slots (long heads of a ragged batch get more); four waves per workgroup take
@@ -36,6 +37,8 @@ namespace kvc {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_MARGIN = 8.0f;      // log2 units
+constexpr float VS_LAZY_MAX = 255.875f;     // 65504 / 2^RESCALE_MARGIN: larger value
+                                            // scales force the rescale (p <= 1)
 constexpr float M_INIT = -1.0e30f;          // finite "minus infinity" for the running max
 #ifndef KVC_DEC_WAVES
 #define KVC_DEC_WAVES 4
@@ -287,12 +290,18 @@ __device__ __forceinline__ void pair_softmax_pv(const f4 &acc, const Vals<HIGH> 
         }
     }
     tmax = max_over_column(tmax);
+    // P' = p * scale_v enters the value product as fp16.  With the lazy running max p can
+    // reach 2^RESCALE_MARGIN, so a value scale above 65504 / 2^8 could overflow fp16: a pair
+    // holding such a scale forces the rescale, after which p <= 1 and P' <= scale_v <= 65504
+    // (value rows spanning more than ~3,800 at 4 bits or ~770 at 2 bits; never for data of
+    // unit scale, whose path is unchanged)
+    const bool big = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])) > VS_LAZY_MAX;
     // the branch is uniform, but written as a per-lane condition (an opaque lane value that
     // is always 1) the compiler predicates it instead of splitting the accumulators' live
     // ranges, which would copy all 32 of them on the common path
     int one = 1;
     asm volatile("" : "+v"(one));
-    if (one && __ballot(tmax > st.m + RESCALE_MARGIN) != 0ull) {
+    if (one && __ballot(tmax > st.m + RESCALE_MARGIN || big) != 0ull) {
         const float mn = fmaxf(st.m, tmax);
         const float corr = __builtin_amdgcn_exp2f(st.m - mn);
         st.l *= corr;

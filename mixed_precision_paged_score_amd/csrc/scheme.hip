@@ -37,6 +37,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float MARGIN = 8.0f;
+constexpr float VS_LAZY_MAX = 255.875f;   // 65504 / 2^MARGIN
 constexpr float M_INIT = -1.0e30f;
 constexpr float CODE_OFF = 1024.0f;
 
@@ -329,9 +330,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             // the branch is uniform; written as a per-lane condition (an opaque lane value that
             // is always 1) the compiler predicates it instead of splitting the accumulators'
             // live ranges, which would copy all 32 of them on the common path
+            // P' = p s_v enters the value product as fp16.  For 1-, 2- and 4-bit values the
+            // scale carries 2^-(10-b), which keeps P' below 65504 for any fp16 input although
+            // the lazy running max lets p reach 2^MARGIN; with unscaled (8-bit or run-time)
+            // widths a pair holding a scale above 65504 / 2^MARGIN forces the rescale, after
+            // which p <= 1
+            bool big = false;
+            if constexpr (!val_offset<VB>())
+                big = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])) > VS_LAZY_MAX;
             int one = 1;
             asm volatile("" : "+v"(one));
-            if (one && __ballot(mx > m + MARGIN) != 0ull) {
+            if (one && __ballot(mx > m + MARGIN || big) != 0ull) {
                 const float mn = fmaxf(m, mx);
                 const float corr = __builtin_amdgcn_exp2f(m - mn);
                 m = mn;
@@ -552,9 +561,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xf,
                                                                    0xf, false)));   // row_ror:8
             mx = fmaxf(mx, M_INIT);
+            // P' = p s_v enters the value product as fp16.  For 1-, 2- and 4-bit values the
+            // scale carries 2^-(10-b), which keeps P' below 65504 for any fp16 input although
+            // the lazy running max lets p reach 2^MARGIN; with unscaled (8-bit or run-time)
+            // widths a pair holding a scale above 65504 / 2^MARGIN forces the rescale, after
+            // which p <= 1
+            bool big = false;
+            if constexpr (!val_offset<VB>())
+                big = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])) > VS_LAZY_MAX;
             int one = 1;
             asm volatile("" : "+v"(one));
-            if (one && __ballot(mx > m + MARGIN) != 0ull) {
+            if (one && __ballot(mx > m + MARGIN || big) != 0ull) {
                 const float mn = fmaxf(m, mx);
                 const float corr = __builtin_amdgcn_exp2f(m - mn);
                 m = mn;
