@@ -16,7 +16,8 @@ stands in for them):
   3  one layer, 16 requests, 64 / 8 heads, N = 32,768, Zipf(1.1) accumulators,
      alpha 1.0 / 0.2, 2^18 pages, 64 decode steps.
   4  chain-of-thought growth: 16 requests, 64 / 8 heads, 4096-token prompt, 16,384 decode
-     steps, a re-tier round every 128 steps, alpha 1.0 / 0.2, 2^18 pages.
+     steps, a re-tier round every 128 steps whose accumulators add the round's Zipf weights
+     to the previous sums (make_acc_zipf_round), alpha 1.0 / 0.2, 2^18 pages.
   5  64 layers, 64 requests, 64 / 8 heads, N log-uniform in [1024, 32768], per-layer key
      outliers x10 on 3 channels, Zipf(1.1) accumulators, alpha 1.0 / 0.2.
 """
@@ -168,6 +169,37 @@ def make_acc_zipf(w, device="cpu", layer=0, s=1.1):
         mean = (ranks.to(torch.float64) + 1.0) ** (-s) / harm             # [hq][t]
         cnt = (n - 1 - torch.arange(n, device=device, dtype=torch.float64))
         acc[lo:hi, :] = (mean * cnt[None, :]).T.to(torch.float32)
+    return acc
+
+
+def make_acc_zipf_round(w, acc_prev, lens_prev, device="cpu", round_id=0, s=1.1):
+    """Accumulators after a generation round: the previous sums plus the weight the round's
+    new queries gave each earlier token.  w.seqlens are the lengths after the round,
+    lens_prev the lengths before it (acc_prev over those, ragged rows).  Per (request, query
+    head) one fresh seeded Zipf(s) permutation gives the mean weight m_t a new query puts on
+    position t; token t gains m_t times the number of new queries strictly after it
+    (N - N_prev for t < N_prev, N - 1 - t for a token added in the round).  The sums stay
+    'weight received from strictly later queries' (float64 increments, float32 result)."""
+    cu = w.cu_seqlens()
+    cu_prev = np.concatenate([[0], np.cumsum(lens_prev)]).astype(np.int64)
+    acc = torch.zeros((w.total_tokens, w.num_q_heads), dtype=torch.float32, device=device)
+    g = _gen(device, w.seed * 1000 + 900 + 7 * round_id)
+    for b in range(w.batch):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n, n0 = hi - lo, int(lens_prev[b])
+        if n == 0:
+            continue
+        ranks = torch.argsort(torch.rand((w.num_q_heads, n), generator=g, device=device),
+                              dim=1)
+        kk = torch.arange(1, n + 1, device=device, dtype=torch.float64)
+        harm = torch.sum(kk ** (-s))
+        mean = (ranks.to(torch.float64) + 1.0) ** (-s) / harm             # [hq][t]
+        t = torch.arange(n, device=device, dtype=torch.float64)
+        later = torch.where(t < n0, torch.full_like(t, float(n - n0)), n - 1 - t)
+        inc = (mean * later[None, :]).T                                   # [t][hq]
+        if n0 > 0:
+            inc[:n0] += acc_prev[int(cu_prev[b]):int(cu_prev[b]) + n0].to(torch.float64)
+        acc[lo:hi, :] = inc.to(torch.float32)
     return acc
 
 

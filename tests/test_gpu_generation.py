@@ -76,6 +76,7 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
     gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
     g = torch.Generator().manual_seed(w.seed + 99)
     rounds = 0
+    acc_cur, lens_prev = acc.to(acc_device), list(w.seqlens)
     for s in range(steps):
         kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
         vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.float16)
@@ -84,8 +85,12 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
         if (s + 1) % round_every == 0:
             import dataclasses
             wr = dataclasses.replace(w, seqlens=list(path.lens), seed=w.seed + 1000 * (s + 1))
-            # drawn where it is cheapest; both sides receive the same float32 values
-            acc_r = workloads.make_acc_zipf(wr, acc_device).to(DEV)
+            # the round's weights added to the sums (drawn where it is cheapest; both sides
+            # receive the same float32 values)
+            acc_cur = workloads.make_acc_zipf_round(wr, acc_cur, lens_prev, acc_device,
+                                                    rounds + 1)
+            lens_prev = list(path.lens)
+            acc_r = acc_cur.to(DEV)
             path.retier(0, acc_r)
             tier_o, _, changed_o = gen.retier(parity.np_(acc_r), w.alpha_h, w.alpha_l, w.window)
             rounds += 1
