@@ -286,6 +286,23 @@ int kvc_paged_decode_attention(const kvc_geom *geom, int32_t layer, const kvc_po
                                int32_t out_is_fp32, void *workspace, size_t workspace_bytes,
                                kvc_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kvc_paged_decode_attention without a workspace
+ * argument.  The split partials go to a device array inside the library, KVC_STATIC_SCRATCH_BYTES
+ * per GPU, which each GPU the call runs on holds until the process ends; its device address is
+ * looked up on the first call on that GPU (the current device, which must be the stream's).
+ * The call allocates nothing and needs nothing cleared: every partial the combine reads is
+ * written first by the same call.  All calls on one GPU share its array, so calls that overlap
+ * on one GPU (other streams, other threads) race; order them on one stream.  Same arguments,
+ * results and errors as kvc_paged_decode_attention, and KVC_E_WORKSPACE (before any device
+ * work) when kvc_workspace_bytes(geom, KVC_OP_DECODE, 0) exceeds KVC_STATIC_SCRATCH_BYTES
+ * (every batch of up to 8,192 KV heads with G <= 8 fits); KVC_E_HIP if the device or the
+ * array's address cannot be queried. */
+#define KVC_STATIC_SCRATCH_BYTES (64u << 20)
+int kvc_paged_decode_attention_static(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                                      const uint16_t *q, float softmax_scale, void *out,
+                                      int32_t out_is_fp32, kvc_stream_t stream);
+
 /* The same decode attention, and it adds each cached token's attention weight from this
  * query into the significance accumulators: the query is a later token for every cached
  * token, so acc_sum[cu_seqlens[b] + pos][hq] += softmax weight of (b, hq) on the live token at

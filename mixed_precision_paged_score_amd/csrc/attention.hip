@@ -29,6 +29,8 @@
 //   * a second kernel merges each query head's S (max, sum, output) partials in float32 (a
 //     fused last-workgroup merge needs device-scope fences, which on a multi-XCD part write
 //     back and invalidate L2 and cost more than the extra launch).
+#include <mutex>
+
 #include "kvc_internal.h"
 #include "page_load.h"
 #include "workspace.h"
@@ -929,6 +931,62 @@ extern "C" int kvc_paged_decode_attention(const kvc_geom *g, int32_t layer, cons
                                           kvc_stream_t stream) {
     return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, nullptr, nullptr, 0, ws,
                        ws_bytes, stream);
+}
+
+// ---- the decode without a workspace argument ------------------------------------------------
+// The split-K partials live in this file-scope device array instead (one per GPU the library
+// runs on, held until the process ends).  Host code never passes `scratch` itself to a kernel
+// (on the host the name is a stand-in, not a device address): the device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[KVC_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES] = {};
+
+// the current device's scratch address (looked up on its first use); nullptr on failure
+void *scratch_of_current_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_error("kvc_paged_decode_attention_static/hipGetDevice", e);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        set_error("kvc_paged_decode_attention_static/device index", hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_error("kvc_paged_decode_attention_static/hipGetSymbolAddress", e);
+            return nullptr;
+        }
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+}  // namespace
+
+extern "C" int kvc_paged_decode_attention_static(const kvc_geom *g, int32_t layer,
+                                                 const kvc_pool *p, const uint16_t *q,
+                                                 float softmax_scale, void *out,
+                                                 int32_t out_is_fp32, kvc_stream_t stream) {
+    int rc = check_geom(g);
+    if (rc) return rc;
+    // the size check needs no device: a geometry whose partials exceed the array is refused
+    // before anything touches the GPU
+    if (DecodeWs(g, false).bytes > size_t(KVC_STATIC_SCRATCH_BYTES)) return KVC_E_WORKSPACE;
+    rc = check_pool(p);
+    if (rc) return rc;
+    if (!q || !out) return KVC_E_NULL;
+    void *ws = scratch_of_current_device();
+    if (!ws) return KVC_E_HIP;
+    return decode_impl(g, layer, p, q, softmax_scale, out, out_is_fp32, nullptr, nullptr, 0, ws,
+                       size_t(KVC_STATIC_SCRATCH_BYTES), stream);
 }
 
 extern "C" int kvc_paged_decode_attention_acc(const kvc_geom *g, int32_t layer,

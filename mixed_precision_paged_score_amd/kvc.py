@@ -18,6 +18,7 @@ PRUNE, LOW, HIGH, FRESH = 0, 1, 2, 3
 OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC, OP_GENERATE = 1, 2, 3, 4, 5, 6
 OP_PREFILL = 7
 HEAD_DIM, HIGH_SLOTS, LOW_SLOTS, PAGE_BYTES = 128, 16, 32, 3456
+STATIC_SCRATCH_BYTES = 64 << 20     # the device array behind kvc_paged_decode_attention_static
 GEN_MAX_WINDOW = 112
 NO_TOKEN = 255      # generation step: no token left the window
 
@@ -25,7 +26,7 @@ EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_ini
            "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
-           "kvc_paged_decode_attention_scheme"]
+           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -74,6 +75,7 @@ _lib.kvc_compact_pages.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _vp, _sz, _
 _lib.kvc_quantize_and_place.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _sz, _vp]
+_lib.kvc_paged_decode_attention_static.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp]
 _lib.kvc_paged_decode_attention_acc.argtypes = [_G, _i32, _P, _vp, _f32, _vp, _i32, _vp, _vp,
                                                 _i32, _vp, _sz, _vp]
 _lib.kvc_append_tokens.argtypes = [_G, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -89,7 +91,7 @@ _lib.kvc_paged_decode_attention_scheme.argtypes = [_G, _S, _i32, _P, _vp, _f32, 
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
-           "kvc_paged_decode_attention_scheme"):
+           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -193,6 +195,17 @@ def paged_decode_attention(geom, layer, pool, q, softmax_scale, out, ws, stream=
                                            _ptr(q), float(softmax_scale), _ptr(out),
                                            int(out.dtype == torch.float32), _ptr(ws), ws.numel(),
                                            _stream(stream)), "kvc_paged_decode_attention")
+
+
+def paged_decode_attention_static(geom, layer, pool, q, softmax_scale, out, stream=None):
+    """kvc_paged_decode_attention with its partials in the library's own device array (no
+    workspace argument, no allocation)."""
+    _check(_lib.kvc_paged_decode_attention_static(ctypes.byref(geom), int(layer),
+                                                  ctypes.byref(pool.c), _ptr(q),
+                                                  float(softmax_scale), _ptr(out),
+                                                  int(out.dtype == torch.float32),
+                                                  _stream(stream)),
+           "kvc_paged_decode_attention_static")
 
 
 def paged_decode_attention_acc(geom, layer, pool, q, softmax_scale, out, acc_sum, cu_seqlens,
