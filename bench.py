@@ -875,9 +875,8 @@ def main():
     print(json.dumps({"progress": "step timed", "value": res["value"],
                       "decode_frac": res["roofline"]["frac"]}), file=sys.stderr, flush=True)
     if not a.no_extras:
-        if w.name != workloads.workload(3).name:
-            res["w3"] = extras_w3(a, stream, spin, flush)
-            print(json.dumps({"progress": "w3 done"}), file=sys.stderr, flush=True)
+        res["w3"] = extras_w3(a, stream, spin, flush)
+        print(json.dumps({"progress": "w3 done"}), file=sys.stderr, flush=True)
         if not a.no_w4:
             res["w4"] = extras_w4(a, stream, flush)
             print(json.dumps({"progress": "w4 done"}), file=sys.stderr, flush=True)

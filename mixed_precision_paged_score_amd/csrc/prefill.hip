@@ -34,8 +34,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #define KVC_PF_WAVES 8           // forward waves per workgroup (32 queries each)
 #endif
 constexpr int BN = 64;           // keys per block
-constexpr int KS = D + 8;        // LDS key row stride (halves): rows 4 banks apart
-constexpr int VS = BN + 8;       // LDS transposed value row stride (halves)
+// LDS row stride (halves) of the staged key and query tiles.  A lane of the 16x16x32 products
+// reads 16 bytes of row c (c < 16) at column group g (g < 4); measured on gfx950 with
+// SQ_LDS_BANK_CONFLICT, 16 such rows 272 bytes apart (D + 8) cost ~3.9 conflict cycles per
+// ds_read_b128 and 288 bytes apart (D + 16) none
+constexpr int KS = D + 16;
+// LDS row stride (halves) of the transposed value tile.  Within each 32-key block the keys are
+// stored permuted (vt_pos) so that the 8 keys one lane feeds to a V^T P^T product are one
+// 16-byte run: one ds_read_b128 per operand, rows 160 bytes apart, which measured free of bank
+// conflicts (two 8-byte reads 32 bytes apart in 144-byte rows cost ~7.9 conflict cycles each)
+constexpr int VS = BN + 16;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float MARGIN = 8.0f;   // the running max moves only when exceeded by this (log2)
 constexpr float M_INIT = -1.0e30f;
@@ -115,9 +123,15 @@ __device__ __forceinline__ void store_k(const KBlock &kb, _Float16 *s_k, int tid
         *reinterpret_cast<uint4 *>(s_k + ((tid >> 4) + (NT / 16) * i) * KS + 8 * (tid & 15)) =
             kb.k[i];
 }
+// position of key k (within the 64-key block) in a transposed value row: the lane (c, g) of
+// operand u reads keys 32u + 4g + e and 32u + 16 + 4g + e (e < 4) as positions 32u + 8g .. + 7
+__device__ __forceinline__ int vt_pos(int k) {
+    return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
+}
 template <int NT>
 __device__ __forceinline__ void store_v(const VBlock &vb, _Float16 *s_vt, int tid) {
     const int m = tid & 31;
+    const int pm = vt_pos(2 * m);            // keys 2m, 2m + 1 stay adjacent
 #pragma unroll
     for (int i = 0; i < 512 / NT; ++i) {
         const int d8 = (tid >> 5) + (NT / 32) * i;
@@ -128,7 +142,7 @@ __device__ __forceinline__ void store_v(const VBlock &vb, _Float16 *s_vt, int ti
         for (int e = 0; e < 8; ++e) {
             const uint32_t lo16 = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
             const uint32_t hi16 = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            *reinterpret_cast<uint32_t *>(s_vt + (8 * d8 + e) * VS + 2 * m) = lo16 | (hi16 << 16);
+            *reinterpret_cast<uint32_t *>(s_vt + (8 * d8 + e) * VS + pm) = lo16 | (hi16 << 16);
         }
     }
 }
@@ -289,15 +303,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
                 issued = true;
             }
             // O^T += V^T P^T; V^T operand: dim row 16 dt + c, keys in the same order as P^T's k
+            // (32u + 4g + e, then 32u + 16 + 4g + e), stored contiguously by vt_pos
             const _Float16 *vt = s_vt[cur];
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                const _Float16 *vrow = vt + (16 * dt + c) * VS + 4 * g;
+                const _Float16 *vrow = vt + (16 * dt + c) * VS + 8 * g;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const h4 a0 = *reinterpret_cast<const h4 *>(vrow + 32 * u);
-                    const h4 a1 = *reinterpret_cast<const h4 *>(vrow + 32 * u + 16);
-                    const h8 a = h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    const h8 a = *reinterpret_cast<const h8 *>(vrow + 32 * u);
                     o[dt][0] = mfma(a, pb[0][u], o[dt][0]);
                     o[dt][1] = mfma(a, pb[1][u], o[dt][1]);
                 }
