@@ -718,7 +718,7 @@ def extras_w4(a, stream, flush):
     steps whose accumulators add that round's Zipf weights to the sums of the rounds before.  Timed: the prompt's
     compaction round, the decode at the grown length (4,096 + 16,384 tokens) and the last
     re-tier round (rerun from a snapshot of the state before it), each after a 1 GiB scratch
-    write, median and minimum over reps."""
+    read, median and minimum over reps."""
     import torch
     from mixed_precision_paged_score_amd import kvc, pipeline, workloads
     dev = "cuda:0"
