@@ -131,14 +131,16 @@ __global__ __launch_bounds__(256) void quant_scan_kernel(
 }
 
 // grid (ntq, B), 4 waves: wave w ranks heads w, w+4, ... over the tile's tokens with 64-lane
-// ballots.  poslist: HIGH ranks from the front, LOW ranks from the back (positions); oldrank
-// (re-tiering): the rank of each position among its previous tier.
+// ballots.  poslist: HIGH ranks from the front, LOW ranks from the back (positions).
+// Re-tiering: srcdesc at the same index as poslist tells the page writer where a kept token's
+// codes are: its previous tier, its rank among that tier (so its old page, through the old
+// row, and its slot there); FRESH and invalid previous tiers carry page 0.
 __global__ __launch_bounds__(256) void quant_select_kernel(
     const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
     const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
     const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_base2,
-    const int32_t *__restrict__ ok, int32_t *__restrict__ poslist,
-    int32_t *__restrict__ oldrank) {
+    const int32_t *__restrict__ ok, const int32_t *__restrict__ old_rows, int C,
+    int32_t *__restrict__ poslist, uint2 *__restrict__ srcdesc) {
     const int b = blockIdx.y, tq = blockIdx.x;
     const int lo = cu[b], N = cu[b + 1] - lo;
     const int t0 = tq * QTILE;
@@ -153,23 +155,37 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
         int rH = tile_base[tb], rL = tile_base[tb + 1];
         int oH = prev ? tile_base2[tb] : 0, oL = prev ? tile_base2[tb + 1] : 0;
         int32_t *pl = poslist + int64_t(i) * max_seqlen;
-        int32_t *orank = prev ? oldrank + int64_t(i) * max_seqlen : nullptr;
+        uint2 *sd = prev ? srcdesc + int64_t(i) * max_seqlen : nullptr;
+        const int32_t *orow = prev ? old_rows + int64_t(i) * C : nullptr;
         for (int c0 = 0; c0 < nt; c0 += 64) {
             const int tt = c0 + lane;
             const int64_t r = (int64_t(lo) + t0 + tt) * Hkv + h;
             const int x = tt < nt ? tier[r] : PRUNE;
             const uint64_t mH = __ballot(x == HIGH);
             const uint64_t mL = __ballot(x == LOW);
-            if (x == HIGH) pl[rH + __popcll(mH & lt)] = t0 + tt;
-            else if (x == LOW) pl[max_seqlen - 1 - (rL + __popcll(mL & lt))] = t0 + tt;
+            int k = -1;                                  // the token's index in poslist
+            if (x == HIGH) k = rH + __popcll(mH & lt);
+            else if (x == LOW) k = max_seqlen - 1 - (rL + __popcll(mL & lt));
+            if (k >= 0) pl[k] = t0 + tt;
             rH += __popcll(mH);
             rL += __popcll(mL);
             if (prev) {
                 const int y = tt < nt ? prev[r] : PRUNE;
                 const uint64_t nH = __ballot(y == HIGH);
                 const uint64_t nL = __ballot(y == LOW);
-                if (y == HIGH) orank[t0 + tt] = oH + __popcll(nH & lt);
-                else if (y == LOW) orank[t0 + tt] = oL + __popcll(nL & lt);
+                // the old rank is below the head's old count (checked by quant_scan), so the
+                // old page index stays within the head's old row
+                int page = 0, osl = 0;
+                if (y == HIGH) {
+                    const int o = oH + __popcll(nH & lt);
+                    osl = o & (HS - 1);
+                    if (k >= 0) page = orow[o / HS];
+                } else if (y == LOW) {
+                    const int o = oL + __popcll(nL & lt);
+                    osl = o & (LS - 1);
+                    if (k >= 0) page = orow[C - 1 - o / LS];
+                }
+                if (k >= 0) sd[k] = make_uint2(uint32_t(page), uint32_t((y << 8) | osl));
                 oH += __popcll(nH);
                 oL += __popcll(nL);
             }
@@ -216,8 +232,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
     const int32_t *__restrict__ ok, const int32_t *__restrict__ poslist,
-    const uint8_t *__restrict__ prev, const int32_t *__restrict__ old_rows,
-    const int32_t *__restrict__ oldrank, uint8_t *__restrict__ pages, int32_t *status) {
+    const uint2 *__restrict__ srcdesc, uint8_t *__restrict__ pages, int32_t *status) {
     __shared__ uint8_t s_v[QP_WAVES][VST_BYTES];
     __shared__ uint16_t s_par[QP_WAVES][LS][4];
     __shared__ uint4 s_ov[REBUILD ? QP_WAVES : 1][4][16];   // re-tier: old value unit groups
@@ -250,7 +265,6 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     const int32_t *pl = poslist + int64_t(i) * max_seqlen;
     const int lo = cu[b];
     const int rg = lane >> 4, c = lane & 15;
-    const int nslots = high ? HS : LS;
     uint8_t *sv = s_v[wave];
     // quantize the lane's 8 channels of slot s from float rows (or store a zero slot), write
     // the key codes to the page and stage value codes and parameters in LDS
@@ -280,53 +294,43 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         if (high) fresh_slots<HS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, true, rg, c, emit_fresh);
         else fresh_slots<LS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, false, rg, c, emit_fresh);
     } else {
-    // re-tier placement.  Every slot's position, previous tier, old rank and old page id are
-    // looked up for all of the page's passes first (four dependent lookups, each issued for
-    // all passes at once); then each pass reads its old codes (or fp16 rows) and emits.
+    // re-tier placement.  Every slot's position and source (previous tier, old page id, old
+    // slot) are loaded for all of the page's passes first; then each pass reads its old codes
+    // (or fp16 rows) and emits.
     auto rebuild = [&](auto np_c) {
         constexpr int NP = decltype(np_c)::value;
-        int pos[NP], src[NP], so[NP], opg[NP];
+        int pos[NP], sy[NP], opg[NP];     // sy: previous tier << 8 | old slot
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int s = 4 * p + rg;
             pos[p] = 0;
-            if (s < m) pos[p] = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            src[p] = int(FRESH);
-            so[p] = 0;
-            if (4 * p + rg < m) {
-                src[p] = int(prev[(int64_t(lo) + pos[p]) * Hkv + h]);
-                so[p] = oldrank[int64_t(i) * max_seqlen + pos[p]];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
+            sy[p] = int(FRESH) << 8;
             opg[p] = 0;
-            if (4 * p + rg < m) {
-                if (src[p] == T && T == LOW)
-                    opg[p] = old_rows[int64_t(i) * C + C - 1 - (so[p] >> 5)];
-                else if (src[p] == HIGH)        // a kept or a demoted HIGH token
-                    opg[p] = old_rows[int64_t(i) * C + (so[p] >> 4)];
+            if (s < m) {
+                const int64_t x = high ? first + s : max_seqlen - 1 - (first + s);
+                pos[p] = pl[x];
+                const uint2 d = srcdesc[int64_t(i) * max_seqlen + x];
+                opg[p] = int(d.x);
+                sy[p] = int(d.y);
             }
         }
+        auto src_of = [&](int p) { return sy[p] >> 8; };
         // a pass's slot validity and, for a slot read from an old page, its old-page words:
         // the 16-byte value unit this lane loads for the row (the row's 16 lanes share the
         // slot and load its 256-byte unit group), key words and parameters
         auto valid_of = [&](int p) {
             if (4 * p + rg >= m) return false;
             // a tier never rises, and a fresh token needs its fp16 rows
-            return src[p] == T || (src[p] == HIGH && T == LOW) || (src[p] == FRESH && K != nullptr);
+            return src_of(p) == T || (src_of(p) == HIGH && T == LOW) || (src_of(p) == FRESH && K != nullptr);
         };
         auto old_words = [&](int p, uint4 &ov, uint2 &okw, uint2 &opar) {
             ov = make_uint4(0u, 0u, 0u, 0u);
             okw = opar = make_uint2(0u, 0u);
-            if (!valid_of(p) || src[p] == FRESH) return;
+            if (!valid_of(p) || src_of(p) == FRESH) return;
             const uint8_t *op = pages + int64_t(opg[p]) * PAGE;
-            const int osl = src[p] == HIGH ? (so[p] & 15) : (so[p] & 31);
+            const int osl = sy[p] & 255;
             ov = *reinterpret_cast<const uint4 *>(op + V_OFF + 16 * (16 * ((osl & 15) >> 2) + c));
-            if (src[p] == HIGH)
+            if (src_of(p) == HIGH)
                 okw = *reinterpret_cast<const uint2 *>(op + K_OFF + osl * 128 + 8 * c);
             else
                 okw.x = *reinterpret_cast<const uint32_t *>(op + K_OFF + osl * 64 + 4 * c);
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
             const bool valid = valid_of(p);
             if (4 * p + rg < m && !valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
             if (p + 1 < NP) old_words(p + 1, ovn, okwn, oparn);
-            const int osl = src[p] == HIGH ? (so[p] & 15) : (so[p] & 31);   // old slot
+            const int osl = sy[p] & 255;                                   // old slot
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             s_ov[wave][rg][c] = ov;
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (!valid) {
                 store_slot(pg, sv, s_par[wave], high, s, c, false, 0, 0, 0, 0, 0, 0, 0, 0);
-            } else if (src[p] == T) {
+            } else if (src_of(p) == T) {
                 // unchanged tier: copy the token's codes and parameters from its old page
                 uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
                 uint32_t kc[8], vc[8];
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
             } else {
                 // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
                 float xk[8], xv[8];
-                if (src[p] == FRESH) {
+                if (src_of(p) == FRESH) {
                     const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
                     load_row8(K + roff, true, xk);
                     load_row8(V + roff, true, xv);
@@ -592,7 +596,7 @@ extern "C" int kvc_quantize_and_place(const kvc_geom *g, int32_t layer, const kv
     int32_t *tile_base2 = rebuild ? reinterpret_cast<int32_t *>(w + L.tile_base2) : nullptr;
     int32_t *ok = reinterpret_cast<int32_t *>(w + L.ok);
     int32_t *poslist = reinterpret_cast<int32_t *>(w + L.poslist);
-    int32_t *oldrank = rebuild ? reinterpret_cast<int32_t *>(w + L.oldrank) : nullptr;
+    uint2 *srcdesc = rebuild ? reinterpret_cast<uint2 *>(w + L.srcdesc) : nullptr;
     const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
     const int nheads = B * Hkv;
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
@@ -608,18 +612,19 @@ extern "C" int kvc_quantize_and_place(const kvc_geom *g, int32_t layer, const kv
     rc = launch_check("kvc_quantize_and_place/scan");
     if (rc) return rc;
     hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
-                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, poslist, oldrank);
+                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, old_rows, C,
+                       poslist, srcdesc);
     rc = launch_check("kvc_quantize_and_place/select");
     if (rc) return rc;
     const dim3 grid((C + QP_WAVES - 1) / QP_WAVES, nheads);
     if (rebuild)
         hipLaunchKernelGGL(quant_pages_kernel<true>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv,
-                           C, max_seqlen, rows_l, count_l, ok, poslist, prev_tier, old_rows,
-                           oldrank, p->pages, p->dev_status);
+                           C, max_seqlen, rows_l, count_l, ok, poslist, srcdesc, p->pages,
+                           p->dev_status);
     else
         hipLaunchKernelGGL(quant_pages_kernel<false>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu,
-                           Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, nullptr, nullptr,
-                           nullptr, p->pages, p->dev_status);
+                           Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, nullptr, p->pages,
+                           p->dev_status);
     return launch_check("kvc_quantize_and_place/pages");
 }
 
@@ -664,7 +669,8 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
     rc = launch_check("kvc_quantize_and_place_scheme/scan");
     if (rc) return rc;
     hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, nullptr, cu,
-                       Hkv, L.ntq, max_seqlen, tile_base, nullptr, ok, poslist, nullptr);
+                       Hkv, L.ntq, max_seqlen, tile_base, nullptr, ok, nullptr, C, poslist,
+                       nullptr);
     rc = launch_check("kvc_quantize_and_place_scheme/select");
     if (rc) return rc;
     hipLaunchKernelGGL(scheme_pages_kernel, dim3((C + QP_WAVES - 1) / QP_WAVES, nheads),

@@ -77,7 +77,7 @@ constexpr int QTILE = 256;        // tokens per rank tile
 
 struct QuantWs {
     int ntq;
-    size_t tile_cnt, tile_base, tile_cnt2, tile_base2, ok, poslist, oldrank, bytes;
+    size_t tile_cnt, tile_base, tile_cnt2, tile_base2, ok, poslist, srcdesc, bytes;
     QuantWs(const kvc_geom *g, int max_seqlen) {
         ntq = (max_seqlen + QTILE - 1) / QTILE;
         if (ntq < 1) ntq = 1;
@@ -90,8 +90,10 @@ struct QuantWs {
         tile_base2 = tile_cnt2 + cnt;
         ok = tile_base2 + cnt;              // per head: write its pages; [heads] = entry status
         poslist = ok + align256(sizeof(int32_t) * (heads + 1));
-        oldrank = poslist + pl;             // per head and position: rank in its old tier
-        bytes = oldrank + pl;
+        // re-tiering: per head and new slot index (as poslist) where the token's codes come
+        // from, {old page id, previous tier << 8 | slot in the old page}
+        srcdesc = poslist + pl;
+        bytes = srcdesc + 2 * pl;
     }
 };
 
