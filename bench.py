@@ -71,6 +71,8 @@ def parse():
                     help="skip the chain-of-thought workload")
     ap.add_argument("--eager", action="store_true",
                     help="launch every library call from Python instead of replaying HIP graphs")
+    ap.add_argument("--group-sweep", action="store_true",
+                    help="only time the decode at G = 1, 2, 4, 8, 16 query heads per KV head")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM counters)")
     return ap.parse_args()
@@ -667,6 +669,48 @@ def time_schemes(w, k, v, acc, qs, stream):
     return res
 
 
+def decode_by_group(a, stream, flush, groups=(1, 2, 4, 8, 16)):
+    """The decode at G = 1, 2, 4, 8 and 16 query heads per KV head, on the 16 x 32,768-token
+    shape with its 8 KV heads and the same keys and values.  The score product is one 16x16
+    matrix-core tile per pair of 16-token tiles (G query heads of tile A and of tile B), so at
+    G < 8 part of its columns are zero: per G, microseconds per call back to back (64 calls)
+    and cold (a 1 GiB scratch read before each), against the algorithmic bytes."""
+    import torch
+    from mixed_precision_paged_score_amd import pipeline, workloads
+    dev = "cuda:0"
+    base = workloads.workload(3)
+    k, v = workloads.make_kv(base, dev)
+    timer = Timer(stream)
+    res = {}
+    for G in groups:
+        w = dataclasses.replace(base, name=f"w3-16x32768-g{G}", num_q_heads=base.num_kv_heads * G)
+        acc = workloads.make_acc(w, k, dev)
+        path = pipeline.PromptPath(w, dev)
+        path.prompt(0, acc, k, v)
+        qs = [workloads.make_queries(w, dev, s) for s in range(8)]
+        out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+        for q in qs[:2]:
+            path.decode(0, q, out)
+        torch.cuda.synchronize()
+        e0 = timer.ev()
+        for _ in range(8):
+            for q in qs:
+                path.decode(0, q, out)
+        e1 = timer.ev()
+        torch.cuda.synchronize()
+        us = timer.us(e0, e1) / (8 * len(qs))
+        cold = cold_reps(max(a.cold_reps // 2, 1), flush,
+                         lambda r: path.decode(0, qs[r % len(qs)], out), timer)
+        cnt = path.new_count.cpu().numpy()
+        byts = decode_algorithmic_bytes(cnt, w.batch, w.num_q_heads)
+        res[str(G)] = {"us_per_call": us, "GBps": byts / us / 1e3,
+                       "frac_hbm": byts / us / 1e3 / HBM_PEAK_GBPS, "algorithmic_bytes": byts,
+                       "cold": stats(cold, byts), "status": path.pool.status()}
+        del path, acc, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def extras_w3(a, stream, spin, flush):
     """The 16 x 32,768-token single-layer workload: its step (compaction round + 64 decode
     steps, graphs) and, on its data, the accumulating decode, the generation loop, the prefill
@@ -815,6 +859,13 @@ def main():
     a = parse()
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.group_sweep:
+        import torch
+        torch.cuda.set_device(0)
+        flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        print(json.dumps({"decode_by_group": decode_by_group(a, torch.cuda.current_stream(),
+                                                             flush)}))
         return
     if a.gpus != 1:
         print(json.dumps({"error": "the benchmark measures one GPU; --gpus above 1 is not supported (the path would shard requests and KV heads across GPUs, each running this same single-GPU step)",

@@ -194,6 +194,13 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
 }
 
 constexpr int QP_WAVES = 4;
+#ifndef KVC_RB_AHEAD
+#define KVC_RB_AHEAD 2
+#endif
+// re-tier passes whose old words are in flight ahead of the pass being written: at 2 the
+// kernel holds 80 VGPRs (6 waves per SIMD); 1 and 3 measured slower on the chain-of-thought
+// re-tier round (325 and 324 us against 308)
+constexpr int RB_AHEAD = KVC_RB_AHEAD;
 constexpr int VST_BYTES = LS * D;     // per-wave staging of value codes (LOW page size)
 
 // prompt placement of one page: NP passes of 4 slots (one 16-lane group per slot).  The
@@ -299,17 +306,16 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     // (or fp16 rows) and emits.
     auto rebuild = [&](auto np_c) {
         constexpr int NP = decltype(np_c)::value;
-        int pos[NP], sy[NP], opg[NP];     // sy: previous tier << 8 | old slot
+        // (a FRESH slot's position, needed only for its fp16 rows, is loaded when used)
+        int sy[NP], opg[NP];     // sy: previous tier << 8 | old slot
+        auto index_of = [&](int s) -> int64_t { return high ? first + s : max_seqlen - 1 - (first + s); };
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int s = 4 * p + rg;
-            pos[p] = 0;
             sy[p] = int(FRESH) << 8;
             opg[p] = 0;
             if (s < m) {
-                const int64_t x = high ? first + s : max_seqlen - 1 - (first + s);
-                pos[p] = pl[x];
-                const uint2 d = srcdesc[int64_t(i) * max_seqlen + x];
+                const uint2 d = srcdesc[int64_t(i) * max_seqlen + index_of(s)];
                 opg[p] = int(d.x);
                 sy[p] = int(d.y);
             }
@@ -336,20 +342,23 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                 okw.x = *reinterpret_cast<const uint32_t *>(op + K_OFF + osl * 64 + 4 * c);
             opar = *reinterpret_cast<const uint2 *>(op + PARAM_OFF + 8 * osl);
         };
-        // pass p + 1's old words are requested before pass p waits on its LDS staging
-        uint4 ov, ovn = make_uint4(0u, 0u, 0u, 0u);
-        uint2 okw, opar, okwn = make_uint2(0u, 0u), oparn = make_uint2(0u, 0u);
-        old_words(0, ov, okw, opar);
+        // the old words of pass p + RB_AHEAD are requested before pass p waits on its LDS
+        // staging (the loop is unrolled: the arrays are registers, RB_AHEAD + 1 sets live)
+        uint4 ov[NP];
+        uint2 okw[NP], opar[NP];
+#pragma unroll
+        for (int p = 0; p < RB_AHEAD && p < NP; ++p) old_words(p, ov[p], okw[p], opar[p]);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int s = 4 * p + rg;
             const bool valid = valid_of(p);
             if (4 * p + rg < m && !valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
-            if (p + 1 < NP) old_words(p + 1, ovn, okwn, oparn);
+            if (p + RB_AHEAD < NP)
+                old_words(p + RB_AHEAD, ov[p + RB_AHEAD], okw[p + RB_AHEAD], opar[p + RB_AHEAD]);
             const int osl = sy[p] & 255;                                   // old slot
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            s_ov[wave][rg][c] = ov;
+            s_ov[wave][rg][c] = ov[p];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -359,8 +368,8 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                 // unchanged tier: copy the token's codes and parameters from its old page
                 uint32_t kw0 = 0, kw1 = 0, vw0 = 0, vw1 = 0;
                 uint32_t kc[8], vc[8];
-                old_codes_staged(okw, s_ov[wave][rg], T, osl, c, kc, vc);
-                const uint32_t kp = opar.x, vp = opar.y;
+                old_codes_staged(okw[p], s_ov[wave][rg], T, osl, c, kc, vc);
+                const uint32_t kp = opar[p].x, vp = opar[p].y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     vw0 |= vc[e] << (8 * e);
@@ -383,13 +392,13 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                 // fresh rows, or a HIGH -> LOW demotion from the old K8V4 reconstruction
                 float xk[8], xv[8];
                 if (src_of(p) == FRESH) {
-                    const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
+                    const int64_t roff = ((int64_t(lo) + pl[index_of(s)]) * Hkv + h) * D + 8 * c;
                     load_row8(K + roff, true, xk);
                     load_row8(V + roff, true, xv);
                 } else {
                     uint32_t kc[8], vc[8];
-                    old_codes_staged(okw, s_ov[wave][rg], HIGH, osl, c, kc, vc);
-                    const uint32_t kp = opar.x, vp = opar.y;
+                    old_codes_staged(okw[p], s_ov[wave][rg], HIGH, osl, c, kc, vc);
+                    const uint32_t kp = opar[p].x, vp = opar[p].y;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         xk[e] = recon16(kc[e], kp);
@@ -398,9 +407,6 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
                 }
                 emit_fresh(s, true, xk, xv);
             }
-            ov = ovn;
-            okw = okwn;
-            opar = oparn;
         }
     };
     if (high) rebuild(std::integral_constant<int, HS / 4>{});
