@@ -14,10 +14,17 @@ token demoted to LOW is re-quantized from the fp16 rounding of its K8V4 reconstr
 The state is a per-(request, KV head) record of every live token: position -> (tier, key
 codes, key scale, key zero, value codes, value scale, value zero).  Page images are a pure
 function of these records.
+
+With a precision scheme (``scheme.Scheme``; the DiffKV review page's free-parameter ledger
+compares K8V4, K4V8, K8V2, K4V2, K2V4 and K4V1) every code width above is the scheme's width
+for the tier -- a generated token enters at the HIGH widths, a demotion re-quantizes the fp16
+rounding of the HIGH reconstruction at the LOW widths -- and the page images are the scheme's
+layout (``scheme.build_page``).
 """
 import numpy as np
 
 from . import layout, quant, score as osc
+from . import scheme as osch
 from .pool import Pool
 
 HIGH, LOW, PRUNE, FRESH = 2, 1, 0, 3
@@ -27,8 +34,10 @@ class Generation:
     """`track`: the (request, KV head) pairs whose code records are kept (default: all).
     Tiers, counts and the allocator are always simulated for every head."""
 
-    def __init__(self, batch, num_kv_heads, row_capacity, num_pages, layer=0, track=None):
+    def __init__(self, batch, num_kv_heads, row_capacity, num_pages, layer=0, track=None,
+                 scheme=None):
         self.B, self.H = batch, num_kv_heads
+        self.scheme = scheme
         self.layer = layer
         self.pool = Pool(1, batch, num_kv_heads, row_capacity, num_pages)
         self.rec = [[dict() for _ in range(num_kv_heads)] for _ in range(batch)]
@@ -39,17 +48,23 @@ class Generation:
                                                            for h in range(num_kv_heads)}
 
     # ---- helpers ---------------------------------------------------------------------
-    @staticmethod
-    def _record(tier, k_row, v_row):
-        kc, ks, kz = quant.quantize_rows(k_row[None], quant.K_BITS[tier])
-        vc, vs, vz = quant.quantize_rows(v_row[None], quant.V_BITS[tier])
+    def bits(self, tier):
+        """(key bits, value bits) of a tier: the scheme's, else K8V4 / K4V2."""
+        if self.scheme is not None:
+            return self.scheme.bits[tier]
+        return quant.K_BITS[tier], quant.V_BITS[tier]
+
+    def _record(self, tier, k_row, v_row):
+        kb, vb = self.bits(tier)
+        kc, ks, kz = quant.quantize_rows(k_row[None], kb)
+        vc, vs, vz = quant.quantize_rows(v_row[None], vb)
         return (tier, kc[0], ks[0], kz[0], vc[0], vs[0], vz[0])
 
-    @staticmethod
-    def _demote(r):
+    def _demote(self, r):
         _, kc, ks, kz, vc, vs, vz = r
-        k2 = quant.requantize_from(kc[None], np.array([ks]), np.array([kz]), quant.K_BITS[LOW])
-        v2 = quant.requantize_from(vc[None], np.array([vs]), np.array([vz]), quant.V_BITS[LOW])
+        kb, vb = self.bits(LOW)
+        k2 = quant.requantize_from(kc[None], np.array([ks]), np.array([kz]), kb)
+        v2 = quant.requantize_from(vc[None], np.array([vs]), np.array([vz]), vb)
         return (LOW, k2[0][0], k2[1][0], k2[2][0], v2[0][0], v2[1][0], v2[2][0])
 
     def counts(self):
@@ -90,8 +105,9 @@ class Generation:
                     pos = np.nonzero(tier[lo:hi, h] == x)[0]
                     if len(pos) == 0:
                         continue
-                    kc, ks, kz = quant.quantize_rows(k[lo + pos, h], quant.K_BITS[x])
-                    vc, vs, vz = quant.quantize_rows(v[lo + pos, h], quant.V_BITS[x])
+                    kb, vb = self.bits(x)
+                    kc, ks, kz = quant.quantize_rows(k[lo + pos, h], kb)
+                    vc, vs, vz = quant.quantize_rows(v[lo + pos, h], vb)
                     for n, t in enumerate(pos):
                         self.rec[b][h][int(t)] = (x, kc[n], ks[n], kz[n], vc[n], vs[n], vz[n])
 
@@ -206,11 +222,14 @@ class Generation:
             pages = []
             for p0 in range(0, len(items), per):
                 chunk = items[p0:p0 + per]
-                pages.append(layout.build_page(
-                    t, np.stack([r[1] for _, r in chunk]), np.stack([r[4] for _, r in chunk]),
-                    [r[2] for _, r in chunk], [r[3] for _, r in chunk],
-                    [r[5] for _, r in chunk], [r[6] for _, r in chunk],
-                    [p for p, _ in chunk]))
+                fields = (np.stack([r[1] for _, r in chunk]), np.stack([r[4] for _, r in chunk]),
+                          [r[2] for _, r in chunk], [r[3] for _, r in chunk],
+                          [r[5] for _, r in chunk], [r[6] for _, r in chunk],
+                          [p for p, _ in chunk])
+                if self.scheme is None:
+                    pages.append(layout.build_page(t, *fields))
+                else:
+                    pages.append(osch.build_page(self.scheme, t, *fields))
             out[t] = pages
         return out
 

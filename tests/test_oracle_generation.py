@@ -184,3 +184,110 @@ def test_step_decisions_follow_the_prompt_scoring_rule():
         seen |= set(dec.ravel().tolist())
     assert seen == {ogen.PRUNE, ogen.LOW, ogen.HIGH}
     g.pool.check_invariants()
+
+
+# ---- precision schemes in the generation phase ---------------------------------------------
+
+def test_scheme_all_high_generation_equals_scheme_prompt_of_the_whole_sequence():
+    # with nothing demoted or pruned, appends and rounds under a scheme leave exactly the
+    # pages a scheme prompt placement of the whole sequence writes (oracle/scheme.head_pages,
+    # pinned by hand-packed bytes in test_oracle_scheme)
+    from oracle import scheme as osch
+    rng = np.random.default_rng(20)
+    B, H, n0, steps = 2, 2, 21, 40
+    sc = osch.Scheme.named("K4V8", "K2V4")
+    ks, vs = zip(*[_data(rng, 1, H, n0 + steps) for _ in range(B)])
+    g = ogen.Generation(B, H, 16, 400, scheme=sc)
+    cu = np.array([0, n0, 2 * n0])
+    g.prompt(np.concatenate([k[:n0] for k in ks]), np.concatenate([v[:n0] for v in vs]),
+             np.full((2 * n0, H), ogen.HIGH, np.uint8), cu)
+    for s in range(steps):
+        g.append(np.stack([k[n0 + s] for k in ks]), np.stack([v[n0 + s] for v in vs]))
+        if s % 16 == 15:
+            n = n0 + s + 1
+            g.retier(np.ones((B * n, 2 * H), np.float32), 0.0, 0.0, 4)
+    for b in range(B):
+        for h in range(H):
+            want = osch.head_pages(ks[b][:, h], vs[b][:, h], np.full(n0 + steps, ogen.HIGH), sc)
+            got = g.head_pages(b, h)
+            assert len(got[ogen.HIGH]) == len(want[ogen.HIGH]) and not got[ogen.LOW]
+            for a, e in zip(got[ogen.HIGH], want[ogen.HIGH]):
+                assert np.array_equal(a, e)
+
+
+def test_scheme_demotion_requantizes_the_high_reconstruction_read_from_the_page():
+    # under K8V2-K4V1 a token demoted by a round carries, in its LOW page, the codes of its
+    # HIGH page's reconstruction (read back from the page bytes before the round) rounded to
+    # fp16 and quantized at 4 / 1 bits; survivors keep their page bytes' codes
+    from oracle import scheme as osch
+    rng = np.random.default_rng(21)
+    B, H, G, n0 = 1, 2, 2, 64
+    sc = osch.Scheme.named("K8V2", "K4V1")
+    k0, v0 = _data(rng, B, H, n0)
+    cu = np.array([0, n0])
+    g = ogen.Generation(B, H, 16, 400, scheme=sc)
+    g.prompt(k0, v0, np.full((n0, H), ogen.HIGH, np.uint8), cu)
+
+    def read_all(h):
+        out = {}
+        pages = g.head_pages(0, h)
+        for t in (ogen.HIGH, ogen.LOW):
+            for img in pages[t]:
+                pos = img[osch.POS_OFF:].copy().view(np.int32)
+                m = int((pos >= 0).sum())
+                kc, vc, ks_, kz, vs_, vz, ps = osch.read_page(img, sc, t, m)
+                for n in range(m):
+                    out[int(ps[n])] = (t, kc[n], ks_[n], kz[n], vc[n], vs_[n], vz[n])
+        return out
+    before = {h: read_all(h) for h in range(H)}
+    acc = np.full((n0, H * G), 1e-6, np.float32)
+    acc[::3] = 10.0                    # every third token keeps HIGH, the rest fall to LOW
+    tier, _, _ = g.retier(acc, 1.0, 1e-30, 4)
+    n_dem = 0
+    for h in range(H):
+        after = read_all(h)
+        for pos, r in after.items():
+            old = before[h][pos]
+            if r[0] == old[0]:
+                assert all(np.array_equal(x, y) for x, y in zip(r[1:], old[1:]))
+                continue
+            assert old[0] == ogen.HIGH and r[0] == ogen.LOW
+            n_dem += 1
+            xk = (old[1].astype(np.float64) * np.float64(old[2]) + np.float64(old[3]))
+            xv = (old[4].astype(np.float64) * np.float64(old[5]) + np.float64(old[6]))
+            kc, kscale, kzero = quant.quantize_rows(xk.astype(np.float32).astype(np.float16)[None], 4)
+            vc, vscale, vzero = quant.quantize_rows(xv.astype(np.float32).astype(np.float16)[None], 1)
+            assert np.array_equal(r[1], kc[0]) and r[2] == kscale[0] and r[3] == kzero[0]
+            assert np.array_equal(r[4], vc[0]) and r[5] == vscale[0] and r[6] == vzero[0]
+            assert set(np.unique(r[4])) <= {0, 1} and r[1].max() <= 15
+    assert n_dem > 20
+
+
+def test_default_scheme_generation_dequantizes_as_the_default_layout():
+    # the K8V4-K4V2 scheme stores the same codes as the default layout in another byte order:
+    # the same steps give the same live tokens, codes and dequantized rows
+    from oracle import scheme as osch
+    rng = np.random.default_rng(22)
+    B, H, G, n0, W = 2, 2, 2, 50, 6
+    k0, v0 = _data(rng, B, H, B * n0)
+    acc0 = (rng.random((B * n0, H * G)) * np.arange(B * n0)[::-1, None] * 0.05).astype(np.float32)
+    cu = np.array([0, n0, 2 * n0])
+    tier0, _, _ = osc.score_tokens(acc0, cu, H, 1.0, 0.2, W)
+    a = ogen.Generation(B, H, 16, 800)
+    b_ = ogen.Generation(B, H, 16, 800, scheme=osch.Scheme.named("K8V4", "K4V2"))
+    a.prompt(k0, v0, tier0, cu)
+    b_.prompt(k0, v0, tier0, cu)
+    for s in range(20):
+        kn, vn = _data(rng, B, H, B)
+        acc = (rng.random((sum(a.lens) + B, H * G)) * 2.0).astype(np.float32)
+        da = a.step(kn, vn, acc, 1.0, 0.2, W)
+        db = b_.step(kn, vn, acc, 1.0, 0.2, W)
+        assert np.array_equal(da, db)
+    for b in range(B):
+        for h in range(H):
+            ka, va = a.head_dequantized(b, h)
+            kb, vb = b_.head_dequantized(b, h)
+            assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+            pa, pb = a.head_pages(b, h), b_.head_pages(b, h)
+            for t in (ogen.HIGH, ogen.LOW):
+                assert len(pa[t]) == len(pb[t])
