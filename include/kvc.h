@@ -223,13 +223,17 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
                            const int32_t *old_rows, const int32_t *old_count,
                            void *workspace, size_t workspace_bytes, kvc_stream_t stream);
 
-/* Prompt placement under a precision scheme (DiffKV review page: the free-parameter ledger's
+/* Placement under a precision scheme (DiffKV review page: the free-parameter ledger's
  * comparison of K8V4, K4V8, K8V2, K4V2, K2V4 and K4V1; referee minor comment 5 for the
- * K8V4-K4V2 / K8V4-Prune configurations).  Same contract as kvc_quantize_and_place in prompt
- * mode (same ranks, pages and slots; the K8V4-Prune and no-prune configurations are threshold
- * settings of kvc_score_tokens), but each tier is quantized at the scheme's bit widths with the
- * same per-token min/max quantizer (2^b - 1 levels) and written in this layout (bits counted
- * little-endian from a field's first byte; S = 16 slots for HIGH, 32 for LOW):
+ * K8V4-K4V2 / K8V4-Prune configurations).  Same contract as kvc_quantize_and_place, in prompt
+ * mode and in re-tier mode (same ranks, pages and slots; the K8V4-Prune and no-prune
+ * configurations are threshold settings of kvc_score_tokens), but each tier is quantized at
+ * the scheme's bit widths with the same per-token min/max quantizer (2^b - 1 levels) and
+ * written in the layout below.  In re-tier mode the layer's pages must hold this scheme's
+ * layout: a token whose tier is unchanged keeps its codes and parameters bit for bit, a HIGH
+ * token demoted to LOW is re-quantized at the LOW widths from the fp16 rounding of its HIGH
+ * reconstruction (referee major comment 3), a FRESH one is quantized from k, v.  Layout (bits
+ * counted little-endian from a field's first byte; S = 16 slots for HIGH, 32 for LOW):
  *   keys, slot-major: slot s's 128 codes at bytes [16 kb s, 16 kb (s + 1)), code i at bits
  *     [i kb, (i + 1) kb);
  *   values from byte 16 kb S in blocks of 16 slots (S / 16 of them), 256 vb bytes each, in the
@@ -244,8 +248,10 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
 int kvc_quantize_and_place_scheme(const kvc_geom *geom, const kvc_scheme *scheme, int32_t layer,
                                   const kvc_pool *pool, const uint16_t *k, const uint16_t *v,
                                   const int32_t *cu_seqlens, int64_t total_tokens,
-                                  int32_t max_seqlen, const uint8_t *tier, void *workspace,
-                                  size_t workspace_bytes, kvc_stream_t stream);
+                                  int32_t max_seqlen, const uint8_t *tier,
+                                  const uint8_t *prev_tier, const uint8_t *changed,
+                                  const int32_t *old_rows, const int32_t *old_count,
+                                  void *workspace, size_t workspace_bytes, kvc_stream_t stream);
 
 /* Decode attention over pages written by kvc_quantize_and_place_scheme with the same scheme:
  * the contract of kvc_paged_decode_attention (codes reconstructed as code * scale + zero, all
@@ -272,6 +278,16 @@ int kvc_paged_decode_attention_scheme(const kvc_geom *geom, const kvc_scheme *sc
 int kvc_append_tokens(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
                       const uint16_t *k_new, const uint16_t *v_new, const int32_t *positions,
                       void *workspace, size_t workspace_bytes, kvc_stream_t stream);
+
+/* kvc_append_tokens for a layer whose pages hold a precision scheme's layout (written by
+ * kvc_quantize_and_place_scheme with the same scheme): the new token's codes are quantized at
+ * the scheme's HIGH widths and set into its slot (keys slot-major, values into the slot's
+ * value words, the other slots' codes kept).  Same allocation, workspace and errors, and
+ * KVC_E_SHAPE for a scheme that does not fit. */
+int kvc_append_tokens_scheme(const kvc_geom *geom, const kvc_scheme *scheme, int32_t layer,
+                             const kvc_pool *pool, const uint16_t *k_new, const uint16_t *v_new,
+                             const int32_t *positions, void *workspace, size_t workspace_bytes,
+                             kvc_stream_t stream);
 
 /* Decode attention of one new query per request over its KV head's live tokens (HIGH
  * slots < n_high, LOW slots < n_low), keys and values reconstructed on the fly as
@@ -362,6 +378,18 @@ int kvc_generation_step(const kvc_geom *geom, int32_t layer, const kvc_pool *poo
                         const float *acc_sum, const int32_t *cu_seqlens, float alpha_h,
                         float alpha_l, int32_t window, uint8_t *tier_out, void *workspace,
                         size_t workspace_bytes, kvc_stream_t stream);
+
+/* kvc_generation_step for a layer whose pages hold a precision scheme's layout: the new token
+ * enters at the scheme's HIGH widths, a token leaving the window that goes LOW is re-quantized
+ * at its LOW widths from the fp16 rounding of its HIGH reconstruction, and the rewritten pages
+ * keep the scheme's layout.  Same workspace, outputs and errors, and KVC_E_SHAPE (or
+ * KVC_E_NULL) for a scheme that does not fit (or is missing). */
+int kvc_generation_step_scheme(const kvc_geom *geom, const kvc_scheme *scheme, int32_t layer,
+                               const kvc_pool *pool, const uint16_t *k_new,
+                               const uint16_t *v_new, const int32_t *positions,
+                               const float *acc_sum, const int32_t *cu_seqlens, float alpha_h,
+                               float alpha_l, int32_t window, uint8_t *tier_out,
+                               void *workspace, size_t workspace_bytes, kvc_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -750,13 +750,18 @@ __device__ __forceinline__ void load_logits(const float *src, float (&l)[GT]) {
 // ACC_R = 64 slots (the chunk's positions), so lane k takes slot s0 + k and all G query heads
 // of its head.  Each (position, query head) has one live slot at most, so every LDS word is
 // added to by one lane: no atomics, deterministic.
+// LDS row stride of the staged accumulator rows (words).  The lanes of a job hold distinct
+// positions of the chunk, i.e. distinct rows, and add into the same columns: with an odd
+// stride the rows of any 64 lanes fall on distinct banks
+__host__ __device__ inline int acc_ldr(int Hq) { return Hq | 1; }
+
 template <int GT>
 __global__ __launch_bounds__(256) void acc_update_kernel(
     const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int G_rt,
     int max_seqlen, int nch_cap, const int32_t *__restrict__ idx,
     const float *__restrict__ lg, int64_t tiles_cap,
     const float *__restrict__ mls, float *__restrict__ acc, int32_t *status) {
-    extern __shared__ float s_acc[];                 // [ACC_R][Hq + 4], then [Hq][2] (M, L)
+    extern __shared__ float s_acc[];                 // [ACC_R][ldr], then [Hq][2] (M, L)
     const int G = GT > 0 ? GT : G_rt;
     const int b = blockIdx.y, c = blockIdx.x;
     const int lo = cu[b], N = cu[b + 1] - lo;
@@ -765,7 +770,7 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
     if (t0 >= N) return;
     const int nr = min(ACC_R, N - t0);
     const int Hq = Hkv * G;
-    const int ldr = Hq + 4;     // LDS row stride: rows 4 banks apart (lanes hold nearby rows)
+    const int ldr = acc_ldr(Hq);
     float *s_ml = s_acc + ACC_R * ldr;
     float *arow = acc + (int64_t(lo) + t0) * Hq;
     const int nw = nr * Hq;
@@ -773,8 +778,12 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
         const int q4 = Hq >> 2;
         for (int k = threadIdx.x; k < nw / 4; k += 256) {
             const int r = k / q4, c4 = k - r * q4;
-            reinterpret_cast<float4 *>(s_acc + r * ldr)[c4] =
-                reinterpret_cast<const float4 *>(arow)[k];
+            const float4 x = reinterpret_cast<const float4 *>(arow)[k];
+            float *d = s_acc + r * ldr + 4 * c4;
+            d[0] = x.x;
+            d[1] = x.y;
+            d[2] = x.z;
+            d[3] = x.w;
         }
     } else {
         for (int k = threadIdx.x; k < nw; k += 256) s_acc[(k / Hq) * ldr + k % Hq] = arow[k];
@@ -837,8 +846,8 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
         const int q4 = Hq >> 2;
         for (int k = threadIdx.x; k < nw / 4; k += 256) {
             const int r = k / q4, c4 = k - r * q4;
-            reinterpret_cast<float4 *>(arow)[k] =
-                reinterpret_cast<const float4 *>(s_acc + r * ldr)[c4];
+            const float *d = s_acc + r * ldr + 4 * c4;
+            reinterpret_cast<float4 *>(arow)[k] = make_float4(d[0], d[1], d[2], d[3]);
         }
     } else {
         for (int k = threadIdx.x; k < nw; k += 256) arow[k] = s_acc[(k / Hq) * ldr + k % Hq];
@@ -912,14 +921,13 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
                        p->dev_status);
     rc = launch_check("kvc_paged_decode_attention_acc/index");
     if (rc) return rc;
-    const size_t lds = sizeof(float) * (size_t(ACC_R) * (g->num_q_heads + 4) +
+    const size_t lds = sizeof(float) * (size_t(ACC_R) * acc_ldr(g->num_q_heads) +
                                         2 * size_t(g->num_q_heads));
     auto upd = G == 8 ? acc_update_kernel<8> : G == 4 ? acc_update_kernel<4>
              : G == 16 ? acc_update_kernel<16> : G == 2 ? acc_update_kernel<2>
              : G == 1 ? acc_update_kernel<1> : acc_update_kernel<0>;
     hipLaunchKernelGGL(upd, dim3(L.nch_cap - 1, B), dim3(256), lds, s, count_l, cu, Hkv, G,
-                       max_seqlen, L.nch_cap, idx, lg,
-                       L.tiles_cap, mls, acc_sum, p->dev_status);
+                       max_seqlen, L.nch_cap, idx, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
     return launch_check("kvc_paged_decode_attention_acc/accumulate");
 }
 

@@ -23,6 +23,7 @@
 #include "kvc_internal.h"
 #include "page_io.h"
 #include "quant_row.h"
+#include "scheme_io.h"
 #include "workspace.h"
 
 #pragma clang fp contract(off)
@@ -137,6 +138,11 @@ __global__ __launch_bounds__(256) void gen_plan_kernel(
     }
 }
 
+// the bit widths of a precision-scheme layer; kh == 0: the default K8V4 / K4V2 layout
+struct SchBits {
+    int kh, vh, kl, vl;
+};
+
 // one workgroup (4 waves) per head.  FUSED: the workgroup first commits its head's part of
 // the allocation round (gen_plan_kernel did the scan), then places
 template <bool FUSED>
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     const uint8_t *__restrict__ decided, uint8_t *__restrict__ pages, int32_t *status,
     const uint8_t *__restrict__ changed, int64_t P, int layer_gid0, uint64_t *ctr,
     int32_t *__restrict__ ring, int32_t *__restrict__ owner, const CompactHdr *hdr,
-    const int32_t *__restrict__ off, const int32_t *__restrict__ foff) {
+    const int32_t *__restrict__ off, const int32_t *__restrict__ foff, SchBits sb) {
     __shared__ uint8_t s_k[GEN_TAIL][D];            // key codes per slot (one per byte)
     __shared__ uint8_t s_v[GEN_TAIL][D];            // value codes per slot
     __shared__ uint32_t s_par[GEN_TAIL][2];         // (key scale|zero, value scale|zero)
@@ -175,6 +181,11 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     const int rg = lane >> 4, c = lane & 15;
     const int b = i / Hkv;
     const int d = decided[i];
+    // a scheme layer reads and writes its own layout; its value codes of a slot come to a lane
+    // as channels 16 n + c (the default layout's as 8 c + n)
+    const bool sch = sb.kh != 0;
+    const int kh = sch ? sb.kh : 8, vh = sch ? sb.vh : 4, kl = sch ? sb.kl : 4,
+              vl = sch ? sb.vl : 2;
     const int nh0 = old_count[2 * i], nl0 = old_count[2 * i + 1];
     const int32_t *row = rows_l + int64_t(i) * C;
     const int pos = positions[b];
@@ -206,8 +217,8 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
             float xk[8], xv[8];
             load_row8(K + int64_t(i) * D + 8 * c, true, xk);
             load_row8(V + int64_t(i) * D + 8 * c, true, xv);
-            const RowQ qk = row_params(xk, 255.0f);
-            const RowQ qv = row_params(xv, 15.0f);
+            const RowQ qk = row_params(xk, float((1 << kh) - 1));
+            const RowQ qv = row_params(xv, float((1 << vh) - 1));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 s_k[dd][8 * c + e] = uint8_t(code_of(xk[e], qk));
@@ -223,11 +234,20 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
             const int src = (leaves && da >= rc) ? da + 1 : da;
             const uint8_t *pg = pages + int64_t(row[src >> 4]) * PAGE;
             uint32_t kc[8], vc[8], kp, vp;
-            old_codes(pg, HIGH, src & (HS - 1), c, kc, vc, kp, vp);
+            if (sch) {
+                sch_key_codes(pg, kh, src & (HS - 1), c, kc);
+                sch_val_codes(pg, kh, vh, HS, src & (HS - 1), c, vc);
+                const uint2 par = *reinterpret_cast<const uint2 *>(pg + PARAM_OFF +
+                                                                   8 * (src & (HS - 1)));
+                kp = par.x;
+                vp = par.y;
+            } else {
+                old_codes(pg, HIGH, src & (HS - 1), c, kc, vc, kp, vp);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 s_k[dd][8 * c + e] = uint8_t(kc[e]);
-                s_v[dd][8 * c + e] = uint8_t(vc[e]);
+                s_v[dd][sch ? 16 * e + c : 8 * c + e] = uint8_t(vc[e]);
             }
             if (c == 0) {
                 s_par[dd][0] = kp;
@@ -243,19 +263,27 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
         const int so = rc & (HS - 1);
         if (d == LOW) {
             uint32_t kc[8], vc[8], kp, vp;
-            old_codes(pg, HIGH, so, c, kc, vc, kp, vp);
+            if (sch) {
+                sch_key_codes(pg, kh, so, c, kc);
+                sch_val_codes(pg, kh, vh, HS, so, c, vc);
+                const uint2 par = *reinterpret_cast<const uint2 *>(pg + PARAM_OFF + 8 * so);
+                kp = par.x;
+                vp = par.y;
+            } else {
+                old_codes(pg, HIGH, so, c, kc, vc, kp, vp);
+            }
             float xk[8], xv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 xk[e] = recon16(kc[e], kp);
                 xv[e] = recon16(vc[e], vp);
             }
-            const RowQ qk = row_params(xk, 15.0f);
-            const RowQ qv = row_params(xv, 3.0f);
+            const RowQ qk = row_params(xk, float((1 << kl) - 1));
+            const RowQ qv = row_params(xv, float((1 << vl) - 1));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 s_lk[8 * c + e] = uint8_t(code_of(xk[e], qk));
-                s_lv[8 * c + e] = uint8_t(code_of(xv[e], qv));
+                s_lv[sch ? 16 * e + c : 8 * c + e] = uint8_t(code_of(xv[e], qv));
             }
             if (c == 0) {
                 s_lpar[0] = uint32_t(qk.s16) | (uint32_t(qk.z16) << 16);
@@ -270,13 +298,36 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
         uint8_t *pg = pages + int64_t(row[p]) * PAGE;
         const int s0 = HS * p - base;
         const int live = min(HS, end - HS * p);
-        for (int k = lane; k < HS * 8; k += 64) {              // keys: 16 slots x 8 x 16 B
-            const int slot = k >> 3, off = (k & 7) * 16;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (slot < live) x = *reinterpret_cast<const uint4 *>(&s_k[s0 + slot][off]);
-            *reinterpret_cast<uint4 *>(pg + K_OFF + slot * 128 + off) = x;
+        if (sch) {
+            // keys slot-major at kh bits: (slot, channel group) items, 4 per lane
+            for (int k = lane; k < HS * 16; k += 64) {
+                const int slot = k >> 4, cg = k & 15;
+                uint64_t wk = 0;
+                if (slot < live) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        wk |= uint64_t(s_k[s0 + slot][8 * cg + e]) << (kh * e);
+                }
+                store_codes(pg + 16 * kh * slot + cg * kh, wk, kh);
+            }
+            // one value block (16 slots); rows past `live` hold the padding's zero codes
+            uint8_t *dst = pg + 16 * kh * HS + 4 * vh * lane;
+            const uint8_t (*vc)[D] = reinterpret_cast<const uint8_t (*)[D]>(&s_v[s0][0]);
+            if (vh == 8) pack_value_block<8>(dst, vc, 0, rg, c);
+            else if (vh == 4) pack_value_block<4>(dst, vc, 0, rg, c);
+            else if (vh == 2) pack_value_block<2>(dst, vc, 0, rg, c);
+            else pack_value_block<1>(dst, vc, 0, rg, c);
+            for (int k = HS * (kh + vh) + lane; k < PARAM_OFF / 16; k += 64)
+                st_page16(pg + 16 * k, 0u, 0u, 0u, 0u);
+        } else {
+            for (int k = lane; k < HS * 8; k += 64) {          // keys: 16 slots x 8 x 16 B
+                const int slot = k >> 3, off = (k & 7) * 16;
+                uint4 x = make_uint4(0, 0, 0, 0);
+                if (slot < live) x = *reinterpret_cast<const uint4 *>(&s_k[s0 + slot][off]);
+                *reinterpret_cast<uint4 *>(pg + K_OFF + slot * 128 + off) = x;
+            }
+            pack_values(pg, &s_v[s0][0], true, lane);
         }
-        pack_values(pg, &s_v[s0][0], true, lane);
         if (lane < LS) {
             const bool on = lane < live;
             const uint2 par = on ? make_uint2(s_par[s0 + lane][0], s_par[s0 + lane][1])
@@ -299,7 +350,16 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < 16) {
+        if (lane < 16 && sch) {
+            uint64_t wk = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wk |= uint64_t(s_lk[8 * c + e]) << (kl * e);
+            store_codes(pg + 16 * kl * so + c * kl, wk, kl);
+            uint32_t vc[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) vc[n] = s_lv[16 * n + c];
+            sch_set_val_codes(pg, kl, vl, LS, so, c, vc, so == 0);
+        } else if (lane < 16) {
             // keys: lane c packs channels 8c..8c+7 (nibble order of a LOW key word)
             uint32_t kw = 0;
 #pragma unroll
@@ -332,12 +392,13 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
 
 using namespace kvc;
 
-extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_pool *p,
-                                   const uint16_t *k_new, const uint16_t *v_new,
-                                   const int32_t *positions, const float *acc_sum,
-                                   const int32_t *cu_seqlens, float alpha_h, float alpha_l,
-                                   int32_t window, uint8_t *tier_out, void *ws, size_t ws_bytes,
-                                   kvc_stream_t stream) {
+namespace {
+
+int generation_step_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                         const uint16_t *k_new, const uint16_t *v_new, const int32_t *positions,
+                         const float *acc_sum, const int32_t *cu_seqlens, float alpha_h,
+                         float alpha_l, int32_t window, uint8_t *tier_out, void *ws,
+                         size_t ws_bytes, SchBits sb, kvc_stream_t stream) {
     int rc = check_geom(g);
     if (rc) return rc;
     rc = check_pool(p);
@@ -379,7 +440,7 @@ extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_p
                            positions, g->num_kv_heads, C, nheads, window, rows_w, count_w,
                            new_count, old_count, decided, p->pages, p->dev_status, changed,
                            g->num_pages, layer * nheads, p->ring_ctr, p->free_ring, p->owner, hdr,
-                           off, foff);
+                           off, foff, sb);
         return launch_check("kvc_generation_step/place");
     }
     hipLaunchKernelGGL(gen_decide_kernel, dim3((nheads + 255) / 256), dim3(256), 0, s, count_l,
@@ -393,6 +454,34 @@ extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_p
     hipLaunchKernelGGL(gen_place_kernel<false>, dim3(nheads), dim3(256), 0, s, k_new, v_new,
                        positions, g->num_kv_heads, C, nheads, window, rows_w, count_w, new_count,
                        old_count, decided, p->pages, p->dev_status, nullptr, int64_t(0), 0,
-                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, sb);
     return launch_check("kvc_generation_step/place");
+}
+
+}  // namespace
+
+extern "C" int kvc_generation_step(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                                   const uint16_t *k_new, const uint16_t *v_new,
+                                   const int32_t *positions, const float *acc_sum,
+                                   const int32_t *cu_seqlens, float alpha_h, float alpha_l,
+                                   int32_t window, uint8_t *tier_out, void *ws, size_t ws_bytes,
+                                   kvc_stream_t stream) {
+    return generation_step_impl(g, layer, p, k_new, v_new, positions, acc_sum, cu_seqlens,
+                                alpha_h, alpha_l, window, tier_out, ws, ws_bytes,
+                                SchBits{0, 0, 0, 0}, stream);
+}
+
+extern "C" int kvc_generation_step_scheme(const kvc_geom *g, const kvc_scheme *sc, int32_t layer,
+                                          const kvc_pool *p, const uint16_t *k_new,
+                                          const uint16_t *v_new, const int32_t *positions,
+                                          const float *acc_sum, const int32_t *cu_seqlens,
+                                          float alpha_h, float alpha_l, int32_t window,
+                                          uint8_t *tier_out, void *ws, size_t ws_bytes,
+                                          kvc_stream_t stream) {
+    const int rc = check_scheme(sc);
+    if (rc) return rc;
+    return generation_step_impl(g, layer, p, k_new, v_new, positions, acc_sum, cu_seqlens,
+                                alpha_h, alpha_l, window, tier_out, ws, ws_bytes,
+                                SchBits{sc->k_bits_high, sc->v_bits_high, sc->k_bits_low,
+                                        sc->v_bits_low}, stream);
 }

@@ -21,6 +21,7 @@
 #include "workspace.h"
 #include "quant_row.h"
 #include "page_io.h"
+#include "scheme_io.h"
 
 #pragma clang fp contract(off)
 
@@ -432,45 +433,6 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
 }
 
 // ---- precision schemes: slot-major pages --------------------------------------------------
-// the lane's 8 codes (b bits each, channels 8c .. 8c + 7) as b bytes at dst (b = 1, 2, 4, 8:
-// naturally aligned stores)
-__device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t w, int b) {
-    if (b == 8) st_page8(dst, uint32_t(w), uint32_t(w >> 32));
-    else if (b == 4) st_page4(dst, uint32_t(w));
-    else if (b == 2) *reinterpret_cast<uint16_t *>(dst) = uint16_t(w);
-    else *dst = uint8_t(w);
-}
-
-// one lane's share of a value block (16 slots) in the decode's operand order: lane L = 16 g + c
-// packs the codes of channels 16 n + c (n < 8) for slots 16 f + 4 g + r (r < 4), code (n, r)
-// at bit 32 (n / p) + 16 (r % 2) + VB (2 (n % p) + r / 2) with p = 8 / VB, and stores its
-// 4 VB bytes at dst (naturally aligned)
-template <int VB>
-__device__ __forceinline__ void pack_value_block(uint8_t *dst, const uint8_t (*vc)[D], int f,
-                                                 int g, int c) {
-    constexpr int P = 8 / VB;
-    uint32_t w[VB];
-#pragma unroll
-    for (int j = 0; j < VB; ++j) w[j] = 0u;
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t code = vc[16 * f + 4 * g + r][16 * n + c];
-            w[n / P] |= code << (16 * (r & 1) + VB * (2 * (n % P) + (r >> 1)));
-        }
-    if constexpr (VB == 8) {
-        st_page16(dst, w[0], w[1], w[2], w[3]);
-        st_page16(dst + 16, w[4], w[5], w[6], w[7]);
-    } else if constexpr (VB == 4) {
-        st_page16(dst, w[0], w[1], w[2], w[3]);
-    } else if constexpr (VB == 2) {
-        st_page8(dst, w[0], w[1]);
-    } else {
-        st_page4(dst, w[0]);
-    }
-}
-
 // grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
 // Keys slot-major (16 lanes per row, channels 8c .. 8c + 7, four slots per pass, stored from
 // registers); values in blocks of 16 slots in the decode's operand order: the slots' codes
@@ -567,6 +529,141 @@ __global__ __launch_bounds__(256) void scheme_pages_kernel(
     }
 }
 
+// Re-tier placement in a precision scheme's layout (grid and waves as scheme_pages_kernel).
+// Each slot of a rebuilt head comes from its source record (quant_select): its codes and
+// parameters copied bit for bit from its old page when its tier is unchanged (the key bytes
+// as they are, the value codes through the LDS staging), re-quantized at the LOW widths from
+// the fp16 rounding of its HIGH reconstruction when demoted, or quantized from its fp16 rows
+// when FRESH.
+__global__ __launch_bounds__(256) void scheme_rebuild_pages_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
+    const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ ok, const int32_t *__restrict__ poslist,
+    const uint2 *__restrict__ srcdesc, int kh, int vh, int kl, int vl,
+    uint8_t *__restrict__ pages, int32_t *status) {
+    __shared__ uint8_t s_vc[QP_WAVES][LS][D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.y;
+    const int nheads = gridDim.y;
+    if (ok[nheads] != 0 || !ok[i]) return;
+    const int b = i / Hkv, h = i - b * Hkv;
+    const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    const int qH = ceil_div(nh, HS), qL = ceil_div(nl, LS);
+    const int pi = blockIdx.x * QP_WAVES + wave;
+    bool high;
+    int first, m, page;
+    if (pi < qH) {
+        high = true;
+        first = pi * HS;
+        m = min(HS, nh - first);
+        page = rows_l[int64_t(i) * C + pi];
+    } else if (pi - qH < qL) {
+        high = false;
+        first = (pi - qH) * LS;
+        m = min(LS, nl - first);
+        page = rows_l[int64_t(i) * C + C - 1 - (pi - qH)];
+    } else {
+        return;
+    }
+    const int T = high ? HIGH : LOW;
+    const int kb = high ? kh : kl, vb = high ? vh : vl;
+    const int S = high ? HS : LS;
+    uint8_t *pg = pages + int64_t(page) * PAGE;
+    const int32_t *pl = poslist + int64_t(i) * max_seqlen;
+    const uint2 *sd = srcdesc + int64_t(i) * max_seqlen;
+    const int lo = cu[b];
+    const int rg = lane >> 4, c = lane & 15;
+    const float lk = float((1 << kb) - 1), lv = float((1 << vb) - 1);
+    uint8_t (*vc)[D] = s_vc[wave];
+    for (int pass = 0; pass < S / 4; ++pass) {
+        const int sl = 4 * pass + rg;
+        const bool live = sl < m;
+        const int64_t x = high ? first + sl : max_seqlen - 1 - (first + sl);
+        int pos = 0, src = FRESH, osl = 0;
+        const uint8_t *op = pages;
+        if (live) {
+            pos = pl[x];
+            const uint2 d = sd[x];
+            op = pages + int64_t(d.x) * PAGE;
+            src = int(d.y >> 8);
+            osl = int(d.y & 255u);
+        }
+        // a tier never rises, and a fresh token needs its fp16 rows
+        const bool valid = live && (src == T || (src == HIGH && T == LOW) ||
+                                    (src == FRESH && K != nullptr));
+        if (live && !valid && c == 0) atomicOr(status, KVC_DEV_BAD_TIER);
+        uint64_t wk = 0;
+        uint32_t a = 0u, bb = 0u;
+        uint32_t vcode[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        bool by16 = true;            // vcode[n] is channel 16 n + c (else 8 c + n)
+        if (valid && src == T) {
+            // unchanged tier: the old slot's key bytes as they are, its value codes unpacked
+            const uint8_t *ks = op + 16 * kb * osl + c * kb;
+            if (kb == 8) wk = *reinterpret_cast<const uint64_t *>(ks);
+            else if (kb == 4) wk = *reinterpret_cast<const uint32_t *>(ks);
+            else if (kb == 2) wk = *reinterpret_cast<const uint16_t *>(ks);
+            else wk = *ks;
+            sch_val_codes(op, kb, vb, S, osl, c, vcode);
+            const uint2 par = *reinterpret_cast<const uint2 *>(op + PARAM_OFF + 8 * osl);
+            a = par.x;
+            bb = par.y;
+        } else if (valid) {
+            float xk[8], xv[8];
+            if (src == HIGH) {
+                // HIGH -> LOW: the fp16 rounding of the old HIGH page's reconstruction
+                uint32_t kc[8], vo[8];
+                sch_key_codes(op, kh, osl, c, kc);
+                sch_val_codes(op, kh, vh, HS, osl, c, vo);
+                const uint2 par = *reinterpret_cast<const uint2 *>(op + PARAM_OFF + 8 * osl);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xk[e] = recon16(kc[e], par.x);
+                    xv[e] = recon16(vo[e], par.y);
+                }
+            } else {
+                const int64_t roff = ((int64_t(lo) + pos) * Hkv + h) * D + 8 * c;
+                load_row8(K + roff, true, xk);
+                load_row8(V + roff, true, xv);
+                by16 = false;
+            }
+            const RowQ qk = row_params(xk, lk);
+            const RowQ qv = row_params(xv, lv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wk |= uint64_t(code_of(xk[e], qk)) << (kb * e);
+                vcode[e] = code_of(xv[e], qv);
+            }
+            a = uint32_t(qk.s16) | (uint32_t(qk.z16) << 16);
+            bb = uint32_t(qv.s16) | (uint32_t(qv.z16) << 16);
+        }
+        store_codes(pg + 16 * kb * sl + c * kb, wk, kb);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) vc[sl][by16 ? 16 * n + c : 8 * c + n] = uint8_t(vcode[n]);
+        if (c == 0) {
+            st_page8(pg + PARAM_OFF + 8 * sl, a, bb);
+            st_page4(pg + POS_OFF + 4 * sl, uint32_t(valid ? pos : -1));
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint8_t *vbase = pg + 16 * kb * S;
+    for (int f = 0; f < S / 16; ++f) {
+        uint8_t *dst = vbase + 256 * vb * f + 4 * vb * lane;
+        if (vb == 8) pack_value_block<8>(dst, vc, f, rg, c);
+        else if (vb == 4) pack_value_block<4>(dst, vc, f, rg, c);
+        else if (vb == 2) pack_value_block<2>(dst, vc, f, rg, c);
+        else pack_value_block<1>(dst, vc, f, rg, c);
+    }
+    for (int k = S * (kb + vb) + lane; k < PARAM_OFF / 16; k += 64)
+        st_page16(pg + 16 * k, 0u, 0u, 0u, 0u);
+    if (lane >= S && lane < LS) {
+        st_page8(pg + PARAM_OFF + 8 * lane, 0u, 0u);
+        st_page4(pg + POS_OFF + 4 * lane, uint32_t(-1));
+    }
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -638,7 +735,9 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
                                              int32_t layer, const kvc_pool *p, const uint16_t *k,
                                              const uint16_t *v, const int32_t *cu,
                                              int64_t total_tokens, int32_t max_seqlen,
-                                             const uint8_t *tier, void *ws, size_t ws_bytes,
+                                             const uint8_t *tier, const uint8_t *prev_tier,
+                                             const uint8_t *changed, const int32_t *old_rows,
+                                             const int32_t *old_count, void *ws, size_t ws_bytes,
                                              kvc_stream_t stream) {
     int rc = check_geom(g);
     if (rc) return rc;
@@ -646,8 +745,12 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
     if (rc) return rc;
     rc = check_scheme(sc);
     if (rc) return rc;
+    const bool rebuild = prev_tier != nullptr;
+    if (rebuild && (!changed || !old_rows || !old_count)) return KVC_E_NULL;
+    if (!rebuild && (changed || old_rows || old_count)) return KVC_E_UNSUPPORTED;
     if (!cu) return KVC_E_NULL;
-    if (total_tokens > 0 && (!tier || !k || !v)) return KVC_E_NULL;
+    if (total_tokens > 0 && !tier) return KVC_E_NULL;
+    if (!rebuild && total_tokens > 0 && (!k || !v)) return KVC_E_NULL;
     if (layer < 0 || layer >= g->num_layers || max_seqlen < 0 || total_tokens < 0)
         return KVC_E_SHAPE;
     if (g->num_kv_heads > 256) return KVC_E_SHAPE;
@@ -658,30 +761,39 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
     char *w = static_cast<char *>(ws);
     int32_t *tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     int32_t *tile_base = reinterpret_cast<int32_t *>(w + L.tile_base);
+    int32_t *tile_cnt2 = rebuild ? reinterpret_cast<int32_t *>(w + L.tile_cnt2) : nullptr;
+    int32_t *tile_base2 = rebuild ? reinterpret_cast<int32_t *>(w + L.tile_base2) : nullptr;
     int32_t *ok = reinterpret_cast<int32_t *>(w + L.ok);
     int32_t *poslist = reinterpret_cast<int32_t *>(w + L.poslist);
+    uint2 *srcdesc = rebuild ? reinterpret_cast<uint2 *>(w + L.srcdesc) : nullptr;
     const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
     const int nheads = B * Hkv;
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(quant_count_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, nullptr, cu,
-                       Hkv, L.ntq, max_seqlen, p->dev_status, tile_cnt, nullptr, ok, nheads);
+    hipLaunchKernelGGL(quant_count_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
+                       Hkv, L.ntq, max_seqlen, p->dev_status, tile_cnt, tile_cnt2, ok, nheads);
     rc = launch_check("kvc_quantize_and_place_scheme/count");
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_scan_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, nullptr, cu,
-                       Hkv, L.ntq, max_seqlen, count_l, nullptr, nullptr, tile_base, nullptr, ok,
-                       p->dev_status);
+    hipLaunchKernelGGL(quant_scan_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, tile_cnt2, cu,
+                       Hkv, L.ntq, max_seqlen, count_l, changed, old_count, tile_base,
+                       tile_base2, ok, p->dev_status);
     rc = launch_check("kvc_quantize_and_place_scheme/scan");
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, nullptr, cu,
-                       Hkv, L.ntq, max_seqlen, tile_base, nullptr, ok, nullptr, C, poslist,
-                       nullptr);
+    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
+                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, old_rows, C, poslist,
+                       srcdesc);
     rc = launch_check("kvc_quantize_and_place_scheme/select");
     if (rc) return rc;
-    hipLaunchKernelGGL(scheme_pages_kernel, dim3((C + QP_WAVES - 1) / QP_WAVES, nheads),
-                       dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv, C, max_seqlen, rows_l, count_l,
-                       ok, poslist, sc->k_bits_high, sc->v_bits_high, sc->k_bits_low,
-                       sc->v_bits_low, p->pages);
+    const dim3 grid((C + QP_WAVES - 1) / QP_WAVES, nheads);
+    if (rebuild)
+        hipLaunchKernelGGL(scheme_rebuild_pages_kernel, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu,
+                           Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, srcdesc,
+                           sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low,
+                           p->pages, p->dev_status);
+    else
+        hipLaunchKernelGGL(scheme_pages_kernel, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv,
+                           C, max_seqlen, rows_l, count_l, ok, poslist, sc->k_bits_high,
+                           sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, p->pages);
     return launch_check("kvc_quantize_and_place_scheme/pages");
 }

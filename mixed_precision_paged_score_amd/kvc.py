@@ -26,7 +26,8 @@ EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_ini
            "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
-           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static"]
+           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
+           "kvc_append_tokens_scheme", "kvc_generation_step_scheme"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -85,13 +86,17 @@ _lib.kvc_prefill_attention.argtypes = [_G, _vp, _vp, _vp, _vp, _i32, _f32, _vp, 
                                        _vp, _sz, _vp]
 _S = ctypes.POINTER(Scheme)
 _lib.kvc_quantize_and_place_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _i64, _i32, _vp,
-                                               _vp, _sz, _vp]
+                                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.kvc_append_tokens_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.kvc_generation_step_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _vp, _vp, _f32,
+                                            _f32, _i32, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention_scheme.argtypes = [_G, _S, _i32, _P, _vp, _f32, _vp, _i32, _vp,
                                                    _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
-           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static"):
+           "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
+           "kvc_append_tokens_scheme", "kvc_generation_step_scheme"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -233,6 +238,16 @@ def generation_step(geom, layer, pool, k_new, v_new, positions, acc_sum, cu_seql
                                     _stream(stream)), "kvc_generation_step")
 
 
+def generation_step_scheme(geom, scheme, layer, pool, k_new, v_new, positions, acc_sum,
+                           cu_seqlens, alpha_h, alpha_l, window, tier_out, ws, stream=None):
+    _check(_lib.kvc_generation_step_scheme(ctypes.byref(geom), ctypes.byref(scheme), int(layer),
+                                           ctypes.byref(pool.c), _ptr(k_new), _ptr(v_new),
+                                           _ptr(positions), _ptr(acc_sum), _ptr(cu_seqlens),
+                                           float(alpha_h), float(alpha_l), int(window),
+                                           _ptr(tier_out), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "kvc_generation_step_scheme")
+
+
 def prefill_attention(geom, q, k, v, cu_seqlens, max_seqlen, softmax_scale, out, acc_sum, ws,
                       dev_status=None, stream=None):
     _check(_lib.kvc_prefill_attention(ctypes.byref(geom), _ptr(q), _ptr(k), _ptr(v),
@@ -245,12 +260,22 @@ def prefill_attention(geom, q, k, v, cu_seqlens, max_seqlen, softmax_scale, out,
 
 
 def quantize_and_place_scheme(geom, scheme, layer, pool, k, v, cu_seqlens, total_tokens,
-                              max_seqlen, tier, ws, stream=None):
+                              max_seqlen, tier, ws, prev_tier=None, changed=None, old_rows=None,
+                              old_count=None, stream=None):
     _check(_lib.kvc_quantize_and_place_scheme(ctypes.byref(geom), ctypes.byref(scheme),
                                               int(layer), ctypes.byref(pool.c), _ptr(k), _ptr(v),
                                               _ptr(cu_seqlens), int(total_tokens),
-                                              int(max_seqlen), _ptr(tier), _ptr(ws), ws.numel(),
-                                              _stream(stream)), "kvc_quantize_and_place_scheme")
+                                              int(max_seqlen), _ptr(tier), _ptr(prev_tier),
+                                              _ptr(changed), _ptr(old_rows), _ptr(old_count),
+                                              _ptr(ws), ws.numel(), _stream(stream)),
+           "kvc_quantize_and_place_scheme")
+
+
+def append_tokens_scheme(geom, scheme, layer, pool, k_new, v_new, positions, ws, stream=None):
+    _check(_lib.kvc_append_tokens_scheme(ctypes.byref(geom), ctypes.byref(scheme), int(layer),
+                                         ctypes.byref(pool.c), _ptr(k_new), _ptr(v_new),
+                                         _ptr(positions), _ptr(ws), ws.numel(), _stream(stream)),
+           "kvc_append_tokens_scheme")
 
 
 def paged_decode_attention_scheme(geom, scheme, layer, pool, q, softmax_scale, out, ws,

@@ -112,12 +112,13 @@ class GenerationPath(PromptPath):
     caller's bookkeeping: it is kept here as [B][max_len][Hkv] and packed to the ragged layout
     the library reads (a device copy, outside the library calls)."""
 
-    def __init__(self, w, max_len, device="cuda", num_pages=None):
+    def __init__(self, w, max_len, device="cuda", num_pages=None, scheme=None):
         import dataclasses
         # size workspaces and row capacity for the longest sequence the run reaches
         wl = dataclasses.replace(w, seqlens=[max_len] * w.batch)
         super().__init__(wl, device, num_pages)
         self.w = w
+        self.scheme = scheme        # a kvc.Scheme: every page of the run in its layout
         self.lens = list(w.seqlens)
         H = w.num_kv_heads
         self.state = torch.full((w.batch, max_len, H), kvc.PRUNE, dtype=torch.uint8, device=device)
@@ -151,12 +152,25 @@ class GenerationPath(PromptPath):
 
     def prompt(self, layer, acc, k, v):
         self._set_layout()
-        super().prompt(layer, acc, k, v)
+        if self.scheme is None:
+            super().prompt(layer, acc, k, v)
+        else:
+            self.prompt_scheme(layer, acc, k, v, self.scheme)
         self.unpack_state(self.tier[:self.T])
 
+    def decode(self, layer, q, out):
+        if self.scheme is None:
+            super().decode(layer, q, out)
+        else:
+            self.decode_scheme(layer, q, out, self.scheme)
+
     def append(self, layer, k_new, v_new):
-        kvc.append_tokens(self.geom, layer, self.pool, k_new, v_new, self.lens_dev,
-                          self.ws_append)
+        if self.scheme is None:
+            kvc.append_tokens(self.geom, layer, self.pool, k_new, v_new, self.lens_dev,
+                              self.ws_append)
+        else:
+            kvc.append_tokens_scheme(self.geom, self.scheme, layer, self.pool, k_new, v_new,
+                                     self.lens_dev, self.ws_append)
         # bookkeeping: the new positions are HIGH, every request is one token longer
         self.state[self._bidx, self.lens_dev.long()] = kvc.HIGH
         self.lens_dev.add_(1)
@@ -179,9 +193,15 @@ class GenerationPath(PromptPath):
         if self.ws_gen is None:
             self.ws_gen = kvc.workspace(self.geom, kvc.OP_GENERATE, device=self.device)
         cu_next = self.cu + self._cu_step
-        kvc.generation_step(self.geom, layer, self.pool, k_new, v_new, self.lens_dev, acc,
-                            cu_next if cu is None else cu, w.alpha_h, w.alpha_l, w.window,
-                            self.decided, self.ws_gen)
+        if self.scheme is None:
+            kvc.generation_step(self.geom, layer, self.pool, k_new, v_new, self.lens_dev, acc,
+                                cu_next if cu is None else cu, w.alpha_h, w.alpha_l, w.window,
+                                self.decided, self.ws_gen)
+        else:
+            kvc.generation_step_scheme(self.geom, self.scheme, layer, self.pool, k_new, v_new,
+                                       self.lens_dev, acc, cu_next if cu is None else cu,
+                                       w.alpha_h, w.alpha_l, w.window, self.decided,
+                                       self.ws_gen)
         # bookkeeping: the new positions are HIGH, the leaving token takes its tier
         pos = self.lens_dev.long()
         self.state[self._bidx, pos] = kvc.HIGH
@@ -203,8 +223,14 @@ class GenerationPath(PromptPath):
                          changed=self.changed, dev_status=self.score_status)
         kvc.compact_pages(self.geom, layer, self.pool, self.new_count, self.ws_compact,
                           changed=self.changed, old_rows=self.old_rows, old_count=self.old_count)
-        kvc.quantize_and_place(self.geom, layer, self.pool, None, None, self.cu, self.T,
-                               self.max_seqlen, self.tier, self.ws_quant, prev_tier=prev,
-                               changed=self.changed, old_rows=self.old_rows,
-                               old_count=self.old_count)
+        if self.scheme is None:
+            kvc.quantize_and_place(self.geom, layer, self.pool, None, None, self.cu, self.T,
+                                   self.max_seqlen, self.tier, self.ws_quant, prev_tier=prev,
+                                   changed=self.changed, old_rows=self.old_rows,
+                                   old_count=self.old_count)
+        else:
+            kvc.quantize_and_place_scheme(self.geom, self.scheme, layer, self.pool, None, None,
+                                          self.cu, self.T, self.max_seqlen, self.tier,
+                                          self.ws_quant, prev_tier=prev, changed=self.changed,
+                                          old_rows=self.old_rows, old_count=self.old_count)
         self.unpack_state(self.tier[:self.T])

@@ -114,11 +114,27 @@ def test_synchronous_errors_enqueue_nothing():
                                                  ctypes.byref(p), 16, 1.0, 16, 1, 256, 8,
                                                  None) == kvc.E_WORKSPACE
     assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(kvc.Scheme(8, 4, 4, 4)),
-                                             0, ctypes.byref(p), 16, 16, 16, 10, 5, 16, 256,
-                                             1 << 20, None) == kvc.E_SHAPE
+                                             0, ctypes.byref(p), 16, 16, 16, 10, 5, 16, None,
+                                             None, None, None, 256, 1 << 20, None) == kvc.E_SHAPE
     assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0,
-                                             ctypes.byref(p), 16, 18, 16, 10, 5, 16, 256,
-                                             1 << 20, None) == kvc.E_ALIGN
+                                             ctypes.byref(p), 16, 18, 16, 10, 5, 16, None, None,
+                                             None, None, 256, 1 << 20, None) == kvc.E_ALIGN
+    # re-tier mode needs all four re-tier arguments; only some of them is refused
+    assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0,
+                                             ctypes.byref(p), 16, 16, 16, 10, 5, 16, 16, None,
+                                             16, 16, 256, 1 << 20, None) == kvc.E_NULL
+    assert lib.kvc_quantize_and_place_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0,
+                                             ctypes.byref(p), 16, 16, 16, 10, 5, 16, None, 16,
+                                             None, None, 256, 1 << 20, None) == kvc.E_UNSUPPORTED
+    # scheme append: no scheme, a scheme that does not fit, misaligned rows, small workspace
+    assert lib.kvc_append_tokens_scheme(ctypes.byref(g), None, 0, ctypes.byref(p), 16, 16, 16,
+                                        256, 1 << 20, None) == kvc.E_NULL
+    assert lib.kvc_append_tokens_scheme(ctypes.byref(g), ctypes.byref(sc_bad), 0, ctypes.byref(p),
+                                        16, 16, 16, 256, 1 << 20, None) == kvc.E_SHAPE
+    assert lib.kvc_append_tokens_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0, ctypes.byref(p),
+                                        18, 16, 16, 256, 1 << 20, None) == kvc.E_ALIGN
+    assert lib.kvc_append_tokens_scheme(ctypes.byref(g), ctypes.byref(sc_ok), 0, ctypes.byref(p),
+                                        16, 16, 16, 256, 8, None) == kvc.E_WORKSPACE
     # score: negative window
     assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
                                 ctypes.c_float(0.1), -1, None, 16, 16, None, None,

@@ -1,7 +1,9 @@
 """Generation phase on the GPU vs the oracle's record simulation (MI355X only): per-step
 appends (kvc_append_tokens) and re-tier rounds (score with previous tiers, compact with the
 rebuilt heads, quantize/place in re-tier mode), compared bit-exactly after every round; the
-chain-of-thought workload runs its full 16,384 generated tokens (128 rounds)."""
+chain-of-thought workload runs its full 16,384 generated tokens (128 rounds).  The same runs
+under precision schemes (kvc_append_tokens_scheme, kvc_quantize_and_place_scheme in re-tier
+mode, the scheme decode) against the oracle's scheme generation."""
 import os
 import sys
 
@@ -57,14 +59,19 @@ def _check_attention(w, path, gen, sample_heads, seed):
 
 
 def run_generation(w, steps, round_every, sample_heads=None, check_every_round=True,
-                   attn_every=None, acc_device="cpu"):
-    from mixed_precision_paged_score_amd import pipeline
+                   attn_every=None, acc_device="cpu", scheme=None):
+    """scheme: (HIGH format, LOW format) names, e.g. ("K4V8", "K2V4"), or None (K8V4-K4V2 in
+    the default layout)."""
+    from mixed_precision_paged_score_amd import kvc, pipeline
+    from oracle import scheme as osch
     print(f"[generation] B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-          f"prompt={w.seqlens} steps={steps} round={round_every} P={w.num_pages}", flush=True)
+          f"prompt={w.seqlens} steps={steps} round={round_every} P={w.num_pages} "
+          f"scheme={scheme}", flush=True)
     k, v = workloads.make_kv(w)
     acc = workloads.make_acc(w, k)
     max_len = max(w.seqlens) + steps
-    path = pipeline.GenerationPath(w, max_len, DEV)
+    path = pipeline.GenerationPath(w, max_len, DEV,
+                                   scheme=kvc.make_scheme(*scheme) if scheme else None)
     path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
     tier0, _, _ = parity.oracle_score(w, acc)
     if isinstance(sample_heads, int):
@@ -72,7 +79,8 @@ def run_generation(w, steps, round_every, sample_heads=None, check_every_round=T
         allh = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
         sample_heads = [allh[i] for i in rng.choice(len(allh), sample_heads, replace=False)]
     gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages,
-                          track=sample_heads)
+                          track=sample_heads,
+                          scheme=osch.Scheme.named(*scheme) if scheme else None)
     gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
     g = torch.Generator().manual_seed(w.seed + 99)
     rounds = 0
@@ -138,3 +146,30 @@ def test_workload4_full_length():
     w = workloads.workload(4)
     run_generation(w, steps=16384, round_every=128, sample_heads=6, attn_every=1024,
                    acc_device=DEV)
+
+
+# ---- precision schemes --------------------------------------------------------------------
+
+@pytest.mark.parametrize("scheme", [("K4V8", "K2V4"), ("K8V2", "K4V1"), ("K4V2", "K4V1"),
+                                    ("K2V4", "K4V2")])
+def test_scheme_generation_small_ragged(scheme):
+    # every bit width in both tiers: appends set single slots of the value blocks, rounds copy
+    # survivors, re-quantize demotions at the LOW widths and return the old pages
+    w = workloads.Workload("gen-small-sch", 1, 3, 16, 4, [300, 160, 500], 1.0, 0.2, 16, 2048,
+                           "zipf", seed=51)
+    run_generation(w, steps=96, round_every=32, scheme=scheme, attn_every=48)
+
+
+def test_scheme_generation_group8_with_pruning_and_page_boundaries():
+    w = workloads.Workload("gen-g8-sch", 1, 2, 16, 2, [129, 77], 1.0, 0.5, 8, 1024, "zipf",
+                           seed=52)
+    run_generation(w, steps=70, round_every=20, scheme=("K8V2", "K4V1"))
+
+
+def test_scheme_generation_workload4_shape():
+    # workload 4's shape (16 x 4,096-token prompts, 64 query / 8 KV heads) for 512 steps and
+    # 4 rounds in the K4V8-K2V4 scheme: allocator state of all heads after every round, page
+    # bytes and attention of 6 sampled heads
+    w = workloads.workload(4)
+    run_generation(w, steps=512, round_every=128, sample_heads=6, attn_every=256,
+                   acc_device=DEV, scheme=("K4V8", "K2V4"))

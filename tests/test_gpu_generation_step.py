@@ -22,14 +22,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_steps(w, steps, sample_heads=None, check_every=1, acc_device="cpu"):
+def run_steps(w, steps, sample_heads=None, check_every=1, acc_device="cpu", scheme=None):
+    """scheme: (HIGH format, LOW format) names, or None for the default layout."""
     from mixed_precision_paged_score_amd import pipeline, kvc
+    from oracle import scheme as osch
     print(f"[step] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
           f"prompt={w.seqlens[:6]} W={w.window} alpha=({w.alpha_h},{w.alpha_l}) steps={steps} "
-          f"P={w.num_pages}", flush=True)
+          f"P={w.num_pages} scheme={scheme}", flush=True)
     k, v = workloads.make_kv(w)
     acc = workloads.make_acc(w, k)
-    path = pipeline.GenerationPath(w, max(w.seqlens) + steps, DEV)
+    path = pipeline.GenerationPath(w, max(w.seqlens) + steps, DEV,
+                                   scheme=kvc.make_scheme(*scheme) if scheme else None)
     path.prompt(0, acc.to(DEV), k.to(DEV), v.to(DEV))
     tier0, _, _ = parity.oracle_score(w, acc)
     if isinstance(sample_heads, int):
@@ -37,7 +40,8 @@ def run_steps(w, steps, sample_heads=None, check_every=1, acc_device="cpu"):
         allh = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
         sample_heads = [allh[i] for i in rng.choice(len(allh), sample_heads, replace=False)]
     gen = ogen.Generation(w.batch, w.num_kv_heads, path.geom.row_capacity, path.geom.num_pages,
-                          track=sample_heads)
+                          track=sample_heads,
+                          scheme=osch.Scheme.named(*scheme) if scheme else None)
     gen.prompt(k.numpy(), v.numpy(), tier0, w.cu_seqlens())
     g = torch.Generator().manual_seed(w.seed + 77)
     seen = np.zeros(256, np.int64)
@@ -238,3 +242,22 @@ def test_full_loop_on_padded_accumulators():
     print(f"[loop] decisions high {seen[2]} low {seen[1]} pruned {seen[0]} none {seen[255]}",
           flush=True)
     assert seen[2] > 0 and seen[1] > 0
+
+
+# ---- precision schemes --------------------------------------------------------------------
+
+@pytest.mark.parametrize("scheme", [("K4V8", "K2V4"), ("K8V2", "K4V1"), ("K2V4", "K4V2")])
+def test_scheme_steps_ragged(scheme):
+    # the per-step policy on scheme pages: the HIGH tail rewritten in the scheme's layout, the
+    # demoted token set into its LOW slot at the LOW widths
+    w = workloads.Workload("step-ragged-sch", 1, 4, 16, 4, [300, 0, 9, 517], 1.0, 0.2, 16, 2048,
+                           "zipf", seed=61)
+    c = run_steps(w, steps=80, check_every=4, scheme=scheme)
+    assert min(c["high"], c["low"], c["pruned"]) > 0, c
+
+
+def test_scheme_steps_largest_window():
+    w = workloads.Workload("step-w112-sch", 1, 3, 32, 4, [200, 129, 64], 1.0, 0.3, 112, 4096,
+                           "zipf", seed=62)
+    c = run_steps(w, steps=70, check_every=7, scheme=("K4V2", "K4V1"))
+    assert c["low"] > 0 and c["pruned"] > 0, c
