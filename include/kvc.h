@@ -265,6 +265,19 @@ int kvc_paged_decode_attention_scheme(const kvc_geom *geom, const kvc_scheme *sc
                                       void *workspace, size_t workspace_bytes,
                                       kvc_stream_t stream);
 
+/* kvc_paged_decode_attention_acc over pages written in a precision scheme's layout (with the
+ * same scheme): the scheme decode's output, and every live token's softmax weight per query
+ * head added into acc_sum (the contract, workspace and errors of
+ * kvc_paged_decode_attention_acc), for groups of up to 8 query heads per KV head
+ * (KVC_E_UNSUPPORTED above). */
+int kvc_paged_decode_attention_scheme_acc(const kvc_geom *geom, const kvc_scheme *scheme,
+                                          int32_t layer, const kvc_pool *pool,
+                                          const uint16_t *q, float softmax_scale, void *out,
+                                          int32_t out_is_fp32, float *acc_sum,
+                                          const int32_t *cu_seqlens, int32_t max_seqlen,
+                                          void *workspace, size_t workspace_bytes,
+                                          kvc_stream_t stream);
+
 /* Append one freshly generated token per (request, KV head) to layer `layer` during
  * decoding: the token enters its head's HIGH tier (DiffKV review page, free-parameter ledger:
  * the recent window is always high precision) as K8V4 codes in the next HIGH slot; a head

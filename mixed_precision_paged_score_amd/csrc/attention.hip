@@ -854,6 +854,33 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
     }
 }
 
+// the score accumulation after a decode that wrote its tile records and whose combine wrote
+// each query head's (M, L): the chunk index, then the accumulator update (shared with the
+// precision-scheme decode)
+int launch_score_accumulation(const kvc_geom *g, const kvc_pool *p, const int32_t *count_l,
+                              const int32_t *cu, int max_seqlen, float *acc_sum, char *w,
+                              hipStream_t s) {
+    if (max_seqlen == 0) return KVC_OK;
+    const DecodeWs L(g, true, max_seqlen);
+    const int B = g->batch, Hkv = g->num_kv_heads, G = g->num_q_heads / Hkv;
+    const float *mls = reinterpret_cast<const float *>(w + L.mls);
+    const float *lg = reinterpret_cast<const float *>(w + L.lg);
+    int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);
+    hipLaunchKernelGGL(acc_index_kernel, dim3(B * Hkv, 2 * ACC_IDX_BLOCKS), dim3(256), 0, s,
+                       count_l, cu, Hkv, G, max_seqlen, L.nch_cap, lg, L.tiles_cap, idx,
+                       p->dev_status);
+    int rc = launch_check("score accumulation/index");
+    if (rc) return rc;
+    const size_t lds = sizeof(float) * (size_t(ACC_R) * acc_ldr(g->num_q_heads) +
+                                        2 * size_t(g->num_q_heads));
+    auto upd = G == 8 ? acc_update_kernel<8> : G == 4 ? acc_update_kernel<4>
+             : G == 16 ? acc_update_kernel<16> : G == 2 ? acc_update_kernel<2>
+             : G == 1 ? acc_update_kernel<1> : acc_update_kernel<0>;
+    hipLaunchKernelGGL(upd, dim3(L.nch_cap - 1, B), dim3(256), lds, s, count_l, cu, Hkv, G,
+                       max_seqlen, L.nch_cap, idx, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
+    return launch_check("score accumulation/update");
+}
+
 // the combine launch of a split-K decode (shared with the precision-scheme decode)
 int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,
                           int out_fp32, float *mls, const int32_t *count_l, int wt,
@@ -914,21 +941,7 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
     rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
                                count_l, L.wt, s);
     if (rc || !accum) return rc;
-    if (max_seqlen == 0) return KVC_OK;
-    int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);
-    hipLaunchKernelGGL(acc_index_kernel, dim3(nheads, 2 * ACC_IDX_BLOCKS), dim3(256), 0, s,
-                       count_l, cu, Hkv, G, max_seqlen, L.nch_cap, lg, L.tiles_cap, idx,
-                       p->dev_status);
-    rc = launch_check("kvc_paged_decode_attention_acc/index");
-    if (rc) return rc;
-    const size_t lds = sizeof(float) * (size_t(ACC_R) * acc_ldr(g->num_q_heads) +
-                                        2 * size_t(g->num_q_heads));
-    auto upd = G == 8 ? acc_update_kernel<8> : G == 4 ? acc_update_kernel<4>
-             : G == 16 ? acc_update_kernel<16> : G == 2 ? acc_update_kernel<2>
-             : G == 1 ? acc_update_kernel<1> : acc_update_kernel<0>;
-    hipLaunchKernelGGL(upd, dim3(L.nch_cap - 1, B), dim3(256), lds, s, count_l, cu, Hkv, G,
-                       max_seqlen, L.nch_cap, idx, lg, L.tiles_cap, mls, acc_sum, p->dev_status);
-    return launch_check("kvc_paged_decode_attention_acc/accumulate");
+    return launch_score_accumulation(g, p, count_l, cu, max_seqlen, acc_sum, w, s);
 }
 
 }  // namespace

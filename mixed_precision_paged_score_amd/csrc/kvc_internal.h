@@ -28,6 +28,11 @@ int launch_compact(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                    const int32_t *new_count, const uint8_t *changed, int32_t *old_rows_out,
                    int32_t *old_count_out, void *ws, hipStream_t s);
 
+// the score accumulation after a decode (attention.hip): w is the decode workspace laid out
+// by DecodeWs(g, true, max_seqlen), its tile records and (M, L) already written
+int launch_score_accumulation(const kvc_geom *g, const kvc_pool *p, const int32_t *count_l,
+                              const int32_t *cu, int max_seqlen, float *acc_sum, char *w,
+                              hipStream_t s);
 // the combine launch of a split-K decode (attention.hip); partials [B*Hkv][S][G][132], of
 // which head i's first active_splits(count_l[2i], count_l[2i+1], S, wt) were written
 int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,

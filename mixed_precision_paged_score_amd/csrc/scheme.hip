@@ -85,10 +85,22 @@ __device__ __forceinline__ void load_codes32(__amdgpu_buffer_rsrc_t rs, uint32_t
     }
 }
 
-// four b-bit codes starting at bit 0 of w as the fp16 numbers 1024 + code (an h4 operand)
+// Key operands.  Codes of b < 8 bits enter the score product as the fp16 numbers
+// 1024 + 2^(10-b) code (the code in the top bits of the mantissa), 8-bit codes as 1024 + code;
+// the tier's key scales are multiplied by key_factor = 2^-(10-b) (exact), so the offset that
+// the float32 sums cancel (1024 sum(q)) is 2^b code steps rather than 1024, which keeps the
+// cancellation error of narrow keys as small as that of 8-bit ones.
+template <int KB>
+__device__ __forceinline__ float key_factor(int kb_rt) {
+    const int b = KB ? KB : kb_rt;
+    return b == 8 ? 1.0f : 1.0f / float(1 << (10 - b));
+}
+// four b-bit codes starting at bit 0 of w as key operand numbers (an h4 operand)
 __device__ __forceinline__ uint2 codes4(uint32_t w, int b) {
     const uint32_t m = (1u << b) - 1u;
-    const uint32_t c0 = w & m, c1 = (w >> b) & m, c2 = (w >> (2 * b)) & m, c3 = (w >> (3 * b)) & m;
+    const int t = b == 8 ? 0 : 10 - b;
+    const uint32_t c0 = (w & m) << t, c1 = ((w >> b) & m) << t, c2 = ((w >> (2 * b)) & m) << t,
+                   c3 = ((w >> (3 * b)) & m) << t;
     return make_uint2((c0 | 0x6400u) | ((c1 | 0x6400u) << 16),
                       (c2 | 0x6400u) | ((c3 | 0x6400u) << 16));
 }
@@ -113,6 +125,9 @@ __device__ __forceinline__ constexpr int key_chan(int ks, int e) {
     }
 }
 constexpr uint32_t MAGIC = 0x64006400u;   // fp16 1024 in both halves
+__device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n) {
+    return __builtin_amdgcn_alignbit(x, x, n);
+}
 // bytes 0, 1 and 2, 3 of x as fp16 pairs (1024 + byte)
 __device__ __forceinline__ h4 bytes4(uint32_t x) {
     return __builtin_bit_cast(h4, make_uint2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
@@ -123,12 +138,14 @@ __device__ __forceinline__ h4 key_op(const uint32_t (&w)[KB ? KB : 8], int ks, i
     if constexpr (KB == 8) {
         return bytes4(w[ks]);
     } else if constexpr (KB > 0) {
-        constexpr int hpw = 8 / KB;
-        constexpr uint32_t M = ((1u << KB) - 1u) * 0x00010001u;
+        // a rotation brings each pair of codes (16 bits apart) to the top of the mantissas
+        constexpr int hpw = 8 / KB, T = 10 - KB;
+        constexpr uint32_t M = (((1u << KB) - 1u) << T) * 0x00010001u;
         const uint32_t x = w[ks / hpw];
         const int u = ks % hpw;
-        return __builtin_bit_cast(h4, make_uint2(((x >> (2 * KB * u)) & M) | MAGIC,
-                                                 ((x >> (KB * (2 * u + 1))) & M) | MAGIC));
+        return __builtin_bit_cast(h4, make_uint2(
+            (rotr(x, uint32_t(2 * KB * u - T) & 31u) & M) | MAGIC,
+            (rotr(x, uint32_t(KB * (2 * u + 1) - T) & 31u) & M) | MAGIC));
     } else {
         const uint32_t word = kb_rt == 8 ? w[ks] : kb_rt == 4 ? w[ks >> 1]
                             : kb_rt == 2 ? w[ks >> 2] : w[0];
@@ -150,9 +167,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t minus1024(uint32_t x) {
     const h2 r = __builtin_bit_cast(h2, x) - h2{(_Float16)1024.0f, (_Float16)1024.0f};
     return __builtin_bit_cast(uint32_t, r);
-}
-__device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n) {
-    return __builtin_amdgcn_alignbit(x, x, n);
 }
 // the lane's value words of one 16-slot block: VB of them (run-time widths: vb)
 template <int VB>
@@ -231,7 +245,8 @@ template <int KH, int VH, int KL, int VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_decode_kernel(
     const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
-    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
+    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part,
+    float *__restrict__ /* lg: no records (groups above 8 heads) */, int64_t /* tiles_cap */) {
     const int kh = KH ? KH : kh_rt, vh = VH ? VH : vh_rt, kl = KL ? KL : kl_rt,
               vl = VL ? VL : vl_rt;
     __shared__ float s_o[WAVES][16][D];
@@ -286,6 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
         if (ta >= tb) return;
         const int kb = KB ? KB : (HIGH ? kh : kl), vb = VB ? VB : (HIGH ? vh : vl);
+        const float kf = key_factor<KB>(kb);
         constexpr int Sp = HIGH ? HS : LS;
         // 16x16x32 product m2: k-steps 2 m2 and 2 m2 + 1 of the key order
         h8 qop[4];
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             float mx = -__builtin_inff();
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu));
+                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu)) * kf;
                 const float kz = h2f(uint16_t(par[q4].x >> 16));
                 vs[q4] = h2f(uint16_t(par[q4].y & 0xffffu)) * val_scale<VB>();
                 vz[q4] = h2f(uint16_t(par[q4].y >> 16));
@@ -421,13 +437,19 @@ struct PairTiles {
     uint32_t wva[VB ? VB : 8], wvb[VB ? VB : 8];
     uint4 pa, pb;        // the lane's own tile's parameters (slots 4 g .. 4 g + 3)
     int live;            // the lane's own tile's live tokens
+    int tile;            // the lane's own tile (-1: none)
+    int ps;              // LG: the position of slot 4 g + (c & 3) of the own tile
 };
 
-template <int KH, int VH, int KL, int VL>
+// LG: also store, per tile of the head (HIGH tiles, then LOW tiles), its 16 slots' positions
+// and every token's logit per query head, in the default decode's record layout
+// lg [head][tile][16 + G * 16], for the score accumulation
+template <int KH, int VH, int KL, int VL, bool LG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scheme_pair_kernel(
     const uint16_t *__restrict__ q, float scale_log2, const uint8_t *__restrict__ pages,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l, int Hkv, int G,
-    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part) {
+    int C, int S, int wt, int kh_rt, int vh_rt, int kl_rt, int vl_rt, float *__restrict__ part,
+    float *__restrict__ lg, int64_t tiles_cap) {
     const int kh = KH ? KH : kh_rt, vh = VH ? VH : vh_rt, kl = KL ? KL : kl_rt,
               vl = VL ? VL : vl_rt;
     __shared__ float s_o[WAVES][16][D];
@@ -504,6 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         constexpr int TIER = HIGH ? 0 : 1;
         if (ta >= tb) return;
         const int kb = KB ? KB : (HIGH ? kh : kl), vb = VB ? VB : (HIGH ? vh : vl);
+        const float kf = key_factor<KB>(kb);
         constexpr int Sp = HIGH ? HS : LS;
         const int nt = HIGH ? nh : nl;
         auto page_of = [&](int t) -> const uint8_t * {
@@ -529,6 +552,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             r.pb = op[1];
             const int tl = own_b ? (t + 1 < tb ? t + 1 : -1) : t;
             r.live = tl < 0 ? 0 : min(16, nt - 16 * tl);
+            r.tile = tl;
+            if constexpr (LG) {
+                r.ps = -1;
+                if (tl >= 0 && hc < 4)
+                    r.ps = reinterpret_cast<const int32_t *>(own + POS_OFF)[16 * (own_b ? fb : fa) +
+                                                                           4 * g + hc];
+            }
         };
         auto compute = [&](const PairTiles<KB, VB> &r) {
             // an opaque lane index keeps the compiler from hoisting the query reads out of the
@@ -549,13 +579,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
             float mx = -__builtin_inff();
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu));
+                const float ksc = h2f(uint16_t(par[q4].x & 0xffffu)) * kf;
                 const float kz = h2f(uint16_t(par[q4].x >> 16));
                 vs[q4] = h2f(uint16_t(par[q4].y & 0xffffu)) * val_scale<VB>();
                 vz[q4] = h2f(uint16_t(par[q4].y >> 16));
                 const float xv = (ksc * acc[q4] + kz * sumq) * scale_log2;
                 x[q4] = 4 * g + q4 < r.live ? xv : -__builtin_inff();
                 mx = fmaxf(mx, x[q4]);
+            }
+            if constexpr (LG) {
+                if (r.tile >= 0) {
+                    float *rec = lg + (int64_t(i) * tiles_cap + (HIGH ? 0 : qH) + r.tile) *
+                                          (16 * (G + 1));
+                    if (hc < G)
+                        *reinterpret_cast<float4 *>(rec + 16 + 16 * hc + 4 * g) =
+                            make_float4(x[0], x[1], x[2], x[3]);
+                    if (hc < 4) reinterpret_cast<int32_t *>(rec)[4 * g + hc] = r.ps;
+                }
             }
             mx = max_col(mx);
             mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xf,
@@ -665,11 +705,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 
 using namespace kvc;
 
-extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_scheme *sc,
-                                                 int32_t layer, const kvc_pool *p,
-                                                 const uint16_t *q, float softmax_scale,
-                                                 void *out, int32_t out_is_fp32, void *ws,
-                                                 size_t ws_bytes, kvc_stream_t stream) {
+namespace {
+
+int scheme_decode_impl(const kvc_geom *g, const kvc_scheme *sc, int32_t layer,
+                       const kvc_pool *p, const uint16_t *q, float softmax_scale, void *out,
+                       int32_t out_is_fp32, float *acc_sum, const int32_t *cu,
+                       int32_t max_seqlen, void *ws, size_t ws_bytes, kvc_stream_t stream) {
     int rc = check_geom(g);
     if (rc) return rc;
     rc = check_pool(p);
@@ -677,28 +718,40 @@ extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_sc
     rc = check_scheme(sc);
     if (rc) return rc;
     if (!q || !out) return KVC_E_NULL;
+    const bool accum = acc_sum != nullptr || cu != nullptr;
+    if (accum && (!acc_sum || !cu)) return KVC_E_NULL;
     if (!aligned16(q) || !aligned16(out)) return KVC_E_ALIGN;
+    if (accum && !aligned16(acc_sum)) return KVC_E_ALIGN;
     if (layer < 0 || layer >= g->num_layers) return KVC_E_SHAPE;
     const int G = g->num_q_heads / g->num_kv_heads;
     if (G > 16) return KVC_E_SHAPE;
-    DecodeWs L(g, false);
+    if (accum && G > 8) return KVC_E_UNSUPPORTED;
+    if (accum && (max_seqlen < 0 || g->num_q_heads > ACC_MAX_HQ)) return KVC_E_SHAPE;
+    DecodeWs L(g, accum, max_seqlen);
     if (!ws || ws_bytes < L.bytes) return KVC_E_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.part);
+    char *w = static_cast<char *>(ws);
+    float *part = reinterpret_cast<float *>(w + L.part);
+    float *mls = accum ? reinterpret_cast<float *>(w + L.mls) : nullptr;
+    float *lg = accum ? reinterpret_cast<float *>(w + L.lg) : nullptr;
     const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
     const int nheads = B * Hkv;
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
-    // the schemes the pages compare are compiled with their widths; others run the generic
-    // instance
+    // the schemes the pages compare are compiled with their widths (others run the generic
+    // instance); the accumulating variant runs the same instance with the record stores
     const int key = sc->k_bits_high * 1000 + sc->v_bits_high * 100 + sc->k_bits_low * 10 +
                     sc->v_bits_low;
     // query groups of up to 8 heads take two tiles per pass
-    auto kern = G <= 8 ? sch::scheme_pair_kernel<0, 0, 0, 0> : sch::scheme_decode_kernel<0, 0, 0, 0>;
+    auto kern = accum ? sch::scheme_pair_kernel<0, 0, 0, 0, true>
+              : G <= 8 ? sch::scheme_pair_kernel<0, 0, 0, 0, false>
+                       : sch::scheme_decode_kernel<0, 0, 0, 0>;
 #define KVC_SCHEME_CASE(k, a, b, c2, d)                                                      \
     case k:                                                                                  \
-        kern = G <= 8 ? sch::scheme_pair_kernel<a, b, c2, d> : sch::scheme_decode_kernel<a, b, c2, d>; \
+        kern = accum ? sch::scheme_pair_kernel<a, b, c2, d, true>                            \
+             : G <= 8 ? sch::scheme_pair_kernel<a, b, c2, d, false>                          \
+                      : sch::scheme_decode_kernel<a, b, c2, d>;                              \
         break;
     switch (key) {
         KVC_SCHEME_CASE(8442, 8, 4, 4, 2)
@@ -712,9 +765,35 @@ extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_sc
 #undef KVC_SCHEME_CASE
     hipLaunchKernelGGL(kern, dim3(L.splits * nheads), dim3(256), 0, s, q,
                        softmax_scale * sch::LOG2E, p->pages, rows_l, count_l, Hkv, G, C, L.splits,
-                       L.wt, sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, part);
+                       L.wt, sc->k_bits_high, sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, part,
+                       lg, L.tiles_cap);
     rc = launch_check("kvc_paged_decode_attention_scheme/main");
     if (rc) return rc;
-    return launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, nullptr,
-                                 count_l, L.wt, s);
+    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
+                               count_l, L.wt, s);
+    if (rc || !accum) return rc;
+    return launch_score_accumulation(g, p, count_l, cu, max_seqlen, acc_sum, w, s);
+}
+
+}  // namespace
+
+extern "C" int kvc_paged_decode_attention_scheme(const kvc_geom *g, const kvc_scheme *sc,
+                                                 int32_t layer, const kvc_pool *p,
+                                                 const uint16_t *q, float softmax_scale,
+                                                 void *out, int32_t out_is_fp32, void *ws,
+                                                 size_t ws_bytes, kvc_stream_t stream) {
+    return scheme_decode_impl(g, sc, layer, p, q, softmax_scale, out, out_is_fp32, nullptr,
+                              nullptr, 0, ws, ws_bytes, stream);
+}
+
+extern "C" int kvc_paged_decode_attention_scheme_acc(const kvc_geom *g, const kvc_scheme *sc,
+                                                     int32_t layer, const kvc_pool *p,
+                                                     const uint16_t *q, float softmax_scale,
+                                                     void *out, int32_t out_is_fp32,
+                                                     float *acc_sum, const int32_t *cu_seqlens,
+                                                     int32_t max_seqlen, void *ws,
+                                                     size_t ws_bytes, kvc_stream_t stream) {
+    if (!acc_sum || !cu_seqlens) return KVC_E_NULL;
+    return scheme_decode_impl(g, sc, layer, p, q, softmax_scale, out, out_is_fp32, acc_sum,
+                              cu_seqlens, max_seqlen, ws, ws_bytes, stream);
 }

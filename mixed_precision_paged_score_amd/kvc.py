@@ -27,7 +27,8 @@ EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_ini
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
            "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
-           "kvc_append_tokens_scheme", "kvc_generation_step_scheme"]
+           "kvc_append_tokens_scheme", "kvc_generation_step_scheme",
+           "kvc_paged_decode_attention_scheme_acc"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -90,13 +91,16 @@ _lib.kvc_quantize_and_place_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, 
 _lib.kvc_append_tokens_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_generation_step_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _vp, _vp, _f32,
                                             _f32, _i32, _vp, _vp, _sz, _vp]
+_lib.kvc_paged_decode_attention_scheme_acc.argtypes = [_G, _S, _i32, _P, _vp, _f32, _vp, _i32,
+                                                       _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention_scheme.argtypes = [_G, _S, _i32, _P, _vp, _f32, _vp, _i32, _vp,
                                                    _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
            "kvc_paged_decode_attention", "kvc_paged_decode_attention_acc", "kvc_append_tokens",
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
            "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
-           "kvc_append_tokens_scheme", "kvc_generation_step_scheme"):
+           "kvc_append_tokens_scheme", "kvc_generation_step_scheme",
+           "kvc_paged_decode_attention_scheme_acc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -269,6 +273,15 @@ def quantize_and_place_scheme(geom, scheme, layer, pool, k, v, cu_seqlens, total
                                               _ptr(changed), _ptr(old_rows), _ptr(old_count),
                                               _ptr(ws), ws.numel(), _stream(stream)),
            "kvc_quantize_and_place_scheme")
+
+
+def paged_decode_attention_scheme_acc(geom, scheme, layer, pool, q, softmax_scale, out, acc_sum,
+                                      cu_seqlens, max_seqlen, ws, stream=None):
+    _check(_lib.kvc_paged_decode_attention_scheme_acc(
+        ctypes.byref(geom), ctypes.byref(scheme), int(layer), ctypes.byref(pool.c), _ptr(q),
+        float(softmax_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(acc_sum),
+        _ptr(cu_seqlens), int(max_seqlen), _ptr(ws), ws.numel(), _stream(stream)),
+        "kvc_paged_decode_attention_scheme_acc")
 
 
 def append_tokens_scheme(geom, scheme, layer, pool, k_new, v_new, positions, ws, stream=None):

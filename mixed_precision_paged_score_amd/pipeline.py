@@ -79,10 +79,17 @@ class PromptPath:
         if self.ws_decode_acc is None:
             self.ws_decode_acc = kvc.workspace(self.geom, kvc.OP_DECODE_ACC, self.seqlen_cap,
                                                device=self.device)
-        kvc.paged_decode_attention_acc(self.geom, layer, self.pool, q, self.scale, out, acc,
-                                       self.cu if cu is None else cu,
-                                       self.max_seqlen if cu is None else self.seqlen_cap,
-                                       self.ws_decode_acc)
+        scheme = getattr(self, "scheme", None)
+        if scheme is None:
+            kvc.paged_decode_attention_acc(self.geom, layer, self.pool, q, self.scale, out, acc,
+                                           self.cu if cu is None else cu,
+                                           self.max_seqlen if cu is None else self.seqlen_cap,
+                                           self.ws_decode_acc)
+        else:
+            kvc.paged_decode_attention_scheme_acc(
+                self.geom, scheme, layer, self.pool, q, self.scale, out, acc,
+                self.cu if cu is None else cu,
+                self.max_seqlen if cu is None else self.seqlen_cap, self.ws_decode_acc)
 
     # -- HIP graphs -------------------------------------------------------------------------
     # Every library call is asynchronous on the current stream, reads its sizes from device

@@ -21,7 +21,9 @@ DEV = "cuda:0"
 RTOL_W, ATOL_W = 1e-4, 1e-7
 
 
-def _oracle_delta(w, k, v, tier, q, scale, heads=None):
+def _oracle_delta(w, k, v, tier, q, scale, heads=None, scheme=None):
+    """scheme: an oracle.scheme.Scheme whose widths the keys were stored at (None: K8V4/K4V2)"""
+    from oracle import scheme as osch
     cu = w.cu_seqlens()
     delta = np.zeros((w.total_tokens, w.num_q_heads))
 
@@ -31,6 +33,8 @@ def _oracle_delta(w, k, v, tier, q, scale, heads=None):
 
     def k_of(b, h):
         lo, hi = rows(b, h)
+        if scheme is not None:
+            return osch.head_dequantized(k[lo:hi, h], v[lo:hi, h], tier[lo:hi, h], scheme)[0]
         return place.head_dequantized(k[lo:hi, h], v[lo:hi, h], tier[lo:hi, h])[0]
 
     def pos_of(b, h):
@@ -56,16 +60,24 @@ def _check(got, want, mask=None):
     assert bad.size == 0, f"{len(bad)} weights off, worst {err.max():.3e}"
 
 
-def run_case(w, steps=1, sample_heads=None):
-    from mixed_precision_paged_score_amd import pipeline
+def run_case(w, steps=1, sample_heads=None, scheme=None):
+    """scheme: (HIGH format, LOW format) names: the prompt placed in that scheme's layout,
+    the accumulating scheme decode against the plain scheme decode and the oracle's weights
+    over the scheme's dequantized keys."""
+    from mixed_precision_paged_score_amd import kvc, pipeline
+    from oracle import scheme as osch
     print(f"[acc] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-          f"lens={w.seqlens[:6]} steps={steps}", flush=True)
+          f"lens={w.seqlens[:6]} steps={steps} scheme={scheme}", flush=True)
     gen = "cpu" if w.total_tokens * w.num_q_heads < (1 << 22) else DEV
     k, v = workloads.make_kv(w, gen)
     acc = workloads.make_acc(w, k, gen)
     k, v, acc = k.to(DEV), v.to(DEV), acc.to(DEV)
     path = pipeline.PromptPath(w, DEV)
-    path.prompt(0, acc, k, v)
+    if scheme is None:
+        path.prompt(0, acc, k, v)
+    else:
+        path.scheme = kvc.make_scheme(*scheme)      # decode_acc then takes the scheme decode
+        path.prompt_scheme(0, acc, k, v, path.scheme)
     tier = parity.np_(path.tier[:w.total_tokens])
     acc_gpu = torch.zeros_like(acc)     # accumulators start at zero: the sums stay exact
     out_a = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=DEV)
@@ -73,7 +85,10 @@ def run_case(w, steps=1, sample_heads=None):
     qs = [workloads.make_queries(w, DEV, s) for s in range(steps)]
     for q in qs:
         path.decode_acc(0, q, out_a, acc_gpu)
-        path.decode(0, q, out_p)
+        if scheme is None:
+            path.decode(0, q, out_p)
+        else:
+            path.decode_scheme(0, q, out_p, path.scheme)
     torch.cuda.synchronize()
     assert path.pool.status() == 0
     # the output is the plain decode's
@@ -86,8 +101,9 @@ def run_case(w, steps=1, sample_heads=None):
         allh = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
         heads = [allh[i] for i in rng.choice(len(allh), sample_heads, replace=False)]
     want = np.zeros_like(delta)
+    osc_ = osch.Scheme.named(*scheme) if scheme else None
     for q in qs:
-        want += _oracle_delta(w, kc, vc, tier, parity.np_(q), path.scale, heads)
+        want += _oracle_delta(w, kc, vc, tier, parity.np_(q), path.scale, heads, osc_)
     if heads is None:
         _check(delta, want)
     else:
@@ -125,3 +141,16 @@ def test_workload2_full():
 
 def test_workload3_sampled():
     run_case(workloads.workload(3), sample_heads=6)
+
+
+@pytest.mark.parametrize("scheme", [("K4V8", "K2V4"), ("K8V2", "K4V1"), ("K2V4", "K4V2")])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 4)])
+def test_scheme_pages_ragged(scheme, hq, hkv):
+    # the accumulating decode over precision-scheme pages (groups of 1, 4 and 8 query heads)
+    w = workloads.Workload(f"acc-sch-{hq}-{hkv}", 1, 5, hq, hkv, [1, 0, 37, 300, 777], 1.0, 0.2,
+                           16, 4096, "causal", seed=43)
+    run_case(w, steps=2, scheme=scheme)
+
+
+def test_scheme_pages_workload2_full():
+    run_case(workloads.workload(2), scheme=("K4V8", "K2V4"))
