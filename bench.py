@@ -73,6 +73,9 @@ def parse():
                     help="launch every library call from Python instead of replaying HIP graphs")
     ap.add_argument("--group-sweep", action="store_true",
                     help="only time the decode at G = 1, 2, 4, 8, 16 query heads per KV head")
+    ap.add_argument("--three-calls", action="store_true",
+                    help="run each layer's round as the three calls (score, compact, quantize/place) "
+                         "instead of kvc_compaction_round")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM counters)")
     return ap.parse_args()
@@ -379,15 +382,18 @@ def run_step_workload(a, w, stream, spin, flush, steps, warmup, nsteps_dec, grap
     path = pipeline.PromptPath(w, dev)
     out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
     timer = Timer(stream)
+    # a layer's round: kvc_compaction_round (up to 1024 KV heads), else the three calls
+    fused = not a.three_calls and w.batch * w.num_kv_heads <= 1024
+    round_fn = path.prompt_fused if fused else path.prompt
     # the first pass places every layer (and, in graph mode, makes the workspaces before capture)
     for layer in range(L):
         k, v, acc, _ = ins[layer]
-        path.prompt(layer, acc, k, v)
+        round_fn(layer, acc, k, v)
     torch.cuda.synchronize()
     counts = [path.pool.count[layer].cpu().numpy() for layer in range(L)]
     g_prompt = g_dec = None
     if graphs:
-        g_prompt = path.capture_prompt(0, ins[0][2], ins[0][0], ins[0][1])
+        g_prompt = path.capture_prompt(0, ins[0][2], ins[0][0], ins[0][1], fused=fused)
         g_dec = path.capture_decode(0, ins[0][3], out)
         torch.cuda.synchronize()
 
@@ -402,7 +408,7 @@ def run_step_workload(a, w, stream, spin, flush, steps, warmup, nsteps_dec, grap
                 g_prompt.replay()
             else:
                 k, v, acc, _ = ins[layer]
-                path.prompt(layer, acc, k, v)
+                round_fn(layer, acc, k, v)
         ev.append(timer.ev())
         for layer in range(L):
             if graphs:
@@ -441,7 +447,9 @@ def run_step_workload(a, w, stream, spin, flush, steps, warmup, nsteps_dec, grap
     res = {
         "value": token_heads / comp_s,
         "ms_per_step": wall / steps * 1e3,
-        "compaction": {"us_per_layer_round": comp_round_us, "ms_all_layers": comp_s * 1e3,
+        "compaction": {"path": "kvc_compaction_round" if fused else
+                               "kvc_score_tokens + kvc_compact_pages + kvc_quantize_and_place",
+                       "us_per_layer_round": comp_round_us, "ms_all_layers": comp_s * 1e3,
                        "GBps": comp_gbps, "frac_hbm": comp_gbps / HBM_PEAK_GBPS,
                        "algorithmic_bytes_per_layer": float(cbytes.mean()),
                        "token_heads": token_heads, "high": nh, "low": nl,
@@ -464,6 +472,11 @@ def run_step_workload(a, w, stream, spin, flush, steps, warmup, nsteps_dec, grap
     def comp_one(r):
         layer = (r * 37) % L
         k, v, acc, _ = ins[layer]
+        round_fn(layer, acc, k, v)
+
+    def comp_three(r):
+        layer = (r * 37) % L
+        k, v, acc, _ = ins[layer]
         path.prompt(layer, acc, k, v)
     lay = [(r * 37) % L for r in range(reps)]
     res["cold"] = {
@@ -472,6 +485,10 @@ def run_step_workload(a, w, stream, spin, flush, steps, warmup, nsteps_dec, grap
         "protocol": "a 1 GiB scratch read before each rep (evicts the L2s and the Infinity "
                     "Cache, leaves no dirty lines); one call per rep, layers in turn",
     }
+    if fused:
+        # the same rounds as the three separate calls, for comparison
+        res["cold"]["compaction_round_three_calls"] = stats(
+            cold_reps(reps, flush, comp_three, timer), cbytes[lay])
     res["pool_status"] |= path.pool.status()
     return res, path, ins, counts
 
@@ -776,9 +793,14 @@ def extras_w4(a, stream, flush):
     # the prompt round (prompt mode: each rep returns the previous rep's pages to the ring)
     pp = pipeline.PromptPath(w, dev)
     pp.prompt(0, acc, k, v)
-    pr_us = cold_reps(reps, flush, lambda r: pp.prompt(0, acc, k, v), timer)
+    pp.prompt_fused(0, acc, k, v)
+    pr_us = cold_reps(reps, flush, lambda r: pp.prompt_fused(0, acc, k, v), timer)
+    pr3_us = cold_reps(reps, flush, lambda r: pp.prompt(0, acc, k, v), timer)
     cnt0 = pp.new_count.cpu().numpy()
-    res = {"prompt_round": stats(pr_us, compaction_algorithmic_bytes(cnt0, T0, Hkv, Hq))}
+    pbytes = compaction_algorithmic_bytes(cnt0, T0, Hkv, Hq)
+    res = {"prompt_round": stats(pr_us, pbytes),
+           "prompt_round_three_calls": stats(pr3_us, pbytes)}
+    res["prompt_round"]["path"] = "kvc_compaction_round"
     status = pp.pool.status()
     del pp
     path = pipeline.GenerationPath(w, max(w.seqlens) + steps, dev)
@@ -819,34 +841,51 @@ def extras_w4(a, stream, flush):
             t.copy_(s0)
         evict(flush)
 
-    rt_us = []
-    for r in range(reps + 1):             # the first round is a warm-up
-        round_one(r)
-        prev = path.packed_state()
-        e0 = timer.ev()
-        kvc.score_tokens(path.geom, last, path.cu, path.T, path.max_seqlen, w.alpha_h, w.alpha_l,
-                         w.window, path.tier, path.new_count, prev_tier=prev,
-                         changed=path.changed, dev_status=path.score_status)
-        kvc.compact_pages(path.geom, 0, pool, path.new_count, path.ws_compact,
-                          changed=path.changed, old_rows=path.old_rows, old_count=path.old_count)
-        kvc.quantize_and_place(path.geom, 0, pool, None, None, path.cu, path.T, path.max_seqlen,
-                               path.tier, path.ws_quant, prev_tier=prev, changed=path.changed,
-                               old_rows=path.old_rows, old_count=path.old_count)
-        e1 = timer.ev()
-        torch.cuda.synchronize()
-        status |= pool.status()
-        if r > 0:
-            rt_us.append(timer.us(e0, e1))
+    ws_round = kvc.workspace(path.geom, kvc.OP_ROUND, path.seqlen_cap, device=dev)
+
+    def timed_rounds(fused):
+        us = []
+        for r in range(reps + 1):             # the first round is a warm-up
+            round_one(r)
+            prev = path.packed_state()
+            e0 = timer.ev()
+            if fused:
+                kvc.compaction_round(path.geom, 0, pool, last, path.cu, path.T, path.max_seqlen,
+                                     w.alpha_h, w.alpha_l, w.window, None, None, path.tier,
+                                     path.new_count, ws_round, prev_tier=prev,
+                                     changed=path.changed)
+            else:
+                kvc.score_tokens(path.geom, last, path.cu, path.T, path.max_seqlen, w.alpha_h,
+                                 w.alpha_l, w.window, path.tier, path.new_count, prev_tier=prev,
+                                 changed=path.changed, dev_status=path.score_status)
+                kvc.compact_pages(path.geom, 0, pool, path.new_count, path.ws_compact,
+                                  changed=path.changed, old_rows=path.old_rows,
+                                  old_count=path.old_count)
+                kvc.quantize_and_place(path.geom, 0, pool, None, None, path.cu, path.T,
+                                       path.max_seqlen, path.tier, path.ws_quant, prev_tier=prev,
+                                       changed=path.changed, old_rows=path.old_rows,
+                                       old_count=path.old_count)
+            e1 = timer.ev()
+            torch.cuda.synchronize()
+            if r > 0:
+                us.append(timer.us(e0, e1))
+        return us
+    rt3_us = timed_rounds(False)
+    status |= pool.status()
+    rt_us = timed_rounds(True)
+    status |= pool.status()
     chg = path.changed.cpu().numpy().astype(bool)
-    old_c = path.old_count.cpu().numpy()[chg]
+    old_c = snap[2][0].cpu().numpy()[chg]               # the counts before the round
     new_c = path.new_count.cpu().numpy()[chg]
     T = path.T
     # algorithmic bytes of a round: the accumulators, previous and new tiers, and for every
     # rebuilt head its old pages read and its new pages written
     rbytes = T * Hq * 4 + 2 * T * Hkv + (pages_of(old_c) + pages_of(new_c)) * kvc.PAGE_BYTES
     res["retier_round"] = stats(rt_us, rbytes)
-    res["retier_round"].update({"algorithmic_bytes": rbytes, "heads_rebuilt": int(chg.sum()),
-                                "token_heads": T * Hkv, "tokens_per_request": path.lens[0]})
+    res["retier_round"].update({"path": "kvc_compaction_round", "algorithmic_bytes": rbytes,
+                                "heads_rebuilt": int(chg.sum()), "token_heads": T * Hkv,
+                                "tokens_per_request": path.lens[0]})
+    res["retier_round_three_calls"] = stats(rt3_us, rbytes)
     res["status"] = status
     res["config"] = {"workload": w.name, "batch": B, "prompt": max(w.seqlens),
                      "generated": steps, "round_every": R, "q_heads": Hq, "kv_heads": Hkv}

@@ -113,7 +113,7 @@ typedef struct {
 
 /* Operation ids for kvc_workspace_bytes */
 enum { KVC_OP_COMPACT = 1, KVC_OP_QUANTIZE = 2, KVC_OP_DECODE = 3, KVC_OP_APPEND = 4,
-       KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6, KVC_OP_PREFILL = 7 };
+       KVC_OP_DECODE_ACC = 5, KVC_OP_GENERATE = 6, KVC_OP_PREFILL = 7, KVC_OP_ROUND = 8 };
 
 /* Version string of the library. */
 const char *kvc_version(void);
@@ -122,8 +122,8 @@ const char *kvc_version(void);
 const char *kvc_last_error(void);
 
 /* Bytes of workspace `op` needs for this geometry.  max_seqlen is the longest request
- * (KVC_OP_QUANTIZE, KVC_OP_DECODE_ACC, KVC_OP_PREFILL), unused otherwise.  Returns 0 for an
- * unknown op. */
+ * (KVC_OP_QUANTIZE, KVC_OP_DECODE_ACC, KVC_OP_PREFILL, KVC_OP_ROUND), unused otherwise.
+ * Returns 0 for an unknown op. */
 size_t kvc_workspace_bytes(const kvc_geom *geom, int32_t op, int32_t max_seqlen);
 
 /* Empty pool: free_ring = 0..P-1, head = 0, tail = P, page table and owner = -1,
@@ -222,6 +222,30 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
                            const uint8_t *prev_tier, const uint8_t *changed,
                            const int32_t *old_rows, const int32_t *old_count,
                            void *workspace, size_t workspace_bytes, kvc_stream_t stream);
+
+/* One whole compaction round of a layer: kvc_score_tokens, kvc_compact_pages and
+ * kvc_quantize_and_place in sequence (DiffKV review page, "What carries the argument": score,
+ * per-head page demand, prefix-sum allocation over the circular free list, placement), with the
+ * same results bit for bit, in five launches instead of nine: the score also counts each
+ * 256-token tile's tiers per head (nothing to clear, no separate count launch) and one planning
+ * workgroup turns the tile counts into the heads' totals, the rank bases and the allocation
+ * scan.  For batches of at most 1024 KV heads (KVC_E_SHAPE above: use the three calls).
+ *   prev_tier NULL: prompt mode (every head rebuilt, the layer's previous pages returned first;
+ *     k, v required, changed may be NULL); else re-tier mode (changed required; k, v only for
+ *     FRESH tokens; the old rows and counts are kept in the workspace).
+ *   Inputs and outputs as in the three calls: acc_sum fp32 [T][Hq] (16-byte aligned), tier u8
+ *   [T][Hkv], new_count i32 [B][Hkv][2], changed u8 [B][Hkv]; device failures are the same
+ *   status bits in pool->dev_status, the score's included (a request longer than max_seqlen:
+ *   KVC_DEV_SEQLEN, as kvc_score_tokens given the pool's status), and a round that does not
+ *   commit changes nothing.
+ *   workspace >= kvc_workspace_bytes(geom, KVC_OP_ROUND, max_seqlen) bytes, 256-B aligned
+ * Errors: the union of the three calls' errors. */
+int kvc_compaction_round(const kvc_geom *geom, int32_t layer, const kvc_pool *pool,
+                         const float *acc_sum, const int32_t *cu_seqlens, int64_t total_tokens,
+                         int32_t max_seqlen, float alpha_h, float alpha_l, int32_t window,
+                         const uint16_t *k, const uint16_t *v, const uint8_t *prev_tier,
+                         uint8_t *tier, int32_t *new_count, uint8_t *changed, void *workspace,
+                         size_t workspace_bytes, kvc_stream_t stream);
 
 /* Placement under a precision scheme (DiffKV review page: the free-parameter ledger's
  * comparison of K8V4, K4V8, K8V2, K4V2, K2V4 and K4V1; referee minor comment 5 for the

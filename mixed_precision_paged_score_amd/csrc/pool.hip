@@ -53,6 +53,7 @@ extern "C" size_t kvc_workspace_bytes(const kvc_geom *g, int32_t op, int32_t max
         case KVC_OP_APPEND: return AppendWs(g).bytes;
         case KVC_OP_GENERATE: return GenWs(g).bytes;
         case KVC_OP_PREFILL: return max_seqlen < 0 ? 0 : PrefillWs(g, max_seqlen).bytes;
+        case KVC_OP_ROUND: return max_seqlen < 0 ? 0 : RoundWs(g, max_seqlen).bytes;
         default: return 0;
     }
 }

@@ -797,3 +797,77 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
                            sc->v_bits_high, sc->k_bits_low, sc->v_bits_low, p->pages);
     return launch_check("kvc_quantize_and_place_scheme/pages");
 }
+
+// ---- the fused compaction round -------------------------------------------------------------
+// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in five launches for up to
+// ROUND_MAX_HEADS heads: score with per-tile counts (no counters to clear, no separate count
+// launch), one planning workgroup (totals, tile bases, page demands, the allocation scan), the
+// commit, the ranks and the page writer.
+extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                                    const float *acc, const int32_t *cu, int64_t total_tokens,
+                                    int32_t max_seqlen, float alpha_h, float alpha_l,
+                                    int32_t window, const uint16_t *k, const uint16_t *v,
+                                    const uint8_t *prev_tier, uint8_t *tier, int32_t *new_count,
+                                    uint8_t *changed, void *ws, size_t ws_bytes,
+                                    kvc_stream_t stream) {
+    int rc = check_geom(g);
+    if (rc) return rc;
+    rc = check_pool(p);
+    if (rc) return rc;
+    const bool retier = prev_tier != nullptr;
+    if (!cu || !new_count || (total_tokens > 0 && (!acc || !tier))) return KVC_E_NULL;
+    if (retier && !changed) return KVC_E_NULL;
+    if (!retier && total_tokens > 0 && (!k || !v)) return KVC_E_NULL;
+    if (total_tokens < 0 || window < 0 || max_seqlen < 0) return KVC_E_SHAPE;
+    if (layer < 0 || layer >= g->num_layers) return KVC_E_SHAPE;
+    const int B = g->batch, Hkv = g->num_kv_heads, C = g->row_capacity;
+    const int nheads = B * Hkv;
+    if (Hkv > 256 || nheads > ROUND_MAX_HEADS) return KVC_E_SHAPE;
+    if (int64_t(nheads) * C >= (int64_t(1) << 31)) return KVC_E_SHAPE;
+    if (acc && (reinterpret_cast<uintptr_t>(acc) & 15u) != 0) return KVC_E_ALIGN;
+    if ((k && !aligned16(k)) || (v && !aligned16(v))) return KVC_E_ALIGN;
+    RoundWs R(g, max_seqlen);
+    if (!ws || ws_bytes < R.bytes) return KVC_E_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return KVC_E_ALIGN;
+    char *w = static_cast<char *>(ws);
+    const QuantWs L(g, max_seqlen);
+    int32_t *tile_cnt = reinterpret_cast<int32_t *>(w + R.quant + L.tile_cnt);
+    int32_t *tile_base = reinterpret_cast<int32_t *>(w + R.quant + L.tile_base);
+    int32_t *tile_cnt2 = retier ? reinterpret_cast<int32_t *>(w + R.quant + L.tile_cnt2) : nullptr;
+    int32_t *tile_base2 = retier ? reinterpret_cast<int32_t *>(w + R.quant + L.tile_base2) : nullptr;
+    int32_t *ok = reinterpret_cast<int32_t *>(w + R.quant + L.ok);
+    int32_t *poslist = reinterpret_cast<int32_t *>(w + R.quant + L.poslist);
+    uint2 *srcdesc = retier ? reinterpret_cast<uint2 *>(w + R.quant + L.srcdesc) : nullptr;
+    uint8_t *tile_chg = reinterpret_cast<uint8_t *>(w + R.tile_chg);
+    int32_t *old_rows = retier ? reinterpret_cast<int32_t *>(w + R.old_rows) : nullptr;
+    int32_t *old_count = retier ? reinterpret_cast<int32_t *>(w + R.old_count) : nullptr;
+    const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
+    const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
+    hipStream_t s = (hipStream_t)stream;
+    rc = launch_round_score(g, acc, cu, max_seqlen, alpha_h, alpha_l, window, prev_tier, tier,
+                            tile_cnt, tile_cnt2, tile_chg, p->dev_status, s);
+    if (rc) return rc;
+    rc = launch_round_plan(g, cu, max_seqlen, L.ntq, tile_cnt, tile_cnt2, tile_chg, tile_base,
+                           tile_base2, count_l, new_count, retier ? changed : nullptr, ok, p,
+                           w + R.compact, s);
+    if (rc) return rc;
+    rc = launch_commit(g, layer, p, new_count, retier ? changed : nullptr, old_rows, old_count,
+                       w + R.compact, s);
+    if (rc) return rc;
+    if (max_seqlen == 0 || total_tokens == 0) return KVC_OK;
+    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
+                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, old_rows, C, poslist,
+                       srcdesc);
+    rc = launch_check("kvc_compaction_round/select");
+    if (rc) return rc;
+    const dim3 grid((C + QP_WAVES - 1) / QP_WAVES, nheads);
+    if (retier)
+        hipLaunchKernelGGL(quant_pages_kernel<true>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv,
+                           C, max_seqlen, rows_l, count_l, ok, poslist, srcdesc, p->pages,
+                           p->dev_status);
+    else
+        hipLaunchKernelGGL(quant_pages_kernel<false>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu,
+                           Hkv, C, max_seqlen, rows_l, count_l, ok, poslist, nullptr, p->pages,
+                           p->dev_status);
+    return launch_check("kvc_compaction_round/pages");
+}

@@ -11,6 +11,7 @@
 // division per (token, head) suffices.  Per-head counts are reduced in LDS and added to
 // global memory with one atomic per (workgroup, head, tier).
 #include "kvc_internal.h"
+#include "workspace.h"
 
 namespace kvc {
 
@@ -27,13 +28,17 @@ __global__ void score_zero_kernel(int32_t *count, int n, uint8_t *changed, int n
     if (changed && i < nc) changed[i] = 0;
 }
 
-template <int G>   // G > 0: compile-time group size; G == 0: runtime group size `g`
+// TILES (the fused round): instead of adding the workgroup's counts into count[B][Hkv][2] and
+// setting changed[B][Hkv], store them per tile: count -> [B][ntq][Hkv][2] (new tiers),
+// count2 -> the same for the previous tiers, changed -> [B][ntq][Hkv] (a tier dropped)
+template <int G, bool TILES>   // G > 0: compile-time group size; G == 0: runtime group size `g`
 __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const float *__restrict__ acc, const int32_t *__restrict__ cu, int B, int Hkv, int g,
     int max_seqlen, float alpha_h, float alpha_l, int window,
     const uint8_t *__restrict__ prev, uint8_t *__restrict__ tier, int32_t *__restrict__ count,
-    uint8_t *__restrict__ changed, int32_t *status) {
+    uint8_t *__restrict__ changed, int32_t *status, int32_t *__restrict__ count2) {
     __shared__ int s_cnt[MAX_HKV_LDS * 2];
+    __shared__ int s_cnt2[TILES ? MAX_HKV_LDS * 2 : 1];
     __shared__ int s_chg[MAX_HKV_LDS];
     const int b = blockIdx.y;
     const int lo = cu[b];
@@ -47,6 +52,8 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const int gs = G > 0 ? G : g;
     const int Hq = Hkv * gs;
     for (int i = threadIdx.x; i < Hkv * 2; i += blockDim.x) s_cnt[i] = 0;
+    if constexpr (TILES)
+        for (int i = threadIdx.x; i < Hkv * 2; i += blockDim.x) s_cnt2[i] = 0;
     for (int i = threadIdx.x; i < Hkv; i += blockDim.x) s_chg[i] = 0;
     __syncthreads();
     const float fN = float(N);
@@ -77,6 +84,10 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
         if (t >= N - window) x = HIGH;
         if (prev) {
             const int p = prev[r * Hkv + h];
+            if constexpr (TILES) {
+                if (p == HIGH) atomicAdd(&s_cnt2[2 * h], 1);
+                else if (p == LOW) atomicAdd(&s_cnt2[2 * h + 1], 1);
+            }
             if (p != FRESH) {
                 if (x < p) s_chg[h] = 1;
                 x = min(x, p);
@@ -89,13 +100,49 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
         else if (x == LOW) atomicAdd(&s_cnt[2 * h + 1], 1);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < Hkv * 2; i += blockDim.x) {
-        const int c = s_cnt[i];
-        if (c) atomicAdd(&count[(b * Hkv) * 2 + i], c);
+    if constexpr (TILES) {
+        const int64_t tb = int64_t(b) * gridDim.x + blockIdx.x;      // (request, tile)
+        for (int i = threadIdx.x; i < Hkv * 2; i += blockDim.x) {
+            count[tb * Hkv * 2 + i] = s_cnt[i];
+            if (prev) count2[tb * Hkv * 2 + i] = s_cnt2[i];
+        }
+        if (prev)
+            for (int i = threadIdx.x; i < Hkv; i += blockDim.x)
+                changed[tb * Hkv + i] = uint8_t(s_chg[i]);
+    } else {
+        for (int i = threadIdx.x; i < Hkv * 2; i += blockDim.x) {
+            const int c = s_cnt[i];
+            if (c) atomicAdd(&count[(b * Hkv) * 2 + i], c);
+        }
+        if (changed)
+            for (int i = threadIdx.x; i < Hkv; i += blockDim.x)
+                if (s_chg[i]) changed[b * Hkv + i] = 1;
     }
-    if (changed)
-        for (int i = threadIdx.x; i < Hkv; i += blockDim.x)
-            if (s_chg[i]) changed[b * Hkv + i] = 1;
+}
+
+static_assert(SCORE_TILE == QTILE, "a fused round's score tiles are its rank tiles");
+
+// the score launch of a fused round: tiers, per-tile counts (new and previous tiers) and
+// per-tile dropped-tier flags; grid (ntq, B) with ntq = ceil(max_seqlen / QTILE)
+int launch_round_score(const kvc_geom *g, const float *acc, const int32_t *cu, int max_seqlen,
+                       float alpha_h, float alpha_l, int window, const uint8_t *prev_tier,
+                       uint8_t *tier, int32_t *tile_cnt, int32_t *tile_cnt2, uint8_t *tile_chg,
+                       int32_t *status, hipStream_t s) {
+    const int B = g->batch, Hkv = g->num_kv_heads, G = g->num_q_heads / g->num_kv_heads;
+    const int ntq = max(1, (max_seqlen + QTILE - 1) / QTILE);
+    const dim3 grid(ntq, B), block(SCORE_THREADS);
+#define KVC_ROUND_SCORE(GG)                                                                    \
+    hipLaunchKernelGGL((score_kernel<GG, true>), grid, block, 0, s, acc, cu, B, Hkv, G,         \
+                       max_seqlen, alpha_h, alpha_l, window, prev_tier, tier, tile_cnt, tile_chg, \
+                       status, tile_cnt2)
+    switch (G) {
+        case 4: KVC_ROUND_SCORE(4); break;
+        case 8: KVC_ROUND_SCORE(8); break;
+        case 16: KVC_ROUND_SCORE(16); break;
+        default: KVC_ROUND_SCORE(0); break;
+    }
+#undef KVC_ROUND_SCORE
+    return launch_check("kvc_compaction_round/score");
 }
 
 }  // namespace kvc
@@ -125,9 +172,9 @@ extern "C" int kvc_score_tokens(const kvc_geom *g, const float *acc, const int32
     dim3 grid((max_seqlen + SCORE_TILE - 1) / SCORE_TILE, B);
     dim3 block(SCORE_THREADS);
 #define KVC_SCORE_LAUNCH(GG)                                                                  \
-    hipLaunchKernelGGL(score_kernel<GG>, grid, block, 0, s, acc, cu, B, Hkv, G, max_seqlen,   \
-                       alpha_h, alpha_l, window, prev_tier, tier, new_count, changed,         \
-                       dev_status)
+    hipLaunchKernelGGL((score_kernel<GG, false>), grid, block, 0, s, acc, cu, B, Hkv, G,      \
+                       max_seqlen, alpha_h, alpha_l, window, prev_tier, tier, new_count,      \
+                       changed, dev_status, nullptr)
     switch (G) {
         case 4: KVC_SCORE_LAUNCH(4); break;
         case 8: KVC_SCORE_LAUNCH(8); break;

@@ -73,7 +73,7 @@ struct PrefillWs {
 };
 
 // ---- quantize_and_place ----------------------------------------------------------------
-constexpr int QTILE = 256;        // tokens per rank tile
+constexpr int QTILE = 256;        // tokens per rank tile (and per score tile of a fused round)
 
 struct QuantWs {
     int ntq;
@@ -94,6 +94,22 @@ struct QuantWs {
         // from, {old page id, previous tier << 8 | slot in the old page}
         srcdesc = poslist + pl;
         bytes = srcdesc + 2 * pl;
+    }
+};
+
+// ---- the fused compaction round (kvc_compaction_round) -----------------------------------
+constexpr int ROUND_MAX_HEADS = 1024;    // the planning workgroup's heads: 4 per thread
+struct RoundWs {
+    size_t quant, compact, tile_chg, old_rows, old_count, bytes;
+    RoundWs(const kvc_geom *g, int max_seqlen) {
+        const QuantWs Q(g, max_seqlen);
+        const size_t heads = size_t(g->batch) * g->num_kv_heads;
+        quant = 0;                        // the QuantWs layout: tile counts, bases, ok, lists
+        compact = Q.bytes;                // the CompactWs layout: header, offsets
+        tile_chg = compact + CompactWs(g).bytes;     // per tile and head: a tier dropped
+        old_rows = tile_chg + align256(size_t(g->batch) * Q.ntq * g->num_kv_heads);
+        old_count = old_rows + align256(sizeof(int32_t) * heads * size_t(g->row_capacity));
+        bytes = old_count + align256(sizeof(int32_t) * 2 * heads);
     }
 };
 

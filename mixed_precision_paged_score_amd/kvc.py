@@ -16,6 +16,7 @@ DEV_POOL_EXHAUSTED, DEV_ROW_OVERFLOW, DEV_SHRINK, DEV_COUNT_MISMATCH, DEV_SEQLEN
 DEV_INTERNAL, DEV_BAD_TIER = 32, 64
 PRUNE, LOW, HIGH, FRESH = 0, 1, 2, 3
 OP_COMPACT, OP_QUANTIZE, OP_DECODE, OP_APPEND, OP_DECODE_ACC, OP_GENERATE = 1, 2, 3, 4, 5, 6
+OP_ROUND = 8
 OP_PREFILL = 7
 HEAD_DIM, HIGH_SLOTS, LOW_SLOTS, PAGE_BYTES = 128, 16, 32, 3456
 STATIC_SCRATCH_BYTES = 64 << 20     # the device array behind kvc_paged_decode_attention_static
@@ -28,7 +29,7 @@ EXPORTS = ["kvc_version", "kvc_last_error", "kvc_workspace_bytes", "kvc_pool_ini
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
            "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
            "kvc_append_tokens_scheme", "kvc_generation_step_scheme",
-           "kvc_paged_decode_attention_scheme_acc"]
+           "kvc_paged_decode_attention_scheme_acc", "kvc_compaction_round"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mixed_precision_paged_score_amd.build`")
@@ -93,6 +94,8 @@ _lib.kvc_generation_step_scheme.argtypes = [_G, _S, _i32, _P, _vp, _vp, _vp, _vp
                                             _f32, _i32, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention_scheme_acc.argtypes = [_G, _S, _i32, _P, _vp, _f32, _vp, _i32,
                                                        _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.kvc_compaction_round.argtypes = [_G, _i32, _P, _vp, _vp, _i64, _i32, _f32, _f32, _i32, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.kvc_paged_decode_attention_scheme.argtypes = [_G, _S, _i32, _P, _vp, _f32, _vp, _i32, _vp,
                                                    _sz, _vp]
 for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quantize_and_place",
@@ -100,7 +103,7 @@ for _f in ("kvc_pool_init", "kvc_score_tokens", "kvc_compact_pages", "kvc_quanti
            "kvc_generation_step", "kvc_prefill_attention", "kvc_quantize_and_place_scheme",
            "kvc_paged_decode_attention_scheme", "kvc_paged_decode_attention_static",
            "kvc_append_tokens_scheme", "kvc_generation_step_scheme",
-           "kvc_paged_decode_attention_scheme_acc"):
+           "kvc_paged_decode_attention_scheme_acc", "kvc_compaction_round"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -282,6 +285,17 @@ def paged_decode_attention_scheme_acc(geom, scheme, layer, pool, q, softmax_scal
         float(softmax_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(acc_sum),
         _ptr(cu_seqlens), int(max_seqlen), _ptr(ws), ws.numel(), _stream(stream)),
         "kvc_paged_decode_attention_scheme_acc")
+
+
+def compaction_round(geom, layer, pool, acc_sum, cu_seqlens, total_tokens, max_seqlen, alpha_h,
+                     alpha_l, window, k, v, tier, new_count, ws, prev_tier=None, changed=None,
+                     stream=None):
+    _check(_lib.kvc_compaction_round(ctypes.byref(geom), int(layer), ctypes.byref(pool.c),
+                                     _ptr(acc_sum), _ptr(cu_seqlens), int(total_tokens),
+                                     int(max_seqlen), float(alpha_h), float(alpha_l), int(window),
+                                     _ptr(k), _ptr(v), _ptr(prev_tier), _ptr(tier),
+                                     _ptr(new_count), _ptr(changed), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "kvc_compaction_round")
 
 
 def append_tokens_scheme(geom, scheme, layer, pool, k_new, v_new, positions, ws, stream=None):

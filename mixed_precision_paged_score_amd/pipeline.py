@@ -29,6 +29,7 @@ class PromptPath:
         self.ws_quant = kvc.workspace(self.geom, kvc.OP_QUANTIZE, self.max_seqlen, device=device)
         self.ws_decode = kvc.workspace(self.geom, kvc.OP_DECODE, device=device)
         self.ws_decode_acc = None           # made on first use (it holds every live logit)
+        self.ws_round = None                # made on first use of the fused round
         self.seqlen_cap = self.max_seqlen   # longest request the workspaces are sized for
         self.scale = 1.0 / math.sqrt(kvc.HEAD_DIM)
 
@@ -55,6 +56,16 @@ class PromptPath:
         self.score(acc)
         self.compact(layer)
         self.place(layer, k, v)
+
+    def prompt_fused(self, layer, acc, k, v):
+        """The same round as prompt() through kvc_compaction_round (up to 1024 KV heads)."""
+        w = self.w
+        if self.ws_round is None:
+            self.ws_round = kvc.workspace(self.geom, kvc.OP_ROUND, self.max_seqlen,
+                                          device=self.device)
+        kvc.compaction_round(self.geom, layer, self.pool, acc, self.cu, self.T, self.max_seqlen,
+                             w.alpha_h, w.alpha_l, w.window, k, v, self.tier, self.new_count,
+                             self.ws_round)
 
     def prompt_scheme(self, layer, acc, k, v, scheme):
         """A prompt round whose pages use a precision scheme (kvc.make_scheme): score,
@@ -95,12 +106,16 @@ class PromptPath:
     # Every library call is asynchronous on the current stream, reads its sizes from device
     # memory and clears its own scratch with kernels (no memset nodes), so a sequence of calls
     # can be captured once and replayed; each replay redoes all the work on the current data.
-    def capture_prompt(self, layer, acc, k, v):
+    def capture_prompt(self, layer, acc, k, v, fused=False):
         """Graph of one prompt round of a layer: score, compact (prompt mode: the layer's
-        current pages go back to the ring, new ones are assigned) and quantize/place."""
+        current pages go back to the ring, new ones are assigned) and quantize/place, as the
+        three calls or (fused) as kvc_compaction_round."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.prompt(layer, acc, k, v)
+            if fused:
+                self.prompt_fused(layer, acc, k, v)
+            else:
+                self.prompt(layer, acc, k, v)
         return g
 
     def capture_decode(self, layer, qs, out):
@@ -221,6 +236,18 @@ class GenerationPath(PromptPath):
         self.lens = [n + 1 for n in self.lens]
         self.T += self.w.batch
         self.max_seqlen += 1
+
+    def retier_fused(self, layer, acc):
+        """The same round as retier() through kvc_compaction_round (up to 1024 KV heads)."""
+        w = self.w
+        if self.ws_round is None:
+            self.ws_round = kvc.workspace(self.geom, kvc.OP_ROUND, self.seqlen_cap,
+                                          device=self.device)
+        prev = self.packed_state()
+        kvc.compaction_round(self.geom, layer, self.pool, acc, self.cu, self.T, self.max_seqlen,
+                             w.alpha_h, w.alpha_l, w.window, None, None, self.tier,
+                             self.new_count, self.ws_round, prev_tier=prev, changed=self.changed)
+        self.unpack_state(self.tier[:self.T])
 
     def retier(self, layer, acc):
         w = self.w

@@ -38,6 +38,10 @@ def test_version_and_workspace_sizes():
     assert kvc.workspace_bytes(g, kvc.OP_DECODE_ACC, -1) == 0
     assert kvc.workspace_bytes(g, kvc.OP_GENERATE) > kvc.workspace_bytes(g, kvc.OP_COMPACT)
     assert kvc.workspace_bytes(g, kvc.OP_PREFILL, 32768) >= 16 * 32768 * 64 * 8
+    # the fused round holds the quantize workspace, the allocation scan and the old rows
+    assert kvc.workspace_bytes(g, kvc.OP_ROUND, 32768) >= \
+        kvc.workspace_bytes(g, kvc.OP_QUANTIZE, 32768) + kvc.workspace_bytes(g, kvc.OP_COMPACT) + \
+        16 * 8 * 2049 * 4
     assert kvc.workspace_bytes(g, 99) == 0
     bad = kvc.make_geom(1, 16, 60, 8, 2049, 1 << 18)        # Hq % Hkv != 0
     assert kvc.workspace_bytes(bad, kvc.OP_COMPACT) == 0
@@ -139,3 +143,26 @@ def test_synchronous_errors_enqueue_nothing():
     assert lib.kvc_score_tokens(ctypes.byref(g), 16, 16, 10, 5, ctypes.c_float(1.0),
                                 ctypes.c_float(0.1), -1, None, 16, 16, None, None,
                                 None) == kvc.E_SHAPE
+
+
+def test_compaction_round_rejects_bad_arguments():
+    import ctypes as ct
+    from mixed_precision_paged_score_amd import kvc
+    lib = kvc._lib                     # with the argument types (int64 and size_t arguments)
+    f1 = ct.c_float(1.0)
+    g = kvc.make_geom(1, 4, 16, 4, 64, 1 << 12)
+    p = kvc.PoolPtrs(16, 16, 16, 16, 16, 16, 16)
+
+    def call(geom, acc=16, cu=16, k=16, v=16, prev=None, tier=16, cnt=16, chg=None, ws=256,
+             wsb=1 << 28, total=10, max_seqlen=5, window=4):
+        return lib.kvc_compaction_round(ct.byref(geom), 0, ct.byref(p), acc, cu, total,
+                                        max_seqlen, f1, f1, window, k, v, prev, tier, cnt, chg,
+                                        ws, wsb, None)
+    assert call(g, k=None) == kvc.E_NULL                 # prompt mode needs the rows
+    assert call(g, prev=16) == kvc.E_NULL                # re-tier mode needs changed
+    assert call(g, cnt=None) == kvc.E_NULL
+    assert call(g, acc=18) == kvc.E_ALIGN
+    assert call(g, window=-1) == kvc.E_SHAPE
+    assert call(g, wsb=8) == kvc.E_WORKSPACE
+    big = kvc.make_geom(1, 129, 64, 8, 64, 1 << 12)      # 1,032 KV heads
+    assert call(big) == kvc.E_SHAPE
