@@ -159,64 +159,35 @@ __global__ __launch_bounds__(256) void compact_commit_kernel(
 }
 
 // The planning launch of a fused round (kvc_compaction_round), one workgroup for up to
-// ROUND_MAX_HEADS heads, thread t taking heads 4t .. 4t + 3: each head's tier totals over its
-// request's tiles (new_count), the tiles' exclusive bases for the rank kernel, re-tiering its
-// changed flag, whether its pages are written (ok), its page demand; then the block scan of the
-// demands, the round's header, and ok[nheads] = 0 exactly when the round commits (the pool
-// status clear, no head overflowed or shrank, the total demand fits the free pages).
+// ROUND_MAX_HEADS heads, thread t taking heads 4t .. 4t + 3 (their totals are in new_count
+// and their changed flags set by round_head_kernel): each head's page demand, the block scan
+// of the demands, the round's header, and ok[nheads] = 0 exactly when the round commits (the
+// pool status clear, no head overflowed or shrank, the total demand fits the free pages).
 __global__ __launch_bounds__(256) void round_plan_kernel(
-    const int32_t *__restrict__ cu, int B, int Hkv, int ntq, int max_seqlen, int C,
-    const int32_t *__restrict__ tile_cnt, const int32_t *__restrict__ tile_cnt2,
-    const uint8_t *__restrict__ tile_chg, int32_t *__restrict__ tile_base,
-    int32_t *__restrict__ tile_base2, const int32_t *__restrict__ count_l,
-    int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok,
-    const int32_t *status, const uint64_t *ctr, CompactHdr *hdr, int32_t *__restrict__ off,
-    int32_t *__restrict__ foff) {
+    int nheads, int C, const int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed,
+    int32_t *__restrict__ ok, const int32_t *status, const uint64_t *ctr, CompactHdr *hdr,
+    int32_t *__restrict__ off, int32_t *__restrict__ foff) {
     __shared__ int s_wa[4], s_wf[4];
     __shared__ uint32_t s_err;
     if (threadIdx.x == 0) s_err = 0u;
     __syncthreads();
-    const int nheads = B * Hkv;
-    const bool retier = tile_cnt2 != nullptr;
     int da[4], df[4];
     int sa = 0, sf = 0;
+    uint32_t err = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = 4 * threadIdx.x + k;
         da[k] = df[k] = 0;
         if (i >= nheads) continue;
-        const int b = i / Hkv, h = i - b * Hkv;
-        const int N = cu[b + 1] - cu[b];
-        // a request longer than max_seqlen was skipped by the score launch (status set)
-        const int nt = (N < 0 || N > max_seqlen) ? 0 : (N + QTILE - 1) / QTILE;
-        int rH = 0, rL = 0, oH = 0, oL = 0, chg = 0;
-        for (int tq = 0; tq < nt; ++tq) {
-            const int64_t e = ((int64_t(b) * ntq + tq) * Hkv + h) * 2;
-            const int cH = tile_cnt[e], cL = tile_cnt[e + 1];
-            tile_base[e] = rH;
-            tile_base[e + 1] = rL;
-            rH += cH;
-            rL += cL;
-            if (retier) {
-                const int pH = tile_cnt2[e], pL = tile_cnt2[e + 1];
-                tile_base2[e] = oH;
-                tile_base2[e + 1] = oL;
-                oH += pH;
-                oL += pL;
-                chg |= tile_chg[e >> 1];
-            }
-        }
-        new_count[2 * i] = rH;
-        new_count[2 * i + 1] = rL;
-        if (retier) changed[i] = uint8_t(chg != 0);
-        ok[i] = retier ? int(chg != 0) : 1;
-        const HeadDemand d = head_demand(count_l, new_count, retier ? changed : nullptr, i, C);
-        if (d.err) atomicOr(&s_err, uint32_t(d.err));
+        const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
+        err |= uint32_t(d.err);
         da[k] = d.alloc;
         df[k] = d.free;
         sa += d.alloc;
         sf += d.free;
     }
+    if (err) atomicOr(&s_err, err);
     int a = sa, f = sf;
     block_scan2(a, f, s_wa, s_wf);       // inclusive over threads
     int ea = a - sa, ef = f - sf;        // exclusive: this thread's first head
@@ -232,15 +203,15 @@ __global__ __launch_bounds__(256) void round_plan_kernel(
     }
     __syncthreads();
     if (threadIdx.x == blockDim.x - 1) {
-        const uint32_t err = s_err;
+        const uint32_t e = s_err;
         const int32_t entry = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hdr->err = err;
+        hdr->err = e;
         hdr->total_alloc = a;
         hdr->total_free = f;
         hdr->head0 = ctr[0];
         hdr->tail0 = ctr[1];
         hdr->entry_status = entry;
-        const bool commits = entry == 0 && err == 0 && uint64_t(a) <= ctr[1] - ctr[0];
+        const bool commits = entry == 0 && e == 0 && uint64_t(a) <= ctr[1] - ctr[0];
         ok[nheads] = commits ? 0 : 1;
     }
 }
@@ -251,17 +222,14 @@ using namespace kvc;
 
 namespace kvc {
 
-int launch_round_plan(const kvc_geom *g, const int32_t *cu, int max_seqlen, int ntq,
-                      const int32_t *tile_cnt, const int32_t *tile_cnt2, const uint8_t *tile_chg,
-                      int32_t *tile_base, int32_t *tile_base2, const int32_t *count_l,
-                      int32_t *new_count, uint8_t *changed, int32_t *ok, const kvc_pool *p,
-                      void *compact_ws, hipStream_t s) {
+int launch_round_plan(const kvc_geom *g, const int32_t *count_l, const int32_t *new_count,
+                      const uint8_t *changed, int32_t *ok, const kvc_pool *p, void *compact_ws,
+                      hipStream_t s) {
     const CompactWs L(g);
     char *w = static_cast<char *>(compact_ws);
-    hipLaunchKernelGGL(round_plan_kernel, dim3(1), dim3(256), 0, s, cu, g->batch,
-                       g->num_kv_heads, ntq, max_seqlen, g->row_capacity, tile_cnt, tile_cnt2,
-                       tile_chg, tile_base, tile_base2, count_l, new_count, changed, ok,
-                       p->dev_status, p->ring_ctr, reinterpret_cast<CompactHdr *>(w + L.hdr),
+    hipLaunchKernelGGL(round_plan_kernel, dim3(1), dim3(256), 0, s, L.nheads, g->row_capacity,
+                       count_l, new_count, changed, ok, p->dev_status, p->ring_ctr,
+                       reinterpret_cast<CompactHdr *>(w + L.hdr),
                        reinterpret_cast<int32_t *>(w + L.off),
                        reinterpret_cast<int32_t *>(w + L.foff));
     return launch_check("kvc_compaction_round/plan");

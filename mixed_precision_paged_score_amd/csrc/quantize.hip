@@ -131,6 +131,42 @@ __global__ __launch_bounds__(256) void quant_scan_kernel(
     }
 }
 
+// The per-head launch of a fused round: grid (Hkv, B).  The head's tier totals over its
+// request's tiles (new_count, the round's counts), the tiles' exclusive bases for the rank
+// kernel, for the previous tiers too when re-tiering (with the changed flag: some tile dropped
+// a tier), and ok[i] = the head's pages are written (every head in prompt mode, a changed one
+// when re-tiering; the planning launch clears the round's ok[nheads] when it does not commit).
+__global__ __launch_bounds__(256) void round_head_kernel(
+    const int32_t *__restrict__ tile_cnt, const int32_t *__restrict__ tile_cnt2,
+    const uint8_t *__restrict__ tile_chg, const int32_t *__restrict__ cu, int Hkv, int ntq,
+    int max_seqlen, int32_t *__restrict__ tile_base, int32_t *__restrict__ tile_base2,
+    int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok) {
+    __shared__ int s_sum[2][128];
+    __shared__ int s_tot[2], s_tot2[2];
+    __shared__ int s_chg;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int i = b * Hkv + h;
+    const bool retier = tile_cnt2 != nullptr;
+    const int N = cu[b + 1] - cu[b];
+    // a request longer than max_seqlen was skipped by the score launch (its status bit set)
+    const int nt = (N < 0 || N > max_seqlen) ? 0 : (N + QTILE - 1) / QTILE;
+    if (threadIdx.x == 0) s_chg = 0;
+    const int64_t col0 = (int64_t(b) * ntq) * Hkv * 2 + h * 2;
+    scan_columns(tile_cnt, tile_base, col0, Hkv, nt, s_sum, s_tot);
+    if (retier) {
+        scan_columns(tile_cnt2, tile_base2, col0, Hkv, nt, s_sum, s_tot2);
+        for (int tq = threadIdx.x; tq < nt; tq += blockDim.x)
+            if (tile_chg[(int64_t(b) * ntq + tq) * Hkv + h]) s_chg = 1;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        new_count[2 * i] = s_tot[0];
+        new_count[2 * i + 1] = s_tot[1];
+        if (retier) changed[i] = uint8_t(s_chg);
+        ok[i] = retier ? s_chg : 1;
+    }
+}
+
 // grid (ntq, B), 4 waves: wave w ranks heads w, w+4, ... over the tile's tokens with 64-lane
 // ballots.  poslist: HIGH ranks from the front, LOW ranks from the back (positions).
 // Re-tiering: srcdesc at the same index as poslist tells the page writer where a kept token's
@@ -799,10 +835,10 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
 }
 
 // ---- the fused compaction round -------------------------------------------------------------
-// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in five launches for up to
+// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in six launches for up to
 // ROUND_MAX_HEADS heads: score with per-tile counts (no counters to clear, no separate count
-// launch), one planning workgroup (totals, tile bases, page demands, the allocation scan), the
-// commit, the ranks and the page writer.
+// launch), the per-head tile scans (totals, rank bases), one planning workgroup (page demands,
+// the allocation scan, the commit decision), the commit, the ranks and the page writer.
 extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                                     const float *acc, const int32_t *cu, int64_t total_tokens,
                                     int32_t max_seqlen, float alpha_h, float alpha_l,
@@ -847,8 +883,12 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
     rc = launch_round_score(g, acc, cu, max_seqlen, alpha_h, alpha_l, window, prev_tier, tier,
                             tile_cnt, tile_cnt2, tile_chg, p->dev_status, s);
     if (rc) return rc;
-    rc = launch_round_plan(g, cu, max_seqlen, L.ntq, tile_cnt, tile_cnt2, tile_chg, tile_base,
-                           tile_base2, count_l, new_count, retier ? changed : nullptr, ok, p,
+    hipLaunchKernelGGL(round_head_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, tile_cnt2,
+                       tile_chg, cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, new_count,
+                       retier ? changed : nullptr, ok);
+    rc = launch_check("kvc_compaction_round/heads");
+    if (rc) return rc;
+    rc = launch_round_plan(g, count_l, new_count, retier ? changed : nullptr, ok, p,
                            w + R.compact, s);
     if (rc) return rc;
     rc = launch_commit(g, layer, p, new_count, retier ? changed : nullptr, old_rows, old_count,
