@@ -775,47 +775,72 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
     float *arow = acc + (int64_t(lo) + t0) * Hq;
     const int nw = nr * Hq;
     if ((Hq & 3) == 0) {
-        const int q4 = Hq >> 2;
-        for (int k = threadIdx.x; k < nw / 4; k += 256) {
-            const int r = k / q4, c4 = k - r * q4;
-            const float4 x = reinterpret_cast<const float4 *>(arow)[k];
-            float *d = s_acc + r * ldr + 4 * c4;
-            d[0] = x.x;
-            d[1] = x.y;
-            d[2] = x.z;
-            d[3] = x.w;
+        // the chunk's rows: every thread's loads are issued before the first LDS write
+        constexpr int SU = 4;
+        const int q4 = Hq >> 2, n4 = nw / 4;
+        for (int k0 = threadIdx.x; k0 < n4; k0 += SU * 256) {
+            float4 x[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int k = k0 + u * 256;
+                if (k < n4) x[u] = reinterpret_cast<const float4 *>(arow)[k];
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int k = k0 + u * 256;
+                if (k < n4) {
+                    const int r = k / q4, c4 = k - r * q4;
+                    float *d = s_acc + r * ldr + 4 * c4;
+                    d[0] = x[u].x;
+                    d[1] = x[u].y;
+                    d[2] = x[u].z;
+                    d[3] = x[u].w;
+                }
+            }
         }
     } else {
         for (int k = threadIdx.x; k < nw; k += 256) s_acc[(k / Hq) * ldr + k % Hq] = arow[k];
     }
     for (int k = threadIdx.x; k < 2 * Hq; k += 256) s_ml[k] = mls[int64_t(b) * 2 * Hq + k];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // per job: its slot, position and logits, loaded before the barrier so that the loads
-    // of all of a wave's jobs are in flight together
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loads
+    // per job: its slot, position and logits.  All of a pass's jobs' counts and chunk bounds
+    // (scalar loads) are requested together, then all of their lanes' records (a lane past
+    // its range reads a record of the head's first tile and drops it), so a pass waits for
+    // two round trips, and the first pass's before the barrier
     constexpr int JMAX = 4;                          // jobs per wave per pass (Hkv <= 8)
     for (int j0 = 0; j0 < 2 * Hkv; j0 += 4 * JMAX) {
+        int nh_j[JMAX], n_j[JMAX], st0[JMAX], st1[JMAX];
+#pragma unroll
+        for (int u = 0; u < JMAX; ++u) {
+            const int seg = min(j0 + wave + 4 * u, 2 * Hkv - 1);
+            const bool high = (seg & 1) == 0;
+            const int i = b * Hkv + (seg >> 1);
+            nh_j[u] = count_l[2 * i];
+            n_j[u] = count_l[2 * i + 1];
+            const int32_t *st = idx + (int64_t(i) * 2 + (high ? 0 : 1)) * nch_cap;
+            st0[u] = st[c];
+            st1[u] = st[c + 1];
+        }
         int pj[JMAX], hj[JMAX];
         int64_t lj[JMAX];                            // the slot's logits: lg + lj
         float l[JMAX][GT > 0 ? GT : 1];
 #pragma unroll
         for (int u = 0; u < JMAX; ++u) {
             const int seg = j0 + wave + 4 * u;
-            pj[u] = -1;
             hj[u] = seg >> 1;
-            if (seg >= 2 * Hkv) continue;
             const bool high = (seg & 1) == 0;
-            const int i = b * Hkv + hj[u];
-            const int nh = count_l[2 * i], n = high ? nh : count_l[2 * i + 1];
-            const int32_t *st = idx + (int64_t(i) * 2 + (high ? 0 : 1)) * nch_cap;
-            const int s0 = min(max(st[c], 0), n), s1 = min(max(st[c + 1], s0), n);
+            const int i = b * Hkv + (min(seg, 2 * Hkv - 1) >> 1);
+            const int nh = nh_j[u], n = high ? nh : n_j[u];
+            const int s0 = min(max(st0[u], 0), n), s1 = min(max(st1[u], s0), n);
             const int sl = s0 + lane;
-            if (sl >= s1) continue;
             const int tile = (high ? 0 : ceil_div(nh, HS)) + (sl >> 4);
-            if (tile >= tiles_cap) continue;
-            const int64_t rb = (int64_t(i) * tiles_cap + tile) * (16 * (G + 1));
-            pj[u] = reinterpret_cast<const int32_t *>(lg)[rb + (sl & 15)];
+            const bool live = seg < 2 * Hkv && sl < s1 && tile < tiles_cap;
+            const int64_t rb = (int64_t(i) * tiles_cap + (live ? tile : 0)) * (16 * (G + 1));
+            const int32_t pos = reinterpret_cast<const int32_t *>(lg)[rb + (sl & 15)];
             lj[u] = rb + 16 + (sl & 15);
             if constexpr (GT > 0) load_logits<GT>(lg + lj[u], l[u]);
+            pj[u] = live ? pos : -1;
         }
         if (j0 == 0) __syncthreads();                // the rows and (M, L) are in LDS
 #pragma unroll

@@ -232,23 +232,23 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
 
 constexpr int QP_WAVES = 4;
 #ifndef KVC_RB_AHEAD
-#define KVC_RB_AHEAD 2
+#define KVC_RB_AHEAD 1
 #endif
-// re-tier passes whose old words are in flight ahead of the pass being written: at 2 the
-// kernel holds 80 VGPRs (6 waves per SIMD); 1 and 3 measured slower on the chain-of-thought
-// re-tier round (325 and 324 us against 308)
+// re-tier passes whose old words are in flight ahead of the pass being written: at 1 the
+// kernel holds 77 VGPRs (6 waves per SIMD); 2 and 3 measured slower on the chain-of-thought
+// re-tier round (284 us against 278) once every slot's source record is requested at once
 constexpr int RB_AHEAD = KVC_RB_AHEAD;
 constexpr int VST_BYTES = LS * D;     // per-wave staging of value codes (LOW page size)
 
 // prompt placement of one page: NP passes of 4 slots (one 16-lane group per slot).  The
 // slots' positions are all loaded first, so each pass waits for one round trip (its K/V
 // rows, 16 bytes of each per lane) instead of two.
-template <int NP, typename Emit>
+template <int NP, typename Page, typename Emit>
 __device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
                                             const uint16_t *__restrict__ V,
                                             const int32_t *__restrict__ pl, int lo, int Hkv, int h,
                                             int max_seqlen, int first, int m, bool high, int rg,
-                                            int c, Emit &emit) {
+                                            int c, Page &load_page, Emit &emit) {
     int pos[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -256,6 +256,7 @@ __device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
         pos[p] = 0;
         if (s < m) pos[p] = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
     }
+    load_page();
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const bool live = 4 * p + rg < m;
@@ -283,30 +284,34 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = blockIdx.y;
     const int nheads = gridDim.y;
-    if (ok[nheads] != 0 || !ok[i]) return;     // pool failed earlier, head mismatched or kept
-    const int b = i / Hkv, h = i - b * Hkv;
+    // the flags and the head's counts are requested together (no branch between them)
+    const int ok_all = ok[nheads], ok_i = ok[i];
     const int nh = count_l[2 * i], nl = count_l[2 * i + 1];
+    asm volatile("" ::"s"(nh), "s"(nl));   // (keeps the counts' loads above the branch)
+    if (ok_all != 0 || !ok_i) return;     // pool failed earlier, head mismatched or kept
+    const int b = i / Hkv, h = i - b * Hkv;
     const int qH = ceil_div(nh, HS), qL = ceil_div(nl, LS);
     const int pi = blockIdx.x * QP_WAVES + wave;
-    bool high;
-    int first, m, page;
-    if (pi < qH) {
-        high = true;
-        first = pi * HS;
-        m = min(HS, nh - first);
-        page = rows_l[int64_t(i) * C + pi];
-    } else if (pi - qH < qL) {
-        high = false;
-        const int lp = pi - qH;
-        first = lp * LS;
-        m = min(LS, nl - first);
-        page = rows_l[int64_t(i) * C + C - 1 - lp];
-    } else {
-        return;
-    }
+    if (pi >= qH + qL) return;
+    // HIGH page pi of the head's row, or LOW page lp = pi - qH (taken from the row's end);
+    // no branch around the page id's load, so it is in flight with the slots' first loads
+    const bool high = pi < qH;
+    const int lp = high ? pi : pi - qH;
+    const int first = lp * (high ? HS : LS);
+    const int m = min(high ? HS : LS, (high ? nh : nl) - first);
+    const int64_t row_at = int64_t(i) * C + (high ? pi : C - 1 - lp);
     const int T = high ? HIGH : LOW;
-    uint8_t *pg = pages + int64_t(page) * PAGE;
+    // the page id is loaded after each path's first per-slot loads (positions or source
+    // records), so that no wait for it stands before them
+    uint8_t *pg = nullptr;
+    int32_t pos_end = -1;     // position of slot `lane` (lanes < LS), for the final store
     const int32_t *pl = poslist + int64_t(i) * max_seqlen;
+    auto load_page = [&]() {
+        asm volatile("" ::: "memory");
+        pg = pages + int64_t(rows_l[row_at]) * PAGE;
+        const int sl = min(lane, m - 1);
+        pos_end = pl[high ? first + sl : max_seqlen - 1 - (first + sl)];
+    };
     const int lo = cu[b];
     const int rg = lane >> 4, c = lane & 15;
     uint8_t *sv = s_v[wave];
@@ -335,8 +340,8 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
     };
     if constexpr (!REBUILD) {
         // every row of the page is requested before the first one is quantized
-        if (high) fresh_slots<HS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, true, rg, c, emit_fresh);
-        else fresh_slots<LS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, false, rg, c, emit_fresh);
+        if (high) fresh_slots<HS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, true, rg, c, load_page, emit_fresh);
+        else fresh_slots<LS / 4>(K, V, pl, lo, Hkv, h, max_seqlen, first, m, false, rg, c, load_page, emit_fresh);
     } else {
     // re-tier placement.  Every slot's position and source (previous tier, old page id, old
     // slot) are loaded for all of the page's passes first; then each pass reads its old codes
@@ -346,16 +351,19 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         // (a FRESH slot's position, needed only for its fp16 rows, is loaded when used)
         int sy[NP], opg[NP];     // sy: previous tier << 8 | old slot
         auto index_of = [&](int s) -> int64_t { return high ? first + s : max_seqlen - 1 - (first + s); };
+        // every pass's record is requested before any is used: a slot past the page's tokens
+        // reads the page's last token's record (in the list, no branch around the load) and
+        // then counts as empty
+        uint2 d[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            d[p] = srcdesc[int64_t(i) * max_seqlen + index_of(min(4 * p + rg, m - 1))];
+        load_page();
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int s = 4 * p + rg;
-            sy[p] = int(FRESH) << 8;
-            opg[p] = 0;
-            if (s < m) {
-                const uint2 d = srcdesc[int64_t(i) * max_seqlen + index_of(s)];
-                opg[p] = int(d.x);
-                sy[p] = int(d.y);
-            }
+            const bool in = 4 * p + rg < m;
+            opg[p] = in ? int(d[p].x) : 0;
+            sy[p] = in ? int(d[p].y) : int(FRESH) << 8;
         }
         auto src_of = [&](int p) { return sy[p] >> 8; };
         // a pass's slot validity and, for a slot read from an old page, its old-page words:
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(256) void quant_pages_kernel(
         if (s < m) {
             a = uint32_t(s_par[wave][s][0]) | (uint32_t(s_par[wave][s][1]) << 16);
             bb = uint32_t(s_par[wave][s][2]) | (uint32_t(s_par[wave][s][3]) << 16);
-            pos = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
+            pos = pos_end;
         }
         st_page8(pg + PARAM_OFF + 8 * s, a, bb);
         st_page4(pg + POS_OFF + 4 * s, uint32_t(pos));
