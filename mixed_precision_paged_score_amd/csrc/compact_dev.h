@@ -75,29 +75,65 @@ __device__ __forceinline__ bool commit_head(
     int32_t *__restrict__ owner, const CompactHdr *hdr, const int32_t *__restrict__ off,
     const int32_t *__restrict__ foff, int32_t *__restrict__ old_rows,
     int32_t *__restrict__ old_count) {
-    if (hdr->entry_status != 0) return false;          // sticky failure: no-op
-    int32_t *row = rows_l + int64_t(i) * C;
-    if (old_rows)
-        for (int p = threadIdx.x; p < C; p += blockDim.x) old_rows[int64_t(i) * C + p] = row[p];
-    if (old_count && threadIdx.x < 2) old_count[2 * i + threadIdx.x] = count_l[2 * i + threadIdx.x];
+    // every input of the head's commit is requested at once: the round's header, the head's
+    // old and new counts and changed flag, and its offsets into the round's regions
+    const int32_t entry = hdr->entry_status;
     const uint64_t head0 = hdr->head0, tail0 = hdr->tail0;
-    uint32_t err = hdr->err;
-    if (uint64_t(hdr->total_alloc) > tail0 - head0) err |= KVC_DEV_POOL_EXHAUSTED;
+    const uint32_t herr = hdr->err;
+    const int64_t total_alloc = hdr->total_alloc, total_free = hdr->total_free;
+    const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
+    const int oi = off[i], fi = foff[i];
+    asm volatile("" ::"s"(entry), "s"(d.alloc), "s"(d.free), "s"(oi), "s"(fi));
+    if (entry != 0) return false;                      // sticky failure: no-op
+    int32_t *row = rows_l + int64_t(i) * C;
+    constexpr int U = 4;                               // loads in flight per thread
+    if (old_rows) {
+        for (int p0 = threadIdx.x; p0 < C; p0 += U * blockDim.x) {
+            int v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * blockDim.x;
+                v[u] = p < C ? row[p] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * blockDim.x;
+                if (p < C) old_rows[int64_t(i) * C + p] = v[u];
+            }
+        }
+    }
+    if (old_count && threadIdx.x < 2) old_count[2 * i + threadIdx.x] = count_l[2 * i + threadIdx.x];
+    uint32_t err = herr;
+    if (uint64_t(total_alloc) > tail0 - head0) err |= KVC_DEV_POOL_EXHAUSTED;
     if (err) {
         if (i == 0 && threadIdx.x == 0) atomicOr(status, int(err));
         return false;
     }
-    const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
     __syncthreads();   // every thread has read the old counts and row before they change
     const int gid = layer_gid0 + i;
+    // ring index base + k modulo P for base < 2P, k < P
+    auto wrap = [&](int64_t j) {
+        j -= j >= P ? P : 0;
+        return j >= P ? j - P : j;
+    };
     if (d.rebuilt) {
         // return the old pages to the ring's tail: HIGH in row order, then LOW from the end
-        const int64_t base = int64_t(tail0 % uint64_t(P)) + foff[i];
-        for (int k = threadIdx.x; k < d.free; k += blockDim.x) {
-            const int p = k < d.pH ? k : C - 1 - (k - d.pH);
-            const int page = row[p];
-            ring[(base + k) % P] = page;
-            owner[page] = -1;
+        const int64_t base = int64_t(tail0 % uint64_t(P)) + fi;
+        for (int k0 = threadIdx.x; k0 < d.free; k0 += U * blockDim.x) {
+            int page[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * blockDim.x;
+                page[u] = k < d.free ? row[k < d.pH ? k : C - 1 - (k - d.pH)] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * blockDim.x;
+                if (k < d.free) {
+                    ring[wrap(base + k)] = page[u];
+                    owner[page[u]] = -1;
+                }
+            }
         }
         __syncthreads();
         for (int p = threadIdx.x; p < C; p += blockDim.x) row[p] = -1;
@@ -106,17 +142,28 @@ __device__ __forceinline__ bool commit_head(
     const int h0 = d.rebuilt ? 0 : d.pH;       // first new HIGH row position
     const int l0 = d.rebuilt ? 0 : d.pL;       // first new LOW page index (from the right)
     const int nH = d.qH - h0;
-    const int64_t abase = int64_t(head0 % uint64_t(P)) + off[i];
-    for (int k = threadIdx.x; k < d.alloc; k += blockDim.x) {
-        const int page = ring[(abase + k) % P];
-        const int p = k < nH ? h0 + k : C - 1 - (l0 + (k - nH));
-        row[p] = page;
-        owner[page] = gid * C + p;
+    const int64_t abase = int64_t(head0 % uint64_t(P)) + oi;
+    for (int k0 = threadIdx.x; k0 < d.alloc; k0 += U * blockDim.x) {
+        int page[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + u * blockDim.x;
+            page[u] = k < d.alloc ? ring[wrap(abase + k)] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + u * blockDim.x;
+            if (k < d.alloc) {
+                const int p = k < nH ? h0 + k : C - 1 - (l0 + (k - nH));
+                row[p] = page[u];
+                owner[page[u]] = gid * C + p;
+            }
+        }
     }
     if (threadIdx.x < 2) count_l[2 * i + threadIdx.x] = new_count[2 * i + threadIdx.x];
     if (i == 0 && threadIdx.x == 0) {
-        ctr[0] = head0 + uint64_t(hdr->total_alloc);
-        ctr[1] = tail0 + uint64_t(hdr->total_free);
+        ctr[0] = head0 + uint64_t(total_alloc);
+        ctr[1] = tail0 + uint64_t(total_free);
     }
     return true;
 }

@@ -182,49 +182,93 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
     const int lo = cu[b], N = cu[b + 1] - lo;
     const int t0 = tq * QTILE;
     if (N > max_seqlen || t0 >= N) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loads
     const int nt = min(QTILE, N - t0);
     const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-    for (int h = wave; h < Hkv; h += 4) {
-        const int i = b * Hkv + h;
-        if (!ok[i]) continue;
-        const int64_t tb = ((int64_t(b) * ntq + tq) * Hkv + h) * 2;
-        int rH = tile_base[tb], rL = tile_base[tb + 1];
-        int oH = prev ? tile_base2[tb] : 0, oL = prev ? tile_base2[tb + 1] : 0;
-        int32_t *pl = poslist + int64_t(i) * max_seqlen;
-        uint2 *sd = prev ? srcdesc + int64_t(i) * max_seqlen : nullptr;
-        const int32_t *orow = prev ? old_rows + int64_t(i) * C : nullptr;
-        for (int c0 = 0; c0 < nt; c0 += 64) {
-            const int tt = c0 + lane;
-            const int64_t r = (int64_t(lo) + t0 + tt) * Hkv + h;
-            const int x = tt < nt ? tier[r] : PRUNE;
-            const uint64_t mH = __ballot(x == HIGH);
-            const uint64_t mL = __ballot(x == LOW);
-            int k = -1;                                  // the token's index in poslist
-            if (x == HIGH) k = rH + __popcll(mH & lt);
-            else if (x == LOW) k = max_seqlen - 1 - (rL + __popcll(mL & lt));
-            if (k >= 0) pl[k] = t0 + tt;
-            rH += __popcll(mH);
-            rL += __popcll(mL);
-            if (prev) {
-                const int y = tt < nt ? prev[r] : PRUNE;
-                const uint64_t nH = __ballot(y == HIGH);
-                const uint64_t nL = __ballot(y == LOW);
-                // the old rank is below the head's old count (checked by quant_scan), so the
-                // old page index stays within the head's old row
-                int page = 0, osl = 0;
-                if (y == HIGH) {
-                    const int o = oH + __popcll(nH & lt);
-                    osl = o & (HS - 1);
-                    if (k >= 0) page = orow[o / HS];
-                } else if (y == LOW) {
-                    const int o = oL + __popcll(nL & lt);
-                    osl = o & (LS - 1);
-                    if (k >= 0) page = orow[C - 1 - o / LS];
+    constexpr int NC = QTILE / 64;          // 64-token chunks of a tile
+    constexpr int HW = 2;                   // heads per wave per pass
+    for (int h0 = wave; h0 < Hkv; h0 += 4 * HW) {
+        // every load of the pass's heads is requested before any is used: the heads' flags
+        // and rank bases (scalar), the tier bytes of every chunk (a lane past the tile reads
+        // its last token and counts as PRUNE)
+        int okh[HW], bH[HW], bL[HW], b2H[HW], b2L[HW];
+        int xs[HW][NC], ys[HW][NC];
+#pragma unroll
+        for (int j = 0; j < HW; ++j) {
+            const int h = min(h0 + 4 * j, Hkv - 1);
+            const int i = b * Hkv + h;
+            okh[j] = ok[i];
+            const int64_t tb = ((int64_t(b) * ntq + tq) * Hkv + h) * 2;
+            bH[j] = tile_base[tb];
+            bL[j] = tile_base[tb + 1];
+            b2H[j] = prev ? tile_base2[tb] : 0;
+            b2L[j] = prev ? tile_base2[tb + 1] : 0;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const int64_t r = (int64_t(lo) + t0 + min(64 * q + lane, nt - 1)) * Hkv + h;
+                xs[j][q] = tier[r];
+                ys[j][q] = prev ? prev[r] : int(PRUNE);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < HW; ++j) {
+            const int h = h0 + 4 * j;
+            if (h >= Hkv || !okh[j]) continue;
+            const int i = b * Hkv + h;
+            int rH = bH[j], rL = bL[j], oH = b2H[j], oL = b2L[j];
+            int32_t *pl = poslist + int64_t(i) * max_seqlen;
+            uint2 *sd = prev ? srcdesc + int64_t(i) * max_seqlen : nullptr;
+            const int32_t *orow = prev ? old_rows + int64_t(i) * C : nullptr;
+            // re-tier: each chunk's record (index in the head's list, old row entry, tag), the
+            // old page ids then loaded together
+            int sk[NC], so[NC];
+            uint32_t stag[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) sk[q] = -1;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const int tt = 64 * q + lane;
+                if (64 * q >= nt) break;
+                const int x = tt < nt ? xs[j][q] : int(PRUNE);
+                const uint64_t mH = __ballot(x == HIGH);
+                const uint64_t mL = __ballot(x == LOW);
+                int k = -1;                                  // the token's index in poslist
+                if (x == HIGH) k = rH + __popcll(mH & lt);
+                else if (x == LOW) k = max_seqlen - 1 - (rL + __popcll(mL & lt));
+                if (k >= 0) pl[k] = t0 + tt;
+                rH += __popcll(mH);
+                rL += __popcll(mL);
+                if (prev) {
+                    const int y = tt < nt ? ys[j][q] : int(PRUNE);
+                    const uint64_t nH = __ballot(y == HIGH);
+                    const uint64_t nL = __ballot(y == LOW);
+                    // the old rank is below the head's old count (checked by the scan), so
+                    // the old page index stays within the head's old row
+                    int orw = -1, osl = 0;
+                    if (y == HIGH) {
+                        const int o = oH + __popcll(nH & lt);
+                        osl = o & (HS - 1);
+                        orw = o / HS;
+                    } else if (y == LOW) {
+                        const int o = oL + __popcll(nL & lt);
+                        osl = o & (LS - 1);
+                        orw = C - 1 - o / LS;
+                    }
+                    sk[q] = k;
+                    so[q] = orw;
+                    stag[q] = uint32_t((y << 8) | osl);
+                    oH += __popcll(nH);
+                    oL += __popcll(nL);
                 }
-                if (k >= 0) sd[k] = make_uint2(uint32_t(page), uint32_t((y << 8) | osl));
-                oH += __popcll(nH);
-                oL += __popcll(nL);
+            }
+            if (prev) {
+                int pg[NC];
+#pragma unroll
+                for (int q = 0; q < NC; ++q) pg[q] = (sk[q] >= 0 && so[q] >= 0) ? orow[so[q]] : 0;
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    if (sk[q] >= 0) sd[sk[q]] = make_uint2(uint32_t(pg[q]), stag[q]);
             }
         }
     }
