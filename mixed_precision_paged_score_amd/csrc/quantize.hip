@@ -285,8 +285,8 @@ constexpr int RB_AHEAD = KVC_RB_AHEAD;
 constexpr int VST_BYTES = LS * D;     // per-wave staging of value codes (LOW page size)
 
 // prompt placement of one page: NP passes of 4 slots (one 16-lane group per slot).  The
-// slots' positions are all loaded first, so each pass waits for one round trip (its K/V
-// rows, 16 bytes of each per lane) instead of two.
+// slots' positions are all loaded first, and each pass's K/V rows (16 bytes of each per lane)
+// are requested while the pass before is quantized.
 template <int NP, typename Page, typename Emit>
 __device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
                                             const uint16_t *__restrict__ V,
@@ -301,13 +301,28 @@ __device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
         if (s < m) pos[p] = high ? pl[first + s] : pl[max_seqlen - 1 - (first + s)];
     }
     load_page();
+    // the rows of pass p + 1 are requested before pass p is quantized (a slot past the page's
+    // tokens reads the rows of position 0, unconditionally, and is written as zeros)
+    typedef unsigned int fs_u4 __attribute__((ext_vector_type(4)));
+    fs_u4 rk[NP], rv[NP];
+    auto issue = [&](int p) {
+        const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
+        rk[p] = __builtin_nontemporal_load(reinterpret_cast<const fs_u4 *>(K + roff));
+        rv[p] = __builtin_nontemporal_load(reinterpret_cast<const fs_u4 *>(V + roff));
+    };
+    issue(0);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
+        if (p + 1 < NP) issue(p + 1);
         const bool live = 4 * p + rg < m;
-        const int64_t roff = ((int64_t(lo) + pos[p]) * Hkv + h) * D + 8 * c;
         float xk[8], xv[8];
-        load_row8(K + roff, live, xk);
-        load_row8(V + roff, live, xv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xk[2 * e] = h2f(uint16_t(rk[p][e] & 0xffffu));
+            xk[2 * e + 1] = h2f(uint16_t(rk[p][e] >> 16));
+            xv[2 * e] = h2f(uint16_t(rv[p][e] & 0xffffu));
+            xv[2 * e + 1] = h2f(uint16_t(rv[p][e] >> 16));
+        }
         emit(4 * p + rg, live, xk, xv);
     }
 }
