@@ -195,6 +195,13 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     const int base = leaves ? (rc & ~(HS - 1)) : (nh0 & ~(HS - 1));
     const int ns = end - base;                       // slots rewritten, <= window + 16
     const int ns16 = (ns + HS - 1) & ~(HS - 1);
+    // the head's row entries for the HIGH pages the step reads and writes (pages base / 16 ..),
+    // loaded once, so that no pass of the gather waits for a page id
+    __shared__ int32_t s_row[GEN_TAIL / HS + 2];
+    const int pg0 = base >> 4;
+    const int npg = max((end - 1) >> 4, (nh0 - 1) >> 4) - pg0 + 1;
+    for (int k = threadIdx.x; k < npg; k += blockDim.x) s_row[k] = row[pg0 + k];
+    __syncthreads();
     // ---- gather: 16 lanes per slot, 16 slots per pass -----------------------------------
     for (int d0 = 0; d0 < ns16; d0 += 16) {
         const int dd = d0 + 4 * wave + rg;           // destination slot, relative to base
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
         } else {
             // an existing token: its old rank skips the leaving token
             const int src = (leaves && da >= rc) ? da + 1 : da;
-            const uint8_t *pg = pages + int64_t(row[src >> 4]) * PAGE;
+            const uint8_t *pg = pages + int64_t(s_row[(src >> 4) - pg0]) * PAGE;
             uint32_t kc[8], vc[8], kp, vp;
             if (sch) {
                 sch_key_codes(pg, kh, src & (HS - 1), c, kc);
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     if (leaves && wave == 0 && rg == 0) {
         // the leaving token (its position was checked by gen_decide): LOW re-quantizes the
         // fp16 rounding of its K8V4 reconstruction
-        const uint8_t *pg = pages + int64_t(row[rc >> 4]) * PAGE;
+        const uint8_t *pg = pages + int64_t(s_row[(rc >> 4) - pg0]) * PAGE;
         const int so = rc & (HS - 1);
         if (d == LOW) {
             uint32_t kc[8], vc[8], kp, vp;
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(256) void gen_place_kernel(
     // ---- HIGH tail pages, written whole: wave w takes pages base/16 + w, + 4, ... ----------
     const int p_last = (end - 1) >> 4;
     for (int p = (base >> 4) + wave; p <= p_last; p += 4) {
-        uint8_t *pg = pages + int64_t(row[p]) * PAGE;
+        uint8_t *pg = pages + int64_t(s_row[p - pg0]) * PAGE;
         const int s0 = HS * p - base;
         const int live = min(HS, end - HS * p);
         if (sch) {
