@@ -158,62 +158,71 @@ __global__ __launch_bounds__(256) void compact_commit_kernel(
                 ring, owner, hdr, off, foff, old_rows, old_count);
 }
 
-// The planning launch of a fused round (kvc_compaction_round), one workgroup for up to
-// ROUND_MAX_HEADS heads, thread t taking heads 4t .. 4t + 3 (their totals are in new_count
-// and their changed flags set by round_head_kernel): each head's page demand, the block scan
-// of the demands, the round's header, and ok[nheads] = 0 exactly when the round commits (the
-// pool status clear, no head overflowed or shrank, the total demand fits the free pages).
-__global__ __launch_bounds__(256) void round_plan_kernel(
-    int nheads, int C, const int32_t *__restrict__ count_l,
-    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed,
-    int32_t *__restrict__ ok, const int32_t *status, const uint64_t *ctr, CompactHdr *hdr,
-    int32_t *__restrict__ off, int32_t *__restrict__ foff) {
-    __shared__ int s_wa[4], s_wf[4];
-    __shared__ uint32_t s_err;
-    if (threadIdx.x == 0) s_err = 0u;
-    __syncthreads();
-    int da[4], df[4];
-    int sa = 0, sf = 0;
+// The planning and the commits of a fused round (kvc_compaction_round) in one launch, one
+// workgroup per head: every workgroup sums all heads' demands itself (thread t takes heads
+// 4t .. 4t + 3, as the planning workgroup did) for the round's totals, error bits and its
+// own head's offsets, so no planning launch stands between the per-head scans and the
+// commits.  The pool status and ring counters at the round's start come from *snap, taken by
+// the per-head scan launch: no workgroup here reads them after another may have moved them.
+// Workgroup 0 records in ok[nheads] whether the round commits (0) or not (1).
+__global__ __launch_bounds__(256) void round_commit_kernel(
+    int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C,
+    int64_t P, int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
+    int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
+    int32_t *__restrict__ old_rows, int32_t *__restrict__ old_count) {
+    __shared__ int s_r[4][4];
+    __shared__ uint32_t s_err[4];
+    const int i = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t entry = snap->entry_status;
+    const uint64_t head0 = snap->head0, tail0 = snap->tail0;
+    const HeadDemand mine = head_demand(count_l, new_count, changed, i, C);
+    int ta = 0, tf = 0, pa = 0, pf = 0;
     uint32_t err = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int i = 4 * threadIdx.x + k;
-        da[k] = df[k] = 0;
-        if (i >= nheads) continue;
-        const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
+        const int j = 4 * threadIdx.x + k;
+        if (j >= nheads) continue;
+        const HeadDemand d = head_demand(count_l, new_count, changed, j, C);
         err |= uint32_t(d.err);
-        da[k] = d.alloc;
-        df[k] = d.free;
-        sa += d.alloc;
-        sf += d.free;
-    }
-    if (err) atomicOr(&s_err, err);
-    int a = sa, f = sf;
-    block_scan2(a, f, s_wa, s_wf);       // inclusive over threads
-    int ea = a - sa, ef = f - sf;        // exclusive: this thread's first head
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int i = 4 * threadIdx.x + k;
-        if (i < nheads) {
-            off[i] = ea;
-            foff[i] = ef;
+        ta += d.alloc;
+        tf += d.free;
+        if (j < i) {
+            pa += d.alloc;
+            pf += d.free;
         }
-        ea += da[k];
-        ef += df[k];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        ta += __shfl_xor(ta, o, 64);
+        tf += __shfl_xor(tf, o, 64);
+        pa += __shfl_xor(pa, o, 64);
+        pf += __shfl_xor(pf, o, 64);
+        err |= uint32_t(__shfl_xor(int(err), o, 64));
+    }
+    if (lane == 0) {
+        s_r[wave][0] = ta;
+        s_r[wave][1] = tf;
+        s_r[wave][2] = pa;
+        s_r[wave][3] = pf;
+        s_err[wave] = err;
     }
     __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) {
-        const uint32_t e = s_err;
-        const int32_t entry = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hdr->err = e;
-        hdr->total_alloc = a;
-        hdr->total_free = f;
-        hdr->head0 = ctr[0];
-        hdr->tail0 = ctr[1];
-        hdr->entry_status = entry;
-        const bool commits = entry == 0 && e == 0 && uint64_t(a) <= ctr[1] - ctr[0];
-        ok[nheads] = commits ? 0 : 1;
+    ta = tf = pa = pf = 0;
+    err = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        ta += s_r[w][0];
+        tf += s_r[w][1];
+        pa += s_r[w][2];
+        pf += s_r[w][3];
+        err |= s_err[w];
     }
+    if (i == 0 && threadIdx.x == 0)
+        ok[nheads] = (entry == 0 && err == 0 && uint64_t(ta) <= tail0 - head0) ? 0 : 1;
+    commit_head_with(i, rows_l, count_l, new_count, C, P, layer_gid0, status, ctr, ring, owner,
+                     entry, head0, tail0, err, ta, tf, mine, pa, pf, old_rows, old_count);
 }
 
 }  // namespace kvc
@@ -222,34 +231,21 @@ using namespace kvc;
 
 namespace kvc {
 
-int launch_round_plan(const kvc_geom *g, const int32_t *count_l, const int32_t *new_count,
-                      const uint8_t *changed, int32_t *ok, const kvc_pool *p, void *compact_ws,
-                      hipStream_t s) {
-    const CompactWs L(g);
-    char *w = static_cast<char *>(compact_ws);
-    hipLaunchKernelGGL(round_plan_kernel, dim3(1), dim3(256), 0, s, L.nheads, g->row_capacity,
-                       count_l, new_count, changed, ok, p->dev_status, p->ring_ctr,
-                       reinterpret_cast<CompactHdr *>(w + L.hdr),
-                       reinterpret_cast<int32_t *>(w + L.off),
-                       reinterpret_cast<int32_t *>(w + L.foff));
-    return launch_check("kvc_compaction_round/plan");
-}
-
-// the commit launch of an allocation round whose scan is done (hdr, off, foff in compact_ws)
-int launch_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p, const int32_t *new_count,
-                  const uint8_t *changed, int32_t *old_rows_out, int32_t *old_count_out,
-                  void *compact_ws, hipStream_t s) {
+// the planning and commit launch of a fused round (round_commit_kernel); the round's start
+// was snapshotted into the compact workspace's header by the per-head scan launch
+int launch_round_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                        const int32_t *new_count, const uint8_t *changed, int32_t *ok,
+                        int32_t *old_rows_out, int32_t *old_count_out, void *compact_ws,
+                        hipStream_t s) {
     const CompactWs L(g);
     char *w = static_cast<char *>(compact_ws);
     const int C = g->row_capacity;
     int32_t *rows_l = p->page_table + int64_t(layer) * L.nheads * C;
     int32_t *count_l = p->count + int64_t(layer) * L.nheads * 2;
-    hipLaunchKernelGGL(compact_commit_kernel, dim3(L.nheads), dim3(256), 0, s, rows_l, count_l,
-                       new_count, changed, C, g->num_pages, layer * L.nheads, p->dev_status,
-                       p->ring_ctr, p->free_ring, p->owner,
-                       reinterpret_cast<const CompactHdr *>(w + L.hdr),
-                       reinterpret_cast<const int32_t *>(w + L.off),
-                       reinterpret_cast<const int32_t *>(w + L.foff), old_rows_out,
+    hipLaunchKernelGGL(round_commit_kernel, dim3(L.nheads), dim3(256), 0, s, L.nheads, rows_l,
+                       count_l, new_count, changed, C, g->num_pages, layer * L.nheads,
+                       p->dev_status, p->ring_ctr, p->free_ring, p->owner,
+                       reinterpret_cast<const CompactHdr *>(w + L.hdr), ok, old_rows_out,
                        old_count_out);
     return launch_check("kvc_compaction_round/commit");
 }

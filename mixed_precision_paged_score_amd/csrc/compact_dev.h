@@ -62,28 +62,16 @@ __device__ __forceinline__ void block_scan2(int &a, int &f, int *s_wa, int *s_wf
     f += pf;
 }
 
-// Head i's commit by one workgroup (all its threads call it): snapshot the old row and counts
-// when asked, then, if the round commits (pool status clear at entry, no head overflowed or
-// shrank, the total demand fits the free pages), return the rebuilt head's old pages to the
-// ring's tail, take its new pages from the ring's head (off[i] / foff[i] into the round's
-// regions), rewrite its row, the reverse map and its counts; head 0 moves the ring counters.
-// Returns whether the round committed (the same answer in every workgroup).
-__device__ __forceinline__ bool commit_head(
+// The commit of head i given the round's inputs (entry status, ring counters, the OR of every
+// head's error bits, the round's totals, the head's demand d and its offsets oi / fi into the
+// round's allocation and free regions); commit_head below loads them from a scan's header.
+__device__ __forceinline__ bool commit_head_with(
     int i, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
-    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C, int64_t P,
-    int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
-    int32_t *__restrict__ owner, const CompactHdr *hdr, const int32_t *__restrict__ off,
-    const int32_t *__restrict__ foff, int32_t *__restrict__ old_rows,
+    const int32_t *__restrict__ new_count, int C, int64_t P, int layer_gid0, int32_t *status,
+    uint64_t *ctr, int32_t *__restrict__ ring, int32_t *__restrict__ owner, int32_t entry,
+    uint64_t head0, uint64_t tail0, uint32_t herr, int64_t total_alloc, int64_t total_free,
+    const HeadDemand &d, int oi, int fi, int32_t *__restrict__ old_rows,
     int32_t *__restrict__ old_count) {
-    // every input of the head's commit is requested at once: the round's header, the head's
-    // old and new counts and changed flag, and its offsets into the round's regions
-    const int32_t entry = hdr->entry_status;
-    const uint64_t head0 = hdr->head0, tail0 = hdr->tail0;
-    const uint32_t herr = hdr->err;
-    const int64_t total_alloc = hdr->total_alloc, total_free = hdr->total_free;
-    const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
-    const int oi = off[i], fi = foff[i];
-    asm volatile("" ::"s"(entry), "s"(d.alloc), "s"(d.free), "s"(oi), "s"(fi));
     if (entry != 0) return false;                      // sticky failure: no-op
     int32_t *row = rows_l + int64_t(i) * C;
     constexpr int U = 4;                               // loads in flight per thread
@@ -166,6 +154,33 @@ __device__ __forceinline__ bool commit_head(
         ctr[1] = tail0 + uint64_t(total_free);
     }
     return true;
+}
+
+// Head i's commit by one workgroup (all its threads call it): snapshot the old row and counts
+// when asked, then, if the round commits (pool status clear at entry, no head overflowed or
+// shrank, the total demand fits the free pages), return the rebuilt head's old pages to the
+// ring's tail, take its new pages from the ring's head (off[i] / foff[i] into the round's
+// regions), rewrite its row, the reverse map and its counts; head 0 moves the ring counters.
+// Returns whether the round committed (the same answer in every workgroup).
+__device__ __forceinline__ bool commit_head(
+    int i, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C, int64_t P,
+    int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
+    int32_t *__restrict__ owner, const CompactHdr *hdr, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ foff, int32_t *__restrict__ old_rows,
+    int32_t *__restrict__ old_count) {
+    // every input of the head's commit is requested at once: the round's header, the head's
+    // old and new counts and changed flag, and its offsets into the round's regions
+    const int32_t entry = hdr->entry_status;
+    const uint64_t head0 = hdr->head0, tail0 = hdr->tail0;
+    const uint32_t herr = hdr->err;
+    const int64_t total_alloc = hdr->total_alloc, total_free = hdr->total_free;
+    const HeadDemand d = head_demand(count_l, new_count, changed, i, C);
+    const int oi = off[i], fi = foff[i];
+    asm volatile("" ::"s"(entry), "s"(d.alloc), "s"(d.free), "s"(oi), "s"(fi));
+    return commit_head_with(i, rows_l, count_l, new_count, C, P, layer_gid0, status, ctr, ring,
+                            owner, entry, head0, tail0, herr, total_alloc, total_free, d, oi, fi,
+                            old_rows, old_count);
 }
 
 }  // namespace kvc

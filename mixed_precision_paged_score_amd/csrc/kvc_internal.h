@@ -33,12 +33,10 @@ int launch_round_score(const kvc_geom *g, const float *acc, const int32_t *cu, i
                        float alpha_h, float alpha_l, int window, const uint8_t *prev_tier,
                        uint8_t *tier, int32_t *tile_cnt, int32_t *tile_cnt2, uint8_t *tile_chg,
                        int32_t *status, hipStream_t s);
-int launch_round_plan(const kvc_geom *g, const int32_t *count_l, const int32_t *new_count,
-                      const uint8_t *changed, int32_t *ok, const kvc_pool *p, void *compact_ws,
-                      hipStream_t s);
-int launch_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p, const int32_t *new_count,
-                  const uint8_t *changed, int32_t *old_rows_out, int32_t *old_count_out,
-                  void *compact_ws, hipStream_t s);
+int launch_round_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p,
+                        const int32_t *new_count, const uint8_t *changed, int32_t *ok,
+                        int32_t *old_rows_out, int32_t *old_count_out, void *compact_ws,
+                        hipStream_t s);
 
 // the score accumulation after a decode (attention.hip): w is the decode workspace laid out
 // by DecodeWs(g, true, max_seqlen), its tile records and (M, L) already written

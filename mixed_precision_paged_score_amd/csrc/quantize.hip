@@ -140,11 +140,19 @@ __global__ __launch_bounds__(256) void round_head_kernel(
     const int32_t *__restrict__ tile_cnt, const int32_t *__restrict__ tile_cnt2,
     const uint8_t *__restrict__ tile_chg, const int32_t *__restrict__ cu, int Hkv, int ntq,
     int max_seqlen, int32_t *__restrict__ tile_base, int32_t *__restrict__ tile_base2,
-    int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok) {
+    int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok,
+    const int32_t *status, const uint64_t *ctr, CompactHdr *snap) {
     __shared__ int s_sum[2][128];
     __shared__ int s_tot[2], s_tot2[2];
     __shared__ int s_chg;
     const int h = blockIdx.x, b = blockIdx.y;
+    if (h == 0 && b == 0 && threadIdx.x == 0) {
+        // the round's start for the commit launch: the pool status (the score launch's bits
+        // included) and the ring counters, before any commit of this round moves them
+        snap->entry_status = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        snap->head0 = ctr[0];
+        snap->tail0 = ctr[1];
+    }
     const int i = b * Hkv + h;
     const bool retier = tile_cnt2 != nullptr;
     const int N = cu[b + 1] - cu[b];
@@ -902,10 +910,11 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
 }
 
 // ---- the fused compaction round -------------------------------------------------------------
-// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in six launches for up to
+// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in five launches for up to
 // ROUND_MAX_HEADS heads: score with per-tile counts (no counters to clear, no separate count
-// launch), the per-head tile scans (totals, rank bases), one planning workgroup (page demands,
-// the allocation scan, the commit decision), the commit, the ranks and the page writer.
+// launch), the per-head tile scans (totals, rank bases; the first workgroup also takes the
+// round's start: pool status and ring counters), the commit (every workgroup makes the page
+// demands' scan and the commit decision for itself), the ranks and the page writer.
 extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                                     const float *acc, const int32_t *cu, int64_t total_tokens,
                                     int32_t max_seqlen, float alpha_h, float alpha_l,
@@ -950,16 +959,15 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
     rc = launch_round_score(g, acc, cu, max_seqlen, alpha_h, alpha_l, window, prev_tier, tier,
                             tile_cnt, tile_cnt2, tile_chg, p->dev_status, s);
     if (rc) return rc;
+    const CompactWs CL(g);
     hipLaunchKernelGGL(round_head_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, tile_cnt2,
                        tile_chg, cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, new_count,
-                       retier ? changed : nullptr, ok);
+                       retier ? changed : nullptr, ok, p->dev_status, p->ring_ctr,
+                       reinterpret_cast<CompactHdr *>(w + R.compact + CL.hdr));
     rc = launch_check("kvc_compaction_round/heads");
     if (rc) return rc;
-    rc = launch_round_plan(g, count_l, new_count, retier ? changed : nullptr, ok, p,
-                           w + R.compact, s);
-    if (rc) return rc;
-    rc = launch_commit(g, layer, p, new_count, retier ? changed : nullptr, old_rows, old_count,
-                       w + R.compact, s);
+    rc = launch_round_commit(g, layer, p, new_count, retier ? changed : nullptr, ok, old_rows,
+                             old_count, w + R.compact, s);
     if (rc) return rc;
     if (max_seqlen == 0 || total_tokens == 0) return KVC_OK;
     hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
