@@ -611,14 +611,12 @@ void decode_mfma_kernel(const uint16_t *__restrict__ q, float scale_log2,
 // one wave per (request, query head): lanes first hold the splits' (m, l) (S <= 64), then
 // two output channels each; the splits' partial rows are loaded eight at a time, all
 // independent, and weighted with exp2(m_s - M) read from the owning lane
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
-                                                             int Hq, int G, int S, int nqh,
-                                                             void *out, int out_fp32,
-                                                             float *__restrict__ mls,
-                                                             const int32_t *__restrict__ count_l,
-                                                             int wt) {
+__device__ __forceinline__ void combine_block(int bx, const float *__restrict__ part, int Hq,
+                                              int G, int S, int nqh, void *out, int out_fp32,
+                                              float *__restrict__ mls,
+                                              const int32_t *__restrict__ count_l, int wt) {
     const int lane = threadIdx.x & 63;
-    const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);    // b*Hq + hq
+    const int qh = bx * 4 + (threadIdx.x >> 6);            // b*Hq + hq
     if (qh >= nqh) return;
     const int b = qh / Hq, hq = qh - b * Hq;
     const int h = hq / G, gg = hq - h * G;
@@ -682,6 +680,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
 }
 
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part,
+                                                             int Hq, int G, int S, int nqh,
+                                                             void *out, int out_fp32,
+                                                             float *__restrict__ mls,
+                                                             const int32_t *__restrict__ count_l,
+                                                             int wt) {
+    combine_block(blockIdx.x, part, Hq, G, S, nqh, out, out_fp32, mls, count_l, wt);
+}
+
 // ---- score accumulation: acc_sum[cu[b] + pos][hq] += exp2(logit - M) / L -------------------
 // The decode kernel leaves, per tile of each head (HIGH tiles, then LOW tiles of 16 slots),
 // the tile's 16 positions and its logits; one accumulator row holds all query heads of one
@@ -697,17 +704,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
 // writes start[c] = s for every c with prev < c*R <= p; the last slot also writes
 // start[c] = n for c*R > p up to c = ceil(N/R).
 constexpr int ACC_IDX_BLOCKS = 16;
-__global__ __launch_bounds__(256) void acc_index_kernel(
-    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int G,
-    int max_seqlen, int nch_cap, const float *__restrict__ lg, int64_t tiles_cap,
+__device__ __forceinline__ void index_block(
+    int i, int by, const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv,
+    int G, int max_seqlen, int nch_cap, const float *__restrict__ lg, int64_t tiles_cap,
     int32_t *__restrict__ idx, int32_t *status) {
-    const int i = blockIdx.x;
-    const bool high = (blockIdx.y & 1) == 0;
-    const int part = blockIdx.y >> 1;
+    const bool high = (by & 1) == 0;
+    const int part = by >> 1;
     const int b = i / Hkv;
     const int N = cu[b + 1] - cu[b];
     if (N < 0 || N > max_seqlen) {
-        if (blockIdx.y == 0 && threadIdx.x == 0) atomicOr(status, KVC_DEV_SEQLEN);
+        if (by == 0 && threadIdx.x == 0) atomicOr(status, KVC_DEV_SEQLEN);
         return;
     }
     const int nh = count_l[2 * i];
@@ -735,6 +741,32 @@ __global__ __launch_bounds__(256) void acc_index_kernel(
         for (int c = prev < 0 ? 0 : prev / ACC_R + 1; c <= c_hi; ++c) st[c] = sl;
         if (sl == n - 1)
             for (int c = c_hi + 1; c <= nch; ++c) st[c] = n;
+    }
+}
+
+__global__ __launch_bounds__(256) void acc_index_kernel(
+    const int32_t *__restrict__ count_l, const int32_t *__restrict__ cu, int Hkv, int G,
+    int max_seqlen, int nch_cap, const float *__restrict__ lg, int64_t tiles_cap,
+    int32_t *__restrict__ idx, int32_t *status) {
+    index_block(blockIdx.x, blockIdx.y, count_l, cu, Hkv, G, max_seqlen, nch_cap, lg, tiles_cap,
+                idx, status);
+}
+
+// The combine and the chunk index of a score-accumulating decode in one launch (both read
+// only what the main kernel wrote): workgroups [0, ncomb) combine four query heads each, the
+// rest are the index's (head, part and tier) workgroups, head fastest
+__global__ __launch_bounds__(256) void combine_index_kernel(
+    int ncomb, int nidx_x, const float *__restrict__ part, int Hq, int G, int S, int nqh,
+    void *out, int out_fp32, float *__restrict__ mls, const int32_t *__restrict__ count_l,
+    int wt, const int32_t *__restrict__ cu, int Hkv, int max_seqlen, int nch_cap,
+    const float *__restrict__ lg, int64_t tiles_cap, int32_t *__restrict__ idx,
+    int32_t *status) {
+    if (int(blockIdx.x) < ncomb) {
+        combine_block(blockIdx.x, part, Hq, G, S, nqh, out, out_fp32, mls, count_l, wt);
+    } else {
+        const int k = int(blockIdx.x) - ncomb;
+        index_block(k % nidx_x, k / nidx_x, count_l, cu, Hkv, G, max_seqlen, nch_cap, lg,
+                    tiles_cap, idx, status);
     }
 }
 
@@ -879,23 +911,25 @@ __global__ __launch_bounds__(256) void acc_update_kernel(
     }
 }
 
-// the score accumulation after a decode that wrote its tile records and whose combine wrote
-// each query head's (M, L): the chunk index, then the accumulator update (shared with the
-// precision-scheme decode)
-int launch_score_accumulation(const kvc_geom *g, const kvc_pool *p, const int32_t *count_l,
-                              const int32_t *cu, int max_seqlen, float *acc_sum, char *w,
-                              hipStream_t s) {
-    if (max_seqlen == 0) return KVC_OK;
+// The combine and the score accumulation after a decode that wrote its partials and tile
+// records: one launch for the combine (which writes each query head's (M, L)) and the chunk
+// index, then the accumulator update (shared with the precision-scheme decode)
+int launch_combine_and_accumulation(const kvc_geom *g, const kvc_pool *p, const float *part,
+                                    int S, int wt, void *out, int out_fp32,
+                                    const int32_t *count_l, const int32_t *cu, int max_seqlen,
+                                    float *acc_sum, char *w, hipStream_t s) {
     const DecodeWs L(g, true, max_seqlen);
-    const int B = g->batch, Hkv = g->num_kv_heads, G = g->num_q_heads / Hkv;
-    const float *mls = reinterpret_cast<const float *>(w + L.mls);
+    const int B = g->batch, Hkv = g->num_kv_heads, Hq = g->num_q_heads, G = Hq / Hkv;
+    float *mls = reinterpret_cast<float *>(w + L.mls);
     const float *lg = reinterpret_cast<const float *>(w + L.lg);
     int32_t *idx = reinterpret_cast<int32_t *>(w + L.idx);
-    hipLaunchKernelGGL(acc_index_kernel, dim3(B * Hkv, 2 * ACC_IDX_BLOCKS), dim3(256), 0, s,
-                       count_l, cu, Hkv, G, max_seqlen, L.nch_cap, lg, L.tiles_cap, idx,
-                       p->dev_status);
-    int rc = launch_check("score accumulation/index");
-    if (rc) return rc;
+    const int nqh = B * Hq, ncomb = (nqh + 3) / 4, nidx_x = B * Hkv;
+    const int nblk = max_seqlen == 0 ? ncomb : ncomb + nidx_x * 2 * ACC_IDX_BLOCKS;
+    hipLaunchKernelGGL(combine_index_kernel, dim3(nblk), dim3(256), 0, s, ncomb, nidx_x, part, Hq,
+                       G, S, nqh, out, out_fp32, mls, count_l, wt, cu, Hkv, max_seqlen,
+                       L.nch_cap, lg, L.tiles_cap, idx, p->dev_status);
+    int rc = launch_check("score accumulation/combine and index");
+    if (rc || max_seqlen == 0) return rc;
     const size_t lds = sizeof(float) * (size_t(ACC_R) * acc_ldr(g->num_q_heads) +
                                         2 * size_t(g->num_q_heads));
     auto upd = G == 8 ? acc_update_kernel<8> : G == 4 ? acc_update_kernel<4>
@@ -963,10 +997,11 @@ int decode_impl(const kvc_geom *g, int32_t layer, const kvc_pool *p, const uint1
                            L.wt, part, nullptr, int64_t(0));
     rc = launch_check("kvc_paged_decode_attention/main");
     if (rc) return rc;
-    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
-                               count_l, L.wt, s);
-    if (rc || !accum) return rc;
-    return launch_score_accumulation(g, p, count_l, cu, max_seqlen, acc_sum, w, s);
+    if (accum)
+        return launch_combine_and_accumulation(g, p, part, L.splits, L.wt, out, out_is_fp32,
+                                               count_l, cu, max_seqlen, acc_sum, w, s);
+    return launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
+                                 count_l, L.wt, s);
 }
 
 }  // namespace

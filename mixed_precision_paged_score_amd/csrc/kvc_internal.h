@@ -38,11 +38,13 @@ int launch_round_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                         int32_t *old_rows_out, int32_t *old_count_out, void *compact_ws,
                         hipStream_t s);
 
-// the score accumulation after a decode (attention.hip): w is the decode workspace laid out
-// by DecodeWs(g, true, max_seqlen), its tile records and (M, L) already written
-int launch_score_accumulation(const kvc_geom *g, const kvc_pool *p, const int32_t *count_l,
-                              const int32_t *cu, int max_seqlen, float *acc_sum, char *w,
-                              hipStream_t s);
+// the combine and the score accumulation after a score-accumulating decode (attention.hip):
+// w is the decode workspace laid out by DecodeWs(g, true, max_seqlen), its partials and tile
+// records already written
+int launch_combine_and_accumulation(const kvc_geom *g, const kvc_pool *p, const float *part,
+                                    int S, int wt, void *out, int out_fp32,
+                                    const int32_t *count_l, const int32_t *cu, int max_seqlen,
+                                    float *acc_sum, char *w, hipStream_t s);
 // the combine launch of a split-K decode (attention.hip); partials [B*Hkv][S][G][132], of
 // which head i's first active_splits(count_l[2i], count_l[2i+1], S, wt) were written
 int launch_decode_combine(const float *part, int Hq, int G, int S, int B, void *out,

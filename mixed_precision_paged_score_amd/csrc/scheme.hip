@@ -769,10 +769,11 @@ int scheme_decode_impl(const kvc_geom *g, const kvc_scheme *sc, int32_t layer,
                        lg, L.tiles_cap);
     rc = launch_check("kvc_paged_decode_attention_scheme/main");
     if (rc) return rc;
-    rc = launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
-                               count_l, L.wt, s);
-    if (rc || !accum) return rc;
-    return launch_score_accumulation(g, p, count_l, cu, max_seqlen, acc_sum, w, s);
+    if (accum)
+        return launch_combine_and_accumulation(g, p, part, L.splits, L.wt, out, out_is_fp32,
+                                               count_l, cu, max_seqlen, acc_sum, w, s);
+    return launch_decode_combine(part, g->num_q_heads, G, L.splits, B, out, out_is_fp32, mls,
+                                 count_l, L.wt, s);
 }
 
 }  // namespace
