@@ -45,7 +45,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
-MAX_CPU_WORKERS = 16                # the host-core share of one GPU on the GPU machine
+MAX_CPU_WORKERS = 16                # the host-core share of one GPU of an 8-GPU node
 FLUSH_BYTES = 1 << 30               # scratch read before a cold rep
 
 
