@@ -52,14 +52,22 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups of one query column)
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups of one query column): each
+// permlane swap leaves the lane's own value in one operand and its partner's in the other.
+// Written out so that the maxima skip the NaN quieting a library max adds (scores are never
+// NaN); the two wait states before each swap are the ones it needs after a VALU write.
 __device__ __forceinline__ float max_col(float x) {
-    uint32_t u = __float_as_uint(x);
-    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    u = __float_as_uint(x);
-    const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    float t;
+    asm("v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "v_max_f32 %0, %0, %1\n\t"
+        "v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %1\n\t"
+        "v_max_f32 %0, %0, %1"
+        : "+v"(x), "=&v"(t));
+    return x;
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin by flat index, and each XCD has its own
@@ -95,26 +103,35 @@ __device__ __forceinline__ uint4 ld_row(const uint16_t *base, int64_t row, bool 
 }
 
 // NT threads stage a block: K rows (tid / 16) + (NT / 16) i, V row pairs (tid % 32) at
-// columns 8 ((tid / 32) + (NT / 32) i)
-template <int NT>
-__device__ __forceinline__ void load_k(KBlock &kb, const uint16_t *K, int64_t lo, int N, int kb0,
-                                       int Hkv, int h, int tid) {
+// columns 8 ((tid / 32) + (NT / 32) i).  Rows past the request's end (last block only) read
+// as zeros; every other block loads without a per-row test.  Keys and values are requested
+// together in either case, so that neither waits for the other.
+template <int NT, bool FULL>
+__device__ __forceinline__ void load_kv_rows(KBlock &kb, VBlock &vb, const uint16_t *K,
+                                             const uint16_t *V, int64_t lo, int N, int kb0,
+                                             int Hkv, int h, int tid) {
 #pragma unroll
     for (int i = 0; i < 1024 / NT; ++i) {
         const int key = (tid >> 4) + (NT / 16) * i;
-        kb.k[i] = ld_row(K, (lo + kb0 + key) * Hkv + h, kb0 + key < N, tid & 15);
+        kb.k[i] = ld_row(K, (lo + kb0 + key) * Hkv + h, FULL || kb0 + key < N, tid & 15);
     }
-}
-template <int NT>
-__device__ __forceinline__ void load_v(VBlock &vb, const uint16_t *V, int64_t lo, int N, int kb0,
-                                       int Hkv, int h, int tid) {
     const int m = tid & 31;
 #pragma unroll
     for (int i = 0; i < 512 / NT; ++i) {
         const int d8 = (tid >> 5) + (NT / 32) * i;
-        vb.v[2 * i] = ld_row(V, (lo + kb0 + 2 * m) * Hkv + h, kb0 + 2 * m < N, d8);
-        vb.v[2 * i + 1] = ld_row(V, (lo + kb0 + 2 * m + 1) * Hkv + h, kb0 + 2 * m + 1 < N, d8);
+        vb.v[2 * i] = ld_row(V, (lo + kb0 + 2 * m) * Hkv + h, FULL || kb0 + 2 * m < N, d8);
+        vb.v[2 * i + 1] =
+            ld_row(V, (lo + kb0 + 2 * m + 1) * Hkv + h, FULL || kb0 + 2 * m + 1 < N, d8);
     }
+}
+template <int NT>
+__device__ __forceinline__ void load_kv(KBlock &kb, VBlock &vb, const uint16_t *K,
+                                        const uint16_t *V, int64_t lo, int N, int kb0, int Hkv,
+                                        int h, int tid) {
+    if (kb0 + BN <= N)
+        load_kv_rows<NT, true>(kb, vb, K, V, lo, N, kb0, Hkv, h, tid);
+    else
+        load_kv_rows<NT, false>(kb, vb, K, V, lo, N, kb0, Hkv, h, tid);
 }
 template <int NT>
 __device__ __forceinline__ void store_k(const KBlock &kb, _Float16 *s_k, int tid) {
@@ -140,9 +157,10 @@ __device__ __forceinline__ void store_v(const VBlock &vb, _Float16 *s_vt, int ti
                                vb.v[2 * i + 1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t lo16 = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t hi16 = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            *reinterpret_cast<uint32_t *>(s_vt + (8 * d8 + e) * VS + pm) = lo16 | (hi16 << 16);
+            // half e of row 2m in the low 16 bits, of row 2m + 1 in the high 16 (byte select)
+            const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1],
+                                                     (e & 1) ? 0x07060302u : 0x05040100u);
+            *reinterpret_cast<uint32_t *>(s_vt + (8 * d8 + e) * VS + pm) = w;
         }
     }
 }
@@ -223,8 +241,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     load_q(qop, Q, lo, N, qw, Hq, hq, lane);
     KBlock kb;
     VBlock vb;
-    load_k<NT>(kb, K, lo, N, 0, Hkv, h, tid);
-    load_v<NT>(vb, V, lo, N, 0, Hkv, h, tid);
+    load_kv<NT>(kb, vb, K, V, lo, N, 0, Hkv, h, tid);
     store_k<NT>(kb, s_k[0], tid);
     store_v<NT>(vb, s_vt[0], tid);
     __syncthreads();
@@ -234,6 +251,79 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int dt = 0; dt < 8; ++dt) o[dt][0] = o[dt][1] = f4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {M_INIT, M_INIT}, l[2] = {0.f, 0.f};
 
+    // softmax of one block's S^T tiles into the P^T operands [qt][u], rescaling o, m, l when the
+    // running max moves
+    auto softmax_block = [&](const f4 (&s)[4][2], int kb0, h8 (&pb)[2][2]) {
+        const bool diag = kb0 + BN - 1 > qw;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            // raw scores; keys after the query (diagonal blocks only) become -inf.  The max
+            // is taken before scaling (scale_log2 > 0 and rounding are monotone)
+            float x[16];
+            float mx = -__builtin_inff();
+            if (diag) {
+                // key kb0 + 16 kt + 4 g + r is after query qw + 16 qt + c when 16 kt + r > thr
+                const int thr = qw + 16 * qt + c - kb0 - 4 * g;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = 16 * kt + r > thr ? -__builtin_inff() : s[kt][qt][r];
+                        x[4 * kt + r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        x[4 * kt + r] = s[kt][qt][r];
+                        mx = fmaxf(mx, s[kt][qt][r]);
+                    }
+            }
+            mx = fmaxf(max_col(mx) * scale_log2, M_INIT);
+            if (__ballot(mx > m[qt] + MARGIN) != 0ull) {
+                const float mn = fmaxf(m[qt], mx);
+                const float corr = __builtin_amdgcn_exp2f(m[qt] - mn);
+                m[qt] = mn;
+                l[qt] *= corr;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= corr;
+            }
+            float pe[16];
+            _Float16 p[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m[qt]));
+                p[e] = _Float16(pe[e]);
+            }
+            float ls = pe[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) ls += pe[e];
+            l[qt] += ls;
+            // P^T operand u: keys 32u + 4g + e (e < 4) from tile 2u, 32u + 16 + 4g + e - 4
+            // from tile 2u + 1
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                pb[qt][u] = h8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
+                               p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]};
+        }
+    };
+    // O^T += V^T P^T; V^T operand: dim row 16 dt + c, keys in the same order as P^T's k
+    // (32u + 4g + e, then 32u + 16 + 4g + e), stored contiguously by vt_pos
+    auto pv_block = [&](const h8 (&pb)[2][2], const _Float16 *vt) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const _Float16 *vrow = vt + (16 * dt + c) * VS + 8 * g;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const h8 a = *reinterpret_cast<const h8 *>(vrow + 32 * u);
+                o[dt][0] = mfma(a, pb[0][u], o[dt][0]);
+                o[dt][1] = mfma(a, pb[1][u], o[dt][1]);
+            }
+        }
+    };
+
     for (int j = 0; j < nblk; ++j) {
         const int cur = j & 1;
         const int kb0 = j * BN;
@@ -242,84 +332,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (kb0 <= qw + 31) {                        // else every key is after the wave's queries
             f4 s[4][2];
             scores(s, s_k[cur], qop, lane);
-            const bool diag = kb0 + BN - 1 > qw;
             h8 pb[2][2];                             // P^T operands [qt][u]
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const int qi = qw + 16 * qt + c;
-                // raw scores; keys after the query (diagonal blocks only) become -inf.  The max
-                // is taken before scaling (scale_log2 > 0 and rounding are monotone)
-                float x[16];
-                float mx = -__builtin_inff();
-                if (diag) {
-#pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float v = kb0 + 16 * kt + 4 * g + r > qi ? -__builtin_inff()
-                                                                         : s[kt][qt][r];
-                            x[4 * kt + r] = v;
-                            mx = fmaxf(mx, v);
-                        }
-                } else {
-#pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            x[4 * kt + r] = s[kt][qt][r];
-                            mx = fmaxf(mx, s[kt][qt][r]);
-                        }
-                }
-                mx = fmaxf(max_col(mx) * scale_log2, M_INIT);
-                if (__ballot(mx > m[qt] + MARGIN) != 0ull) {
-                    const float mn = fmaxf(m[qt], mx);
-                    const float corr = __builtin_amdgcn_exp2f(m[qt] - mn);
-                    m[qt] = mn;
-                    l[qt] *= corr;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= corr;
-                }
-                float ls = 0.f;
-                _Float16 p[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m[qt]));
-                    ls += pe;
-                    p[e] = _Float16(pe);
-                }
-                l[qt] += ls;
-                // P^T operand u: keys 32u + 4g + e (e < 4) from tile 2u, 32u + 16 + 4g + e - 4
-                // from tile 2u + 1
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    pb[qt][u] = h8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3],
-                                   p[8 * u + 4], p[8 * u + 5], p[8 * u + 6], p[8 * u + 7]};
-            }
+            softmax_block(s, kb0, pb);
             // the next block's rows are requested now (the score registers are free) and land
             // while the PV products run
             if (more) {
-                load_k<NT>(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
-                load_v<NT>(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+                load_kv<NT>(kb, vb, K, V, lo, N, kb0 + BN, Hkv, h, tid);
                 issued = true;
             }
-            // O^T += V^T P^T; V^T operand: dim row 16 dt + c, keys in the same order as P^T's k
-            // (32u + 4g + e, then 32u + 16 + 4g + e), stored contiguously by vt_pos
-            const _Float16 *vt = s_vt[cur];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const _Float16 *vrow = vt + (16 * dt + c) * VS + 8 * g;
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const h8 a = *reinterpret_cast<const h8 *>(vrow + 32 * u);
-                    o[dt][0] = mfma(a, pb[0][u], o[dt][0]);
-                    o[dt][1] = mfma(a, pb[1][u], o[dt][1]);
-                }
-            }
+            pv_block(pb, s_vt[cur]);
         }
         if (more) {
             if (!issued) {
-                load_k<NT>(kb, K, lo, N, kb0 + BN, Hkv, h, tid);
-                load_v<NT>(vb, V, lo, N, kb0 + BN, Hkv, h, tid);
+                load_kv<NT>(kb, vb, K, V, lo, N, kb0 + BN, Hkv, h, tid);
             }
             store_k<NT>(kb, s_k[cur ^ 1], tid);
             store_v<NT>(vb, s_vt[cur ^ 1], tid);
@@ -361,7 +386,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // kb0, so the group's workgroups on one XCD read the same query tiles at about the same time.
 constexpr int CK = 4 * BN;       // keys per column-sum workgroup
 constexpr int QT = 32;           // queries per staged tile
-__global__ __launch_bounds__(256) void prefill_colsum_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_colsum_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const int32_t *__restrict__ cu,
     int Hq, int Hkv, int max_seqlen, int B, float scale_log2, const float *__restrict__ ml,
     float *__restrict__ acc) {
@@ -400,14 +425,20 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
         for (int r = 0; r < 4; ++r) cs[kt][r] = 0.f;
     // staging: thread t loads query row t / 8 of the tile, 32 bytes at column 16 (t % 8); lanes
     // 0..31 of wave 0 also load the rows' (max, sum), stored as m + log2(sum) (+inf past the end)
-    auto load_tile = [&](uint4 (&u)[2], float &mq, int q0) {
+    // (only the last tile, staged first, can run past the end: `full` skips the row tests)
+    // per-thread row addresses at query 0; a tile adds q0 rows (uniform) to them
+    const uint16_t *qbase = Q + ((lo + (tid >> 3)) * Hq + hq) * D + 16 * (tid & 7);
+    const float *mlbase = ml + 2 * ((lo + tid) * Hq + hq);
+    const int64_t qstep = int64_t(Hq) * D;
+    auto load_tile = [&](uint4 (&u)[2], float &mq, int q0, bool full) {
         const int qi = q0 + (tid >> 3);
-        const uint16_t *row = Q + ((lo + qi) * Hq + hq) * D + 16 * (tid & 7);
-        u[0] = qi < N ? *reinterpret_cast<const uint4 *>(row) : make_uint4(0, 0, 0, 0);
-        u[1] = qi < N ? *reinterpret_cast<const uint4 *>(row + 8) : make_uint4(0, 0, 0, 0);
+        const uint16_t *row = qbase + q0 * qstep;
+        const bool ok = full || qi < N;
+        u[0] = ok ? *reinterpret_cast<const uint4 *>(row) : make_uint4(0, 0, 0, 0);
+        u[1] = ok ? *reinterpret_cast<const uint4 *>(row + 8) : make_uint4(0, 0, 0, 0);
         mq = __builtin_inff();
-        if (tid < QT && q0 + tid < N) {
-            const float2 x = *reinterpret_cast<const float2 *>(ml + 2 * ((lo + q0 + tid) * Hq + hq));
+        if (tid < QT && (full || q0 + tid < N)) {
+            const float2 x = *reinterpret_cast<const float2 *>(mlbase + 2 * int64_t(q0) * Hq);
             mq = x.y > 0.f ? x.x + __builtin_amdgcn_logf(x.y) : __builtin_inff();
         }
     };
@@ -420,14 +451,14 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
     uint4 u[2];
     float mq;
     const int ntile = (N - kb0 + QT - 1) / QT;
-    load_tile(u, mq, kb0 + QT * (ntile - 1));
+    load_tile(u, mq, kb0 + QT * (ntile - 1), false);
     store_tile(u, mq, 0);
     __syncthreads();
     for (int it = 0; it < ntile; ++it) {
         const int buf = it & 1;
         const int q0 = kb0 + QT * (ntile - 1 - it);  // last tile first
         const bool more = it + 1 < ntile;
-        if (more) load_tile(u, mq, q0 - QT);
+        if (more) load_tile(u, mq, q0 - QT, true);
         // queries q0 .. q0 + 31 against the wave's keys: nothing if every query precedes or
         // is the first key; masks only where the ranges overlap
         if (q0 + QT - 1 > kw) {
@@ -448,16 +479,17 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(
             const bool diag = q0 <= kw + BN - 1;
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                const int qi = q0 + 16 * qt + c;
                 const float m = s_m[buf][16 * qt + c];
                 if (diag) {
+                    // query q0 + 16 qt + c is after key kw + 16 kt + 4 g + r when 16 kt + r < thr
+                    const int thr = q0 + 16 * qt + c - kw - 4 * g;
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float p = __builtin_amdgcn_exp2f(
                                 __builtin_fmaf(sc[kt][qt][r], scale_log2, -m));
-                            cs[kt][r] += qi > kw + 16 * kt + 4 * g + r ? p : 0.f;
+                            cs[kt][r] += 16 * kt + r < thr ? p : 0.f;
                         }
                 } else {
 #pragma unroll
