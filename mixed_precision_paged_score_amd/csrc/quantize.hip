@@ -287,8 +287,9 @@ constexpr int QP_WAVES = 4;
 #define KVC_RB_AHEAD 1
 #endif
 // re-tier passes whose old words are in flight ahead of the pass being written: at 1 the
-// kernel holds 77 VGPRs (6 waves per SIMD); 2 and 3 measured slower on the chain-of-thought
-// re-tier round (284 us against 278) once every slot's source record is requested at once
+// re-tier kernel fits 72 VGPRs when asked for 6 or more waves per EU, so 7 waves per SIMD run
+// (the LDS staging allows no more); 2 and 3 measured slower on the chain-of-thought re-tier
+// round (284 us against 278 at the time) once every slot's source record is requested at once
 constexpr int RB_AHEAD = KVC_RB_AHEAD;
 constexpr int VST_BYTES = LS * D;     // per-wave staging of value codes (LOW page size)
 
@@ -338,8 +339,10 @@ __device__ __forceinline__ void fresh_slots(const uint16_t *__restrict__ K,
 // grid (ceil(C / 4), B*Hkv): wave w of block x writes page index 4x + w of head y, whole.
 // REBUILD: each token's codes come from the fp16 rows (previous tier FRESH), are copied from
 // its old page (tier unchanged), or are re-quantized from its old K8V4 codes (HIGH -> LOW).
+// (at least 6 waves per EU requested: the re-tier instance then fits 7, which measured 5%
+// faster on the chain-of-thought re-tier round than the compiler's own 77-VGPR choice)
 template <bool REBUILD>
-__global__ __launch_bounds__(256) void quant_pages_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void quant_pages_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ cu, int Hkv, int C, int max_seqlen,
     const int32_t *__restrict__ rows_l, const int32_t *__restrict__ count_l,
