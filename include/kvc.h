@@ -226,10 +226,12 @@ int kvc_quantize_and_place(const kvc_geom *geom, int32_t layer, const kvc_pool *
 /* One whole compaction round of a layer: kvc_score_tokens, kvc_compact_pages and
  * kvc_quantize_and_place in sequence (DiffKV review page, "What carries the argument": score,
  * per-head page demand, prefix-sum allocation over the circular free list, placement), with the
- * same results bit for bit, in five launches instead of nine: the score also counts each
+ * same results bit for bit, in four launches instead of nine: the score also counts each
  * 256-token tile's tiers per head (nothing to clear, no separate count launch), a per-head
- * launch turns the tile counts into the heads' totals and rank bases, and each commit
- * workgroup makes the allocation scan for itself.  For batches of at most 1024 KV heads
+ * launch turns the tile counts into the heads' totals and rank bases (and, re-tiering, keeps
+ * each changed head's old row), one launch holds the commits, each commit workgroup making
+ * the allocation scan for itself, beside the ranks, and the last writes the pages.  For
+ * batches of at most 1024 KV heads
  * (KVC_E_SHAPE above: use the three calls).
  *   prev_tier NULL: prompt mode (every head rebuilt, the layer's previous pages returned first;
  *     k, v required, changed may be NULL); else re-tier mode (changed required; k, v only for

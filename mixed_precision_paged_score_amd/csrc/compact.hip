@@ -171,58 +171,8 @@ __global__ __launch_bounds__(256) void round_commit_kernel(
     int64_t P, int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
     int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
     int32_t *__restrict__ old_rows, int32_t *__restrict__ old_count) {
-    __shared__ int s_r[4][4];
-    __shared__ uint32_t s_err[4];
-    const int i = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int32_t entry = snap->entry_status;
-    const uint64_t head0 = snap->head0, tail0 = snap->tail0;
-    const HeadDemand mine = head_demand(count_l, new_count, changed, i, C);
-    int ta = 0, tf = 0, pa = 0, pf = 0;
-    uint32_t err = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int j = 4 * threadIdx.x + k;
-        if (j >= nheads) continue;
-        const HeadDemand d = head_demand(count_l, new_count, changed, j, C);
-        err |= uint32_t(d.err);
-        ta += d.alloc;
-        tf += d.free;
-        if (j < i) {
-            pa += d.alloc;
-            pf += d.free;
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        ta += __shfl_xor(ta, o, 64);
-        tf += __shfl_xor(tf, o, 64);
-        pa += __shfl_xor(pa, o, 64);
-        pf += __shfl_xor(pf, o, 64);
-        err |= uint32_t(__shfl_xor(int(err), o, 64));
-    }
-    if (lane == 0) {
-        s_r[wave][0] = ta;
-        s_r[wave][1] = tf;
-        s_r[wave][2] = pa;
-        s_r[wave][3] = pf;
-        s_err[wave] = err;
-    }
-    __syncthreads();
-    ta = tf = pa = pf = 0;
-    err = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        ta += s_r[w][0];
-        tf += s_r[w][1];
-        pa += s_r[w][2];
-        pf += s_r[w][3];
-        err |= s_err[w];
-    }
-    if (i == 0 && threadIdx.x == 0)
-        ok[nheads] = (entry == 0 && err == 0 && uint64_t(ta) <= tail0 - head0) ? 0 : 1;
-    commit_head_with(i, rows_l, count_l, new_count, C, P, layer_gid0, status, ctr, ring, owner,
-                     entry, head0, tail0, err, ta, tf, mine, pa, pf, old_rows, old_count);
+    round_commit_block(blockIdx.x, nheads, rows_l, count_l, new_count, changed, C, P, layer_gid0,
+                       status, ctr, ring, owner, snap, ok, old_rows, old_count);
 }
 
 }  // namespace kvc

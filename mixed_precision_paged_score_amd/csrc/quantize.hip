@@ -22,6 +22,7 @@
 #include "quant_row.h"
 #include "page_io.h"
 #include "scheme_io.h"
+#include "compact_dev.h"
 
 #pragma clang fp contract(off)
 
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(256) void round_head_kernel(
     const uint8_t *__restrict__ tile_chg, const int32_t *__restrict__ cu, int Hkv, int ntq,
     int max_seqlen, int32_t *__restrict__ tile_base, int32_t *__restrict__ tile_base2,
     int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok,
-    const int32_t *status, const uint64_t *ctr, CompactHdr *snap) {
+    const int32_t *status, const uint64_t *ctr, CompactHdr *snap,
+    const int32_t *__restrict__ rows_l, int C, int32_t *__restrict__ old_rows) {
     __shared__ int s_sum[2][128];
     __shared__ int s_tot[2], s_tot2[2];
     __shared__ int s_chg;
@@ -173,6 +175,12 @@ __global__ __launch_bounds__(256) void round_head_kernel(
         if (retier) changed[i] = uint8_t(s_chg);
         ok[i] = retier ? s_chg : 1;
     }
+    // re-tier: a changed head's row as it stands before this round's commit, where the rank
+    // launch looks up the old page of every kept token (the commit then overwrites the row)
+    if (old_rows && s_chg) {
+        const int32_t *row = rows_l + int64_t(i) * C;
+        for (int p = threadIdx.x; p < C; p += blockDim.x) old_rows[int64_t(i) * C + p] = row[p];
+    }
 }
 
 // grid (ntq, B), 4 waves: wave w ranks heads w, w+4, ... over the tile's tokens with 64-lane
@@ -180,13 +188,12 @@ __global__ __launch_bounds__(256) void round_head_kernel(
 // Re-tiering: srcdesc at the same index as poslist tells the page writer where a kept token's
 // codes are: its previous tier, its rank among that tier (so its old page, through the old
 // row, and its slot there); FRESH and invalid previous tiers carry page 0.
-__global__ __launch_bounds__(256) void quant_select_kernel(
-    const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
+__device__ __forceinline__ void select_block(
+    const int tq, const int b, const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
     const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
     const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_base2,
     const int32_t *__restrict__ ok, const int32_t *__restrict__ old_rows, int C,
     int32_t *__restrict__ poslist, uint2 *__restrict__ srcdesc) {
-    const int b = blockIdx.y, tq = blockIdx.x;
     const int lo = cu[b], N = cu[b + 1] - lo;
     const int t0 = tq * QTILE;
     if (N > max_seqlen || t0 >= N) return;
@@ -282,7 +289,46 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
     }
 }
 
+__global__ __launch_bounds__(256) void quant_select_kernel(
+    const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
+    const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
+    const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_base2,
+    const int32_t *__restrict__ ok, const int32_t *__restrict__ old_rows, int C,
+    int32_t *__restrict__ poslist, uint2 *__restrict__ srcdesc) {
+    select_block(blockIdx.x, blockIdx.y, tier, prev, cu, Hkv, ntq, max_seqlen, tile_base,
+                 tile_base2, ok, old_rows, C, poslist, srcdesc);
+}
+
+// The commits (workgroups 0 .. nheads - 1, one per head) and the ranks (the rest, one per
+// (request, 256-token tile)) of a fused round in one launch.  The ranks read only what the
+// per-head scan launch wrote (tile bases, head flags and, when re-tiering, the changed heads'
+// old rows) and write the position lists and source records, none of which the commits read
+// or write, so the two need no order between them.
+__global__ __launch_bounds__(256) void round_commit_select_kernel(
+    int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C, int64_t P,
+    int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
+    int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
+    const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
+    const int32_t *__restrict__ cu, int Hkv, int ntq, int max_seqlen,
+    const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_base2,
+    const int32_t *__restrict__ old_rows, int32_t *__restrict__ poslist,
+    uint2 *__restrict__ srcdesc) {
+    const int x = blockIdx.x;
+    if (x < nheads) {
+        round_commit_block(x, nheads, rows_l, count_l, new_count, changed, C, P, layer_gid0,
+                           status, ctr, ring, owner, snap, ok, nullptr, nullptr);
+    } else {
+        const int k = x - nheads;
+        select_block(k % ntq, k / ntq, tier, prev, cu, Hkv, ntq, max_seqlen, tile_base,
+                     tile_base2, ok, old_rows, C, poslist, srcdesc);
+    }
+}
+
 constexpr int QP_WAVES = 4;
+#ifndef KVC_ROUND_MERGE
+#define KVC_ROUND_MERGE 1        // prompt-mode rounds: commits and ranks in one launch
+#endif
 #ifndef KVC_RB_AHEAD
 #define KVC_RB_AHEAD 1
 #endif
@@ -913,11 +959,13 @@ extern "C" int kvc_quantize_and_place_scheme(const kvc_geom *g, const kvc_scheme
 }
 
 // ---- the fused compaction round -------------------------------------------------------------
-// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in five launches for up to
+// kvc_score_tokens -> kvc_compact_pages -> kvc_quantize_and_place in four launches for up to
 // ROUND_MAX_HEADS heads: score with per-tile counts (no counters to clear, no separate count
-// launch), the per-head tile scans (totals, rank bases; the first workgroup also takes the
-// round's start: pool status and ring counters), the commit (every workgroup makes the page
-// demands' scan and the commit decision for itself), the ranks and the page writer.
+// launch), the per-head tile scans (totals, rank bases, a changed head's old row; the first
+// workgroup also takes the round's start: pool status and ring counters), the commits (every
+// workgroup makes the page demands' scan and the commit decision for itself) with the ranks
+// beside them in the same launch, and the page writer.  (A round with no tokens runs the
+// commits alone, as the separate commit launch, which also keeps the old rows.)
 extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_pool *p,
                                     const float *acc, const int32_t *cu, int64_t total_tokens,
                                     int32_t max_seqlen, float alpha_h, float alpha_l,
@@ -963,21 +1011,38 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
                             tile_cnt, tile_cnt2, tile_chg, p->dev_status, s);
     if (rc) return rc;
     const CompactWs CL(g);
+    const bool work = max_seqlen > 0 && total_tokens > 0;
+    const bool merge = KVC_ROUND_MERGE && work;
     hipLaunchKernelGGL(round_head_kernel, dim3(Hkv, B), dim3(256), 0, s, tile_cnt, tile_cnt2,
                        tile_chg, cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, new_count,
                        retier ? changed : nullptr, ok, p->dev_status, p->ring_ctr,
-                       reinterpret_cast<CompactHdr *>(w + R.compact + CL.hdr));
+                       reinterpret_cast<CompactHdr *>(w + R.compact + CL.hdr), rows_l, C,
+                       merge ? old_rows : nullptr);
     rc = launch_check("kvc_compaction_round/heads");
     if (rc) return rc;
-    rc = launch_round_commit(g, layer, p, new_count, retier ? changed : nullptr, ok, old_rows,
-                             old_count, w + R.compact, s);
-    if (rc) return rc;
-    if (max_seqlen == 0 || total_tokens == 0) return KVC_OK;
-    hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier, cu,
-                       Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, old_rows, C, poslist,
-                       srcdesc);
-    rc = launch_check("kvc_compaction_round/select");
-    if (rc) return rc;
+    if (merge) {
+        // commits and ranks in one launch (the old rows were taken by the per-head scans)
+        hipLaunchKernelGGL(round_commit_select_kernel, dim3(nheads + L.ntq * B), dim3(256), 0, s,
+                           nheads, p->page_table + int64_t(layer) * nheads * C,
+                           p->count + int64_t(layer) * nheads * 2, new_count,
+                           retier ? changed : nullptr, C, g->num_pages, layer * nheads,
+                           p->dev_status, p->ring_ctr, p->free_ring, p->owner,
+                           reinterpret_cast<const CompactHdr *>(w + R.compact + CL.hdr), ok, tier,
+                           prev_tier, cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, old_rows,
+                           poslist, srcdesc);
+        rc = launch_check("kvc_compaction_round/commit+select");
+        if (rc) return rc;
+    } else {
+        rc = launch_round_commit(g, layer, p, new_count, retier ? changed : nullptr, ok, old_rows,
+                                 old_count, w + R.compact, s);
+        if (rc) return rc;
+        if (!work) return KVC_OK;
+        hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier,
+                           cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, ok, old_rows, C,
+                           poslist, srcdesc);
+        rc = launch_check("kvc_compaction_round/select");
+        if (rc) return rc;
+    }
     const dim3 grid((C + QP_WAVES - 1) / QP_WAVES, nheads);
     if (retier)
         hipLaunchKernelGGL(quant_pages_kernel<true>, grid, dim3(64 * QP_WAVES), 0, s, k, v, cu, Hkv,
