@@ -145,9 +145,10 @@ def test_request_longer_than_max_seqlen_sets_status():
     assert int((b.pool.page_table >= 0).sum()) == 0          # nothing committed
 
 
-def run_retier_pair(w, steps, round_every):
+def run_retier_pair(w, steps, round_every, repeat=False):
     """Two generation runs in lockstep: appends on both, rounds through the three calls on one
-    and the fused round on the other; everything compared after every round."""
+    and the fused round on the other; everything compared after every round.  With repeat,
+    every round is run a second time on the same accumulators, where no head changes."""
     from mixed_precision_paged_score_amd import pipeline
     print(f"[round] re-tier {w.name} B={w.batch} steps={steps} round={round_every}", flush=True)
     k, v = workloads.make_kv(w)
@@ -178,6 +179,14 @@ def run_retier_pair(w, steps, round_every):
             assert torch.equal(a.changed, b.changed), f"round {rounds}: changed flags differ"
             assert_same_state(a, b, a.T)
             assert b.pool.status() == 0
+            if repeat:
+                a.retier(0, acc_r)
+                b.retier_fused(0, acc_r)
+                torch.cuda.synchronize()
+                assert int(b.changed.sum()) == 0, f"round {rounds} repeated: a head changed"
+                assert torch.equal(a.changed, b.changed)
+                assert_same_state(a, b, a.T)
+                assert b.pool.status() == 0
     print(f"[round] re-tier ok: {rounds} rounds", flush=True)
 
 
@@ -185,6 +194,12 @@ def test_retier_ragged():
     w = workloads.Workload("round-gen", 1, 3, 16, 4, [300, 160, 500], 1.0, 0.2, 16, 2048, "zipf",
                            seed=86)
     run_retier_pair(w, steps=96, round_every=32)
+
+
+def test_retier_repeated_round_changes_nothing():
+    w = workloads.Workload("round-gen-rep", 1, 2, 16, 4, [200, 420], 1.0, 0.2, 16, 2048, "zipf",
+                           seed=87)
+    run_retier_pair(w, steps=64, round_every=32, repeat=True)
 
 
 def test_retier_workload4_shape():
