@@ -15,6 +15,9 @@
 
 namespace kvc {
 
+#ifndef KVC_SCORE_UNROLL
+#define KVC_SCORE_UNROLL 4       // (token, head) items per thread whose loads are in flight together
+#endif
 #ifndef KVC_SCORE_TILE
 #define KVC_SCORE_TILE 256
 #endif
@@ -60,10 +63,19 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
     const float th = alpha_h / fN;   // correctly rounded float32 division
     const float tl = alpha_l / fN;
     const int nt = min(SCORE_TILE, N - t0);
-    for (int idx = threadIdx.x; idx < nt * Hkv; idx += blockDim.x) {
+    const int total = nt * Hkv;
+    // SU items per thread per pass: every item's accumulators (and previous tier) are requested
+    // before the first is used, so a pass waits for one round trip, not one per item (an item
+    // past the tile loads the tile's last item and is dropped)
+    constexpr int SU = (G > 0 && G % 4 == 0) ? KVC_SCORE_UNROLL : 1;
+    for (int base = threadIdx.x; base < total; base += SU * blockDim.x) {
+    float mxs[SU];
+    int pvs[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+        const int idx = min(base + u * int(blockDim.x), total - 1);
         const int tt = idx / Hkv, h = idx - tt * Hkv;
-        const int t = t0 + tt;
-        const int64_t r = int64_t(lo) + t;
+        const int64_t r = int64_t(lo) + t0 + tt;
         const float *a = acc + r * Hq + h * gs;
         float mx;
         if constexpr (G > 0 && G % 4 == 0) {
@@ -71,19 +83,30 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
             mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 #pragma unroll
             for (int k = 4; k < G; k += 4) {
-                float4 u = *reinterpret_cast<const float4 *>(a + k);
-                mx = fmaxf(mx, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+                float4 w = *reinterpret_cast<const float4 *>(a + k);
+                mx = fmaxf(mx, fmaxf(fmaxf(w.x, w.y), fmaxf(w.z, w.w)));
             }
         } else {
             mx = a[0];
             for (int k = 1; k < gs; ++k) mx = fmaxf(mx, a[k]);
         }
+        mxs[u] = mx;
+        pvs[u] = prev ? int(prev[r * Hkv + h]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+        const int idx = base + u * int(blockDim.x);
+        if (idx >= total) break;
+        const int tt = idx / Hkv, h = idx - tt * Hkv;
+        const int t = t0 + tt;
+        const int64_t r = int64_t(lo) + t;
+        const float mx = mxs[u];
         const int cnt = N - 1 - t;
         const float score = cnt == 0 ? __builtin_inff() : mx / float(cnt);
         int x = score >= th ? HIGH : (score >= tl ? LOW : PRUNE);
         if (t >= N - window) x = HIGH;
         if (prev) {
-            const int p = prev[r * Hkv + h];
+            const int p = pvs[u];
             if constexpr (TILES) {
                 if (p == HIGH) atomicAdd(&s_cnt2[2 * h], 1);
                 else if (p == LOW) atomicAdd(&s_cnt2[2 * h + 1], 1);
@@ -98,6 +121,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void score_kernel(
         tier[r * Hkv + h] = uint8_t(x);
         if (x == HIGH) atomicAdd(&s_cnt[2 * h], 1);
         else if (x == LOW) atomicAdd(&s_cnt[2 * h + 1], 1);
+    }
     }
     __syncthreads();
     if constexpr (TILES) {
