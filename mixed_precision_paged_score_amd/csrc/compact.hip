@@ -164,9 +164,7 @@ __global__ __launch_bounds__(256) void compact_commit_kernel(
 // own head's offsets, so no planning launch stands between the per-head scans and the
 // commits.  The pool status and ring counters at the round's start come from *snap, taken by
 // the per-head scan launch: no workgroup here reads them after another may have moved them.
-// Workgroup 0 records in ok[nheads] whether the round commits (0) or not (1).  A round with
-// tokens runs the same code (round_commit_block) in round_commit_select_kernel, beside the
-// ranks; this launch serves a round with none, and keeps the old rows when re-tiering.
+// Workgroup 0 records in ok[nheads] whether the round commits (0) or not (1).
 __global__ __launch_bounds__(256) void round_commit_kernel(
     int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
     const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C,
