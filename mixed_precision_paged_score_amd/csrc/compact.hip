@@ -167,12 +167,12 @@ __global__ __launch_bounds__(256) void compact_commit_kernel(
 // Workgroup 0 records in ok[nheads] whether the round commits (0) or not (1).
 __global__ __launch_bounds__(256) void round_commit_kernel(
     int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
-    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C,
-    int64_t P, int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
-    int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
-    int32_t *__restrict__ old_rows, int32_t *__restrict__ old_count) {
-    round_commit_block(blockIdx.x, nheads, rows_l, count_l, new_count, changed, C, P, layer_gid0,
-                       status, ctr, ring, owner, snap, ok, old_rows, old_count);
+    const int32_t *__restrict__ cnt0, const int32_t *__restrict__ new_count,
+    const uint8_t *__restrict__ changed, int C, int64_t P, int layer_gid0, int32_t *status,
+    uint64_t *ctr, int32_t *__restrict__ ring, int32_t *__restrict__ owner,
+    const CompactHdr *snap, int32_t *__restrict__ ok, int32_t *__restrict__ old_rows) {
+    round_commit_block(blockIdx.x, nheads, rows_l, count_l, cnt0, new_count, changed, C, P,
+                       layer_gid0, status, ctr, ring, owner, snap, ok, old_rows, nullptr);
 }
 
 }  // namespace kvc
@@ -184,19 +184,17 @@ namespace kvc {
 // the planning and commit launch of a fused round (round_commit_kernel); the round's start
 // was snapshotted into the compact workspace's header by the per-head scan launch
 int launch_round_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p,
-                        const int32_t *new_count, const uint8_t *changed, int32_t *ok,
-                        int32_t *old_rows_out, int32_t *old_count_out, void *compact_ws,
-                        hipStream_t s) {
+                        const int32_t *cnt0, const int32_t *new_count, const uint8_t *changed,
+                        int32_t *ok, int32_t *old_rows_out, void *compact_ws, hipStream_t s) {
     const CompactWs L(g);
     char *w = static_cast<char *>(compact_ws);
     const int C = g->row_capacity;
     int32_t *rows_l = p->page_table + int64_t(layer) * L.nheads * C;
     int32_t *count_l = p->count + int64_t(layer) * L.nheads * 2;
     hipLaunchKernelGGL(round_commit_kernel, dim3(L.nheads), dim3(256), 0, s, L.nheads, rows_l,
-                       count_l, new_count, changed, C, g->num_pages, layer * L.nheads,
+                       count_l, cnt0, new_count, changed, C, g->num_pages, layer * L.nheads,
                        p->dev_status, p->ring_ctr, p->free_ring, p->owner,
-                       reinterpret_cast<const CompactHdr *>(w + L.hdr), ok, old_rows_out,
-                       old_count_out);
+                       reinterpret_cast<const CompactHdr *>(w + L.hdr), ok, old_rows_out);
     return launch_check("kvc_compaction_round/commit");
 }
 

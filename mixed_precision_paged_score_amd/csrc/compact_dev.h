@@ -183,9 +183,13 @@ __device__ __forceinline__ bool commit_head(
                             old_rows, old_count);
 }
 
-// one workgroup (256 threads) of the fused round's commit launch, for head i
+// one workgroup (256 threads) of the fused round's commit launch, for head i.  Every head's
+// demand comes from cnt0, the old counts as the per-head scan launch recorded them: count_l
+// itself is rewritten by each head's workgroup as it commits, and another workgroup may still
+// be summing the demands then.
 __device__ __forceinline__ void round_commit_block(
     int i, int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
+    const int32_t *__restrict__ cnt0,
     const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C,
     int64_t P, int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
     int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
@@ -195,14 +199,14 @@ __device__ __forceinline__ void round_commit_block(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int32_t entry = snap->entry_status;
     const uint64_t head0 = snap->head0, tail0 = snap->tail0;
-    const HeadDemand mine = head_demand(count_l, new_count, changed, i, C);
+    const HeadDemand mine = head_demand(cnt0, new_count, changed, i, C);
     int ta = 0, tf = 0, pa = 0, pf = 0;
     uint32_t err = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int j = 4 * threadIdx.x + k;
         if (j >= nheads) continue;
-        const HeadDemand d = head_demand(count_l, new_count, changed, j, C);
+        const HeadDemand d = head_demand(cnt0, new_count, changed, j, C);
         err |= uint32_t(d.err);
         ta += d.alloc;
         tf += d.free;

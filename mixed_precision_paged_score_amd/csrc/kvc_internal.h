@@ -34,9 +34,8 @@ int launch_round_score(const kvc_geom *g, const float *acc, const int32_t *cu, i
                        uint8_t *tier, int32_t *tile_cnt, int32_t *tile_cnt2, uint8_t *tile_chg,
                        int32_t *status, hipStream_t s);
 int launch_round_commit(const kvc_geom *g, int32_t layer, const kvc_pool *p,
-                        const int32_t *new_count, const uint8_t *changed, int32_t *ok,
-                        int32_t *old_rows_out, int32_t *old_count_out, void *compact_ws,
-                        hipStream_t s);
+                        const int32_t *cnt0, const int32_t *new_count, const uint8_t *changed,
+                        int32_t *ok, int32_t *old_rows_out, void *compact_ws, hipStream_t s);
 
 // the combine and the score accumulation after a score-accumulating decode (attention.hip):
 // w is the decode workspace laid out by DecodeWs(g, true, max_seqlen), its partials and tile

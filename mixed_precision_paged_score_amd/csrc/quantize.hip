@@ -143,7 +143,8 @@ __global__ __launch_bounds__(256) void round_head_kernel(
     int max_seqlen, int32_t *__restrict__ tile_base, int32_t *__restrict__ tile_base2,
     int32_t *__restrict__ new_count, uint8_t *__restrict__ changed, int32_t *__restrict__ ok,
     const int32_t *status, const uint64_t *ctr, CompactHdr *snap,
-    const int32_t *__restrict__ rows_l, int C, int32_t *__restrict__ old_rows) {
+    const int32_t *__restrict__ rows_l, int C, int32_t *__restrict__ old_rows,
+    const int32_t *__restrict__ count_l, int32_t *__restrict__ cnt0) {
     __shared__ int s_sum[2][128];
     __shared__ int s_tot[2], s_tot2[2];
     __shared__ int s_chg;
@@ -174,6 +175,9 @@ __global__ __launch_bounds__(256) void round_head_kernel(
         new_count[2 * i + 1] = s_tot[1];
         if (retier) changed[i] = uint8_t(s_chg);
         ok[i] = retier ? s_chg : 1;
+        // the head's counts before the round, for the commit launch's demands
+        cnt0[2 * i] = count_l[2 * i];
+        cnt0[2 * i + 1] = count_l[2 * i + 1];
     }
     // re-tier: a changed head's row as it stands before this round's commit, where the rank
     // launch looks up the old page of every kept token (the commit then overwrites the row)
@@ -306,7 +310,8 @@ __global__ __launch_bounds__(256) void quant_select_kernel(
 // or write, so the two need no order between them.
 __global__ __launch_bounds__(256) void round_commit_select_kernel(
     int nheads, int32_t *__restrict__ rows_l, int32_t *__restrict__ count_l,
-    const int32_t *__restrict__ new_count, const uint8_t *__restrict__ changed, int C, int64_t P,
+    const int32_t *__restrict__ cnt0, const int32_t *__restrict__ new_count,
+    const uint8_t *__restrict__ changed, int C, int64_t P,
     int layer_gid0, int32_t *status, uint64_t *ctr, int32_t *__restrict__ ring,
     int32_t *__restrict__ owner, const CompactHdr *snap, int32_t *__restrict__ ok,
     const uint8_t *__restrict__ tier, const uint8_t *__restrict__ prev,
@@ -316,8 +321,8 @@ __global__ __launch_bounds__(256) void round_commit_select_kernel(
     uint2 *__restrict__ srcdesc) {
     const int x = blockIdx.x;
     if (x < nheads) {
-        round_commit_block(x, nheads, rows_l, count_l, new_count, changed, C, P, layer_gid0,
-                           status, ctr, ring, owner, snap, ok, nullptr, nullptr);
+        round_commit_block(x, nheads, rows_l, count_l, cnt0, new_count, changed, C, P,
+                           layer_gid0, status, ctr, ring, owner, snap, ok, nullptr, nullptr);
     } else {
         const int k = x - nheads;
         select_block(k % ntq, k / ntq, tier, prev, cu, Hkv, ntq, max_seqlen, tile_base,
@@ -1003,7 +1008,8 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
     uint2 *srcdesc = retier ? reinterpret_cast<uint2 *>(w + R.quant + L.srcdesc) : nullptr;
     uint8_t *tile_chg = reinterpret_cast<uint8_t *>(w + R.tile_chg);
     int32_t *old_rows = retier ? reinterpret_cast<int32_t *>(w + R.old_rows) : nullptr;
-    int32_t *old_count = retier ? reinterpret_cast<int32_t *>(w + R.old_count) : nullptr;
+    // every head's counts before the round (written by the per-head scans, read by the commits)
+    int32_t *cnt0 = reinterpret_cast<int32_t *>(w + R.old_count);
     const int32_t *rows_l = p->page_table + int64_t(layer) * nheads * C;
     const int32_t *count_l = p->count + int64_t(layer) * nheads * 2;
     hipStream_t s = (hipStream_t)stream;
@@ -1017,14 +1023,14 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
                        tile_chg, cu, Hkv, L.ntq, max_seqlen, tile_base, tile_base2, new_count,
                        retier ? changed : nullptr, ok, p->dev_status, p->ring_ctr,
                        reinterpret_cast<CompactHdr *>(w + R.compact + CL.hdr), rows_l, C,
-                       merge ? old_rows : nullptr);
+                       merge ? old_rows : nullptr, count_l, cnt0);
     rc = launch_check("kvc_compaction_round/heads");
     if (rc) return rc;
     if (merge) {
         // commits and ranks in one launch (the old rows were taken by the per-head scans)
         hipLaunchKernelGGL(round_commit_select_kernel, dim3(nheads + L.ntq * B), dim3(256), 0, s,
                            nheads, p->page_table + int64_t(layer) * nheads * C,
-                           p->count + int64_t(layer) * nheads * 2, new_count,
+                           p->count + int64_t(layer) * nheads * 2, cnt0, new_count,
                            retier ? changed : nullptr, C, g->num_pages, layer * nheads,
                            p->dev_status, p->ring_ctr, p->free_ring, p->owner,
                            reinterpret_cast<const CompactHdr *>(w + R.compact + CL.hdr), ok, tier,
@@ -1033,8 +1039,8 @@ extern "C" int kvc_compaction_round(const kvc_geom *g, int32_t layer, const kvc_
         rc = launch_check("kvc_compaction_round/commit+select");
         if (rc) return rc;
     } else {
-        rc = launch_round_commit(g, layer, p, new_count, retier ? changed : nullptr, ok, old_rows,
-                                 old_count, w + R.compact, s);
+        rc = launch_round_commit(g, layer, p, cnt0, new_count, retier ? changed : nullptr, ok,
+                                 old_rows, w + R.compact, s);
         if (rc) return rc;
         if (!work) return KVC_OK;
         hipLaunchKernelGGL(quant_select_kernel, dim3(L.ntq, B), dim3(256), 0, s, tier, prev_tier,
